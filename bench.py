@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Throughput of DSpark block drafting on one MI355X.
+
+A step is one dspark_draft_block call over the Qwen3-4B-shaped workload:
+B = 32 anchors, gamma = 7 positions, V = 151936, Markov rank r = 256, hidden
+d = 2560, bf16 weights and base logits, temperature 1 (Gumbel-max sampling).
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+Each step uses a new noise offset (offset = step index).
+
+Prints one JSON line: drafted tokens/s over the K timed steps, the roofline
+of the dominant kernel (the V-streaming step kernel, timed with HIP events on
+the library's stream during the timed region) and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "drafted block-tokens/s (V=151936, r=256, γ=7) + % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+WORKLOAD_CFG = 2
+COUNTERS = os.path.join(ROOT, "profiles", "stream_kernel_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "semi_autoregressive_draft_markov_amd", "csrc", f)
+                  for f in ("draft.hip", "device_common.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the stream kernel from committed rocprofv3
+    counter runs (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel
+    calibration), or None if absent or taken on a different kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("bytes_per_launch")
+
+
+def cpu_threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(inp, seconds: float):
+    """The CPU oracle on the same inputs, repeated whole-batch calls until
+    `seconds` of wall time have passed (at least one)."""
+    import oracle
+    threads = cpu_threads()
+    oracle.draft_block(synth_subset(inp, [0]), nthreads=1)  # load the library
+    t0 = time.perf_counter()
+    calls = 0
+    while True:
+        oracle.draft_block(inp, seed=0, offset=calls, nthreads=threads)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    toks = calls * inp.B * inp.gamma
+    return dict(value=toks / el, unit="tokens/s", cores=threads, kind="oracle",
+                sample="%d whole-batch call(s) of the workload (%d blocks x %d positions), "
+                       "%.1f s wall, fp64 C oracle, OpenMP over blocks"
+                       % (calls, inp.B, inp.gamma, el))
+
+
+def synth_subset(inp, idx):
+    import synth
+    return synth.subset(inp, idx)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time of the CPU oracle sample (0 skips it)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the drafting path has no cross-GPU work "
+              "(blocks are independent); run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from semi_autoregressive_draft_markov_amd import binding, ops
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load()
+    dev = torch.device("cuda:0")
+    inp = synth.config_inputs(WORKLOAD_CFG)
+    t = synth.to_torch(inp, dev)
+    B, gamma, V, r, d = inp.B, inp.gamma, inp.V, inp.r, inp.d
+    dims = ops.draft_dims(t["U"], t["h"], t["W1"])
+    ws = ops.workspace(dims, binding.DSPARK_CALL_DRAFT, dev)
+    out = dict(tokens=torch.empty((B, gamma), dtype=torch.int32, device=dev),
+               logp=torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               conf=torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               survival=torch.empty((B, gamma), dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        binding.dspark_draft_block(dims, t["U"], t["h"], t["anchor"], t["W1"], t["W2"],
+                                   t["w_conf"], None, t["temperature"], 0, i, out["tokens"],
+                                   out["logp"], out["conf"], out["survival"], ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    binding.dspark_profile_enable(True)
+    binding.dspark_profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms, launches = binding.dspark_profile_read()
+    binding.dspark_profile_enable(False)
+    assert launches == args.steps * gamma, (launches, args.steps)
+    tokens = out["tokens"].cpu().numpy()
+    assert np.all((tokens >= 0) & (tokens < V)), "bad tokens"
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = B * gamma * args.steps / elapsed
+    avg_kernel_s = kernel_ms * 1e-3 / launches
+    # algorithmic bytes of one stream launch: all of W2 plus the step's slice of U
+    alg_bytes = (r + B) * V * 2
+    achieved = alg_bytes / avg_kernel_s / 1e9
+    traffic = measured_traffic()
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-4b-shaped markov-head block sampling",
+                   "V": V, "r": r, "d": d, "gamma": gamma, "B": B, "temperature": 1.0,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "k_stream_mfma<8,1>",
+                     "kernel_us": round(avg_kernel_s * 1e6, 3),
+                     "algorithmic_bytes_per_launch": alg_bytes},
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

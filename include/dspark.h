@@ -1,0 +1,186 @@
+/*
+ * dspark.h - C ABI of the MI355X (gfx950) DSpark sequential-head library.
+ *
+ * DSpark drafts a block of gamma tokens after an anchor token x_0.  A parallel
+ * backbone gives base logits U_k and hidden states h_k for every position; a
+ * light sequential head then samples left to right (DSpark paper, arXiv
+ * 2607.05147, as transcribed on the dormouse "DSpark - paper verification"
+ * page, section 1):
+ *   Eq 4  p_k = softmax(U_k + B_k)
+ *   Eq 5  Markov head  B_k = W1[x_{k-1}] W2,  W1 [V x r], W2 [r x V]
+ *   Eq 6  RNN head     z_k = [s_{k-1}; W1[x_{k-1}]; h_k], joint projection
+ *                      split into gate/candidate/output, s_0 = 0,
+ *                      B_k = W2^T tanh(W_o z_k)
+ *   Eq 7  confidence   c_k = sigmoid(w^T [h_k; W1[x_{k-1}]])
+ * and the prefix survival is the running product of the c_k (Meridian
+ * "Phase-Conditioned Speculative Decoding", section 3).  Training is teacher
+ * forced (mainlymatmul "DSpark: Wait It's All Autoregressive?", section
+ * "Training DSpark") with the Eq 8-12 objective.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers unless stated, C-contiguous,
+ *    row-major, owned by the caller, and must stay alive until the work
+ *    enqueued on `hip_stream` has finished.  The library allocates nothing
+ *    and keeps no pointer after a call returns.  Weights are never written.
+ *  - `hip_stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous: a status of DSPARK_OK means the work was enqueued.
+ *  - Floating tensors are float32 or bfloat16 as `dims->dtype` says (the
+ *    temperature and all outputs are float32).  Accumulation is float32.
+ *  - Results are deterministic: the same inputs, seed and offset give
+ *    bitwise-identical outputs (no floating-point atomics).
+ *  - No exceptions cross the ABI.  On failure the status says why and
+ *    dspark_last_error() (thread-local) holds a message.  Token ids out of
+ *    [0, V) are found on the device: the block's outputs become token -1 and
+ *    NaN, and that block's flag in the workspace is raised; read the flags
+ *    with dspark_read_device_error().
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSPARK_VERSION 1
+
+typedef enum dspark_status {
+    DSPARK_OK = 0,
+    DSPARK_EINVAL = 1,       /* null required pointer or meaningless size */
+    DSPARK_EUNSUPPORTED = 2, /* a shape / dtype / head combination not built */
+    DSPARK_EWORKSPACE = 3,   /* workspace smaller than dspark_workspace_size() */
+    DSPARK_EDEVICE = 4       /* a HIP runtime call or kernel launch failed */
+} dspark_status;
+
+typedef enum dspark_dtype { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+typedef enum dspark_head { DSPARK_HEAD_MARKOV = 0, DSPARK_HEAD_RNN = 1 } dspark_head;
+
+/* Problem sizes.  V vocabulary, r Markov rank, d hidden width, gamma block
+ * length (also the position-weight decay length, one gamma for both as the
+ * dormouse delta table, row D2, requires), B blocks (anchors).
+ * Limits: V >= 2, 1 <= r <= 1024, d >= 1, 1 <= gamma <= 64, B >= 1.
+ * bf16 data with r a multiple of 32 (r <= 256) and V a multiple of 8 runs
+ * on the matrix cores; other shapes take a plain vector path. */
+typedef struct dspark_dims {
+    int32_t V, r, d, gamma, B;
+    int32_t dtype; /* dspark_dtype of U, h, W1, W2, w_conf, W_rnn, T_logits */
+    int32_t head;  /* dspark_head */
+} dspark_dims;
+
+#define DSPARK_CALL_DRAFT 0
+#define DSPARK_CALL_LOSS 1
+
+/* Bytes of device workspace `which` (DSPARK_CALL_DRAFT or DSPARK_CALL_LOSS)
+ * needs for `dims`; 0 if dims are invalid.  Host function, no device work. */
+size_t dspark_workspace_size(const dspark_dims* dims, int which);
+
+/* Semi-autoregressive block drafting: Eq 4 with the Eq 5 (Markov) or Eq 6
+ * (RNN) bias, Gumbel-max sampling, Eq 7 confidence and prefix survival.
+ *
+ * Inputs (device):
+ *   U        [B, gamma, V]  base logits U_k of the parallel backbone
+ *   h        [B, gamma, d]  hidden states h_k
+ *   anchor   [B] int32      x_0, the anchor token of each block
+ *   W1       [V, r]         Markov embedding table
+ *   W2       [r, V]         logit projection
+ *   w_conf   [d + r]        confidence weights, h part first (Eq 7)
+ *   W_rnn    [3r, 2r + d]   RNN joint projection, rows (gate, candidate,
+ *                           output), columns (s, W1[x], h); NULL for Markov
+ *   temperature [B] float   per-block temperature; T_b > 0 samples
+ *                           x_k = argmax_v (z_v / T_b + g_v) with standard
+ *                           Gumbel noise g; T_b <= 0 is greedy argmax z.
+ *                           Ties go to the lowest token id.
+ *   seed, offset            Gumbel noise for element v of block b at 0-based
+ *                           step k is -ln(-ln u), u = (2 m + 1) / 2^24 with m
+ *                           the top 23 bits of word (v mod 4) of
+ *                           Philox4x32-10(counter = (v/4, k, b, offset mod
+ *                           2^32), key = (seed mod 2^32, seed >> 32)).
+ * Outputs (device, [B, gamma]):
+ *   tokens   int32  sampled x_k (-1 for a block with a bad token id)
+ *   logp     float  log p_k(x_k) under softmax(z / T_b) (softmax(z) when
+ *                   greedy); nullable
+ *   conf     float  c_k (Eq 7) on the previous token actually drafted
+ *   survival float  prod_{i <= k} c_i
+ * workspace: device scratch of at least dspark_workspace_size(dims,
+ *   DSPARK_CALL_DRAFT) bytes, 256-byte aligned; contents need not be
+ *   initialised; afterwards only the per-block error flags at its start
+ *   are defined (see dspark_read_device_error).
+ * The whole block is always drafted (all gamma positions). */
+dspark_status dspark_draft_block(const dspark_dims* dims, const void* U, const void* h,
+                                 const int32_t* anchor, const void* W1, const void* W2,
+                                 const void* w_conf, const void* W_rnn,
+                                 const float* temperature, uint64_t seed, uint64_t offset,
+                                 int32_t* tokens, float* logp, float* conf, float* survival,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Teacher-forced DSpark objective (Eq 8-12) with dL/dlogits and dW2, Markov
+ * head.  dims->B is the number of blocks N; rows i = n * gamma + k.
+ * Position k is fed the previous ground-truth token (anchor[n] at k = 0,
+ * labels[n, k-1] after) and predicts labels[n, k] (the alignment the dormouse
+ * page's off-by-one discussion, section 2, calls correct).
+ *
+ * Inputs (device):
+ *   U        [N, gamma, V]  draft base logits;  z_d = U + W1[prev] W2
+ *   T_logits [N, gamma, V]  frozen target logits z_t (read only)
+ *   h        [N, gamma, d]; anchor [N] int32; labels [N, gamma] int32
+ *   W1, W2, w_conf          as for dspark_draft_block
+ *   alpha    HOST float[3]  (alpha_ce, alpha_tv, alpha_conf); NULL means
+ *                           (0.1, 0.9, 1.0), the Eq 12 defaults
+ *   pos_weight HOST float[gamma]; NULL means w_k = exp(-(k-1)/gamma)
+ * Per row: p_d = softmax(z_d), p_t = softmax(z_t), tv = sum |p_d - p_t|,
+ *   c* = clamp(1 - tv/2, 0, 1) (Eq 8, clamp per delta-table row D7),
+ *   ce = -log p_d(label), c = sigmoid(w^T [h; W1[prev]]),
+ *   bce = -(c* log c + (1 - c*) log(1 - c)).
+ * Outputs (device):
+ *   loss4    float[4]  (L, L_ce, L_tv, L_conf), L_* = (1/N) sum_i w_k term_i,
+ *                      L = alpha . (L_ce, L_tv, L_conf)
+ *   c_star   [N, gamma] float; conf [N, gamma] float (nullable)
+ *   dlogits  [N, gamma, V] dL/dz_d (= dL/dU), float32 or bfloat16 per
+ *            dlogits_dtype; nullable.  c* is held constant (it is a label):
+ *            dZ = (w_k/N)[alpha_ce (p_d - onehot) + alpha_tv p_d (s - sum p_d s)]
+ *            with s = sign(p_d - p_t).
+ *   dW2      [r, V] float32, overwritten with W1[prev]^T dZ; nullable
+ *   dconf_logit [N, gamma] float dL/d(confidence logit) =
+ *            (w_k/N) alpha_conf (c - c*); nullable
+ * workspace: at least dspark_workspace_size(dims, DSPARK_CALL_LOSS) bytes. */
+dspark_status dspark_block_loss(const dspark_dims* dims, const void* U, const void* T_logits,
+                                const void* h, const int32_t* anchor, const int32_t* labels,
+                                const void* W1, const void* W2, const void* w_conf,
+                                const float* alpha, const float* pos_weight,
+                                float* loss4, float* c_star, float* conf,
+                                void* dlogits, int32_t dlogits_dtype, float* dW2,
+                                float* dconf_logit,
+                                void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Synchronises `hip_stream`, then reads the per-block error flags the last
+ * call with these dims left at the start of `workspace`: *code (HOST
+ * pointer) = the number of blocks that met a token id outside [0, V) (0
+ * when all were valid).  Returns DSPARK_EDEVICE if the synchronisation or
+ * the copy fails. */
+dspark_status dspark_read_device_error(const dspark_dims* dims, const void* workspace,
+                                       int32_t* code, void* hip_stream);
+
+/* Kernel timing for measurement.  While enabled on the calling thread, each
+ * dspark_draft_block / dspark_block_loss call also records a pair of HIP
+ * events on `hip_stream` around every launch of its dominant kernel (the
+ * V-streaming step kernel when drafting, the V-streaming passes of the
+ * loss).  dspark_profile_read() waits for those events and returns (HOST
+ * out-pointers) the summed milliseconds and the number of timed launches
+ * since the previous read, then forgets them.  Events are created on first
+ * use and reused; enable = 0 stops recording.  Returns DSPARK_EDEVICE if a
+ * HIP event call fails. */
+dspark_status dspark_profile_enable(int enable);
+dspark_status dspark_profile_read(float* kernel_ms, int32_t* launches);
+
+/* Message describing the last failure on this thread ("" if none). */
+const char* dspark_last_error(void);
+
+/* DSPARK_VERSION of the built library. */
+int dspark_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSPARK_H */

@@ -49,7 +49,7 @@ def _load():
         lib.oracle_uniform.restype = ctypes.c_double
         lib.oracle_gumbel.argtypes = [U64, U64, I, I, I]
         lib.oracle_gumbel.restype = ctypes.c_double
-        lib.oracle_draft_block.argtypes = [I, I, I, I, I, I, I] + [P] * 8 + [U64, U64] + [P] * 7 + [I]
+        lib.oracle_draft_block.argtypes = [I, I, I, I, I, I, I] + [P] * 8 + [U64, U64] + [P] * 8 + [I]
         lib.oracle_draft_block.restype = I
         lib.oracle_block_logprob.argtypes = [I, I, I, I, I, I, I] + [P] * 8 + [P, I]
         lib.oracle_block_logprob.restype = I
@@ -95,14 +95,16 @@ def gumbel(seed: int, offset: int, b: int, k: int, v: int) -> float:
 
 
 def draft_block(inp, seed: int = 0, offset: int = 0, forced_prev=None,
-                temperature=None, nthreads: int = 0) -> dict:
-    """Sample gamma tokens for each of the B blocks of `inp` (a synth.Inputs)."""
+                temperature=None, block_ids=None, nthreads: int = 0) -> dict:
+    """Sample gamma tokens for each of the B blocks of `inp` (a synth.Inputs).
+    `block_ids` gives each block's index for the noise counter (default 0..B-1)."""
     B, g = inp.B, inp.gamma
     dt = inp.dtype
     temp = np.ascontiguousarray(inp.temperature if temperature is None else temperature,
                                 dtype=np.float32)
     anchor = np.ascontiguousarray(inp.anchor, dtype=np.int32)
     fp = None if forced_prev is None else np.ascontiguousarray(forced_prev, dtype=np.int32)
+    ids = None if block_ids is None else np.ascontiguousarray(block_ids, dtype=np.int32)
     out = dict(
         tokens=np.zeros((B, g), np.int32), logp=np.zeros((B, g)), conf=np.zeros((B, g)),
         surv=np.zeros((B, g)), gap=np.zeros((B, g)), second=np.zeros((B, g), np.int32),
@@ -111,7 +113,7 @@ def draft_block(inp, seed: int = 0, offset: int = 0, forced_prev=None,
         inp.V, inp.r, inp.d, g, B, _dtype_code(dt), 1 if inp.head == "rnn" else 0,
         _ptr(_arr(inp.U, dt)), _ptr(_arr(inp.h, dt)), _ptr(anchor),
         _ptr(_arr(inp.W1, dt)), _ptr(_arr(inp.W2, dt)), _ptr(_arr(inp.w_conf, dt)),
-        _ptr(_arr(inp.W_rnn, dt)), _ptr(temp), seed, offset, _ptr(fp),
+        _ptr(_arr(inp.W_rnn, dt)), _ptr(temp), seed, offset, _ptr(fp), _ptr(ids),
         _ptr(out["tokens"]), _ptr(out["logp"]), _ptr(out["conf"]), _ptr(out["surv"]),
         _ptr(out["gap"]), _ptr(out["second"]), nthreads)
     if rc != 0:

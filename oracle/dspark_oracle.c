@@ -174,6 +174,7 @@ static int sample_one_block(int V, int r, int d, int gamma, int b, int dtype, in
                             const void* W1, const void* W2, const void* w_conf,
                             const void* W_rnn, const float* temperature,
                             uint64_t seed, uint64_t offset, const int32_t* forced_prev,
+                            int noise_id,
                             int32_t* tokens, double* logp, double* conf, double* surv,
                             double* gap, int32_t* second,
                             double* z, double* y, double* e, double* s, double* coef,
@@ -203,7 +204,7 @@ static int sample_one_block(int V, int r, int d, int gamma, int b, int dtype, in
         for (int v = 0; v < V; ++v) {
             const double zs = T > 0.0 ? z[v] / T : z[v];
             z[v] = zs;
-            y[v] = T > 0.0 ? zs + oracle_gumbel(seed, offset, b, k, v) : zs;
+            y[v] = T > 0.0 ? zs + oracle_gumbel(seed, offset, noise_id, k, v) : zs;
         }
         int best = 0;
         for (int v = 1; v < V; ++v)
@@ -269,6 +270,7 @@ int oracle_draft_block(int V, int r, int d, int gamma, int B, int dtype, int hea
                        const void* W1, const void* W2, const void* w_conf,
                        const void* W_rnn, const float* temperature,
                        uint64_t seed, uint64_t offset, const int32_t* forced_prev,
+                       const int32_t* block_ids,
                        int32_t* tokens, double* logp, double* conf, double* surv,
                        double* gap, int32_t* second, int nthreads)
 {
@@ -290,7 +292,7 @@ int oracle_draft_block(int V, int r, int d, int gamma, int B, int dtype, int hea
         for (int b = 0; b < B; ++b)
             failed |= sample_one_block(V, r, d, gamma, b, dtype, head, U, h, anchor, W1, W2,
                                        w_conf, W_rnn, temperature, seed, offset, forced_prev,
-                                       tokens, logp, conf, surv, gap, second,
+                                       block_ids ? block_ids[b] : b, tokens, logp, conf, surv, gap, second,
                                        z, y, e, s, coef, zeta, G) != 0;
         free(z); free(y); free(e); free(s); free(coef); free(zeta); free(G);
     }

@@ -50,6 +50,9 @@ double oracle_gumbel(uint64_t seed, uint64_t offset, int b, int k, int v);
  *   forced_prev [B,gamma] nullable: when set, the previous token fed to step
  *   k+1 is forced_prev[b,k] instead of the oracle's own sample (so a parity
  *   test can condition on another implementation's prefix).
+ *   block_ids [B] nullable: the block index b that selects the Gumbel noise
+ *   of each block (default: its position), so a subset of a larger batch
+ *   can be recomputed with its original noise.
  * Outputs (all [B,gamma]): tokens, logp, conf, surv, and for tie analysis gap
  * (largest minus second-largest perturbed logit) and second (its index).
  * Returns 0, or -1 on an out-of-range token id / bad argument. */
@@ -58,6 +61,7 @@ int oracle_draft_block(int V, int r, int d, int gamma, int B, int dtype, int hea
                        const void* W1, const void* W2, const void* w_conf,
                        const void* W_rnn, const float* temperature,
                        uint64_t seed, uint64_t offset, const int32_t* forced_prev,
+                       const int32_t* block_ids,
                        int32_t* tokens, double* logp, double* conf, double* surv,
                        double* gap, int32_t* second, int nthreads);
 

@@ -1,0 +1,201 @@
+// C ABI of the DSpark sequential-head library: argument checks, workspace
+// sizing and dispatch.  Declarations and the contract live in
+// include/dspark.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dspark_status fail(dspark_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dspark_status fail(dspark_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+dspark_status ok() {
+    g_last_error.clear();
+    return DSPARK_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks shared by both calls; returns DSPARK_OK or a failure with a message.
+dspark_status check_dims(const dspark_dims* d) {
+    if (!d) return fail(DSPARK_EINVAL, "dims is NULL");
+    if (d->V < 2) return fail(DSPARK_EINVAL, "V = %d, need V >= 2", d->V);
+    if (d->r < 1 || d->r > 1024) return fail(DSPARK_EINVAL, "r = %d, need 1 <= r <= 1024", d->r);
+    if (d->d < 1) return fail(DSPARK_EINVAL, "d = %d, need d >= 1", d->d);
+    if (d->gamma < 1 || d->gamma > 64)
+        return fail(DSPARK_EINVAL, "gamma = %d, need 1 <= gamma <= 64", d->gamma);
+    if (d->B < 1) return fail(DSPARK_EINVAL, "B = %d, need B >= 1", d->B);
+    if (d->dtype != DSPARK_F32 && d->dtype != DSPARK_BF16)
+        return fail(DSPARK_EINVAL, "dtype = %d is neither DSPARK_F32 nor DSPARK_BF16", d->dtype);
+    if (d->head != DSPARK_HEAD_MARKOV && d->head != DSPARK_HEAD_RNN)
+        return fail(DSPARK_EINVAL, "head = %d is neither MARKOV nor RNN", d->head);
+    const int64_t rows = static_cast<int64_t>(d->B) * d->gamma;
+    if (rows * d->V > (int64_t(1) << 40) || rows * d->d > (int64_t(1) << 40))
+        return fail(DSPARK_EUNSUPPORTED, "tensor sizes beyond 2^40 elements are not supported");
+    return DSPARK_OK;
+}
+
+}  // namespace
+
+namespace dspark {
+
+namespace {
+struct Profile {
+    bool on = false;
+    std::vector<hipEvent_t> pool;  // even index = start, odd = end
+    size_t used = 0;               // events recorded since the last read
+};
+thread_local Profile g_prof;
+
+hipError_t record(hipStream_t s) {
+    if (g_prof.used == g_prof.pool.size()) {
+        hipEvent_t e;
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) return err;
+        g_prof.pool.push_back(e);
+    }
+    return hipEventRecord(g_prof.pool[g_prof.used++], s);
+}
+}  // namespace
+
+bool profiling_enabled() { return g_prof.on; }
+hipError_t profile_begin(hipStream_t s) { return g_prof.on ? record(s) : hipSuccess; }
+hipError_t profile_end(hipStream_t s) { return g_prof.on ? record(s) : hipSuccess; }
+
+LossLayout loss_layout(const dspark_dims& d) {
+    LossLayout L{};
+    L.bad = 0;
+    L.total = align_up(sizeof(int32_t) * d.B, 256);
+    return L;
+}
+
+}  // namespace dspark
+
+extern "C" {
+
+size_t dspark_workspace_size(const dspark_dims* dims, int which) {
+    if (check_dims(dims) != DSPARK_OK) return 0;
+    if (which == DSPARK_CALL_DRAFT) return dspark::draft_layout(*dims).total;
+    if (which == DSPARK_CALL_LOSS) return dspark::loss_layout(*dims).total;
+    return 0;
+}
+
+dspark_status dspark_draft_block(const dspark_dims* dims, const void* U, const void* h,
+                                 const int32_t* anchor, const void* W1, const void* W2,
+                                 const void* w_conf, const void* W_rnn,
+                                 const float* temperature, uint64_t seed, uint64_t offset,
+                                 int32_t* tokens, float* logp, float* conf, float* survival,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+    dspark_status s = check_dims(dims);
+    if (s != DSPARK_OK) return s;
+    const char* missing = !U ? "U" : !h ? "h" : !anchor ? "anchor" : !W1 ? "W1" : !W2 ? "W2"
+                        : !w_conf ? "w_conf" : !temperature ? "temperature" : !tokens ? "tokens"
+                        : !conf ? "conf" : !survival ? "survival" : !workspace ? "workspace"
+                        : (dims->head == DSPARK_HEAD_RNN && !W_rnn) ? "W_rnn" : nullptr;
+    if (missing) return fail(DSPARK_EINVAL, "required pointer %s is NULL", missing);
+    if (!aligned(workspace, 256)) return fail(DSPARK_EINVAL, "workspace is not 256-byte aligned");
+    const size_t need = dspark::draft_layout(*dims).total;
+    if (workspace_bytes < need)
+        return fail(DSPARK_EWORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, need);
+    dspark_dims d = *dims;
+    const size_t esz = d.dtype == DSPARK_BF16 ? 2 : 4;
+    if (!aligned(U, esz) || !aligned(h, esz) || !aligned(W1, esz) || !aligned(W2, esz) ||
+        !aligned(w_conf, esz) || (W_rnn && !aligned(W_rnn, esz)))
+        return fail(DSPARK_EINVAL, "a tensor is not aligned to its element size");
+    if (dspark::mfma_path_ok(d) && (!aligned(U, 16) || !aligned(W2, 16)))
+        return fail(DSPARK_EUNSUPPORTED, "bf16 U and W2 must be 16-byte aligned");
+
+    dspark::DraftArgs a{};
+    a.dims = d;
+    a.U = U; a.h = h; a.W1 = W1; a.W2 = W2; a.w_conf = w_conf; a.W_rnn = W_rnn;
+    a.anchor = anchor; a.temperature = temperature; a.seed = seed; a.offset = offset;
+    a.tokens = tokens; a.logp = logp; a.conf = conf; a.survival = survival;
+    a.ws = static_cast<char*>(workspace);
+    a.stream = static_cast<hipStream_t>(hip_stream);
+    const hipError_t e = dspark::launch_draft(a);
+    if (e != hipSuccess) return fail(DSPARK_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+dspark_status dspark_block_loss(const dspark_dims* dims, const void* U, const void* T_logits,
+                                const void* h, const int32_t* anchor, const int32_t* labels,
+                                const void* W1, const void* W2, const void* w_conf,
+                                const float* alpha, const float* pos_weight,
+                                float* loss4, float* c_star, float* conf,
+                                void* dlogits, int32_t dlogits_dtype, float* dW2,
+                                float* dconf_logit,
+                                void* workspace, size_t workspace_bytes, void* hip_stream) {
+    dspark_status s = check_dims(dims);
+    if (s != DSPARK_OK) return s;
+    return fail(DSPARK_EUNSUPPORTED, "dspark_block_loss is not built yet");
+}
+
+dspark_status dspark_read_device_error(const dspark_dims* dims, const void* workspace,
+                                       int32_t* code, void* hip_stream) {
+    dspark_status s = check_dims(dims);
+    if (s != DSPARK_OK) return s;
+    if (!workspace || !code) return fail(DSPARK_EINVAL, "workspace and code must not be NULL");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(DSPARK_EDEVICE, "stream synchronisation failed: %s", hipGetErrorString(e));
+    const int n = dims->B;
+    std::string flags(sizeof(int32_t) * n, '\0');
+    e = hipMemcpy(&flags[0], workspace, sizeof(int32_t) * n, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(DSPARK_EDEVICE, "reading the error flags failed: %s", hipGetErrorString(e));
+    int32_t count = 0;
+    for (int i = 0; i < n; ++i) {
+        int32_t f;
+        memcpy(&f, &flags[sizeof(int32_t) * i], sizeof f);
+        count += f != 0;
+    }
+    *code = count;
+    return ok();
+}
+
+dspark_status dspark_profile_enable(int enable) {
+    dspark::g_prof.on = enable != 0;
+    return ok();
+}
+
+dspark_status dspark_profile_read(float* kernel_ms, int32_t* launches) {
+    if (!kernel_ms || !launches) return fail(DSPARK_EINVAL, "kernel_ms and launches must not be NULL");
+    auto& P = dspark::g_prof;
+    float total = 0.0f;
+    const size_t pairs = P.used / 2;
+    for (size_t i = 0; i < pairs; ++i) {
+        hipError_t e = hipEventSynchronize(P.pool[2 * i + 1]);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, P.pool[2 * i], P.pool[2 * i + 1]);
+        if (e != hipSuccess) {
+            P.used = 0;
+            return fail(DSPARK_EDEVICE, "profiling event failed: %s", hipGetErrorString(e));
+        }
+        total += ms;
+    }
+    P.used = 0;
+    *kernel_ms = total;
+    *launches = static_cast<int32_t>(pairs);
+    return ok();
+}
+
+const char* dspark_last_error(void) { return g_last_error.c_str(); }
+
+int dspark_version(void) { return DSPARK_VERSION; }
+
+}  // extern "C"

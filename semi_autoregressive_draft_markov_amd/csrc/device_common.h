@@ -1,0 +1,127 @@
+// Device helpers shared by the gfx950 kernels of the DSpark sequential head.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <typename T> __device__ __forceinline__ float load_f(const T* p, int64_t i);
+template <> __device__ __forceinline__ float load_f<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, int64_t i) {
+    return bf16_to_f32(p[i]);
+}
+
+// ---------------------------------------------------------------- Philox
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11): ten rounds, each two 32x32 -> 64-bit products,
+// with the key bumped by the Weyl constants between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 x, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint32_t a = x[0], b = x[1], c = x[2], d = x[3];
+        const uint32_t lo_a = 0xD2511F53u * a, hi_a = __umulhi(0xD2511F53u, a);
+        const uint32_t lo_c = 0xCD9E8D57u * c, hi_c = __umulhi(0xCD9E8D57u, c);
+        x[0] = hi_c ^ b ^ k0;
+        x[1] = lo_c;
+        x[2] = hi_a ^ d ^ k1;
+        x[3] = lo_a;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return x;
+}
+
+// Standard Gumbel draw from one 32-bit word: u = (2 m + 1) 2^-24 with m the
+// top 23 bits (exact in float, never 0 or 1), then g = -ln(-ln u).  For
+// u >= 1/2, -ln u is taken as -log1p(u - 1) (u - 1 is exact), which keeps
+// its relative accuracy when u is close to 1.
+__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
+    const float u = static_cast<float>(2u * (w >> 9) + 1u) * 5.9604644775390625e-8f;
+    const float e = (u >= 0.5f) ? -log1pf(u - 1.0f) : -logf(u);
+    return -logf(e);
+}
+
+// ------------------------------------------------------- ordered argmax key
+// 64-bit key whose unsigned maximum is the largest value, lowest index on a
+// tie: order-preserving bits of the float (with -0 folded onto +0) in the
+// high word, the complemented index in the low word.
+__device__ __forceinline__ uint64_t argmax_key(float y, uint32_t idx) {
+    uint32_t u = __float_as_uint(y + 0.0f);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (static_cast<uint64_t>(u) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t key) {
+    return 0xFFFFFFFFu - static_cast<uint32_t>(key);
+}
+constexpr uint64_t kKeyNone = 0;  // below every real key
+
+// Softmax statistics of a slice: running max m, sum of exp(z - m), plus the
+// argmax key of the (perturbed) logits and the tempered logit at that index.
+struct Stats {
+    float m;
+    float s;
+    uint64_t key;
+    float zx;
+};
+
+__device__ __forceinline__ Stats stats_empty() { return Stats{-INFINITY, 0.0f, kKeyNone, 0.0f}; }
+
+__device__ __forceinline__ Stats stats_merge(const Stats& a, const Stats& b) {
+    Stats r;
+    r.m = fmaxf(a.m, b.m);
+    const float sa = (a.s > 0.0f) ? a.s * __expf(a.m - r.m) : 0.0f;
+    const float sb = (b.s > 0.0f) ? b.s * __expf(b.m - r.m) : 0.0f;
+    r.s = sa + sb;
+    const bool take_b = b.key > a.key;
+    r.key = take_b ? b.key : a.key;
+    r.zx = take_b ? b.zx : a.zx;
+    return r;
+}
+
+__device__ __forceinline__ Stats shfl_xor_stats(const Stats& a, int mask) {
+    Stats r;
+    r.m = __shfl_xor(a.m, mask);
+    r.s = __shfl_xor(a.s, mask);
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(a.key), mask);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(a.key >> 32), mask);
+    r.key = (static_cast<uint64_t>(hi) << 32) | lo;
+    r.zx = __shfl_xor(a.zx, mask);
+    return r;
+}
+
+__device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+// Block-wide float sum over blockDim.x threads (multiple of 64), fixed order.
+__device__ __forceinline__ float block_sum(float v, float* lds /* >= 16 */) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int nw = blockDim.x / kWave;
+    __syncthreads();
+    if (lane == 0) lds[wave] = v;
+    __syncthreads();
+    float t = 0.0f;
+    for (int i = 0; i < nw; ++i) t += lds[i];
+    __syncthreads();
+    return t;
+}
+
+}  // namespace dspark

@@ -1,0 +1,557 @@
+// DSpark block drafting on gfx950: Eq 4 sampling with the Eq 5 (Markov) or
+// Eq 6 (RNN) transition bias, Eq 7 confidence and the prefix survival
+// product (DSpark paper as transcribed on the dormouse "DSpark - paper
+// verification" page, section 1; survival per the Meridian note, section 3).
+//
+// One call runs the whole left-to-right loop on the device:
+//   init                      e = W1[x_0], c_1, S_1
+//   for k = 0 .. gamma-1:
+//     [RNN] gates + update    G = W_rnn [s; e; h_k]; s, o = tanh(G_o)
+//     stream                  z = U_k + coef W2 over V tiles -> per-tile
+//                             softmax / Gumbel-argmax partial statistics
+//     combine                 x_k, log p_k; e = W1[x_k]; c_{k+1}, S_{k+1}
+// The only step-to-step dependency is the reduction over V inside combine.
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace dspark {
+
+constexpr int kTileV = 64;                       // columns per wave (MFMA path)
+constexpr int kWavesPerWG = 4;
+constexpr int kColsPerWG = kTileV * kWavesPerWG;  // 256 columns per workgroup
+constexpr int kGenericCols = 4 * 256;             // generic path: 4 columns per thread
+
+bool mfma_path_ok(const dspark_dims& d) {
+    return d.dtype == DSPARK_BF16 && d.r % 32 == 0 && d.r <= 256 && d.V % 8 == 0;
+}
+
+int draft_partials(const dspark_dims& d) {
+    return mfma_path_ok(d) ? (d.V + kColsPerWG - 1) / kColsPerWG
+                           : (d.V + kGenericCols - 1) / kGenericCols;
+}
+
+DraftLayout draft_layout(const dspark_dims& d) {
+    DraftLayout L{};
+    L.Bpad = (d.B + 15) / 16 * 16;
+    L.P = draft_partials(d);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const size_t rows = static_cast<size_t>(L.Bpad);
+    L.dead = take(sizeof(int32_t) * d.B);
+    L.emb = take(sizeof(float) * rows * d.r);
+    L.coef = take(sizeof(float) * rows * d.r);
+    L.ebf = take(sizeof(uint16_t) * 2 * rows * d.r);
+    L.state = take(sizeof(float) * rows * d.r);
+    L.gates = take(sizeof(float) * rows * 3 * d.r);
+    const size_t np = static_cast<size_t>(d.B) * L.P;
+    L.pm = take(sizeof(float) * np);
+    L.ps = take(sizeof(float) * np);
+    L.pkey = take(sizeof(uint64_t) * np);
+    L.pzx = take(sizeof(float) * np);
+    L.total = off;
+    return L;
+}
+
+// ------------------------------------------------------------------ init
+
+// Block b: e = W1[anchor_b] (Eq 5 at k = 1), c_1 and S_1 (Eq 7).  Blocks
+// b in [B, Bpad) only clear the padding rows of the MFMA operand.
+template <typename T>
+__global__ __launch_bounds__(256) void k_draft_init(
+    const int32_t* __restrict__ anchor, const T* __restrict__ W1, const T* __restrict__ w_conf,
+    const T* __restrict__ h, int V, int r, int d, int gamma, int B, int Bpad, int head,
+    int32_t* __restrict__ dead, float* __restrict__ emb, float* __restrict__ coef,
+    uint16_t* __restrict__ ebf, float* __restrict__ state,
+    float* __restrict__ conf, float* __restrict__ survival) {
+    __shared__ float red[16];
+    const int b = blockIdx.x;
+    const size_t row = static_cast<size_t>(b) * r;
+    if (b >= B) {
+        for (int j = threadIdx.x; j < r; j += blockDim.x) {
+            emb[row + j] = 0.0f;
+            coef[row + j] = 0.0f;
+            state[row + j] = 0.0f;
+            ebf[row + j] = 0;
+            ebf[static_cast<size_t>(Bpad) * r + row + j] = 0;
+        }
+        return;
+    }
+    const int prev = anchor[b];
+    const bool bad = prev < 0 || prev >= V;
+    if (threadIdx.x == 0) dead[b] = bad ? 1 : 0;
+    float part = 0.0f;
+    for (int j = threadIdx.x; j < r; j += blockDim.x) {
+        const float ej = bad ? 0.0f : load_f(W1, static_cast<int64_t>(prev) * r + j);
+        emb[row + j] = ej;
+        state[row + j] = 0.0f;  // Eq 6: s_0 = 0
+        if (head == DSPARK_HEAD_MARKOV) {
+            coef[row + j] = ej;
+            ebf[row + j] = static_cast<uint16_t>(f32_to_bf16(ej));  // exact: W1 is bf16 here
+            ebf[static_cast<size_t>(Bpad) * r + row + j] = 0;
+        }
+        part += load_f(w_conf, d + j) * ej;
+    }
+    const int64_t hrow = static_cast<int64_t>(b) * gamma * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) part += load_f(w_conf, i) * load_f(h, hrow + i);
+    const float a = block_sum(part, red);
+    if (threadIdx.x == 0) {
+        const float c = bad ? NAN : sigmoidf_(a);
+        conf[static_cast<size_t>(b) * gamma] = c;
+        survival[static_cast<size_t>(b) * gamma] = c;
+    }
+}
+
+// ------------------------------------------------------------ RNN step
+
+// G[b, q] = sum_c W_rnn[q, c] zeta_b[c] with zeta_b = [s_b; e_b; h_{b,k}]
+// (Eq 6).  A 16 (rows q) x 16 (blocks b) output tile per workgroup, K staged
+// through LDS in slices of 64.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rnn_gates(
+    const T* __restrict__ W_rnn, const float* __restrict__ state, const float* __restrict__ emb,
+    const T* __restrict__ h, int r, int d, int gamma, int k, int B, float* __restrict__ gates) {
+    __shared__ float Ws[16][65];
+    __shared__ float Zs[16][65];
+    const int tq = threadIdx.x & 15, tb = threadIdx.x >> 4;
+    const int q0 = blockIdx.x * 16, b0 = blockIdx.y * 16;
+    const int width = 2 * r + d, Q = 3 * r;
+    float acc = 0.0f;
+    for (int c0 = 0; c0 < width; c0 += 64) {
+        for (int t = threadIdx.x; t < 16 * 64; t += blockDim.x) {
+            const int row = t >> 6, col = t & 63;
+            const int q = q0 + row, c = c0 + col;
+            Ws[row][col] = (q < Q && c < width) ? load_f(W_rnn, static_cast<int64_t>(q) * width + c) : 0.0f;
+            const int b = b0 + row;
+            float zv = 0.0f;
+            if (b < B && c < width) {
+                if (c < r)
+                    zv = state[static_cast<size_t>(b) * r + c];
+                else if (c < 2 * r)
+                    zv = emb[static_cast<size_t>(b) * r + (c - r)];
+                else
+                    zv = load_f(h, (static_cast<int64_t>(b) * gamma + k) * d + (c - 2 * r));
+            }
+            Zs[row][col] = zv;
+        }
+        __syncthreads();
+#pragma unroll 16
+        for (int cc = 0; cc < 64; ++cc) acc = fmaf(Ws[tq][cc], Zs[tb][cc], acc);
+        __syncthreads();
+    }
+    if (q0 + tq < Q && b0 + tb < B) gates[static_cast<size_t>(b0 + tb) * Q + q0 + tq] = acc;
+}
+
+// Gated state update of Eq 6 and the bias coefficients o = tanh(W_o z).
+// o is not exact in bf16, so the MFMA operand carries it as hi + lo planes.
+__global__ __launch_bounds__(256) void k_rnn_update(const float* __restrict__ gates,
+                                                    float* __restrict__ state,
+                                                    float* __restrict__ coef,
+                                                    uint16_t* __restrict__ ebf, int r, int Bpad) {
+    const int b = blockIdx.x;
+    const float* G = gates + static_cast<size_t>(b) * 3 * r;
+    const size_t row = static_cast<size_t>(b) * r;
+    for (int j = threadIdx.x; j < r; j += blockDim.x) {
+        const float gate = 1.0f / (1.0f + expf(-G[j]));
+        const float cand = tanhf(G[r + j]);
+        const float o = tanhf(G[2 * r + j]);
+        state[row + j] = gate * state[row + j] + (1.0f - gate) * cand;
+        coef[row + j] = o;
+        const uint32_t hi = f32_to_bf16(o);
+        const uint32_t lo = f32_to_bf16(o - __uint_as_float(hi << 16));
+        ebf[row + j] = static_cast<uint16_t>(hi);
+        ebf[static_cast<size_t>(Bpad) * r + row + j] = static_cast<uint16_t>(lo);
+    }
+}
+
+// -------------------------------------------------------- stream (MFMA)
+
+// Per-lane statistics of the 16 consecutive columns v0 .. v0+15 of block b.
+// z[j] holds U + bias for column v0 + j.
+__device__ __forceinline__ Stats lane_stats16(const float (&z)[16], int v0, int V, int b, int k,
+                                              bool sampling, float invT, uint32_t key0,
+                                              uint32_t key1, uint32_t ctr3) {
+    Stats st = stats_empty();
+    float zs[16];
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        zs[j] = z[j] * invT;
+        if (v0 + (j & ~3) < V) m = fmaxf(m, zs[j]);
+    }
+    float s = 0.0f;
+    uint64_t best = kKeyNone;
+    float bz = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int vq = v0 + 4 * q;
+        if (vq < V) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (sampling) {
+                const u32x4 ctr = {static_cast<uint32_t>(vq) >> 2, static_cast<uint32_t>(k),
+                                   static_cast<uint32_t>(b), ctr3};
+                w = philox4x32_10(ctr, key0, key1);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float v = zs[4 * q + c];
+                s += __expf(v - m);
+                const float y = sampling ? v + gumbel_from_word(w[c]) : v;
+                const uint64_t key = argmax_key(y, static_cast<uint32_t>(vq + c));
+                if (key > best) {
+                    best = key;
+                    bz = v;
+                }
+            }
+        }
+    }
+    if (best != kKeyNone) {
+        st.m = m;
+        st.s = s;
+        st.key = best;
+        st.zx = bz;
+    }
+    return st;
+}
+
+// One workgroup = 4 waves = 256 columns.  Each wave owns a 64-column tile of
+// W2 for the whole step and keeps it in registers as MFMA A-operand
+// fragments: lane (g = lane / 16, n = lane % 16) loads 8 rows j = 32 kc + 8g
+// + e at the 4 columns vt + 4n .. vt + 4n + 3 (coalesced 8-byte loads) and
+// transposes them with v_perm into 4 fragments, one per column offset c.
+// MFMA c then computes bias[b][vt + 4i + c] for i = 0..15 (A row i) and 16
+// blocks b (B column), so lane (g, n) ends up holding the 16 consecutive
+// columns vt + 16g .. vt + 16g + 15 of block row b = 16 nb + n: all of a
+// lane's softmax and argmax work is for one block row.
+template <int KC, int NPLANES>
+__global__ __launch_bounds__(256) void k_stream_mfma(
+    const uint16_t* __restrict__ U, const uint16_t* __restrict__ W2,
+    const uint16_t* __restrict__ ebf, const float* __restrict__ temperature, int V, int B,
+    int Bpad, int gamma, int k, uint32_t key0, uint32_t key1, uint32_t ctr3,
+    float* __restrict__ pm, float* __restrict__ ps, uint64_t* __restrict__ pkey,
+    float* __restrict__ pzx) {
+    constexpr int r = KC * 32;
+    __shared__ Stats red[kWavesPerWG][16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int vt = (blockIdx.x * kWavesPerWG + wave) * kTileV;
+    const int P = gridDim.x;
+
+    uint32_t frag[KC][4][4];
+    {
+        const int va = vt + 4 * n;
+        const bool ok = va < V;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            uint2 raw[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = kc * 32 + 8 * g + e;
+                raw[e] = ok ? *reinterpret_cast<const uint2*>(W2 + static_cast<size_t>(j) * V + va)
+                            : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                frag[kc][0][p] = __builtin_amdgcn_perm(raw[2 * p + 1].x, raw[2 * p].x, 0x05040100u);
+                frag[kc][1][p] = __builtin_amdgcn_perm(raw[2 * p + 1].x, raw[2 * p].x, 0x07060302u);
+                frag[kc][2][p] = __builtin_amdgcn_perm(raw[2 * p + 1].y, raw[2 * p].y, 0x05040100u);
+                frag[kc][3][p] = __builtin_amdgcn_perm(raw[2 * p + 1].y, raw[2 * p].y, 0x07060302u);
+            }
+        }
+    }
+
+    const int v0 = vt + 16 * g;
+    for (int nb = 0; nb < Bpad / 16; ++nb) {
+        const int b = nb * 16 + n;
+        f32x4 acc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int pl = 0; pl < NPLANES; ++pl) {
+            const uint16_t* erow = ebf + (static_cast<size_t>(pl) * Bpad + b) * r + 8 * g;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const u32x4 ev = *reinterpret_cast<const u32x4*>(erow + kc * 32);
+                const bf16x8 bop = __builtin_bit_cast(bf16x8, ev);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 av = {frag[kc][c][0], frag[kc][c][1], frag[kc][c][2], frag[kc][c][3]};
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bop,
+                                                                     acc[c], 0, 0, 0);
+                }
+            }
+        }
+
+        Stats st = stats_empty();
+        if (b < B && v0 < V) {
+            const float temp = temperature[b];
+            const bool sampling = temp > 0.0f;
+            const float invT = sampling ? 1.0f / temp : 1.0f;
+            const uint16_t* urow = U + (static_cast<size_t>(b) * gamma + k) * V + v0;
+            const u32x4 u0 = *reinterpret_cast<const u32x4*>(urow);
+            u32x4 u1 = {0u, 0u, 0u, 0u};
+            if (v0 + 8 < V) u1 = *reinterpret_cast<const u32x4*>(urow + 8);
+            const uint32_t uw[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+            float z[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int j = 4 * q + c;
+                    const float u = (j & 1) ? hi_bf16(uw[j >> 1]) : lo_bf16(uw[j >> 1]);
+                    z[j] = acc[c][q] + u;
+                }
+            st = lane_stats16(z, v0, V, b, k, sampling, invT, key0, key1, ctr3);
+        }
+        st = stats_merge(st, shfl_xor_stats(st, 16));
+        st = stats_merge(st, shfl_xor_stats(st, 32));
+        if (g == 0) red[wave][n] = st;
+        __syncthreads();
+        if (wave == 0 && g == 0 && b < B) {
+            Stats t = red[0][n];
+#pragma unroll
+            for (int w = 1; w < kWavesPerWG; ++w) t = stats_merge(t, red[w][n]);
+            const size_t o = static_cast<size_t>(b) * P + blockIdx.x;
+            pm[o] = t.m;
+            ps[o] = t.s;
+            pkey[o] = t.key;
+            pzx[o] = t.zx;
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------ stream (generic)
+
+// Any dtype / rank: each thread owns 4 consecutive columns and walks the
+// blocks; the bias is a plain float dot product with coef.
+template <typename T>
+__global__ __launch_bounds__(256) void k_stream_generic(
+    const T* __restrict__ U, const T* __restrict__ W2, const float* __restrict__ coef,
+    const float* __restrict__ temperature, int V, int r, int B, int gamma, int k, uint32_t key0,
+    uint32_t key1, uint32_t ctr3, float* __restrict__ pm, float* __restrict__ ps,
+    uint64_t* __restrict__ pkey, float* __restrict__ pzx) {
+    __shared__ Stats red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int v0 = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    const int P = gridDim.x;
+    for (int b = 0; b < B; ++b) {
+        Stats st = stats_empty();
+        if (v0 < V) {
+            const float temp = temperature[b];
+            const bool sampling = temp > 0.0f;
+            const float invT = sampling ? 1.0f / temp : 1.0f;
+            const int64_t urow = (static_cast<int64_t>(b) * gamma + k) * V;
+            float z[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) z[c] = (v0 + c < V) ? load_f(U, urow + v0 + c) : 0.0f;
+            const float* cb = coef + static_cast<size_t>(b) * r;
+            for (int j = 0; j < r; ++j) {
+                const float cj = cb[j];
+                const int64_t wrow = static_cast<int64_t>(j) * V + v0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (v0 + c < V) z[c] = fmaf(cj, load_f(W2, wrow + c), z[c]);
+            }
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (sampling) {
+                const u32x4 ctr = {static_cast<uint32_t>(v0) >> 2, static_cast<uint32_t>(k),
+                                   static_cast<uint32_t>(b), ctr3};
+                w = philox4x32_10(ctr, key0, key1);
+            }
+            float m = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (v0 + c < V) m = fmaxf(m, z[c] * invT);
+            float s = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (v0 + c < V) {
+                    const float zs = z[c] * invT;
+                    s += __expf(zs - m);
+                    const float y = sampling ? zs + gumbel_from_word(w[c]) : zs;
+                    const uint64_t key = argmax_key(y, static_cast<uint32_t>(v0 + c));
+                    if (key > st.key) {
+                        st.key = key;
+                        st.zx = zs;
+                    }
+                }
+            }
+            st.m = m;
+            st.s = s;
+        }
+        for (int o = 32; o > 0; o >>= 1) st = stats_merge(st, shfl_xor_stats(st, o));
+        if (lane == 0) red[wave] = st;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            Stats t = red[0];
+            for (int w2 = 1; w2 < static_cast<int>(blockDim.x / kWave); ++w2) t = stats_merge(t, red[w2]);
+            const size_t o = static_cast<size_t>(b) * P + blockIdx.x;
+            pm[o] = t.m;
+            ps[o] = t.s;
+            pkey[o] = t.key;
+            pzx[o] = t.zx;
+        }
+        __syncthreads();
+    }
+}
+
+// --------------------------------------------------------------- combine
+
+// Block b: merge the P partial statistics of step k in a fixed order, emit
+// x_k and log p_k, then prepare step k+1: e = W1[x_k], c_{k+1}, S_{k+1}.
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine(
+    const float* __restrict__ pm, const float* __restrict__ ps, const uint64_t* __restrict__ pkey,
+    const float* __restrict__ pzx, int P, const T* __restrict__ W1, const T* __restrict__ w_conf,
+    const T* __restrict__ h, int V, int r, int d, int gamma, int k, int head, int write_bf16,
+    int32_t* __restrict__ dead, float* __restrict__ emb, float* __restrict__ coef,
+    uint16_t* __restrict__ ebf, int32_t* __restrict__ tokens, float* __restrict__ logp,
+    float* __restrict__ conf, float* __restrict__ survival) {
+    __shared__ Stats red[4];
+    __shared__ int sx;
+    __shared__ float rs[16];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    Stats st = stats_empty();
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+        const size_t o = static_cast<size_t>(b) * P + p;
+        st = stats_merge(st, Stats{pm[o], ps[o], pkey[o], pzx[o]});
+    }
+    for (int o = 32; o > 0; o >>= 1) st = stats_merge(st, shfl_xor_stats(st, o));
+    if (lane == 0) red[wave] = st;
+    __syncthreads();
+    const size_t out = static_cast<size_t>(b) * gamma + k;
+    if (threadIdx.x == 0) {
+        Stats t = red[0];
+        for (int w = 1; w < static_cast<int>(blockDim.x / kWave); ++w) t = stats_merge(t, red[w]);
+        int x = static_cast<int>(key_index(t.key));
+        const bool bad = dead[b] != 0 || t.key == kKeyNone || x < 0 || x >= V;
+        if (bad) {
+            dead[b] = 1;
+            x = -1;
+        }
+        tokens[out] = x;
+        if (logp) logp[out] = bad ? NAN : t.zx - (t.m + logf(t.s));
+        sx = x;
+    }
+    __syncthreads();
+    if (k + 1 >= gamma) return;
+    const int x = sx;
+    const size_t row = static_cast<size_t>(b) * r;
+    float part = 0.0f;
+    for (int j = threadIdx.x; j < r; j += blockDim.x) {
+        const float ej = x >= 0 ? load_f(W1, static_cast<int64_t>(x) * r + j) : 0.0f;
+        emb[row + j] = ej;
+        if (head == DSPARK_HEAD_MARKOV) {
+            coef[row + j] = ej;
+            if (write_bf16) ebf[row + j] = static_cast<uint16_t>(f32_to_bf16(ej));
+        }
+        part += load_f(w_conf, d + j) * ej;
+    }
+    const int64_t hrow = (static_cast<int64_t>(b) * gamma + k + 1) * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) part += load_f(w_conf, i) * load_f(h, hrow + i);
+    const float a = block_sum(part, rs);
+    if (threadIdx.x == 0) {
+        const float c = x >= 0 ? sigmoidf_(a) : NAN;
+        conf[out + 1] = c;
+        survival[out + 1] = survival[out] * c;
+    }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int KC, int NPL>
+static void launch_mfma(const DraftArgs& a, const DraftLayout& L, int k, char* ws) {
+    const dspark_dims& D = a.dims;
+    hipLaunchKernelGGL((k_stream_mfma<KC, NPL>), dim3(L.P), dim3(256), 0, a.stream,
+                       static_cast<const uint16_t*>(a.U), static_cast<const uint16_t*>(a.W2),
+                       reinterpret_cast<const uint16_t*>(ws + L.ebf), a.temperature, D.V, D.B, L.Bpad,
+                       D.gamma, k, static_cast<uint32_t>(a.seed), static_cast<uint32_t>(a.seed >> 32),
+                       static_cast<uint32_t>(a.offset), reinterpret_cast<float*>(ws + L.pm),
+                       reinterpret_cast<float*>(ws + L.ps), reinterpret_cast<uint64_t*>(ws + L.pkey),
+                       reinterpret_cast<float*>(ws + L.pzx));
+}
+
+template <int NPL>
+static void launch_mfma_kc(const DraftArgs& a, const DraftLayout& L, int k, char* ws) {
+    switch (a.dims.r / 32) {
+        case 1: launch_mfma<1, NPL>(a, L, k, ws); break;
+        case 2: launch_mfma<2, NPL>(a, L, k, ws); break;
+        case 3: launch_mfma<3, NPL>(a, L, k, ws); break;
+        case 4: launch_mfma<4, NPL>(a, L, k, ws); break;
+        case 5: launch_mfma<5, NPL>(a, L, k, ws); break;
+        case 6: launch_mfma<6, NPL>(a, L, k, ws); break;
+        case 7: launch_mfma<7, NPL>(a, L, k, ws); break;
+        default: launch_mfma<8, NPL>(a, L, k, ws); break;
+    }
+}
+
+template <typename T>
+static hipError_t launch_draft_t(const DraftArgs& a) {
+    const dspark_dims& D = a.dims;
+    const DraftLayout L = draft_layout(D);
+    char* ws = a.ws;
+    const bool mfma = mfma_path_ok(D);
+    int32_t* dead = reinterpret_cast<int32_t*>(ws + L.dead);
+    float* emb = reinterpret_cast<float*>(ws + L.emb);
+    float* coef = reinterpret_cast<float*>(ws + L.coef);
+    uint16_t* ebf = reinterpret_cast<uint16_t*>(ws + L.ebf);
+    float* state = reinterpret_cast<float*>(ws + L.state);
+    float* gates = reinterpret_cast<float*>(ws + L.gates);
+    const T* U = static_cast<const T*>(a.U);
+    const T* h = static_cast<const T*>(a.h);
+    const T* W1 = static_cast<const T*>(a.W1);
+    const T* W2 = static_cast<const T*>(a.W2);
+    const T* wc = static_cast<const T*>(a.w_conf);
+    const T* Wr = static_cast<const T*>(a.W_rnn);
+
+    hipLaunchKernelGGL((k_draft_init<T>), dim3(L.Bpad), dim3(256), 0, a.stream, a.anchor, W1, wc, h,
+                       D.V, D.r, D.d, D.gamma, D.B, L.Bpad, D.head, dead, emb, coef, ebf, state,
+                       a.conf, a.survival);
+    for (int k = 0; k < D.gamma; ++k) {
+        if (D.head == DSPARK_HEAD_RNN) {
+            hipLaunchKernelGGL((k_rnn_gates<T>), dim3((3 * D.r + 15) / 16, (D.B + 15) / 16), dim3(256), 0,
+                               a.stream, Wr, state, emb, h, D.r, D.d, D.gamma, k, D.B, gates);
+            hipLaunchKernelGGL(k_rnn_update, dim3(D.B), dim3(256), 0, a.stream, gates, state, coef, ebf,
+                               D.r, L.Bpad);
+        }
+        hipError_t pe = profile_begin(a.stream);
+        if (pe != hipSuccess) return pe;
+        if (mfma) {
+            if (D.head == DSPARK_HEAD_RNN)
+                launch_mfma_kc<2>(a, L, k, ws);
+            else
+                launch_mfma_kc<1>(a, L, k, ws);
+        } else {
+            hipLaunchKernelGGL((k_stream_generic<T>), dim3(L.P), dim3(256), 0, a.stream, U, W2, coef,
+                               a.temperature, D.V, D.r, D.B, D.gamma, k, static_cast<uint32_t>(a.seed),
+                               static_cast<uint32_t>(a.seed >> 32), static_cast<uint32_t>(a.offset),
+                               reinterpret_cast<float*>(ws + L.pm), reinterpret_cast<float*>(ws + L.ps),
+                               reinterpret_cast<uint64_t*>(ws + L.pkey),
+                               reinterpret_cast<float*>(ws + L.pzx));
+        }
+        pe = profile_end(a.stream);
+        if (pe != hipSuccess) return pe;
+        hipLaunchKernelGGL((k_combine<T>), dim3(D.B), dim3(256), 0, a.stream,
+                           reinterpret_cast<const float*>(ws + L.pm),
+                           reinterpret_cast<const float*>(ws + L.ps),
+                           reinterpret_cast<const uint64_t*>(ws + L.pkey),
+                           reinterpret_cast<const float*>(ws + L.pzx), L.P, W1, wc, h, D.V, D.r, D.d,
+                           D.gamma, k, D.head, mfma ? 1 : 0, dead, emb, coef, ebf, a.tokens, a.logp,
+                           a.conf, a.survival);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_draft(const DraftArgs& a) {
+    if (a.dims.dtype == DSPARK_BF16) return launch_draft_t<uint16_t>(a);
+    return launch_draft_t<float>(a);
+}
+
+}  // namespace dspark

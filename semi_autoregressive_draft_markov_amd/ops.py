@@ -1,0 +1,80 @@
+"""torch-facing wrappers over the C ABI: shape inference, output and
+workspace allocation, then one call into libdspark.so.  All arithmetic runs
+in the HIP library; torch only provides device memory and the stream."""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import binding as _b
+
+_DTYPES = {torch.bfloat16: "bf16", torch.float32: "f32"}
+
+
+def _dtype_of(t: torch.Tensor) -> str:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError("tensors must be bfloat16 or float32, got %s" % t.dtype) from None
+
+
+def draft_dims(U, h, W1, W_rnn=None) -> _b.dspark_dims:
+    B, gamma, V = U.shape
+    return _b.make_dims(V, W1.shape[1], h.shape[-1], gamma, B, _dtype_of(U),
+                        "rnn" if W_rnn is not None else "markov")
+
+
+def workspace(dims: _b.dspark_dims, which: int, device) -> torch.Tensor:
+    n = _b.dspark_workspace_size(dims, which)
+    if n == 0:
+        raise _b.DsparkError(_b.DSPARK_EINVAL, _b.dspark_last_error())
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def draft_block(U, h, anchor, W1, W2, w_conf, temperature, *, W_rnn=None, seed: int = 0,
+                offset: int = 0, out: Optional[dict] = None, ws: Optional[torch.Tensor] = None,
+                stream=None) -> dict:
+    """Draft gamma tokens for each of the B blocks (see dspark_draft_block)."""
+    dims = draft_dims(U, h, W1, W_rnn)
+    dev = U.device
+    B, gamma = dims.B, dims.gamma
+    if out is None:
+        out = dict(tokens=torch.empty((B, gamma), dtype=torch.int32, device=dev),
+                   logp=torch.empty((B, gamma), dtype=torch.float32, device=dev),
+                   conf=torch.empty((B, gamma), dtype=torch.float32, device=dev),
+                   survival=torch.empty((B, gamma), dtype=torch.float32, device=dev))
+    if ws is None:
+        ws = workspace(dims, _b.DSPARK_CALL_DRAFT, dev)
+    _b.dspark_draft_block(dims, U, h, anchor, W1, W2, w_conf, W_rnn, temperature, seed, offset,
+                          out["tokens"], out.get("logp"), out["conf"], out["survival"], ws,
+                          stream=stream)
+    out["_ws"] = ws
+    out["_dims"] = dims
+    return out
+
+
+def block_loss(U, T_logits, h, anchor, labels, W1, W2, w_conf, *, alpha=None, pos_weight=None,
+               dlogits_dtype: Optional[str] = "f32", want_dW2: bool = True,
+               ws: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Teacher-forced loss, dlogits and dW2 (see dspark_block_loss)."""
+    N, gamma, V = U.shape
+    dims = _b.make_dims(V, W1.shape[1], h.shape[-1], gamma, N, _dtype_of(U), "markov")
+    dev = U.device
+    out = dict(loss4=torch.empty(4, dtype=torch.float32, device=dev),
+               c_star=torch.empty((N, gamma), dtype=torch.float32, device=dev),
+               conf=torch.empty((N, gamma), dtype=torch.float32, device=dev),
+               dconf_logit=torch.empty((N, gamma), dtype=torch.float32, device=dev))
+    out["dlogits"] = None
+    if dlogits_dtype is not None:
+        td = torch.float32 if dlogits_dtype == "f32" else torch.bfloat16
+        out["dlogits"] = torch.empty((N, gamma, V), dtype=td, device=dev)
+    out["dW2"] = torch.empty((W1.shape[1], V), dtype=torch.float32, device=dev) if want_dW2 else None
+    if ws is None:
+        ws = workspace(dims, _b.DSPARK_CALL_LOSS, dev)
+    _b.dspark_block_loss(dims, U, T_logits, h, anchor, labels, W1, W2, w_conf, alpha, pos_weight,
+                         out["loss4"], out["c_star"], out["conf"], out["dlogits"],
+                         dlogits_dtype or "f32", out["dW2"], out["dconf_logit"], ws, stream=stream)
+    out["_ws"] = ws
+    out["_dims"] = dims
+    return out

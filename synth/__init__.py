@@ -180,3 +180,37 @@ def config_inputs(cfg: int, **overrides) -> Inputs:
     kw.setdefault("seed", 1000 + cfg)
     kw.update(overrides)
     return make_inputs(**kw)
+
+
+def to_torch(inp: Inputs, device="cuda") -> dict:
+    """Copy the arrays of `inp` to `device` as torch tensors (bf16 bits are
+    reinterpreted as torch.bfloat16, not converted)."""
+    import torch
+
+    def t(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    out = {name: t(getattr(inp, name)) for name in
+           ("U", "h", "W1", "W2", "w_conf", "W_rnn", "target")}
+    out["anchor"] = t(np.ascontiguousarray(inp.anchor, dtype=np.int32))
+    out["temperature"] = t(np.ascontiguousarray(inp.temperature, dtype=np.float32))
+    out["labels"] = None if inp.labels is None else t(np.ascontiguousarray(inp.labels, np.int32))
+    return out
+
+
+def subset(inp: Inputs, blocks) -> Inputs:
+    """The same problem restricted to the listed blocks (weights shared)."""
+    blocks = np.asarray(blocks)
+    c = Inputs(**{f: getattr(inp, f) for f in inp.__dataclass_fields__})
+    c.B = len(blocks)
+    for name in ("anchor", "temperature"):
+        setattr(c, name, np.ascontiguousarray(getattr(inp, name)[blocks]))
+    for name in ("U", "h", "target", "labels"):
+        a = getattr(inp, name)
+        if a is not None:
+            setattr(c, name, np.ascontiguousarray(a[blocks]))
+    return c

@@ -1,0 +1,173 @@
+"""GPU parity of dspark_draft_block against the CPU oracle (through the C ABI).
+
+Sizes span several V tiles with ragged tails, padded block columns, both
+heads, both dtypes, mixed temperatures, and the full workloads (all blocks
+or a sample of blocks recomputed with their original noise).
+"""
+import itertools
+
+import numpy as np
+import pytest
+from scipy import stats
+
+import oracle
+import synth
+from _parity import check_draft, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from semi_autoregressive_draft_markov_amd import binding, ops as _ops
+    binding.load()
+    return _ops
+
+
+def run_gpu(ops, inp, seed=0, offset=0):
+    import torch
+    t = synth.to_torch(inp)
+    out = ops.draft_block(t["U"], t["h"], t["anchor"], t["W1"], t["W2"], t["w_conf"],
+                          t["temperature"], W_rnn=t["W_rnn"], seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    res = {k: out[k].cpu().numpy() for k in ("tokens", "logp", "conf", "survival")}
+    res["_out"] = out
+    return res
+
+
+def small(**kw):
+    base = dict(V=1000, r=64, d=48, gamma=5, B=20, dtype="bf16", head="markov", seed=3,
+                u_std=3.0, h_std=1.0, w1_std=0.25, w2_std=0.25, wconf_std=0.1, wrnn_std=0.1,
+                anchors="uniform", temperature=1.0)
+    base.update(kw)
+    return synth.make_inputs(**base)
+
+
+# -------------------------------------------------------------- small cases
+
+@pytest.mark.parametrize("temp", [1.0, 0.0])
+def test_tiny_fp32_block(ops, temp):
+    inp = synth.config_inputs(1, temperature=temp)
+    note("case: tiny fp32 V1024 r32 B4 T=%s" % temp)
+    g = run_gpu(ops, inp, seed=0)
+    check_draft(inp, g, 0, 0, label="tiny fp32")
+
+
+def test_bf16_matrix_core_ragged_mixed_temperature(ops):
+    # V = 1000: 4 workgroups, last one 232 columns; 64-column wave tiles with
+    # a 40-column tail; B = 20 pads to 32 block columns.  Strong bias.
+    temps = [1.0] * 8 + [0.0] * 6 + [0.7] * 6
+    inp = small(temperature=temps)
+    note("case: bf16 mfma V1000 r64 B20 mixed T")
+    g = run_gpu(ops, inp, seed=11, offset=5)
+    check_draft(inp, g, 11, 5, label="bf16 mfma ragged")
+
+
+@pytest.mark.parametrize("B", [1, 33])
+def test_bf16_rank256_tail_columns(ops, B):
+    inp = small(V=4104, r=256, d=64, gamma=7, B=B, seed=4)
+    note("case: bf16 mfma V4104 r256 B%d" % B)
+    g = run_gpu(ops, inp, seed=2)
+    check_draft(inp, g, 2, 0, label="bf16 r256")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rnn_head_small(ops, dtype):
+    inp = small(V=512, r=32, d=40, gamma=4, B=10, head="rnn", dtype=dtype, seed=8,
+                wrnn_std=0.3, temperature=[1.0] * 5 + [0.0] * 5)
+    note("case: rnn %s V512 r32 B10" % dtype)
+    g = run_gpu(ops, inp, seed=6, offset=1)
+    check_draft(inp, g, 6, 1, label="rnn " + dtype)
+
+
+def test_vector_path_odd_shapes(ops):
+    # V not a multiple of 8 and r not a multiple of 32: the plain vector path
+    inp = small(V=999, r=48, d=20, gamma=3, B=6, seed=9)
+    note("case: bf16 vector path V999 r48")
+    g = run_gpu(ops, inp, seed=1)
+    check_draft(inp, g, 1, 0, label="vector path")
+
+
+def test_zero_confidence_weights(ops):
+    inp = small(B=4, gamma=6)
+    inp.w_conf = np.zeros_like(inp.w_conf)
+    g = run_gpu(ops, inp)
+    assert np.all(g["conf"] == 0.5)
+    assert np.all(g["survival"] == (0.5 ** np.arange(1, 7))[None, :].astype(np.float32))
+
+
+def test_deterministic(ops):
+    inp = small(V=2048, r=128, B=24, seed=12)
+    a = run_gpu(ops, inp, seed=3)
+    b = run_gpu(ops, inp, seed=3)
+    for k in ("tokens", "logp", "conf", "survival"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+    c = run_gpu(ops, inp, seed=3, offset=1)
+    assert not np.array_equal(a["tokens"], c["tokens"])
+
+
+def test_out_of_range_anchor_is_flagged(ops):
+    from semi_autoregressive_draft_markov_amd import binding
+    inp = small(B=5)
+    inp.anchor = np.array([3, inp.V, 7, -1, 0], np.int32)
+    g = run_gpu(ops, inp)
+    assert np.all(g["tokens"][[1, 3]] == -1)
+    assert np.all(np.isnan(g["conf"][[1, 3]]))
+    assert np.all(g["tokens"][[0, 2, 4]] >= 0)
+    out = g["_out"]
+    assert binding.dspark_read_device_error(out["_dims"], out["_ws"]) == 2
+    good = synth.subset(inp, [0, 2, 4])
+    check_draft(good, {k: g[k][[0, 2, 4]] for k in ("tokens", "logp", "conf", "survival")},
+                0, 0, block_ids=[0, 2, 4], label="valid blocks")
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 8), ("f32", 4)])
+def test_sampler_law_on_gpu(ops, dtype, V):
+    # GPU block frequencies follow the exact Eq 4 product (chi-square).
+    gamma, n = 2, 60000
+    inp = small(V=V, r=32, d=8, gamma=gamma, B=1, dtype=dtype, w1_std=0.5, w2_std=0.5,
+                u_std=1.0, seed=5)
+    rep = synth.subset(inp, np.zeros(n, dtype=np.int64))
+    g = run_gpu(ops, rep, seed=77)
+    codes = g["tokens"][:, 0] * V + g["tokens"][:, 1]
+    counts = np.bincount(codes, minlength=V * V)
+    blocks = np.array(list(itertools.product(range(V), repeat=gamma)), np.int32)
+    probs = np.exp(oracle.block_logprob(synth.subset(inp, np.zeros(len(blocks), np.int64)), blocks))
+    exp = probs * n
+    keep = exp > 5
+    chi2 = (((counts - exp) ** 2) / exp)[keep].sum()
+    p = stats.chi2.sf(chi2, keep.sum() - 1)
+    assert p > 1e-4, (chi2, p)
+
+
+# -------------------------------------------------------------- full sizes
+
+def test_qwen3_4b_shape_all_blocks(ops):
+    inp = synth.config_inputs(2)
+    note("case: qwen3-4b-shaped V151936 r256 B32 (all blocks)")
+    g = run_gpu(ops, inp, seed=0)
+    info = check_draft(inp, g, 0, 0, label="qwen3-4b shape")
+    note("  ties allowed: %d, max |dlogp| %.2e" % (info["ties"], info["logp_err"]))
+
+
+def test_qwen3_14b_shape_sampled_blocks(ops):
+    inp = synth.config_inputs(4)
+    note("case: qwen3-14b-shaped V151936 r256 B256 half greedy (16 sampled blocks)")
+    g = run_gpu(ops, inp, seed=0)
+    pick = np.array([0, 1, 37, 64, 100, 126, 127, 128, 129, 150, 200, 201, 222, 250, 254, 255])
+    sub = synth.subset(inp, pick)
+    check_draft(sub, {k: g[k][pick] for k in ("tokens", "logp", "conf", "survival")}, 0, 0,
+                block_ids=pick, label="qwen3-14b shape")
+    assert np.all(g["tokens"] >= 0)
+
+
+def test_gemma4_rnn_shape_sampled_blocks(ops):
+    inp = synth.config_inputs(5)
+    note("case: gemma4-12b-shaped rnn V262144 r256 B128 (8 sampled blocks)")
+    g = run_gpu(ops, inp, seed=0)
+    pick = np.array([0, 5, 31, 64, 77, 100, 126, 127])
+    sub = synth.subset(inp, pick)
+    check_draft(sub, {k: g[k][pick] for k in ("tokens", "logp", "conf", "survival")}, 0, 0,
+                block_ids=pick, label="gemma4 rnn shape")
