@@ -1,6 +1,7 @@
 // C ABI of the DSpark sequential-head library: argument checks, workspace
 // sizing and dispatch.  Declarations and the contract live in
 // include/dspark.h.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -78,13 +79,6 @@ bool profiling_enabled() { return g_prof.on; }
 hipError_t profile_begin(hipStream_t s) { return g_prof.on ? record(s) : hipSuccess; }
 hipError_t profile_end(hipStream_t s) { return g_prof.on ? record(s) : hipSuccess; }
 
-LossLayout loss_layout(const dspark_dims& d) {
-    LossLayout L{};
-    L.bad = 0;
-    L.total = align_up(sizeof(int32_t) * d.B, 256);
-    return L;
-}
-
 }  // namespace dspark
 
 extern "C" {
@@ -143,7 +137,45 @@ dspark_status dspark_block_loss(const dspark_dims* dims, const void* U, const vo
                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
     dspark_status s = check_dims(dims);
     if (s != DSPARK_OK) return s;
-    return fail(DSPARK_EUNSUPPORTED, "dspark_block_loss is not built yet");
+    if (dims->head != DSPARK_HEAD_MARKOV)
+        return fail(DSPARK_EUNSUPPORTED, "the training objective is built for the Markov head only");
+    const char* missing = !U ? "U" : !T_logits ? "T_logits" : !h ? "h" : !anchor ? "anchor"
+                        : !labels ? "labels" : !W1 ? "W1" : !W2 ? "W2" : !w_conf ? "w_conf"
+                        : !loss4 ? "loss4" : !c_star ? "c_star" : !workspace ? "workspace" : nullptr;
+    if (missing) return fail(DSPARK_EINVAL, "required pointer %s is NULL", missing);
+    if (dW2 && !dlogits) return fail(DSPARK_EINVAL, "dW2 is computed from dlogits: pass dlogits too");
+    if (dlogits && dlogits_dtype != DSPARK_F32 && dlogits_dtype != DSPARK_BF16)
+        return fail(DSPARK_EINVAL, "dlogits_dtype = %d is neither DSPARK_F32 nor DSPARK_BF16", dlogits_dtype);
+    if (!aligned(workspace, 256)) return fail(DSPARK_EINVAL, "workspace is not 256-byte aligned");
+    const size_t need = dspark::loss_layout(*dims).total;
+    if (workspace_bytes < need)
+        return fail(DSPARK_EWORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, need);
+    const size_t esz = dims->dtype == DSPARK_BF16 ? 2 : 4;
+    if (!aligned(U, esz) || !aligned(T_logits, esz) || !aligned(h, esz) || !aligned(W1, esz) ||
+        !aligned(W2, esz) || !aligned(w_conf, esz) || (dlogits && !aligned(dlogits, 4)) ||
+        (dW2 && !aligned(dW2, 4)))
+        return fail(DSPARK_EINVAL, "a tensor is not aligned to its element size");
+    if (dspark::loss_mfma_ok(*dims) &&
+        (!aligned(U, 16) || !aligned(T_logits, 16) || !aligned(W2, 16) ||
+         (dlogits && !aligned(dlogits, 16)) || (dW2 && !aligned(dW2, 16))))
+        return fail(DSPARK_EUNSUPPORTED, "bf16 U, T_logits, W2, dlogits and dW2 must be 16-byte aligned");
+
+    dspark::LossArgs a{};
+    a.dims = *dims;
+    a.U = U; a.T_logits = T_logits; a.h = h; a.W1 = W1; a.W2 = W2; a.w_conf = w_conf;
+    a.anchor = anchor; a.labels = labels;
+    const float defaults[3] = {0.1f, 0.9f, 1.0f};  // Eq 12
+    for (int q = 0; q < 3; ++q) a.alpha[q] = alpha ? alpha[q] : defaults[q];
+    for (int k = 0; k < dims->gamma; ++k)
+        a.pos_weight[k] = pos_weight ? pos_weight[k]
+                                     : static_cast<float>(exp(-static_cast<double>(k) / dims->gamma));
+    a.loss4 = loss4; a.c_star = c_star; a.conf = conf; a.dconf_logit = dconf_logit; a.dW2 = dW2;
+    a.dlogits = dlogits; a.dlogits_dtype = dlogits_dtype;
+    a.ws = static_cast<char*>(workspace);
+    a.stream = static_cast<hipStream_t>(hip_stream);
+    const hipError_t e = dspark::launch_loss(a);
+    if (e != hipSuccess) return fail(DSPARK_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 dspark_status dspark_read_device_error(const dspark_dims* dims, const void* workspace,

@@ -15,6 +15,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "mfma_tile.h"
 
 namespace dspark {
 
@@ -228,15 +229,11 @@ __device__ __forceinline__ Stats lane_stats16(const float (&z)[16], int v0, int 
     return Stats{m, s, argmax_key(ybest, static_cast<uint32_t>(v0 + idx)), zx};
 }
 
-// One workgroup = 4 waves = 256 columns.  Each wave owns a 64-column tile of
-// W2 for the whole step and keeps it in registers as MFMA A-operand
-// fragments: lane (g = lane / 16, n = lane % 16) loads 8 rows j = 32 kc + 8g
-// + e at the 4 columns vt + 4n .. vt + 4n + 3 (coalesced 8-byte loads) and
-// transposes them with v_perm into 4 fragments, one per column offset c.
-// MFMA c then computes bias[b][vt + 4i + c] for i = 0..15 (A row i) and 16
-// blocks b (B column), so lane (g, n) ends up holding the 16 consecutive
-// columns vt + 16g .. vt + 16g + 15 of block row b = 16 nb + n: all of a
-// lane's softmax and argmax work is for one block row.
+// One workgroup = 4 waves = 256 columns.  Each wave keeps a 64-column W2
+// tile in registers as MFMA A-fragments (see mfma_tile.h) for the whole step
+// and loops over the blocks 16 at a time; lane (g, n) ends up with the 16
+// consecutive columns vt + 16g .. vt + 16g + 15 of block row b = 16 nb + n,
+// so all of a lane's softmax and argmax work is for one block row.
 template <int KC, int NPLANES>
 __global__ __launch_bounds__(256) void k_stream_mfma(
     const uint16_t* __restrict__ U, const uint16_t* __restrict__ W2,
@@ -251,28 +248,8 @@ __global__ __launch_bounds__(256) void k_stream_mfma(
     const int vt = (blockIdx.x * kWavesPerWG + wave) * kTileV;
     const int P = gridDim.x;
 
-    uint32_t frag[KC][4][4];
-    {
-        const int va = vt + 4 * n;
-        const bool ok = va < V;
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            uint2 raw[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = kc * 32 + 8 * g + e;
-                raw[e] = ok ? *reinterpret_cast<const uint2*>(W2 + static_cast<size_t>(j) * V + va)
-                            : make_uint2(0u, 0u);
-            }
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                frag[kc][0][p] = __builtin_amdgcn_perm(raw[2 * p + 1].x, raw[2 * p].x, 0x05040100u);
-                frag[kc][1][p] = __builtin_amdgcn_perm(raw[2 * p + 1].x, raw[2 * p].x, 0x07060302u);
-                frag[kc][2][p] = __builtin_amdgcn_perm(raw[2 * p + 1].y, raw[2 * p].y, 0x05040100u);
-                frag[kc][3][p] = __builtin_amdgcn_perm(raw[2 * p + 1].y, raw[2 * p].y, 0x07060302u);
-            }
-        }
-    }
+    W2Tile<KC> w2;
+    w2.load(W2, V, vt, g, n);
 
     const int v0 = vt + 16 * g;
     for (int nb = 0; nb < Bpad / 16; ++nb) {
@@ -281,40 +258,20 @@ __global__ __launch_bounds__(256) void k_stream_mfma(
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int pl = 0; pl < NPLANES; ++pl) {
-            const uint16_t* erow = ebf + (static_cast<size_t>(pl) * Bpad + b) * r + 8 * g;
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const u32x4 ev = *reinterpret_cast<const u32x4*>(erow + kc * 32);
-                const bf16x8 bop = __builtin_bit_cast(bf16x8, ev);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const u32x4 av = {frag[kc][c][0], frag[kc][c][1], frag[kc][c][2], frag[kc][c][3]};
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bop,
-                                                                     acc[c], 0, 0, 0);
-                }
-            }
-        }
+        for (int pl = 0; pl < NPLANES; ++pl)
+            w2.mul(ebf + (static_cast<size_t>(pl) * Bpad + b) * r + 8 * g, acc);
 
         Stats st = stats_empty();
         if (b < B && v0 < V) {
             const float temp = temperature[b];
             const bool sampling = temp > 0.0f;
             const float invT = sampling ? 1.0f / temp : 1.0f;
-            const uint16_t* urow = U + (static_cast<size_t>(b) * gamma + k) * V + v0;
-            const u32x4 u0 = *reinterpret_cast<const u32x4*>(urow);
-            u32x4 u1 = {0u, 0u, 0u, 0u};
-            if (v0 + 8 < V) u1 = *reinterpret_cast<const u32x4*>(urow + 8);
-            const uint32_t uw[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
             float z[16];
+            load16_bf16(U + (static_cast<size_t>(b) * gamma + k) * V + v0, v0 + 8 < V, z);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int j = 4 * q + c;
-                    const float u = (j & 1) ? hi_bf16(uw[j >> 1]) : lo_bf16(uw[j >> 1]);
-                    z[j] = acc[c][q] + u;
-                }
+                for (int c = 0; c < 4; ++c) z[4 * q + c] += acc[c][q];
             if (v0 + 16 <= V)
                 st = lane_stats16<true>(z, v0, V, b, k, sampling, invT, key0, key1, ctr3);
             else

@@ -30,11 +30,42 @@ bool mfma_path_ok(const dspark_dims& d);
 int draft_partials(const dspark_dims& d);
 DraftLayout draft_layout(const dspark_dims& d);
 
+// Loss-call workspace carve-up.  Rows i = n * gamma + k, padded to Rpad.
 struct LossLayout {
-    size_t bad;        // int32 [N]   1 if the block saw a token id out of range
+    int R, Rpad;       // rows, rows rounded up to 32
+    bool mfma;         // matrix-core path (bf16, r % 32 == 0, r <= 256, V % 8 == 0)
+    int P;             // column groups (partial slots per row)
+    int nrc;           // row chunks per pass
+    int rb_per_chunk;  // 16-row blocks per chunk
+    size_t bad;        // int32 [N]  1 if the block saw a token id out of range
+    size_t ebf;        // u16 [Rpad, r]  E = W1[prev] rows (MFMA operand)
+    size_t ef;         // f32 [Rpad, r]  E rows (vector path, dW2 vector path)
+    size_t et;         // u16 [r, Rpad]  E transposed (dW2 operand)
+    size_t label;      // i32 [Rpad]  label per row (0 for invalid rows)
+    size_t rowc;       // f32 [Rpad]  w_k / N (0 for invalid rows)
+    size_t alog;       // f32 [Rpad]  confidence logit (NaN for invalid rows)
+    size_t lse_d, lse_t, zlab, tv, cmin, S;  // f32 [Rpad] per-row statistics
+    size_t part[5];    // f32 [P, Rpad] per-pass partials
+    size_t tce, ttv, tbce;  // f32 [Rpad] weighted loss terms
     size_t total;
 };
 LossLayout loss_layout(const dspark_dims& d);
+bool loss_mfma_ok(const dspark_dims& d);
+
+struct LossArgs {
+    dspark_dims dims;
+    const void *U, *T_logits, *h, *W1, *W2, *w_conf;
+    const int32_t *anchor, *labels;
+    float alpha[3];
+    float pos_weight[64];
+    float *loss4, *c_star, *conf, *dconf_logit, *dW2;
+    void* dlogits;
+    int32_t dlogits_dtype;
+    char* ws;
+    hipStream_t stream;
+};
+
+hipError_t launch_loss(const LossArgs& a);
 
 struct DraftArgs {
     dspark_dims dims;

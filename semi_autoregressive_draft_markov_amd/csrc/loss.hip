@@ -1,0 +1,705 @@
+// DSpark teacher-forced objective on gfx950: Eq 8-12 of the DSpark paper as
+// transcribed on the dormouse "DSpark - paper verification" page, section 1,
+// with teacher forcing as in mainlymatmul's "Training DSpark" (position k is
+// fed the ground-truth x_{k-1}), plus dL/dz_d and dW2 = E^T dZ.
+//
+// Rows i = n * gamma + k.  z_d = U + E W2 (E = W1[prev]) is recomputed in
+// each of three sweeps over V rather than stored (storing it in bf16 would
+// break the tolerance, in fp32 it costs more bytes than re-reading U):
+//   prep     prev tokens, E (row-major and transposed), confidence logits
+//   pass 1   per row: log-sum-exp of z_d and z_t, z_d at the label
+//   pass 2   per row: sum |p_d - p_t|, sum min(p_d, p_t), sum p_d sign(p_d - p_t)
+//   finalize c*, CE, BCE, dL/da per row; the four losses (fixed-order sums)
+//   pass 3   dZ = (w_k/N)[a_ce (p_d - onehot) + a_tv p_d (s - S)]  -> dlogits
+//   dW2      E^T dZ, MFMA over rows (split-bf16 when dZ is float32)
+#include <math.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "internal.h"
+#include "mfma_tile.h"
+
+namespace dspark {
+
+constexpr int kLossWaves = 4;                  // waves per workgroup (MFMA passes)
+constexpr int kLossColsPerWG = 64 * kLossWaves;
+constexpr int kLossGenericCols = 4 * 256;
+constexpr int kLossTargetItems = 2048;         // work items per pass (row chunks x column groups)
+
+bool loss_mfma_ok(const dspark_dims& d) {
+    return d.dtype == DSPARK_BF16 && d.r % 32 == 0 && d.r <= 256 && d.V % 8 == 0;
+}
+
+LossLayout loss_layout(const dspark_dims& d) {
+    LossLayout L{};
+    const int64_t R = static_cast<int64_t>(d.B) * d.gamma;
+    L.R = static_cast<int>(R);
+    L.Rpad = static_cast<int>((R + 31) / 32 * 32);
+    L.mfma = loss_mfma_ok(d);
+    L.P = L.mfma ? (d.V + kLossColsPerWG - 1) / kLossColsPerWG
+                 : (d.V + kLossGenericCols - 1) / kLossGenericCols;
+    const int rb = L.Rpad / 16;
+    L.nrc = std::max(1, std::min(rb, (kLossTargetItems + L.P - 1) / L.P));
+    L.rb_per_chunk = (rb + L.nrc - 1) / L.nrc;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const size_t rp = static_cast<size_t>(L.Rpad);
+    L.bad = take(sizeof(int32_t) * d.B);
+    L.ebf = take(sizeof(uint16_t) * rp * d.r);
+    L.ef = take(sizeof(float) * rp * d.r);
+    L.et = take(sizeof(uint16_t) * rp * d.r);
+    L.label = take(sizeof(int32_t) * rp);
+    L.rowc = take(sizeof(float) * rp);
+    L.alog = take(sizeof(float) * rp);
+    L.lse_d = take(sizeof(float) * rp);
+    L.lse_t = take(sizeof(float) * rp);
+    L.zlab = take(sizeof(float) * rp);
+    L.tv = take(sizeof(float) * rp);
+    L.cmin = take(sizeof(float) * rp);
+    L.S = take(sizeof(float) * rp);
+    for (int q = 0; q < 5; ++q) L.part[q] = take(sizeof(float) * rp * L.P);
+    L.tce = take(sizeof(float) * rp);
+    L.ttv = take(sizeof(float) * rp);
+    L.tbce = take(sizeof(float) * rp);
+    L.total = off;
+    return L;
+}
+
+// ------------------------------------------------------------------ prep
+
+struct LossConsts {
+    float alpha[3];
+    float pos_weight[64];  // w_k / N for k < gamma
+};
+
+// Workgroup = one row i (rows in [R, Rpad) only zero their operand rows).
+// Teacher forcing: prev = anchor[n] at k = 0, labels[n, k-1] after.  The row
+// k = 0 workgroup of block n also checks every token id of the block.
+template <typename T>
+__global__ __launch_bounds__(256) void k_loss_prep(
+    const int32_t* __restrict__ anchor, const int32_t* __restrict__ labels,
+    const T* __restrict__ W1, const T* __restrict__ w_conf, const T* __restrict__ h, int V, int r,
+    int d, int gamma, int R, int Rpad, LossConsts cst, int32_t* __restrict__ bad,
+    uint16_t* __restrict__ ebf, float* __restrict__ ef, uint16_t* __restrict__ et,
+    int32_t* __restrict__ label_out, float* __restrict__ rowc, float* __restrict__ alog) {
+    __shared__ float red[16];
+    const int i = blockIdx.x;
+    if (i >= R) {
+        for (int j = threadIdx.x; j < r; j += blockDim.x) {
+            ebf[static_cast<size_t>(i) * r + j] = 0;
+            ef[static_cast<size_t>(i) * r + j] = 0.0f;
+            et[static_cast<size_t>(j) * Rpad + i] = 0;
+        }
+        if (threadIdx.x == 0) {
+            label_out[i] = 0;
+            rowc[i] = 0.0f;
+            alog[i] = 0.0f;
+        }
+        return;
+    }
+    const int n = i / gamma, k = i % gamma;
+    const int prev_raw = k == 0 ? anchor[n] : labels[i - 1];
+    const int lab_raw = labels[i];
+    const bool ok = prev_raw >= 0 && prev_raw < V && lab_raw >= 0 && lab_raw < V;
+    const int prev = ok ? prev_raw : 0;
+    if (k == 0 && threadIdx.x == 0) {
+        bool all = anchor[n] >= 0 && anchor[n] < V;
+        for (int q = 0; q < gamma; ++q) {
+            const int t = labels[static_cast<size_t>(n) * gamma + q];
+            all = all && t >= 0 && t < V;
+        }
+        bad[n] = all ? 0 : 1;
+    }
+    float part = 0.0f;
+    for (int j = threadIdx.x; j < r; j += blockDim.x) {
+        const float e = load_f(W1, static_cast<int64_t>(prev) * r + j);
+        const uint16_t eb = static_cast<uint16_t>(f32_to_bf16(e));
+        ebf[static_cast<size_t>(i) * r + j] = eb;
+        ef[static_cast<size_t>(i) * r + j] = e;
+        et[static_cast<size_t>(j) * Rpad + i] = eb;
+        part += load_f(w_conf, d + j) * e;
+    }
+    const int64_t hrow = static_cast<int64_t>(i) * d;
+    for (int q = threadIdx.x; q < d; q += blockDim.x) part += load_f(w_conf, q) * load_f(h, hrow + q);
+    const float a = block_sum(part, red);
+    if (threadIdx.x == 0) {
+        label_out[i] = ok ? lab_raw : 0;
+        rowc[i] = ok ? cst.pos_weight[k] : 0.0f;  // zero gradient rows for invalid ids
+        alog[i] = ok ? a : NAN;
+    }
+}
+
+// ------------------------------------------------------- pass epilogues
+
+struct PassArgs {
+    const uint16_t* U;     // bf16 (MFMA path)
+    const uint16_t* T;
+    const void* Ug;        // any dtype (vector path)
+    const void* Tg;
+    const void* W2g;
+    const uint16_t* W2;
+    const uint16_t* ebf;
+    const float* ef;
+    int V, r, R, Rpad, P, nrc, rb_per_chunk;
+    const int32_t* label;
+    const float *lse_d, *lse_t, *S, *rowc;
+    float* part[5];        // partials [P][Rpad]
+    void* dz;
+    int dz_bf16;
+    float a_ce, a_tv;
+};
+
+constexpr int kPass1 = 1, kPass2 = 2, kPass3 = 3;
+
+// Partial values one pass contributes for one row and one column slice.
+struct RowPart {
+    float v[5];
+};
+
+__device__ __forceinline__ RowPart rowpart_empty(int pass) {
+    RowPart p;
+    if (pass == kPass1) {
+        p.v[0] = -INFINITY; p.v[1] = 0.0f; p.v[2] = -INFINITY; p.v[3] = 0.0f; p.v[4] = -INFINITY;
+    } else {
+        p.v[0] = 0.0f; p.v[1] = 0.0f; p.v[2] = 0.0f; p.v[3] = 0.0f; p.v[4] = 0.0f;
+    }
+    return p;
+}
+
+// (max, sum exp(x - max)) pairs merge with a rescale; the label logit is a
+// max (exactly one slice holds it); pass-2 values are plain sums.
+__device__ __forceinline__ RowPart rowpart_merge(int pass, const RowPart& a, const RowPart& b) {
+    RowPart r;
+    if (pass == kPass1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float m = fmaxf(a.v[2 * h], b.v[2 * h]);
+            const float sa = a.v[2 * h + 1] > 0.0f ? a.v[2 * h + 1] * __builtin_amdgcn_exp2f((a.v[2 * h] - m) * kLog2e) : 0.0f;
+            const float sb = b.v[2 * h + 1] > 0.0f ? b.v[2 * h + 1] * __builtin_amdgcn_exp2f((b.v[2 * h] - m) * kLog2e) : 0.0f;
+            r.v[2 * h] = m;
+            r.v[2 * h + 1] = sa + sb;
+        }
+        r.v[4] = fmaxf(a.v[4], b.v[4]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 5; ++q) r.v[q] = a.v[q] + b.v[q];
+    }
+    return r;
+}
+
+__device__ __forceinline__ RowPart rowpart_shfl(const RowPart& a, int mask) {
+    RowPart r;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) r.v[q] = __shfl_xor(a.v[q], mask);
+    return r;
+}
+
+// Per-row work on NC consecutive columns v0 .. v0+NC-1 (zd = U + bias,
+// zt = target logits; columns at or past V hold -inf).
+template <int PASS, int NC>
+__device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int v0,
+                                                const float (&zd)[NC], const float (&zt)[NC]) {
+    RowPart p = rowpart_empty(PASS);
+    if (PASS == kPass1) {
+        float md = zd[0], mt = zt[0];
+#pragma unroll
+        for (int j = 1; j < NC; ++j) {
+            md = fmaxf(md, zd[j]);
+            mt = fmaxf(mt, zt[j]);
+        }
+        float sd = 0.0f, st = 0.0f;
+        const float mdl = md * kLog2e, mtl = mt * kLog2e;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            sd += __builtin_amdgcn_exp2f(fmaf(zd[j], kLog2e, -mdl));
+            st += __builtin_amdgcn_exp2f(fmaf(zt[j], kLog2e, -mtl));
+        }
+        const int lab = a.label[row];
+        float zl = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) zl = (lab == v0 + j) ? zd[j] : zl;
+        p.v[0] = md; p.v[1] = sd; p.v[2] = mt; p.v[3] = st; p.v[4] = zl;
+    } else {
+        const float ld = a.lse_d[row] * kLog2e, lt = a.lse_t[row] * kLog2e;
+        if (PASS == kPass2) {
+            float tv = 0.0f, cm = 0.0f, S = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NC; ++j) {
+                const float pd = __builtin_amdgcn_exp2f(fmaf(zd[j], kLog2e, -ld));
+                const float pt = __builtin_amdgcn_exp2f(fmaf(zt[j], kLog2e, -lt));
+                tv += fabsf(pd - pt);
+                cm += fminf(pd, pt);
+                S += pd > pt ? pd : (pd < pt ? -pd : 0.0f);
+            }
+            p.v[0] = tv; p.v[1] = cm; p.v[2] = S;
+        } else {
+            const float coef = a.rowc[row], S = a.S[row];
+            const int lab = a.label[row];
+            float dz[NC];
+#pragma unroll
+            for (int j = 0; j < NC; ++j) {
+                const float pd = __builtin_amdgcn_exp2f(fmaf(zd[j], kLog2e, -ld));
+                const float pt = __builtin_amdgcn_exp2f(fmaf(zt[j], kLog2e, -lt));
+                const float sg = pd > pt ? 1.0f : (pd < pt ? -1.0f : 0.0f);
+                const float onehot = (lab == v0 + j) ? 1.0f : 0.0f;
+                dz[j] = coef * (a.a_ce * (pd - onehot) + a.a_tv * pd * (sg - S));
+            }
+            const size_t o = static_cast<size_t>(row) * a.V + v0;
+            const int nvalid = a.V - v0;
+            if (a.dz_bf16) {
+                uint16_t* dst = static_cast<uint16_t*>(a.dz) + o;
+                if (NC == 16 && nvalid >= 16 && (o % 8) == 0) {
+                    u32x4 w0, w1;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        w0[q] = f32_to_bf16(dz[2 * q]) | (f32_to_bf16(dz[2 * q + 1]) << 16);
+                        w1[q] = f32_to_bf16(dz[8 + 2 * q]) | (f32_to_bf16(dz[8 + 2 * q + 1]) << 16);
+                    }
+                    *reinterpret_cast<u32x4*>(dst) = w0;
+                    *reinterpret_cast<u32x4*>(dst + 8) = w1;
+                } else {
+                    for (int j = 0; j < NC && j < nvalid; ++j) dst[j] = static_cast<uint16_t>(f32_to_bf16(dz[j]));
+                }
+            } else {
+                float* dst = static_cast<float*>(a.dz) + o;
+                if (NC == 16 && nvalid >= 16 && (o % 4) == 0) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<f32x4*>(dst + 4 * q) =
+                            f32x4{dz[4 * q], dz[4 * q + 1], dz[4 * q + 2], dz[4 * q + 3]};
+                } else {
+                    for (int j = 0; j < NC && j < nvalid; ++j) dst[j] = dz[j];
+                }
+            }
+        }
+    }
+    return p;
+}
+
+// ----------------------------------------------------- pass kernels (MFMA)
+
+// Work item = (column group cg of 256 columns, row chunk rc).  The
+// workgroup's 4 waves hold the 4 W2 tiles of cg in registers and walk the
+// chunk 16 rows at a time; the 16 E rows of each step are shared through
+// LDS (row stride padded by 16 bytes against bank conflicts).
+template <int KC, int PASS>
+__global__ __launch_bounds__(256) void k_loss_mfma(PassArgs a) {
+    constexpr int r = KC * 32;
+    constexpr int ldE = r + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t Es[16 * ldE];
+    __shared__ RowPart red[kLossWaves][16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int items = a.P * a.nrc;
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int cg = item % a.P, rc = item / a.P;
+        const int vt = cg * kLossColsPerWG + wave * 64;
+        W2Tile<KC> w2;
+        w2.load(a.W2, a.V, vt, g, n);
+        const int v0 = vt + 16 * g;
+        const int rb0 = rc * a.rb_per_chunk;
+        const int rb1 = min(a.Rpad / 16, rb0 + a.rb_per_chunk);
+        for (int rb = rb0; rb < rb1; ++rb) {
+            __syncthreads();
+            for (int t = threadIdx.x; t < 16 * (r / 8); t += blockDim.x) {
+                const int er = t / (r / 8), ec = t % (r / 8);
+                *reinterpret_cast<u32x4*>(&Es[er * ldE + ec * 8]) =
+                    *reinterpret_cast<const u32x4*>(a.ebf + static_cast<size_t>(rb * 16 + er) * r + ec * 8);
+            }
+            __syncthreads();
+            f32x4 acc[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            w2.mul(&Es[n * ldE + 8 * g], acc);
+
+            const int row = rb * 16 + n;
+            RowPart p = rowpart_empty(PASS);
+            if (row < a.R && v0 < a.V) {
+                const size_t o = static_cast<size_t>(row) * a.V + v0;
+                float zd[16], zt[16];
+                load16_bf16(a.U + o, v0 + 8 < a.V, zd);
+                load16_bf16(a.T + o, v0 + 8 < a.V, zt);
+                const int nvalid = a.V - v0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int j = 4 * q + c;
+                        zd[j] += acc[c][q];
+                        if (j >= nvalid) {
+                            zd[j] = -INFINITY;
+                            zt[j] = -INFINITY;
+                        }
+                    }
+                p = row_epilogue<PASS, 16>(a, row, v0, zd, zt);
+            }
+            if (PASS == kPass3) continue;
+            p = rowpart_merge(PASS, p, rowpart_shfl(p, 16));
+            p = rowpart_merge(PASS, p, rowpart_shfl(p, 32));
+            if (g == 0) red[wave][n] = p;
+            __syncthreads();
+            if (wave == 0 && g == 0 && row < a.R) {
+                RowPart t = red[0][n];
+#pragma unroll
+                for (int w = 1; w < kLossWaves; ++w) t = rowpart_merge(PASS, t, red[w][n]);
+                const size_t o = static_cast<size_t>(cg) * a.Rpad + row;
+                const int nv = PASS == kPass1 ? 5 : 3;
+                for (int q = 0; q < nv; ++q) a.part[q][o] = t.v[q];
+            }
+        }
+    }
+}
+
+// --------------------------------------------------- pass kernels (vector)
+
+// Any dtype / rank: thread = 4 consecutive columns, rows of the item's chunk
+// one at a time, bias as a float dot product with E.
+template <typename T, int PASS>
+__global__ __launch_bounds__(256) void k_loss_generic(PassArgs a) {
+    __shared__ RowPart red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const T* U = static_cast<const T*>(a.Ug);
+    const T* Tl = static_cast<const T*>(a.Tg);
+    const T* W2 = static_cast<const T*>(a.W2g);
+    const int items = a.P * a.nrc;
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int cg = item % a.P, rc = item / a.P;
+        const int v0 = (cg * static_cast<int>(blockDim.x) + static_cast<int>(threadIdx.x)) * 4;
+        const int r0 = rc * a.rb_per_chunk * 16;
+        const int r1 = min(a.R, r0 + a.rb_per_chunk * 16);
+        for (int row = r0; row < r1; ++row) {
+            RowPart p = rowpart_empty(PASS);
+            if (v0 < a.V) {
+                float zd[4], zt[4];
+                const int64_t o = static_cast<int64_t>(row) * a.V + v0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    zd[c] = v0 + c < a.V ? load_f(U, o + c) : -INFINITY;
+                    zt[c] = v0 + c < a.V ? load_f(Tl, o + c) : -INFINITY;
+                }
+                const float* e = a.ef + static_cast<size_t>(row) * a.r;
+                for (int j = 0; j < a.r; ++j) {
+                    const int64_t wrow = static_cast<int64_t>(j) * a.V + v0;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (v0 + c < a.V) zd[c] = fmaf(e[j], load_f(W2, wrow + c), zd[c]);
+                }
+                p = row_epilogue<PASS, 4>(a, row, v0, zd, zt);
+            }
+            if (PASS == kPass3) continue;
+            for (int o = 32; o > 0; o >>= 1) p = rowpart_merge(PASS, p, rowpart_shfl(p, o));
+            if (lane == 0) red[wave] = p;
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                RowPart t = red[0];
+                for (int w = 1; w < static_cast<int>(blockDim.x / kWave); ++w) t = rowpart_merge(PASS, t, red[w]);
+                const size_t o = static_cast<size_t>(cg) * a.Rpad + row;
+                const int nv = PASS == kPass1 ? 5 : 3;
+                for (int q = 0; q < nv; ++q) a.part[q][o] = t.v[q];
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ------------------------------------------------------- row reductions
+
+// Thread = row: merge the P partials of a pass in column order.
+template <int PASS>
+__global__ __launch_bounds__(256) void k_loss_rows(const PassArgs a, float* __restrict__ out0,
+                                                   float* __restrict__ out1, float* __restrict__ out2) {
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= a.R) return;
+    RowPart t = rowpart_empty(PASS);
+    const int nv = PASS == kPass1 ? 5 : 3;
+    for (int p = 0; p < a.P; ++p) {
+        RowPart q = rowpart_empty(PASS);
+        const size_t o = static_cast<size_t>(p) * a.Rpad + row;
+        for (int k = 0; k < nv; ++k) q.v[k] = a.part[k][o];
+        t = rowpart_merge(PASS, t, q);
+    }
+    if (PASS == kPass1) {
+        out0[row] = t.v[0] + logf(t.v[1]);  // lse_d
+        out1[row] = t.v[2] + logf(t.v[3]);  // lse_t
+        out2[row] = t.v[4];                 // z_d at the label
+    } else {
+        out0[row] = t.v[0];  // sum |p_d - p_t|
+        out1[row] = t.v[1];  // sum min(p_d, p_t)
+        out2[row] = t.v[2];  // sum p_d sign(p_d - p_t)
+    }
+}
+
+// Thread = row: Eq 8 (c* as sum min(p_d, p_t), equal to 1 - tv/2 for
+// normalised p, with the delta-table D7 clamp), Eq 9 and Eq 11 terms, the
+// confidence gradient (c* held constant), and w_k/N-weighted loss terms.
+__global__ __launch_bounds__(256) void k_loss_finalize(
+    const float* __restrict__ lse_d, const float* __restrict__ zlab, const float* __restrict__ tv,
+    const float* __restrict__ cmin, const float* __restrict__ alog, const float* __restrict__ rowc,
+    int R, float a_conf, float* __restrict__ c_star, float* __restrict__ conf,
+    float* __restrict__ dconf, float* __restrict__ tce, float* __restrict__ ttv,
+    float* __restrict__ tbce) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= R) return;
+    const float a = alog[i];
+    const float cs = fminf(1.0f, fmaxf(0.0f, cmin[i]));
+    const float c = 1.0f / (1.0f + expf(-a));
+    // -(c* log c + (1 - c*) log(1 - c)) = softplus(a) - c* a
+    const float softplus = fmaxf(a, 0.0f) + log1pf(expf(-fabsf(a)));
+    const float bce = softplus - cs * a;
+    const float ce = lse_d[i] - zlab[i];
+    const float w = rowc[i];
+    const bool ok = !isnan(a);  // invalid token ids make every loss NaN
+    c_star[i] = ok ? cs : NAN;
+    if (conf) conf[i] = c;
+    if (dconf) dconf[i] = ok ? w * a_conf * (c - cs) : NAN;
+    tce[i] = ok ? w * ce : NAN;
+    ttv[i] = ok ? w * tv[i] : NAN;
+    tbce[i] = ok ? w * bce : NAN;
+}
+
+// One workgroup: L_ce, L_tv, L_conf (each already carries w_k / N) in a
+// fixed order, then L = alpha . (L_ce, L_tv, L_conf).
+__global__ __launch_bounds__(256) void k_loss_sum(const float* __restrict__ tce,
+                                                  const float* __restrict__ ttv,
+                                                  const float* __restrict__ tbce, int R,
+                                                  float a_ce, float a_tv, float a_conf,
+                                                  float* __restrict__ loss4) {
+    __shared__ float red[16];
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
+    for (int i = threadIdx.x; i < R; i += blockDim.x) {
+        s0 += tce[i];
+        s1 += ttv[i];
+        s2 += tbce[i];
+    }
+    s0 = block_sum(s0, red);
+    s1 = block_sum(s1, red);
+    s2 = block_sum(s2, red);
+    if (threadIdx.x == 0) {
+        loss4[0] = a_ce * s0 + a_tv * s1 + a_conf * s2;
+        loss4[1] = s0;
+        loss4[2] = s1;
+        loss4[3] = s2;
+    }
+}
+
+// ------------------------------------------------------------------ dW2
+
+// dW2[j, v] = sum_i E[i, j] dZ[i, v].  Workgroup = 64 columns, wave w = rows
+// j in [16w, 16w + 16) of dW2.  Each 32-row slice of dZ is staged in LDS and
+// read back by every wave as B-operand fragments (8 consecutive rows of one
+// column per lane, transposed with v_perm as for W2); A = E^T from its
+// transposed copy.  A float32 dZ is split into bf16 hi + lo, so the product
+// keeps about 16 bits of dZ's mantissa.
+template <int DZF32>
+__global__ __launch_bounds__(1024) void k_dw2_mfma(const void* __restrict__ dz,
+                                                   const uint16_t* __restrict__ et, int V, int r,
+                                                   int R, int Rpad, float* __restrict__ dW2) {
+    constexpr int kEl = DZF32 ? 4 : 2;                 // bytes per dZ element
+    __shared__ __attribute__((aligned(16))) uint8_t S[32 * 64 * kEl];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int vt = blockIdx.x * 64;
+    const int jb = wave * 16;
+    f32x4 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int vbytes = 64 * kEl;
+    for (int i0 = 0; i0 < Rpad; i0 += 32) {
+        __syncthreads();
+        // 32 rows x 64 columns of dZ -> LDS (zero outside R x V)
+        for (int t = threadIdx.x; t < 32 * (vbytes / 16); t += blockDim.x) {
+            const int rr = t / (vbytes / 16), cc = t % (vbytes / 16);
+            const int row = i0 + rr, col = vt + cc * (16 / kEl);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row < R && col < V) {
+                const uint8_t* src = static_cast<const uint8_t*>(dz) + (static_cast<size_t>(row) * V + col) * kEl;
+                v = *reinterpret_cast<const u32x4*>(src);
+            }
+            *reinterpret_cast<u32x4*>(&S[rr * vbytes + cc * 16]) = v;
+        }
+        __syncthreads();
+        if (jb >= r) continue;
+        // A: E^T rows jb + n, columns (rows of E) i0 + 8g .. i0 + 8g + 7
+        const u32x4 ev = *reinterpret_cast<const u32x4*>(et + static_cast<size_t>(jb + n) * Rpad + i0 + 8 * g);
+        const bf16x8 aop = __builtin_bit_cast(bf16x8, ev);
+        // B: rows i0 + 8g + e, columns vt + 4n + c
+        uint32_t hi[4][4], lo[4][4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            float x0[4], x1[4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rr = 8 * g + 2 * p + h;
+                float* x = h ? x1 : x0;
+                if (DZF32) {
+                    const f32x4 q = *reinterpret_cast<const f32x4*>(&S[rr * vbytes + 4 * n * 4]);
+                    x[0] = q[0]; x[1] = q[1]; x[2] = q[2]; x[3] = q[3];
+                } else {
+                    const uint2 q = *reinterpret_cast<const uint2*>(&S[rr * vbytes + 4 * n * 2]);
+                    x[0] = lo_bf16(q.x); x[1] = hi_bf16(q.x); x[2] = lo_bf16(q.y); x[3] = hi_bf16(q.y);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t h0 = f32_to_bf16(x0[c]), h1 = f32_to_bf16(x1[c]);
+                hi[c][p] = h0 | (h1 << 16);
+                if (DZF32) {
+                    const uint32_t l0 = f32_to_bf16(x0[c] - __uint_as_float(h0 << 16));
+                    const uint32_t l1 = f32_to_bf16(x1[c] - __uint_as_float(h1 << 16));
+                    lo[c][p] = l0 | (l1 << 16);
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 bh = {hi[c][0], hi[c][1], hi[c][2], hi[c][3]};
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bh), acc[c], 0, 0, 0);
+            if (DZF32) {
+                const u32x4 bl = {lo[c][0], lo[c][1], lo[c][2], lo[c][3]};
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bl), acc[c], 0, 0, 0);
+            }
+        }
+    }
+    if (jb >= r) return;
+    // lane (g, n): dW2 rows jb + 4g + q, columns vt + 4n + c
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j = jb + 4 * g + q;
+        const int v = vt + 4 * n;
+        if (v < V) {
+            float* dst = dW2 + static_cast<size_t>(j) * V + v;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0][q], acc[1][q], acc[2][q], acc[3][q]};
+        }
+    }
+}
+
+// Vector dW2: thread = (row j of dW2, column v), plain sum over rows.
+template <typename DZ>
+__global__ __launch_bounds__(256) void k_dw2_generic(const DZ* __restrict__ dz,
+                                                     const float* __restrict__ ef, int V, int r,
+                                                     int R, float* __restrict__ dW2) {
+    const int v = blockIdx.x * blockDim.x + threadIdx.x;
+    const int j = blockIdx.y;
+    if (v >= V) return;
+    float acc = 0.0f;
+    for (int i = 0; i < R; ++i) acc = fmaf(ef[static_cast<size_t>(i) * r + j], load_f(dz, static_cast<int64_t>(i) * V + v), acc);
+    dW2[static_cast<size_t>(j) * V + v] = acc;
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int PASS>
+static void launch_pass(const LossArgs& la, const LossLayout& L, PassArgs& a, int grid) {
+    const int r = la.dims.r;
+    if (L.mfma) {
+        switch (r / 32) {
+            case 1: hipLaunchKernelGGL((k_loss_mfma<1, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 2: hipLaunchKernelGGL((k_loss_mfma<2, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 3: hipLaunchKernelGGL((k_loss_mfma<3, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 4: hipLaunchKernelGGL((k_loss_mfma<4, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 5: hipLaunchKernelGGL((k_loss_mfma<5, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 6: hipLaunchKernelGGL((k_loss_mfma<6, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 7: hipLaunchKernelGGL((k_loss_mfma<7, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            default: hipLaunchKernelGGL((k_loss_mfma<8, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
+        }
+    } else if (la.dims.dtype == DSPARK_BF16) {
+        hipLaunchKernelGGL((k_loss_generic<uint16_t, PASS>), dim3(grid), dim3(256), 0, la.stream, a);
+    } else {
+        hipLaunchKernelGGL((k_loss_generic<float, PASS>), dim3(grid), dim3(256), 0, la.stream, a);
+    }
+}
+
+template <typename T>
+static hipError_t launch_loss_t(const LossArgs& la) {
+    const dspark_dims& D = la.dims;
+    const LossLayout L = loss_layout(D);
+    char* ws = la.ws;
+    const int R = L.R;
+    auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+
+    LossConsts cst{};
+    for (int q = 0; q < 3; ++q) cst.alpha[q] = la.alpha[q];
+    for (int k = 0; k < D.gamma; ++k) cst.pos_weight[k] = la.pos_weight[k] / static_cast<float>(D.B);
+
+    hipLaunchKernelGGL((k_loss_prep<T>), dim3(L.Rpad), dim3(256), 0, la.stream, la.anchor, la.labels,
+                       static_cast<const T*>(la.W1), static_cast<const T*>(la.w_conf),
+                       static_cast<const T*>(la.h), D.V, D.r, D.d, D.gamma, R, L.Rpad, cst,
+                       reinterpret_cast<int32_t*>(ws + L.bad), reinterpret_cast<uint16_t*>(ws + L.ebf),
+                       F(L.ef), reinterpret_cast<uint16_t*>(ws + L.et),
+                       reinterpret_cast<int32_t*>(ws + L.label), F(L.rowc), F(L.alog));
+
+    PassArgs a{};
+    a.U = static_cast<const uint16_t*>(la.U);
+    a.T = static_cast<const uint16_t*>(la.T_logits);
+    a.Ug = la.U;
+    a.Tg = la.T_logits;
+    a.W2g = la.W2;
+    a.W2 = static_cast<const uint16_t*>(la.W2);
+    a.ebf = reinterpret_cast<const uint16_t*>(ws + L.ebf);
+    a.ef = F(L.ef);
+    a.V = D.V; a.r = D.r; a.R = R; a.Rpad = L.Rpad; a.P = L.P; a.nrc = L.nrc; a.rb_per_chunk = L.rb_per_chunk;
+    a.label = reinterpret_cast<const int32_t*>(ws + L.label);
+    a.lse_d = F(L.lse_d); a.lse_t = F(L.lse_t); a.S = F(L.S); a.rowc = F(L.rowc);
+    for (int q = 0; q < 5; ++q) a.part[q] = F(L.part[q]);
+    a.dz = la.dlogits;
+    a.dz_bf16 = la.dlogits_dtype == DSPARK_BF16;
+    a.a_ce = la.alpha[0];
+    a.a_tv = la.alpha[1];
+    const int grid = std::min(L.P * L.nrc, 2048);
+    const int rgrid = (R + 255) / 256;
+
+    hipError_t pe = profile_begin(la.stream);
+    if (pe != hipSuccess) return pe;
+    launch_pass<kPass1>(la, L, a, grid);
+    if ((pe = profile_end(la.stream)) != hipSuccess) return pe;
+    hipLaunchKernelGGL((k_loss_rows<kPass1>), dim3(rgrid), dim3(256), 0, la.stream, a, F(L.lse_d),
+                       F(L.lse_t), F(L.zlab));
+    if ((pe = profile_begin(la.stream)) != hipSuccess) return pe;
+    launch_pass<kPass2>(la, L, a, grid);
+    if ((pe = profile_end(la.stream)) != hipSuccess) return pe;
+    hipLaunchKernelGGL((k_loss_rows<kPass2>), dim3(rgrid), dim3(256), 0, la.stream, a, F(L.tv),
+                       F(L.cmin), F(L.S));
+    hipLaunchKernelGGL(k_loss_finalize, dim3(rgrid), dim3(256), 0, la.stream, F(L.lse_d), F(L.zlab),
+                       F(L.tv), F(L.cmin), F(L.alog), F(L.rowc), R, la.alpha[2], la.c_star, la.conf,
+                       la.dconf_logit, F(L.tce), F(L.ttv), F(L.tbce));
+    hipLaunchKernelGGL(k_loss_sum, dim3(1), dim3(256), 0, la.stream, F(L.tce), F(L.ttv), F(L.tbce), R,
+                       la.alpha[0], la.alpha[1], la.alpha[2], la.loss4);
+    if (la.dlogits) {
+        if ((pe = profile_begin(la.stream)) != hipSuccess) return pe;
+        launch_pass<kPass3>(la, L, a, grid);
+        if ((pe = profile_end(la.stream)) != hipSuccess) return pe;
+    }
+    if (la.dW2) {
+        if (L.mfma) {
+            if (a.dz_bf16)
+                hipLaunchKernelGGL((k_dw2_mfma<0>), dim3((D.V + 63) / 64), dim3(64 * (D.r / 16)), 0,
+                                   la.stream, la.dlogits, reinterpret_cast<const uint16_t*>(ws + L.et),
+                                   D.V, D.r, R, L.Rpad, la.dW2);
+            else
+                hipLaunchKernelGGL((k_dw2_mfma<1>), dim3((D.V + 63) / 64), dim3(64 * (D.r / 16)), 0,
+                                   la.stream, la.dlogits, reinterpret_cast<const uint16_t*>(ws + L.et),
+                                   D.V, D.r, R, L.Rpad, la.dW2);
+        } else if (a.dz_bf16) {
+            hipLaunchKernelGGL((k_dw2_generic<uint16_t>), dim3((D.V + 255) / 256, D.r), dim3(256), 0,
+                               la.stream, static_cast<const uint16_t*>(la.dlogits), F(L.ef), D.V, D.r, R,
+                               la.dW2);
+        } else {
+            hipLaunchKernelGGL((k_dw2_generic<float>), dim3((D.V + 255) / 256, D.r), dim3(256), 0,
+                               la.stream, static_cast<const float*>(la.dlogits), F(L.ef), D.V, D.r, R,
+                               la.dW2);
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_loss(const LossArgs& a) {
+    if (a.dims.dtype == DSPARK_BF16) return launch_loss_t<uint16_t>(a);
+    return launch_loss_t<float>(a);
+}
+
+}  // namespace dspark
