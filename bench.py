@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 WORKLOAD_CFG = 2
 COUNTERS = os.path.join(ROOT, "profiles", "stream_kernel_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "semi_autoregressive_draft_markov_amd", "csrc", f)
-                  for f in ("draft.hip", "device_common.h")]
+                  for f in ("draft.hip", "draft_persistent.hip", "mfma_tile.h", "device_common.h")]
 
 
 def kernel_source_hash() -> str:
@@ -40,16 +40,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the stream kernel from committed rocprofv3
-    counter runs (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel
-    calibration), or None if absent or taken on a different kernel source."""
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None
+    if absent, taken on another kernel, or on a different kernel source."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_hash") != kernel_source_hash():
+    if c.get("kernel_source_hash") != kernel_source_hash() or c.get("kernel") != kernel:
         return None
     return c.get("bytes_per_launch")
 
@@ -99,6 +99,63 @@ def copy_calibration() -> int:
     return 0
 
 
+def bench_loss(args) -> int:
+    """Teacher-forced loss over the Qwen3-8B-shaped workload: 1024 blocks x
+    7 positions = 7168 rows, V = 151936, r = 256, d = 4096, bf16 inputs,
+    bf16 dlogits and float32 dW2.  A step is one dspark_block_loss call."""
+    import torch
+
+    import synth
+    from semi_autoregressive_draft_markov_amd import binding, ops
+
+    binding.load()
+    dev = torch.device("cuda:0")
+    inp = synth.config_inputs(3)
+    t = synth.to_torch(inp, dev)
+    R, V, r = inp.B * inp.gamma, inp.V, inp.r
+    out = ops.block_loss(t["U"], t["target"], t["h"], t["anchor"], t["labels"], t["W1"], t["W2"],
+                         t["w_conf"], dlogits_dtype="bf16")
+    dims, ws = out["_dims"], out["_ws"]
+
+    def step():
+        binding.dspark_block_loss(dims, t["U"], t["target"], t["h"], t["anchor"], t["labels"],
+                                  t["W1"], t["W2"], t["w_conf"], None, None, out["loss4"],
+                                  out["c_star"], out["conf"], out["dlogits"], "bf16", out["dW2"],
+                                  out["dconf_logit"], ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    binding.dspark_profile_enable(True)
+    binding.dspark_profile_read()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    pass_ms, launches = binding.dspark_profile_read()
+    binding.dspark_profile_enable(False)
+    # three passes: read U and T each; the third also writes bf16 dlogits
+    alg_bytes = 3 * 2 * R * V * 2 + R * V * 2
+    pass_s = pass_ms * 1e-3 / args.steps
+    line = {
+        "metric": "teacher-forced rows/s (V=151936, r=256, γ=7, 7168 rows)",
+        "value": round(R * args.steps / el, 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(el * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-8b-shaped teacher-forced loss", "V": V, "r": r,
+                   "d": inp.d, "gamma": inp.gamma, "N": inp.B, "dlogits": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(alg_bytes / pass_s / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg_bytes / pass_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_loss_mfma passes 1-3", "passes_ms": round(pass_ms / args.steps, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def synth_subset(inp, idx):
     import synth
     return synth.subset(inp, idx)
@@ -111,6 +168,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time of the CPU oracle sample (0 skips it)")
+    ap.add_argument("--workload", default="qwen3-4b",
+                    choices=["qwen3-4b", "qwen3-14b", "gemma4-rnn", "qwen3-8b-loss"],
+                    help="qwen3-4b (default) is the reported workload; the others are "
+                         "extra measurements of the same kernels at the other shapes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the benchmark, run a plain device copy of 1 GiB "
                          "(reference for HBM byte counters)")
@@ -124,6 +185,9 @@ def main() -> int:
               "(blocks are independent); run it with --gpus 1", file=sys.stderr)
         return 2
 
+    if args.workload == "qwen3-8b-loss":
+        return bench_loss(args)
+
     import numpy as np
     import torch
 
@@ -133,10 +197,11 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
     dev = torch.device("cuda:0")
-    inp = synth.config_inputs(WORKLOAD_CFG)
+    cfg = {"qwen3-4b": 2, "qwen3-14b": 4, "gemma4-rnn": 5}[args.workload]
+    inp = synth.config_inputs(cfg)
     t = synth.to_torch(inp, dev)
     B, gamma, V, r, d = inp.B, inp.gamma, inp.V, inp.r, inp.d
-    dims = ops.draft_dims(t["U"], t["h"], t["W1"])
+    dims = ops.draft_dims(t["U"], t["h"], t["W1"], t["W_rnn"])
     ws = ops.workspace(dims, binding.DSPARK_CALL_DRAFT, dev)
     out = dict(tokens=torch.empty((B, gamma), dtype=torch.int32, device=dev),
                logp=torch.empty((B, gamma), dtype=torch.float32, device=dev),
@@ -146,7 +211,7 @@ def main() -> int:
 
     def step(i):
         binding.dspark_draft_block(dims, t["U"], t["h"], t["anchor"], t["W1"], t["W2"],
-                                   t["w_conf"], None, t["temperature"], 0, i, out["tokens"],
+                                   t["w_conf"], t["W_rnn"], t["temperature"], 0, i, out["tokens"],
                                    out["logp"], out["conf"], out["survival"], ws, stream=stream)
 
     for i in range(args.warmup):
@@ -162,17 +227,27 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     kernel_ms, launches = binding.dspark_profile_read()
     binding.dspark_profile_enable(False)
-    assert launches == args.steps * gamma, (launches, args.steps)
+    per_call = launches // args.steps
+    assert per_call * args.steps == launches and per_call in (1, gamma), (launches, args.steps)
     tokens = out["tokens"].cpu().numpy()
     assert np.all((tokens >= 0) & (tokens < V)), "bad tokens"
 
     ms_per_step = elapsed * 1e3 / args.steps
     value = B * gamma * args.steps / elapsed
     avg_kernel_s = kernel_ms * 1e-3 / launches
-    # algorithmic bytes of one stream launch: all of W2 plus the step's slice of U
-    alg_bytes = (r + B) * V * 2
+    if per_call == 1:
+        # single-launch driver: W2 is read once per call, every step's U slice once
+        driver, kname = "single-launch", "k_draft_persistent<8>"
+        alg_bytes = (r + gamma * B) * V * 2
+    else:
+        # per-step driver: every step streams all of W2 plus its slice of U
+        driver, kname = "per-step", "k_stream_mfma<8,%d>" % (2 if inp.head == "rnn" else 1)
+        alg_bytes = (r + B) * V * 2
+    names = {"qwen3-4b": "qwen3-4b-shaped markov-head block sampling",
+             "qwen3-14b": "qwen3-14b-shaped markov-head block sampling, half greedy",
+             "gemma4-rnn": "gemma4-12b-shaped rnn-head block sampling"}
     achieved = alg_bytes / avg_kernel_s / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(kname)
 
     line = {
         "metric": METRIC,
@@ -187,12 +262,13 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "qwen3-4b-shaped markov-head block sampling",
-                   "V": V, "r": r, "d": d, "gamma": gamma, "B": B, "temperature": 1.0,
-                   "parallelism": "single-gpu"},
+        "config": {"workload": names[args.workload],
+                   "V": V, "r": r, "d": d, "gamma": gamma, "B": B,
+                   "head": inp.head, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "k_stream_mfma<8,1>",
+                     "traffic": traffic if args.workload == "qwen3-4b" else None,
+                     "kernel": kname, "driver": driver,
                      "kernel_us": round(avg_kernel_s * 1e6, 3),
                      "algorithmic_bytes_per_launch": alg_bytes},
     }

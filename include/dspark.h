@@ -162,6 +162,16 @@ dspark_status dspark_block_loss(const dspark_dims* dims, const void* U, const vo
 dspark_status dspark_read_device_error(const dspark_dims* dims, const void* workspace,
                                        int32_t* code, void* hip_stream);
 
+/* Per-thread options.  DSPARK_OPT_DRAFT_PATH selects how dspark_draft_block
+ * runs the gamma steps: 0 (default) = the single-launch kernel when the
+ * problem fits it (Markov head, bf16, r in {32, 64, 128, 256}, V % 8 == 0,
+ * W2 fits in the registers and LDS of the device), else one launch per
+ * step; 1 = always one launch per step; 2 = always the single-launch kernel
+ * (DSPARK_EUNSUPPORTED when the problem does not fit it).  Both paths give
+ * the same results.  Returns DSPARK_EINVAL for an unknown option or value. */
+#define DSPARK_OPT_DRAFT_PATH 1
+dspark_status dspark_set_option(int option, int value);
+
 /* Kernel timing for measurement.  While enabled on the calling thread, each
  * dspark_draft_block / dspark_block_loss call also records a pair of HIP
  * events on `hip_stream` around every launch of its dominant kernel (the

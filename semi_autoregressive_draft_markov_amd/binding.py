@@ -17,6 +17,7 @@ DSPARK_OK, DSPARK_EINVAL, DSPARK_EUNSUPPORTED, DSPARK_EWORKSPACE, DSPARK_EDEVICE
 DSPARK_F32, DSPARK_BF16 = 0, 1
 DSPARK_HEAD_MARKOV, DSPARK_HEAD_RNN = 0, 1
 DSPARK_CALL_DRAFT, DSPARK_CALL_LOSS = 0, 1
+DSPARK_OPT_DRAFT_PATH = 1
 
 STATUS_NAMES = {0: "DSPARK_OK", 1: "DSPARK_EINVAL", 2: "DSPARK_EUNSUPPORTED",
                 3: "DSPARK_EWORKSPACE", 4: "DSPARK_EDEVICE"}
@@ -61,6 +62,8 @@ def load() -> ctypes.CDLL:
     lib.dspark_block_loss.restype = ctypes.c_int
     lib.dspark_read_device_error.argtypes = [D, P, ctypes.POINTER(I32), P]
     lib.dspark_read_device_error.restype = ctypes.c_int
+    lib.dspark_set_option.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.dspark_set_option.restype = ctypes.c_int
     lib.dspark_profile_enable.argtypes = [ctypes.c_int]
     lib.dspark_profile_enable.restype = ctypes.c_int
     lib.dspark_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I32)]
@@ -159,3 +162,7 @@ def dspark_profile_read():
     n = ctypes.c_int32(0)
     _check(load().dspark_profile_read(ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def dspark_set_option(option: int, value: int) -> None:
+    _check(load().dspark_set_option(option, value))

@@ -75,6 +75,9 @@ hipError_t record(hipStream_t s) {
 }
 }  // namespace
 
+thread_local int g_draft_path = 0;
+int draft_path_option() { return g_draft_path; }
+
 bool profiling_enabled() { return g_prof.on; }
 hipError_t profile_begin(hipStream_t s) { return g_prof.on ? record(s) : hipSuccess; }
 hipError_t profile_end(hipStream_t s) { return g_prof.on ? record(s) : hipSuccess; }
@@ -123,6 +126,8 @@ dspark_status dspark_draft_block(const dspark_dims* dims, const void* U, const v
     a.ws = static_cast<char*>(workspace);
     a.stream = static_cast<hipStream_t>(hip_stream);
     const hipError_t e = dspark::launch_draft(a);
+    if (e == hipErrorNotSupported)
+        return fail(DSPARK_EUNSUPPORTED, "the single-launch path does not fit this problem on this device");
     if (e != hipSuccess) return fail(DSPARK_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -198,6 +203,15 @@ dspark_status dspark_read_device_error(const dspark_dims* dims, const void* work
     }
     *code = count;
     return ok();
+}
+
+dspark_status dspark_set_option(int option, int value) {
+    if (option == DSPARK_OPT_DRAFT_PATH) {
+        if (value < 0 || value > 2) return fail(DSPARK_EINVAL, "draft path %d is not 0, 1 or 2", value);
+        dspark::g_draft_path = value;
+        return ok();
+    }
+    return fail(DSPARK_EINVAL, "unknown option %d", option);
 }
 
 dspark_status dspark_profile_enable(int enable) {

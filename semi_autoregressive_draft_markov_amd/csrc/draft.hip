@@ -33,6 +33,18 @@ int draft_partials(const dspark_dims& d) {
                            : (d.V + kGenericCols - 1) / kGenericCols;
 }
 
+// Upper bound on the single-launch grid: two workgroups per compute unit of
+// the current device (256 units if no device can be queried).
+int draft_persist_max_wg() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    return 2 * cus;
+}
+
 DraftLayout draft_layout(const dspark_dims& d) {
     DraftLayout L{};
     L.Bpad = (d.B + 15) / 16 * 16;
@@ -51,6 +63,13 @@ DraftLayout draft_layout(const dspark_dims& d) {
     L.state = take(sizeof(float) * rows * d.r);
     L.gates = take(sizeof(float) * rows * 3 * d.r);
     L.hdot = take(sizeof(float) * static_cast<size_t>(d.B) * d.gamma);
+    L.best = take(sizeof(uint64_t) * 16 * static_cast<size_t>(d.B) * d.gamma);
+    L.bar = take(sizeof(uint32_t) * 64);
+    const size_t nq = 2 * static_cast<size_t>(d.B) * draft_persist_max_wg();
+    L.qm = take(sizeof(float) * nq);
+    L.qs = take(sizeof(float) * nq);
+    L.qkey = take(sizeof(uint64_t) * nq);
+    L.qzx = take(sizeof(float) * nq);
     const size_t np = static_cast<size_t>(d.B) * L.P;
     L.pm = take(sizeof(float) * np);
     L.ps = take(sizeof(float) * np);
@@ -518,6 +537,14 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
 }
 
 hipError_t launch_draft(const DraftArgs& a) {
+    const int opt = draft_path_option();  // 0 auto, 1 multi-kernel, 2 single launch
+    if (opt != 1 && persist_path_ok(a.dims)) {
+        const hipError_t e = launch_draft_persistent(a);
+        if (e == hipSuccess || opt == 2) return e;
+        (void)hipGetLastError();  // fall back to the multi-kernel path
+    } else if (opt == 2) {
+        return hipErrorNotSupported;
+    }
     if (a.dims.dtype == DSPARK_BF16) return launch_draft_t<uint16_t>(a);
     return launch_draft_t<float>(a);
 }

@@ -9,7 +9,7 @@
 
 namespace dspark {
 
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Draft-call workspace carve-up.  Every region starts 256-byte aligned.
 struct DraftLayout {
@@ -22,11 +22,17 @@ struct DraftLayout {
     size_t state;      // f32 [Bpad, r]  RNN state s
     size_t gates;      // f32 [Bpad, 3r] RNN joint projection output
     size_t hdot;       // f32 [B, gamma]  h part of the Eq 7 logit, w[0:d] . h_k
+    size_t best;       // u64 [gamma, B, 16]  argmax keys, one line each (single-launch path)
+    size_t bar;        // u32 [64]  grid barrier: arrivals, timeout flag, release flag
+    size_t qm, qs, qkey, qzx;  // [2, B, max workgroups] step partials (single-launch path)
     size_t pm, ps, pkey, pzx;  // partials [B, P]: max, sum, key (u64), z at key
     size_t total;
 };
 
 bool mfma_path_ok(const dspark_dims& d);
+bool persist_path_ok(const dspark_dims& d);
+int draft_persist_max_wg();
+hipError_t launch_draft_persistent(const struct DraftArgs& a);
 int draft_partials(const dspark_dims& d);
 DraftLayout draft_layout(const dspark_dims& d);
 
@@ -81,6 +87,9 @@ struct DraftArgs {
 
 // Enqueue the whole draft call.  Returns hipSuccess or the first launch error.
 hipError_t launch_draft(const DraftArgs& a);
+
+// Per-thread choice of drafting path (see dspark_set_option).
+int draft_path_option();
 
 // Per-thread event timing of the dominant kernel (see dspark_profile_*).
 bool profiling_enabled();

@@ -26,8 +26,13 @@ def ops():
     return _ops
 
 
-def run_gpu(ops, inp, seed=0, offset=0):
+MULTI, SINGLE = 1, 2  # per-step launches / single-launch kernel
+
+
+def run_gpu(ops, inp, seed=0, offset=0, path=0):
     import torch
+    from semi_autoregressive_draft_markov_amd import binding
+    binding.dspark_set_option(binding.DSPARK_OPT_DRAFT_PATH, path)
     t = synth.to_torch(inp)
     out = ops.draft_block(t["U"], t["h"], t["anchor"], t["W1"], t["W2"], t["w_conf"],
                           t["temperature"], W_rnn=t["W_rnn"], seed=seed, offset=offset)
@@ -55,21 +60,23 @@ def test_tiny_fp32_block(ops, temp):
     check_draft(inp, g, 0, 0, label="tiny fp32")
 
 
-def test_bf16_matrix_core_ragged_mixed_temperature(ops):
+@pytest.mark.parametrize("path", [MULTI, SINGLE])
+def test_bf16_matrix_core_ragged_mixed_temperature(ops, path):
     # V = 1000: 4 workgroups, last one 232 columns; 64-column wave tiles with
     # a 40-column tail; B = 20 pads to 32 block columns.  Strong bias.
     temps = [1.0] * 8 + [0.0] * 6 + [0.7] * 6
     inp = small(temperature=temps)
-    note("case: bf16 mfma V1000 r64 B20 mixed T")
-    g = run_gpu(ops, inp, seed=11, offset=5)
+    note("case: bf16 mfma V1000 r64 B20 mixed T path %d" % path)
+    g = run_gpu(ops, inp, seed=11, offset=5, path=path)
     check_draft(inp, g, 11, 5, label="bf16 mfma ragged")
 
 
+@pytest.mark.parametrize("path", [MULTI, SINGLE])
 @pytest.mark.parametrize("B", [1, 33])
-def test_bf16_rank256_tail_columns(ops, B):
+def test_bf16_rank256_tail_columns(ops, B, path):
     inp = small(V=4104, r=256, d=64, gamma=7, B=B, seed=4)
-    note("case: bf16 mfma V4104 r256 B%d" % B)
-    g = run_gpu(ops, inp, seed=2)
+    note("case: bf16 mfma V4104 r256 B%d path %d" % (B, path))
+    g = run_gpu(ops, inp, seed=2, path=path)
     check_draft(inp, g, 2, 0, label="bf16 r256")
 
 
@@ -98,21 +105,34 @@ def test_zero_confidence_weights(ops):
     assert np.all(g["survival"] == (0.5 ** np.arange(1, 7))[None, :].astype(np.float32))
 
 
-def test_deterministic(ops):
+@pytest.mark.parametrize("path", [MULTI, SINGLE])
+def test_deterministic(ops, path):
     inp = small(V=2048, r=128, B=24, seed=12)
-    a = run_gpu(ops, inp, seed=3)
-    b = run_gpu(ops, inp, seed=3)
+    a = run_gpu(ops, inp, seed=3, path=path)
+    b = run_gpu(ops, inp, seed=3, path=path)
     for k in ("tokens", "logp", "conf", "survival"):
         assert np.array_equal(a[k], b[k], equal_nan=True), k
-    c = run_gpu(ops, inp, seed=3, offset=1)
+    c = run_gpu(ops, inp, seed=3, offset=1, path=path)
     assert not np.array_equal(a["tokens"], c["tokens"])
 
 
-def test_out_of_range_anchor_is_flagged(ops):
+def test_paths_agree(ops):
+    # both drivers compute the same keys; tokens agree exactly and the
+    # float outputs to rounding of the softmax normaliser
+    inp = small(V=4104, r=256, d=64, gamma=7, B=40, seed=13, temperature=[1.0] * 30 + [0.0] * 10)
+    a = run_gpu(ops, inp, seed=9, path=MULTI)
+    b = run_gpu(ops, inp, seed=9, path=SINGLE)
+    assert np.array_equal(a["tokens"], b["tokens"])
+    assert np.allclose(a["logp"], b["logp"], rtol=0, atol=1e-5)
+    assert np.array_equal(a["conf"], b["conf"]) or np.allclose(a["conf"], b["conf"], rtol=1e-6)
+
+
+@pytest.mark.parametrize("path", [MULTI, SINGLE])
+def test_out_of_range_anchor_is_flagged(ops, path):
     from semi_autoregressive_draft_markov_amd import binding
     inp = small(B=5)
     inp.anchor = np.array([3, inp.V, 7, -1, 0], np.int32)
-    g = run_gpu(ops, inp)
+    g = run_gpu(ops, inp, path=path)
     assert np.all(g["tokens"][[1, 3]] == -1)
     assert np.all(np.isnan(g["conf"][[1, 3]]))
     assert np.all(g["tokens"][[0, 2, 4]] >= 0)
@@ -123,15 +143,22 @@ def test_out_of_range_anchor_is_flagged(ops):
                 0, 0, block_ids=[0, 2, 4], label="valid blocks")
 
 
-@pytest.mark.parametrize("dtype,V", [("bf16", 8), ("f32", 4)])
-def test_sampler_law_on_gpu(ops, dtype, V):
+@pytest.mark.parametrize("dtype,V,path", [("bf16", 8, MULTI), ("bf16", 8, SINGLE), ("f32", 4, MULTI)])
+def test_sampler_law_on_gpu(ops, dtype, V, path):
     # GPU block frequencies follow the exact Eq 4 product (chi-square).
     gamma, n = 2, 60000
     inp = small(V=V, r=32, d=8, gamma=gamma, B=1, dtype=dtype, w1_std=0.5, w2_std=0.5,
                 u_std=1.0, seed=5)
-    rep = synth.subset(inp, np.zeros(n, dtype=np.int64))
-    g = run_gpu(ops, rep, seed=77)
-    codes = g["tokens"][:, 0] * V + g["tokens"][:, 1]
+    if path == SINGLE:
+        # the single-launch kernel holds per-block state in LDS: draw the
+        # samples as 200 calls of 300 blocks with distinct noise offsets
+        rep = synth.subset(inp, np.zeros(300, dtype=np.int64))
+        toks = np.concatenate([run_gpu(ops, rep, seed=77, offset=o, path=path)["tokens"]
+                               for o in range(n // 300)])
+    else:
+        rep = synth.subset(inp, np.zeros(n, dtype=np.int64))
+        toks = run_gpu(ops, rep, seed=77, path=path)["tokens"]
+    codes = toks[:, 0] * V + toks[:, 1]
     counts = np.bincount(codes, minlength=V * V)
     blocks = np.array(list(itertools.product(range(V), repeat=gamma)), np.int32)
     probs = np.exp(oracle.block_logprob(synth.subset(inp, np.zeros(len(blocks), np.int64)), blocks))
@@ -144,18 +171,20 @@ def test_sampler_law_on_gpu(ops, dtype, V):
 
 # -------------------------------------------------------------- full sizes
 
-def test_qwen3_4b_shape_all_blocks(ops):
+@pytest.mark.parametrize("path", [MULTI, SINGLE])
+def test_qwen3_4b_shape_all_blocks(ops, path):
     inp = synth.config_inputs(2)
-    note("case: qwen3-4b-shaped V151936 r256 B32 (all blocks)")
-    g = run_gpu(ops, inp, seed=0)
+    note("case: qwen3-4b-shaped V151936 r256 B32 (all blocks) path %d" % path)
+    g = run_gpu(ops, inp, seed=0, path=path)
     info = check_draft(inp, g, 0, 0, label="qwen3-4b shape")
     note("  ties allowed: %d, max |dlogp| %.2e" % (info["ties"], info["logp_err"]))
 
 
-def test_qwen3_14b_shape_sampled_blocks(ops):
+@pytest.mark.parametrize("path", [MULTI, SINGLE])
+def test_qwen3_14b_shape_sampled_blocks(ops, path):
     inp = synth.config_inputs(4)
-    note("case: qwen3-14b-shaped V151936 r256 B256 half greedy (16 sampled blocks)")
-    g = run_gpu(ops, inp, seed=0)
+    note("case: qwen3-14b-shaped V151936 r256 B256 half greedy (16 sampled blocks) path %d" % path)
+    g = run_gpu(ops, inp, seed=0, path=path)
     pick = np.array([0, 1, 37, 64, 100, 126, 127, 128, 129, 150, 200, 201, 222, 250, 254, 255])
     sub = synth.subset(inp, pick)
     check_draft(sub, {k: g[k][pick] for k in ("tokens", "logp", "conf", "survival")}, 0, 0,
