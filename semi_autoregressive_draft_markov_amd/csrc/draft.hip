@@ -65,7 +65,7 @@ DraftLayout draft_layout(const dspark_dims& d) {
     L.hdot = take(sizeof(float) * static_cast<size_t>(d.B) * d.gamma);
     L.best = take(sizeof(uint64_t) * 16 * static_cast<size_t>(d.B) * d.gamma);
     L.bar = take(sizeof(uint32_t) * 64);
-    const size_t nq = 2 * static_cast<size_t>(d.B) * draft_persist_max_wg();
+    const size_t nq = static_cast<size_t>(d.gamma) * d.B * draft_persist_max_wg();
     L.qm = take(sizeof(float) * nq);
     L.qs = take(sizeof(float) * nq);
     L.qkey = take(sizeof(uint64_t) * nq);

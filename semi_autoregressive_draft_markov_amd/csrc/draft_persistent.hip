@@ -16,11 +16,12 @@
 //       workgroup merge -> one 64-bit atomicMax per block on the
 //         (perturbed logit, lowest index) key; softmax partials stored
 //       grid barrier (one monotonic counter, bounded spin, no cache flushes)
-//       read x_k of every block from the keys; designated waves write
-//         x_k, log p_k (from the partials of step k) and c_{k+1}, S_{k+1}
+//       read x_k of every block from the keys; stage W1[x_k] for step k+1
+//   finish (small kernel, grid B x gamma)   x_k, log p_k from the partials,
+//                            c_k and S_k
 //
 // The only cross-workgroup dependency per step is the argmax over V; the
-// softmax normaliser is reduced off that path from double-buffered partials.
+// softmax normaliser and the confidence head are computed after the loop.
 #include <math.h>
 
 #include <algorithm>
@@ -35,7 +36,6 @@ namespace dspark {
 constexpr int kPWaves = 4;        // waves per workgroup
 constexpr int kKeyStride = 16;    // uint64 per argmax key: one 128-byte line each
 constexpr int kReleaseWord = 32;  // barrier release flag, on its own line
-constexpr int kMaxWgPerLane = 16;  // single-launch grid <= 64 x 16 workgroups
 
 struct PersistArgs {
     const uint16_t* U;
@@ -49,7 +49,7 @@ struct PersistArgs {
     uint32_t key0, key1, ctr3;
     uint64_t* best;      // [gamma, B, 16]  argmax keys, one 128-byte line each (cleared by prepare)
     uint32_t* bar;       // [0] arrivals, [1] timeout flag, [32] release flag (cleared by prepare)
-    float* pm;           // [2, B, nWG] softmax partials, double-buffered by step
+    float* pm;           // [gamma, B, nWG] softmax partials of every step
     float* ps;
     uint64_t* pkey;
     float* pzx;
@@ -99,9 +99,10 @@ __global__ __launch_bounds__(256) void k_persist_prepare(
 // ------------------------------------------------------- grid barrier
 
 // Grid barrier number `step` (1, 2, ...).  Everything one workgroup hands
-// to another inside this kernel is a device-scope atomic (the argmax keys,
-// the softmax partials, the barrier words): those are coherent at the device
-// level (sc1), so the barrier needs no L2 write-back or invalidate, which on
+// to another inside this kernel is a device-scope atomic (the argmax keys and
+// the barrier words; the softmax partials are only read after the kernel):
+// those are coherent at the device level (sc1), so the barrier needs no L2
+// write-back or invalidate, which on
 // this chip flush or drop a whole XCD's L2 and cost several microseconds
 // each.  A workgroup-scope release (each wave waits for its own memory
 // operations to complete) and the workgroup barrier come before the arrival;
@@ -131,11 +132,7 @@ __device__ __forceinline__ void grid_barrier(uint32_t* bar, uint32_t step, uint3
     __syncthreads();
 }
 
-// Device-scope (coherent) accesses for data shared across workgroups.
-template <typename T>
-__device__ __forceinline__ void put_shared(T* p, T v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Device-scope (coherent) load of data other workgroups wrote in this kernel.
 template <typename T>
 __device__ __forceinline__ T get_shared(const T* p) {
     return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -288,12 +285,6 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
     };
     stage_rows();
 
-    // designated blocks (emit tokens, logp, conf, survival): block b belongs
-    // to wave 3 of workgroup floor(b * nWG / B) when B <= nWG (wave 3 never
-    // takes a unit of the LDS tile when there are fewer than four 16-block
-    // groups), else spread over all waves
-    const int nwaves = nWG * kPWaves;
-
     for (int k = 0; k < a.gamma; ++k) {
         for (int b = lane; b < a.B; b += 64) slot[wave * a.B + b] = stats_empty();
         // own tile: all block groups; LDS tile: groups nb = wave (mod 4)
@@ -340,7 +331,6 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
         }
         __syncthreads();
         // workgroup merge in wave order, then publish
-        const int buf = k & 1;
         for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
             Stats t = slot[b];
 #pragma unroll
@@ -348,89 +338,83 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
             if (t.key != kKeyNone)
                 __hip_atomic_fetch_max(&a.best[(static_cast<size_t>(k) * a.B + b) * kKeyStride], t.key,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const size_t o = (static_cast<size_t>(buf) * a.B + b) * nWG + wg;
-            put_shared(&a.pm[o], t.m);
-            put_shared(&a.ps[o], t.s);
-            put_shared(&a.pkey[o], t.key);
-            put_shared(&a.pzx[o], t.zx);
+            // softmax partials are read after the kernel (k_persist_finish)
+            const size_t o = (static_cast<size_t>(k) * a.B + b) * nWG + wg;
+            a.pm[o] = t.m;
+            a.ps[o] = t.s;
+            a.pkey[o] = t.key;
+            a.pzx[o] = t.zx;
         }
+        if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
         grid_barrier(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG));
-        __shared__ uint32_t timed_out;
-        if (threadIdx.x == 0)
-            timed_out = __hip_atomic_load(a.bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // x_k of every block from the keys -> the E rows of step k+1
         for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
-            const uint64_t key = __hip_atomic_load(&a.best[(static_cast<size_t>(k) * a.B + b) * kKeyStride],
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t key = get_shared(&a.best[(static_cast<size_t>(k) * a.B + b) * kKeyStride]);
             const uint32_t x = key_index(key);
-            // -1 marks a block with no valid token (kept out of the gathers)
-            prev[b] = (key != kKeyNone && x < static_cast<uint32_t>(a.V)) ? static_cast<int>(x) : -1;
+            prev[b] = (key != kKeyNone && x < static_cast<uint32_t>(a.V)) ? static_cast<int>(x) : 0;
         }
         __syncthreads();
-        // designated blocks read their token before it is clamped for the gathers
-        int my_x[4];
-        int my_b[4];
-        int my_n = 0;
-        if (a.B <= nWG) {
-            if (wave == kPWaves - 1) {
-                const int b0 = (wg * a.B + nWG - 1) / nWG;  // smallest b with floor(b * nWG / B) == wg
-                for (int b = b0; b < a.B && (b * nWG) / a.B == wg && my_n < 4; ++b) {
-                    my_b[my_n] = b;
-                    my_x[my_n++] = prev[b];
-                }
-            }
-        } else {
-            for (int b = wg * kPWaves + wave; b < a.B && my_n < 4; b += nwaves) {
-                my_b[my_n] = b;
-                my_x[my_n++] = prev[b];
-            }
-        }
-        __syncthreads();
-        for (int b = threadIdx.x; b < a.B; b += blockDim.x) prev[b] = prev[b] < 0 ? 0 : prev[b];
-        __syncthreads();
-        if (k + 1 < a.gamma) stage_rows();
+        stage_rows();
+    }
+}
 
-        // designated blocks of this wave (at most 4)
-        {
-            for (int q = 0; q < my_n; ++q) {
-                const int b = my_b[q];
-                const int xr = my_x[q];
-                const bool bad = a.dead[b] != 0 || timed_out != 0 || xr < 0;
-                const int x = bad ? -1 : xr;
-                // log p_k from this step's partials of block b: every load is
-                // issued before the first merge, so the pass costs one memory
-                // round trip rather than one per partial
-                Stats part[kMaxWgPerLane];
-                const size_t base = (static_cast<size_t>(buf) * a.B + b) * nWG;
-#pragma unroll
-                for (int i = 0; i < kMaxWgPerLane; ++i) {
-                    const int p = lane + 64 * i;
-                    part[i] = p < nWG ? Stats{get_shared(&a.pm[base + p]), get_shared(&a.ps[base + p]),
-                                                get_shared(&a.pkey[base + p]), get_shared(&a.pzx[base + p])}
-                                      : stats_empty();
-                }
-                Stats t = part[0];
-#pragma unroll
-                for (int i = 1; i < kMaxWgPerLane; ++i) t = stats_merge(t, part[i]);
-                for (int o = 32; o > 0; o >>= 1) t = stats_merge(t, shfl_xor_stats(t, o));
-                // c_{k+1}: e = W1[x_k], logit = h part + w[d:] . e
-                float ae = 0.0f;
-                if (k + 1 < a.gamma && !bad)
-                    for (int j = lane; j < r; j += 64)
-                        ae += bf16_to_f32(a.w_conf[a.d + j]) * bf16_to_f32(a.W1[static_cast<size_t>(x) * r + j]);
-                for (int o = 32; o > 0; o >>= 1) ae += __shfl_xor(ae, o);
-                if (lane == 0) {
-                    const size_t out = static_cast<size_t>(b) * a.gamma + k;
-                    a.tokens[out] = x;
-                    if (a.logp) a.logp[out] = bad ? NAN : t.zx - (t.m + logf(t.s));
-                    if (k + 1 < a.gamma) {
-                        const float c = bad ? NAN : sigmoidf_(a.hdot[out + 1] + ae);
-                        a.conf[out + 1] = c;
-                        a.survival[out + 1] = a.survival[out] * c;
-                    }
-                    if (bad) a.dead[b] = 1;
-                }
-            }
+// --------------------------------------------------------------- finish
+
+// Workgroup (b, k), after the loop: x_k from the argmax keys, log p_k from
+// the step's softmax partials (merged in workgroup order), c_k (Eq 7 on
+// x_{k-1}) and S_k = c_1 ... c_k.  None of these feed the sampling loop, so
+// they are kept out of it; each workgroup recomputes c_1 .. c_k itself
+// (k <= 64 dot products of length r), which keeps every S_k a fixed-order
+// product without a second pass.
+__global__ __launch_bounds__(256) void k_persist_finish(PersistArgs a, int r) {
+    __shared__ float red[16];
+    __shared__ int xs[64];
+    __shared__ int bad_s;
+    const int b = blockIdx.x, k = blockIdx.y;
+    if (threadIdx.x == 0) {
+        bool bad = a.dead[b] != 0 || a.bar[1] != 0;
+        for (int i = 0; i <= k; ++i) {
+            const uint64_t key = a.best[(static_cast<size_t>(i) * a.B + b) * kKeyStride];
+            const uint32_t x = key_index(key);
+            bad = bad || key == kKeyNone || x >= static_cast<uint32_t>(a.V);
+            xs[i] = static_cast<int>(x);
         }
+        bad_s = bad;
+    }
+    __syncthreads();
+    const bool bad = bad_s != 0;
+    const size_t out = static_cast<size_t>(b) * a.gamma + k;
+    // log p_k
+    Stats t = stats_empty();
+    const size_t base = (static_cast<size_t>(k) * a.B + b) * a.nWG;
+    for (int p = threadIdx.x; p < a.nWG; p += blockDim.x)
+        t = stats_merge(t, Stats{a.pm[base + p], a.ps[base + p], a.pkey[base + p], a.pzx[base + p]});
+    for (int o = 32; o > 0; o >>= 1) t = stats_merge(t, shfl_xor_stats(t, o));
+    __shared__ Stats wred[4];
+    if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Stats m = wred[0];
+        for (int w = 1; w < static_cast<int>(blockDim.x / kWave); ++w) m = stats_merge(m, wred[w]);
+        a.tokens[out] = bad ? -1 : xs[k];
+        if (a.logp) a.logp[out] = bad ? NAN : m.zx - (m.m + logf(m.s));
+        if (bad) a.dead[b] = 1;
+    }
+    // c_1 .. c_k and the survival product
+    float S = a.survival[static_cast<size_t>(b) * a.gamma];  // S_0 = c_0 from prepare
+    float c = S;
+    for (int i = 1; i <= k; ++i) {
+        float part = 0.0f;
+        if (!bad)
+            for (int j = threadIdx.x; j < r; j += blockDim.x)
+                part += bf16_to_f32(a.w_conf[a.d + j]) * bf16_to_f32(a.W1[static_cast<size_t>(xs[i - 1]) * r + j]);
+        const float ae = block_sum(part, red);
+        c = bad ? NAN : sigmoidf_(a.hdot[static_cast<size_t>(b) * a.gamma + i] + ae);
+        S *= c;
+    }
+    if (threadIdx.x == 0 && k > 0) {
+        a.conf[out] = c;
+        a.survival[out] = S;
     }
 }
 
@@ -465,8 +449,7 @@ static PersistPlan plan_for(const dspark_dims& D) {
     const int nWG = std::min(per_cu, 2) * cus;
     const int T = (D.V + 63) / 64;
     if (T > kPWaves * nWG + nWG) return p;  // W2 does not fit on chip
-    if (nWG > draft_persist_max_wg() || nWG > 64 * kMaxWgPerLane) return p;
-    if (D.B > 4 * kPWaves * nWG) return p;  // at most 4 designated blocks per wave
+    if (nWG > draft_persist_max_wg()) return p;
     p.ok = true;
     p.nWG = nWG;
     return p;
@@ -524,7 +507,9 @@ static hipError_t launch_persist_kc(const DraftArgs& A) {
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG),
                                    dim3(256), args, persist_lds<KC>(L.Bpad, D.B), A.stream);
     if (e != hipSuccess) return e;
-    return profile_end(A.stream);
+    if ((e = profile_end(A.stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_persist_finish, dim3(D.B, D.gamma), dim3(256), 0, A.stream, p, D.r);
+    return hipGetLastError();
 }
 
 hipError_t launch_draft_persistent(const DraftArgs& A) {

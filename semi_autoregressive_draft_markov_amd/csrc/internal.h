@@ -24,7 +24,7 @@ struct DraftLayout {
     size_t hdot;       // f32 [B, gamma]  h part of the Eq 7 logit, w[0:d] . h_k
     size_t best;       // u64 [gamma, B, 16]  argmax keys, one line each (single-launch path)
     size_t bar;        // u32 [64]  grid barrier: arrivals, timeout flag, release flag
-    size_t qm, qs, qkey, qzx;  // [2, B, max workgroups] step partials (single-launch path)
+    size_t qm, qs, qkey, qzx;  // [gamma, B, max workgroups] step partials (single-launch path)
     size_t pm, ps, pkey, pzx;  // partials [B, P]: max, sum, key (u64), z at key
     size_t total;
 };
