@@ -172,6 +172,8 @@ def main() -> int:
                     choices=["qwen3-4b", "qwen3-14b", "gemma4-rnn", "qwen3-8b-loss"],
                     help="qwen3-4b (default) is the reported workload; the others are "
                          "extra measurements of the same kernels at the other shapes")
+    ap.add_argument("--launch", default="plain", choices=["plain", "cooperative"],
+                    help="how the single-launch drafting kernel is started (same kernel and grid)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the benchmark, run a plain device copy of 1 GiB "
                          "(reference for HBM byte counters)")
@@ -196,6 +198,7 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
+    binding.dspark_set_option(binding.DSPARK_OPT_PERSIST_LAUNCH, 1 if args.launch == "cooperative" else 0)
     dev = torch.device("cuda:0")
     cfg = {"qwen3-4b": 2, "qwen3-14b": 4, "gemma4-rnn": 5}[args.workload]
     inp = synth.config_inputs(cfg)
@@ -237,7 +240,7 @@ def main() -> int:
     avg_kernel_s = kernel_ms * 1e-3 / launches
     if per_call == 1:
         # single-launch driver: W2 is read once per call, every step's U slice once
-        driver, kname = "single-launch", "k_draft_persistent<8>"
+        driver, kname = "single-launch (%s)" % args.launch, "k_draft_persistent<8>"
         alg_bytes = (r + gamma * B) * V * 2
     else:
         # per-step driver: every step streams all of W2 plus its slice of U

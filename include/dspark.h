@@ -170,6 +170,18 @@ dspark_status dspark_read_device_error(const dspark_dims* dims, const void* work
  * (DSPARK_EUNSUPPORTED when the problem does not fit it).  Both paths give
  * the same results.  Returns DSPARK_EINVAL for an unknown option or value. */
 #define DSPARK_OPT_DRAFT_PATH 1
+/* DSPARK_OPT_PERSIST_LAUNCH selects how the single-launch kernel is started:
+ * 0 (default) = an ordinary launch of a grid with one workgroup per free
+ * slot that the occupancy query reports for the device; 1 =
+ * hipLaunchCooperativeKernel with the same grid (the runtime re-checks that
+ * the grid can be resident; on this hardware it is measurably slower).  The
+ * workgroups meet at grid barriers, so mode 0 assumes that kernels running
+ * concurrently on other streams do not hold the compute units for long: a
+ * workgroup that cannot become resident only delays the call, but if the
+ * barrier wait exceeds about half a second per step the call gives up and
+ * reports every block invalid (tokens -1, counted by
+ * dspark_read_device_error) instead of hanging. */
+#define DSPARK_OPT_PERSIST_LAUNCH 2
 dspark_status dspark_set_option(int option, int value);
 
 /* Kernel timing for measurement.  While enabled on the calling thread, each

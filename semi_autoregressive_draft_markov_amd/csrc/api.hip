@@ -76,7 +76,9 @@ hipError_t record(hipStream_t s) {
 }  // namespace
 
 thread_local int g_draft_path = 0;
+thread_local int g_persist_launch = 0;
 int draft_path_option() { return g_draft_path; }
+int persist_launch_option() { return g_persist_launch; }
 
 bool profiling_enabled() { return g_prof.on; }
 hipError_t profile_begin(hipStream_t s) { return g_prof.on ? record(s) : hipSuccess; }
@@ -209,6 +211,11 @@ dspark_status dspark_set_option(int option, int value) {
     if (option == DSPARK_OPT_DRAFT_PATH) {
         if (value < 0 || value > 2) return fail(DSPARK_EINVAL, "draft path %d is not 0, 1 or 2", value);
         dspark::g_draft_path = value;
+        return ok();
+    }
+    if (option == DSPARK_OPT_PERSIST_LAUNCH) {
+        if (value < 0 || value > 1) return fail(DSPARK_EINVAL, "launch mode %d is not 0 or 1", value);
+        dspark::g_persist_launch = value;
         return ok();
     }
     return fail(DSPARK_EINVAL, "unknown option %d", option);

@@ -63,8 +63,8 @@ DraftLayout draft_layout(const dspark_dims& d) {
     L.state = take(sizeof(float) * rows * d.r);
     L.gates = take(sizeof(float) * rows * 3 * d.r);
     L.hdot = take(sizeof(float) * static_cast<size_t>(d.B) * d.gamma);
-    L.best = take(sizeof(uint64_t) * 16 * static_cast<size_t>(d.B) * d.gamma);
-    L.bar = take(sizeof(uint32_t) * 64);
+    L.best = take(sizeof(uint64_t) * 16 * kDraftKeyCopies * static_cast<size_t>(d.B) * d.gamma);
+    L.bar = take(sizeof(uint32_t) * kDraftBarWords);
     const size_t nq = static_cast<size_t>(d.gamma) * d.B * draft_persist_max_wg();
     L.qm = take(sizeof(float) * nq);
     L.qs = take(sizeof(float) * nq);

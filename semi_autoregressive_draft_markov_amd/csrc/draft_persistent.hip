@@ -1,24 +1,22 @@
 // Single-launch DSpark block drafting (Markov head, bf16, matrix cores):
 // the whole left-to-right loop of Eq 4/5 (DSpark paper as transcribed on the
-// dormouse "DSpark - paper verification" page, section 1) in one cooperative
+// dormouse "DSpark - paper verification" page, section 1) in one persistent
 // kernel, with W2 loaded from HBM once per call instead of once per step.
 //
-//   prepare (small kernel)   h part of every confidence logit, c_1, S_1,
-//                            token checks; clears the argmax keys and the
-//                            barrier counter
+//   prepare (one workgroup)  clears the argmax keys and the barrier words
 //   persistent kernel, grid = every workgroup that can be resident:
 //     load: wave w keeps W2 tile w (64 columns) in registers as MFMA
 //           A-fragments; tiles beyond 4 x grid live, pre-transposed, in the
 //           LDS of workgroup (tile - 4 x grid)
 //     for k = 0 .. gamma-1:
 //       every (tile, 16-block group): bias by MFMA from E = W1[x_{k-1}],
-//         + U_k, Gumbel-max statistics (see lane_stats16)
+//         + U_k, Gumbel-max statistics (see lane_stats16p)
 //       workgroup merge -> one 64-bit atomicMax per block on the
 //         (perturbed logit, lowest index) key; softmax partials stored
 //       grid barrier (one monotonic counter, bounded spin, no cache flushes)
 //       read x_k of every block from the keys; stage W1[x_k] for step k+1
-//   finish (small kernel, grid B x gamma)   x_k, log p_k from the partials,
-//                            c_k and S_k
+//   finish (grid B)          x_k, log p_k from the partials, the Eq 7
+//                            confidences c_k and the survival products S_k
 //
 // The only cross-workgroup dependency per step is the argmax over V; the
 // softmax normaliser and the confidence head are computed after the loop.
@@ -34,8 +32,13 @@
 namespace dspark {
 
 constexpr int kPWaves = 4;        // waves per workgroup
-constexpr int kKeyStride = 16;    // uint64 per argmax key: one 128-byte line each
-constexpr int kReleaseWord = 32;  // barrier release flag, on its own line
+constexpr int kKeyStride = 16;    // uint64 per argmax key copy: one 128-byte line each
+constexpr int kBarGroups = 8;     // arrival counters at bar[32 g]
+constexpr int kBarTop = 256;      // arrivals of the last workgroup of each group
+constexpr int kReleaseWord = 288; // barrier release flag
+constexpr int kTimeoutWord = 320; // set when a barrier wait gave up
+static_assert(kTimeoutWord < kDraftBarWords, "barrier words");
+constexpr int kMaxGamma = 64;     // largest gamma the C ABI accepts
 
 struct PersistArgs {
     const uint16_t* U;
@@ -44,11 +47,11 @@ struct PersistArgs {
     const uint16_t* w_conf;
     const int32_t* anchor;
     const float* temperature;
-    const float* hdot;   // [B, gamma]
-    int V, d, gamma, B, Bpad, T, nWG;
+    const uint16_t* h;   // [B, gamma, d]
+    int V, r, d, gamma, B, Bpad, nWG;
     uint32_t key0, key1, ctr3;
-    uint64_t* best;      // [gamma, B, 16]  argmax keys, one 128-byte line each (cleared by prepare)
-    uint32_t* bar;       // [0] arrivals, [1] timeout flag, [32] release flag (cleared by prepare)
+    uint64_t* best;      // [gamma, B, copies, 16]  argmax keys, one 128-byte line each (cleared by prepare)
+    uint32_t* bar;       // barrier words (cleared by prepare)
     float* pm;           // [gamma, B, nWG] softmax partials of every step
     float* ps;
     uint64_t* pkey;
@@ -62,38 +65,11 @@ struct PersistArgs {
 
 // -------------------------------------------------------------- prepare
 
-// Grid (B, gamma): w[0:d] . h_{b,k}; workgroups (b, 0) also check the
-// anchor and emit c_1, S_1; workgroup (0, 0) clears keys and the barrier.
-__global__ __launch_bounds__(256) void k_persist_prepare(
-    const int32_t* __restrict__ anchor, const uint16_t* __restrict__ W1,
-    const uint16_t* __restrict__ w_conf, const uint16_t* __restrict__ h, int V, int r, int d,
-    int gamma, int B, float* __restrict__ hdot, int32_t* __restrict__ dead,
-    uint64_t* __restrict__ best, uint32_t* __restrict__ bar, float* __restrict__ conf,
-    float* __restrict__ survival) {
-    __shared__ float red[16];
-    const int b = blockIdx.x, k = blockIdx.y;
-    if (b == 0 && k == 0) {
-        for (int i = threadIdx.x; i < gamma * B; i += blockDim.x) best[static_cast<size_t>(i) * kKeyStride] = kKeyNone;
-        if (threadIdx.x < 64) bar[threadIdx.x] = 0u;
-    }
-    const int64_t hrow = (static_cast<int64_t>(b) * gamma + k) * d;
-    float hp = 0.0f;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) hp += bf16_to_f32(w_conf[i]) * bf16_to_f32(h[hrow + i]);
-    const float hk = block_sum(hp, red);
-    if (threadIdx.x == 0) hdot[static_cast<size_t>(b) * gamma + k] = hk;
-    if (k != 0) return;
-    const int prev = anchor[b];
-    const bool bad = prev < 0 || prev >= V;
-    float part = 0.0f;
-    for (int j = threadIdx.x; j < r; j += blockDim.x)
-        part += bad ? 0.0f : bf16_to_f32(w_conf[d + j]) * bf16_to_f32(W1[static_cast<size_t>(prev) * r + j]);
-    const float ae = block_sum(part, red);
-    if (threadIdx.x == 0) {
-        dead[b] = bad ? 1 : 0;
-        const float c = bad ? NAN : sigmoidf_(hk + ae);
-        conf[static_cast<size_t>(b) * gamma] = c;
-        survival[static_cast<size_t>(b) * gamma] = c;
-    }
+// One workgroup: clears the argmax key copies and the barrier words.
+__global__ __launch_bounds__(256) void k_persist_prepare(int n_keys, uint64_t* __restrict__ best,
+                                                         uint32_t* __restrict__ bar) {
+    for (int i = threadIdx.x; i < n_keys; i += blockDim.x) best[static_cast<size_t>(i) * kKeyStride] = kKeyNone;
+    for (int i = threadIdx.x; i < kDraftBarWords; i += blockDim.x) bar[i] = 0u;
 }
 
 // ------------------------------------------------------- grid barrier
@@ -102,28 +78,37 @@ __global__ __launch_bounds__(256) void k_persist_prepare(
 // to another inside this kernel is a device-scope atomic (the argmax keys and
 // the barrier words; the softmax partials are only read after the kernel):
 // those are coherent at the device level (sc1), so the barrier needs no L2
-// write-back or invalidate, which on
-// this chip flush or drop a whole XCD's L2 and cost several microseconds
-// each.  A workgroup-scope release (each wave waits for its own memory
-// operations to complete) and the workgroup barrier come before the arrival;
-// the workgroup whose arrival completes the count publishes `step` on a
-// separate release line, which the others poll about every 0.5 us (polling
-// one line back-to-back from hundreds of workgroups slows the stragglers).
-// The wait is bounded: after ~2^20 polls bar[1] is set and the workgroup
+// write-back or invalidate, which on this chip flush or drop a whole XCD's L2
+// and cost several microseconds each.  A workgroup-scope release (each wave
+// waits for its own memory operations, the key atomics included, to
+// complete) and the workgroup barrier come before the arrival.  Arrivals
+// are counted in two levels to spread the contention: workgroup wg adds to
+// counter wg % 8; the workgroup that completes its group's count adds to the
+// top counter, and the one that completes that publishes `step` on a
+// release line, which the others poll about every 0.5 us.  The wait is
+// bounded: after ~2^20 polls the timeout word is set and the workgroup
 // proceeds, so a broken launch cannot hang the device.
-__device__ __forceinline__ void grid_barrier(uint32_t* bar, uint32_t step, uint32_t nwg) {
+__device__ __forceinline__ void grid_barrier(uint32_t* bar, uint32_t step, uint32_t nwg, uint32_t wg) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t before = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (before + 1 == step * nwg) {
+        const uint32_t grp = wg % kBarGroups;
+        const uint32_t gsize = (nwg - grp + kBarGroups - 1) / kBarGroups;
+        const uint32_t ngroups = nwg < kBarGroups ? nwg : kBarGroups;
+        bool release = false;
+        const uint32_t before = __hip_atomic_fetch_add(bar + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (before + 1 == step * gsize) {
+            const uint32_t top = __hip_atomic_fetch_add(bar + kBarTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            release = top + 1 == step * ngroups;
+        }
+        if (release) {
             __hip_atomic_store(bar + kReleaseWord, step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             uint32_t spins = 0;
             while (__hip_atomic_load(bar + kReleaseWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < step) {
                 __builtin_amdgcn_s_sleep(20);
                 if (++spins > (1u << 20)) {
-                    __hip_atomic_store(bar + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(bar + kTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
             }
@@ -140,99 +125,112 @@ __device__ __forceinline__ T get_shared(const T* p) {
 
 // ---------------------------------------------------------- the kernel
 
-template <int KC>
-struct XTile {  // a W2 tile kept in LDS as ready MFMA A-fragments
-    static constexpr int kWords = KC * 4 * 64 * 4;
-};
+// Columns are split over the waves of the grid as follows: wave wv = 4 wg +
+// wave keeps the 64 columns 64 wv .. 64 wv + 63 in registers (W2Tile), and
+// the 16 columns C0 + 16 wv .. C0 + 16 wv + 15 (C0 = 256 x grid) in its own
+// LDS area as one extra MFMA A-operand (XFrag): every wave then does the
+// same work per (16-block group), 80 columns of it at full size.
 
+// One 16-column W2 fragment as MFMA A-operands: for chunk kc, lane (g, n)
+// keeps W2[32 kc + 8 g + e][c0 + n], e = 0..7, i.e. row n of A is column
+// c0 + n.  The MFMA result in lane (g, n) is then columns c0 + 4 g + q
+// (q = 0..3) of block row n.  Loaded once per call; columns >= V read 0.
 template <int KC>
-__device__ __forceinline__ void build_xtile(const uint16_t* __restrict__ W2, int V, int vt, int g,
-                                            int n, int lane, uint32_t* xf) {
-    const int va = vt + 4 * n;
-    const bool ok = va < V;
+__device__ __forceinline__ void load_xfrag(const uint16_t* __restrict__ W2, int V, int c0, int g,
+                                           int n, int lane, uint32_t* xf) {
+    const int col = c0 + n;
+    const bool ok = col < V;
     for (int kc = 0; kc < KC; ++kc) {
-        uint2 raw[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int j = kc * 32 + 8 * g + e;
-            raw[e] = ok ? *reinterpret_cast<const uint2*>(W2 + static_cast<size_t>(j) * V + va)
-                        : make_uint2(0u, 0u);
-        }
-        u32x4 f[4];
+        uint32_t w[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            f[0][p] = __builtin_amdgcn_perm(raw[2 * p + 1].x, raw[2 * p].x, 0x05040100u);
-            f[1][p] = __builtin_amdgcn_perm(raw[2 * p + 1].x, raw[2 * p].x, 0x07060302u);
-            f[2][p] = __builtin_amdgcn_perm(raw[2 * p + 1].y, raw[2 * p].y, 0x05040100u);
-            f[3][p] = __builtin_amdgcn_perm(raw[2 * p + 1].y, raw[2 * p].y, 0x07060302u);
+            const size_t j = static_cast<size_t>(kc * 32 + 8 * g + 2 * p);
+            const uint32_t lo = ok ? W2[j * V + col] : 0u;
+            const uint32_t hi = ok ? W2[(j + 1) * V + col] : 0u;
+            w[p] = lo | (hi << 16);
         }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(&xf[((kc * 4 + c) * 64 + lane) * 4]) = f[c];
+        *reinterpret_cast<u32x4*>(&xf[(kc * kWave + lane) * 4]) = u32x4{w[0], w[1], w[2], w[3]};
     }
 }
 
-// Bias of 16 blocks x 64 columns from the LDS tile (same layout as W2Tile).
+// acc[c] += bias from the register tile (when `reg`), accx += bias from the
+// LDS fragment (when `xw`), for the 16 block rows whose E rows start at erow
+// (this lane's row, offset 8 g).  One E operand load per chunk feeds both.
 template <int KC>
-__device__ __forceinline__ void xtile_mul(const uint32_t* xf, const uint16_t* erow, int lane,
-                                          f32x4 (&acc)[4]) {
+__device__ __forceinline__ void unit_mul(const W2Tile<KC>& w2, bool reg, const uint32_t* xf, bool xw,
+                                         const uint16_t* erow, int lane, f32x4 (&acc)[4], f32x4& accx) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
         const u32x4 ev = *reinterpret_cast<const u32x4*>(erow + kc * 32);
         const bf16x8 bop = __builtin_bit_cast(bf16x8, ev);
+        if (reg) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 av = *reinterpret_cast<const u32x4*>(&xf[((kc * 4 + c) * 64 + lane) * 4]);
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bop, acc[c], 0, 0, 0);
+            for (int c = 0; c < 4; ++c) {
+                const u32x4 av = {w2.f[kc][c][0], w2.f[kc][c][1], w2.f[kc][c][2], w2.f[kc][c][3]};
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bop,
+                                                                 acc[c], 0, 0, 0);
+            }
+        }
+        if (xw) {
+            const u32x4 av = *reinterpret_cast<const u32x4*>(&xf[(kc * kWave + lane) * 4]);
+            accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bop, accx, 0, 0, 0);
         }
     }
 }
 
-// Statistics of one (tile, 16-block group): lane (g, n) -> block 16 nb + n,
-// columns vt + 16g .. vt + 16g + 15.
-template <bool FULL>
-__device__ __forceinline__ Stats lane_stats16p(const float (&z)[16], int v0, int V, int b, int k,
-                                               bool sampling, float invT, uint32_t key0,
-                                               uint32_t key1, uint32_t ctr3) {
-    float zs[16], y[16];
-    const int nvalid = V - v0;
+// Statistics of 4 * NQ tempered logits of block b at columns
+// col[q] .. col[q] + 3 (q = 0..NQ-1, increasing, each a multiple of 4, all
+// below V), perturbed with Gumbel noise when sampling.  The perturbed
+// values are not kept: a strict running maximum over increasing columns
+// keeps the lowest column among equal maxima.
+template <int NQ>
+__device__ __forceinline__ Stats lane_stats(const float (&z)[4 * NQ], const int (&col)[NQ], int b, int k,
+                                            bool sampling, float invT, uint32_t key0, uint32_t key1,
+                                            uint32_t ctr3) {
+    float zs[4 * NQ];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) zs[j] = (FULL || j < nvalid) ? z[j] * invT : -INFINITY;
-    if (sampling) {
+    for (int j = 0; j < 4 * NQ; ++j) zs[j] = z[j] * invT;
+    float m = -INFINITY, ybest = -INFINITY, zx = zs[0];
+    uint32_t ibest = static_cast<uint32_t>(col[0]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x4 ctr = {static_cast<uint32_t>(v0 + 4 * q) >> 2, static_cast<uint32_t>(k),
+    for (int q = 0; q < NQ; ++q) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (sampling) {
+            const u32x4 ctr = {static_cast<uint32_t>(col[q]) >> 2, static_cast<uint32_t>(k),
                                static_cast<uint32_t>(b), ctr3};
-            const u32x4 w = philox4x32_10(ctr, key0, key1);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) y[4 * q + c] = zs[4 * q + c] + gumbel_from_word(w[c]);
+            w = philox4x32_10(ctr, key0, key1);
         }
-    } else {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) y[j] = zs[j];
-    }
-    float m = zs[0], ybest = y[0];
-#pragma unroll
-    for (int j = 1; j < 16; ++j) {
-        m = fmaxf(m, zs[j]);
-        ybest = fmaxf(ybest, y[j]);
+        for (int c = 0; c < 4; ++c) {
+            const float zj = zs[4 * q + c];
+            const float y = sampling ? zj + gumbel_from_word(w[c]) : zj;
+            const bool up = y > ybest;
+            ybest = up ? y : ybest;
+            zx = up ? zj : zx;
+            ibest = up ? static_cast<uint32_t>(col[q] + c) : ibest;
+            m = fmaxf(m, zj);
+        }
     }
     const float mb = m * kLog2e;
     float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s += __builtin_amdgcn_exp2f(fmaf(zs[j], kLog2e, -mb));
-    int idx = 15;
-    float zx = zs[15];
-#pragma unroll
-    for (int j = 14; j >= 0; --j) {
-        const bool hit = y[j] == ybest;
-        idx = hit ? j : idx;
-        zx = hit ? zs[j] : zx;
-    }
-    return Stats{m, s, argmax_key(ybest, static_cast<uint32_t>(v0 + idx)), zx};
+    for (int j = 0; j < 4 * NQ; ++j) s += __builtin_amdgcn_exp2f(fmaf(zs[j], kLog2e, -mb));
+    return Stats{m, s, argmax_key(ybest, ibest), zx};
 }
 
-// LDS of one workgroup: [LDS W2 tile][E rows (when staged)][prev tokens]
-// [per-wave statistics slots].
+// U values of the register-tile columns of one unit (two 16-byte loads),
+// loaded one unit ahead of use.  The 4 LDS-fragment columns are loaded at the
+// start of their unit and used last.
+struct UAhead {
+    u32x4 a, b;
+};
+
+// LDS of one workgroup: [4 LDS fragments][E rows (when staged)][prev tokens]
+// [temperatures][per-wave statistics slots].
+template <int KC>
+__host__ __device__ constexpr size_t persist_xfrag_bytes() {
+    return static_cast<size_t>(kPWaves) * KC * kWave * 16;
+}
 template <int KC>
 __host__ __device__ constexpr size_t persist_e_bytes(int Bpad) {
     return static_cast<size_t>(Bpad) * (KC * 32 + 8) * 2;
@@ -249,28 +247,35 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const bool stage_e = persist_stage_e<KC>(a.Bpad);
     const size_t e_bytes = stage_e ? persist_e_bytes<KC>(a.Bpad) : 0;
-    uint32_t* xf = reinterpret_cast<uint32_t*>(smem);
-    uint16_t* Es = reinterpret_cast<uint16_t*>(smem + XTile<KC>::kWords * 4);
-    int32_t* prev = reinterpret_cast<int32_t*>(smem + XTile<KC>::kWords * 4 + e_bytes);
-    Stats* slot = reinterpret_cast<Stats*>(smem + XTile<KC>::kWords * 4 + e_bytes +
-                                           align_up(static_cast<size_t>(a.Bpad) * 4, 16));
+    const size_t bp4 = align_up(static_cast<size_t>(a.Bpad) * 4, 16);
+    uint16_t* Es = reinterpret_cast<uint16_t*>(smem + persist_xfrag_bytes<KC>());
+    int32_t* prev = reinterpret_cast<int32_t*>(smem + persist_xfrag_bytes<KC>() + e_bytes);
+    float* temp_s = reinterpret_cast<float*>(smem + persist_xfrag_bytes<KC>() + e_bytes + bp4);
+    Stats* slot = reinterpret_cast<Stats*>(smem + persist_xfrag_bytes<KC>() + e_bytes + 2 * bp4);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int wg = blockIdx.x, nWG = a.nWG;
     const int NB = a.Bpad / 16;
-    const int t_reg = wg * kPWaves + wave;
-    const int t_x = kPWaves * nWG + wg;
-    const bool has_reg = t_reg < a.T, has_x = t_x < a.T;
+    const int wv = wg * kPWaves + wave;
+    uint32_t* xf = reinterpret_cast<uint32_t*>(smem) + wave * (KC * kWave * 4);
+
+    // this wave's columns: register tile (16 per lane) and LDS fragment (4 per lane)
+    const int v0 = wv * 64 + 16 * g;
+    const int c0 = kPWaves * nWG * 64 + 16 * wv;
+    const int vx = c0 + 4 * g;
+    const bool has_reg = wv * 64 < a.V, has_x = c0 < a.V;
+    const bool reg_live = v0 < a.V, x_live = vx < a.V;
 
     W2Tile<KC> w2;
-    if (has_reg) w2.load(a.W2, a.V, t_reg * 64, g, n);
-    if (has_x && wave == 0) build_xtile<KC>(a.W2, a.V, t_x * 64, g, n, lane, xf);
+    if (has_reg) w2.load(a.W2, a.V, wv * 64, g, n);
+    if (has_x) load_xfrag<KC>(a.W2, a.V, c0, g, n, lane, xf);
     // previous tokens of step 0: the anchors (an out-of-range anchor reads
-    // row 0; the prepare kernel marked its block dead)
+    // row 0; the finish kernel marks its block invalid)
     for (int b = threadIdx.x; b < a.Bpad; b += blockDim.x) {
         const int x = b < a.B ? a.anchor[b] : 0;
         prev[b] = (x >= 0 && x < a.V) ? x : 0;
+        temp_s[b] = b < a.B ? a.temperature[b] : 0.0f;
     }
     __syncthreads();
     // E rows of the coming step, W1[prev[b]], staged once per workgroup
@@ -283,47 +288,79 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
         }
         __syncthreads();
     };
+    // U of unit (step kk, block group nb), issued one unit ahead of its use
+    auto fetch_u = [&](int kk, int nb) {
+        UAhead p;
+        p.a = u32x4{0u, 0u, 0u, 0u};
+        p.b = u32x4{0u, 0u, 0u, 0u};
+        const int b = nb * 16 + n;
+        if (b < a.B) {
+            const uint16_t* row = a.U + (static_cast<size_t>(b) * a.gamma + kk) * a.V;
+            if (reg_live) {
+                p.a = *reinterpret_cast<const u32x4*>(row + v0);
+                if (v0 + 8 < a.V) p.b = *reinterpret_cast<const u32x4*>(row + v0 + 8);
+            }
+        }
+        return p;
+    };
     stage_rows();
+    const bool active = has_reg || has_x;
+    UAhead ahead = fetch_u(0, 0);
 
     for (int k = 0; k < a.gamma; ++k) {
         for (int b = lane; b < a.B; b += 64) slot[wave * a.B + b] = stats_empty();
-        // own tile: all block groups; LDS tile: groups nb = wave (mod 4)
-        const int units = (has_reg ? NB : 0) + (has_x ? (NB - wave + kPWaves - 1) / kPWaves : 0);
-        for (int u = 0; u < units; ++u) {
-            const bool from_x = u >= (has_reg ? NB : 0);
-            const int nb = from_x ? wave + kPWaves * (u - (has_reg ? NB : 0)) : u;
-            const int tile = from_x ? t_x : t_reg;
+        const int units = active ? NB : 0;
+        for (int nb = 0; nb < units; ++nb) {
+            const UAhead cur = ahead;
+            if (nb + 1 < NB)
+                ahead = fetch_u(k, nb + 1);
+            else if (k + 1 < a.gamma)
+                ahead = fetch_u(k + 1, 0);
             const int b = nb * 16 + n;
-            const int v0 = tile * 64 + 16 * g;
-            const bool live = b < a.B && v0 < a.V;
-            // U of this unit first: its latency overlaps the MFMA below
-            float z[16];
-            float temp = 0.0f;
-            if (live) {
-                load16_bf16(a.U + (static_cast<size_t>(b) * a.gamma + k) * a.V + v0, v0 + 8 < a.V, z);
-                temp = a.temperature[b];
-            }
+            uint2 ux = make_uint2(0u, 0u);
+            if (x_live && b < a.B)
+                ux = *reinterpret_cast<const uint2*>(a.U + (static_cast<size_t>(b) * a.gamma + k) * a.V + vx);
             const uint16_t* erow = stage_e ? &Es[b * ldE + 8 * g]
                                            : a.W1 + static_cast<size_t>(prev[b]) * r + 8 * g;
-            f32x4 acc[4];
+            f32x4 acc[4], accx;
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (from_x)
-                xtile_mul<KC>(xf, erow, lane, acc);
-            else
-                w2.mul(erow, acc);
+            accx = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            unit_mul<KC>(w2, has_reg, xf, has_x, erow, lane, acc, accx);
             Stats st = stats_empty();
-            if (live) {
+            if (b < a.B) {
+                const float temp = temp_s[b];
                 const bool sampling = temp > 0.0f;
                 const float invT = sampling ? 1.0f / temp : 1.0f;
+                if (reg_live) {
+                    const uint32_t w[8] = {cur.a[0], cur.a[1], cur.a[2], cur.a[3],
+                                           cur.b[0], cur.b[1], cur.b[2], cur.b[3]};
+                    float z[16];
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                    for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) z[4 * q + c] += acc[c][q];
-                if (v0 + 16 <= a.V)
-                    st = lane_stats16p<true>(z, v0, a.V, b, k, sampling, invT, a.key0, a.key1, a.ctr3);
-                else
-                    st = lane_stats16p<false>(z, v0, a.V, b, k, sampling, invT, a.key0, a.key1, a.ctr3);
+                        for (int c = 0; c < 4; ++c) {
+                            const int j = 4 * q + c;
+                            const float u = (j & 1) ? hi_bf16(w[j >> 1]) : lo_bf16(w[j >> 1]);
+                            z[j] = u + acc[c][q];
+                        }
+                    if (v0 + 16 <= a.V) {
+                        const int col[4] = {v0, v0 + 4, v0 + 8, v0 + 12};
+                        st = lane_stats<4>(z, col, b, k, sampling, invT, a.key0, a.key1, a.ctr3);
+                    } else {  // V % 8 == 0: the first 8 columns are in range
+                        float zh[8];
+                        const int col[2] = {v0, v0 + 4};
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) zh[j] = z[j];
+                        st = lane_stats<2>(zh, col, b, k, sampling, invT, a.key0, a.key1, a.ctr3);
+                    }
+                }
+                if (x_live) {
+                    const float zx4[4] = {lo_bf16(ux.x) + accx[0], hi_bf16(ux.x) + accx[1],
+                                          lo_bf16(ux.y) + accx[2], hi_bf16(ux.y) + accx[3]};
+                    const int col[1] = {vx};
+                    st = stats_merge(st, lane_stats<1>(zx4, col, b, k, sampling, invT, a.key0, a.key1, a.ctr3));
+                }
             }
             st = stats_merge(st, shfl_xor_stats(st, 16));
             st = stats_merge(st, shfl_xor_stats(st, 32));
@@ -336,8 +373,9 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
 #pragma unroll
             for (int w = 1; w < kPWaves; ++w) t = stats_merge(t, slot[w * a.B + b]);
             if (t.key != kKeyNone)
-                __hip_atomic_fetch_max(&a.best[(static_cast<size_t>(k) * a.B + b) * kKeyStride], t.key,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_max(&a.best[((static_cast<size_t>(k) * a.B + b) * kDraftKeyCopies +
+                                                wg % kDraftKeyCopies) * kKeyStride],
+                                       t.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // softmax partials are read after the kernel (k_persist_finish)
             const size_t o = (static_cast<size_t>(k) * a.B + b) * nWG + wg;
             a.pm[o] = t.m;
@@ -346,12 +384,21 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
             a.pzx[o] = t.zx;
         }
         if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
-        grid_barrier(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG));
-        // x_k of every block from the keys -> the E rows of step k+1
-        for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
-            const uint64_t key = get_shared(&a.best[(static_cast<size_t>(k) * a.B + b) * kKeyStride]);
+        grid_barrier(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG), static_cast<uint32_t>(wg));
+        // x_k of every block from the keys -> the E rows of step k+1: the
+        // copies of a block's key sit in 8 consecutive lanes
+        for (int t = threadIdx.x; t < a.B * kDraftKeyCopies; t += blockDim.x) {
+            uint64_t key = get_shared(&a.best[(static_cast<size_t>(k) * a.B * kDraftKeyCopies + t) * kKeyStride]);
+#pragma unroll
+            for (int o = 1; o < kDraftKeyCopies; o <<= 1) {
+                const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o);
+                const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key >> 32), o);
+                const uint64_t other = (static_cast<uint64_t>(hi) << 32) | lo;
+                key = other > key ? other : key;
+            }
             const uint32_t x = key_index(key);
-            prev[b] = (key != kKeyNone && x < static_cast<uint32_t>(a.V)) ? static_cast<int>(x) : 0;
+            if (t % kDraftKeyCopies == 0)
+                prev[t / kDraftKeyCopies] = (key != kKeyNone && x < static_cast<uint32_t>(a.V)) ? static_cast<int>(x) : 0;
         }
         __syncthreads();
         stage_rows();
@@ -360,61 +407,98 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
 
 // --------------------------------------------------------------- finish
 
-// Workgroup (b, k), after the loop: x_k from the argmax keys, log p_k from
-// the step's softmax partials (merged in workgroup order), c_k (Eq 7 on
-// x_{k-1}) and S_k = c_1 ... c_k.  None of these feed the sampling loop, so
-// they are kept out of it; each workgroup recomputes c_1 .. c_k itself
-// (k <= 64 dot products of length r), which keeps every S_k a fixed-order
-// product without a second pass.
-__global__ __launch_bounds__(256) void k_persist_finish(PersistArgs a, int r) {
-    __shared__ float red[16];
-    __shared__ int xs[64];
-    __shared__ int bad_s;
-    const int b = blockIdx.x, k = blockIdx.y;
-    if (threadIdx.x == 0) {
-        bool bad = a.dead[b] != 0 || a.bar[1] != 0;
-        for (int i = 0; i <= k; ++i) {
-            const uint64_t key = a.best[(static_cast<size_t>(i) * a.B + b) * kKeyStride];
-            const uint32_t x = key_index(key);
-            bad = bad || key == kKeyNone || x >= static_cast<uint32_t>(a.V);
-            xs[i] = static_cast<int>(x);
+constexpr int kFinishWaves = 8;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// sum over j < n of x[j] * y[j] (bf16), lane-strided, 8 elements per load
+// when both rows are 16-byte aligned; partial sum of this lane.
+__device__ __forceinline__ float lane_dot_bf16(const uint16_t* x, const uint16_t* y, int n, int lane) {
+    float acc = 0.0f;
+    if (n % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+#pragma unroll 4
+        for (int c = lane; c < n / 8; c += kWave) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(x + 8 * c);
+            const u32x4 b = *reinterpret_cast<const u32x4*>(y + 8 * c);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc = fmaf(lo_bf16(a[q]), lo_bf16(b[q]), acc);
+                acc = fmaf(hi_bf16(a[q]), hi_bf16(b[q]), acc);
+            }
         }
-        bad_s = bad;
+    } else {
+#pragma unroll 4
+        for (int j = lane; j < n; j += kWave) acc = fmaf(bf16_to_f32(x[j]), bf16_to_f32(y[j]), acc);
+    }
+    return acc;
+}
+
+// Workgroup b, after the loop.  Wave w handles positions k = w, w + 8, ...:
+// x_k from the argmax keys, log p_k from the step's softmax partials (merged
+// lane-strided, then across the wave), c_k = sigma(w[0:d] . h_{b,k} +
+// w[d:d+r] . W1[x_{k-1}]) (Eq 7, x_{-1} = the anchor); then S_k = c_0 ... c_k
+// in position order.  A block is invalid from its first position whose
+// previous token is out of range, or entirely when a grid barrier gave up.
+__global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(PersistArgs a) {
+    __shared__ int xs[kMaxGamma + 1];  // xs[0] = anchor, xs[k + 1] = x_k
+    __shared__ float cs[kMaxGamma];
+    __shared__ int first_bad_s;
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (wave == 0) {
+        bool inval = false;
+        if (lane < a.gamma) {
+            uint64_t key = kKeyNone;
+            for (int c = 0; c < kDraftKeyCopies; ++c) {
+                const uint64_t kc = a.best[((static_cast<size_t>(lane) * a.B + b) * kDraftKeyCopies + c) * kKeyStride];
+                key = kc > key ? kc : key;
+            }
+            const uint32_t x = key_index(key);
+            inval = key == kKeyNone || x >= static_cast<uint32_t>(a.V);
+            xs[lane + 1] = static_cast<int>(x);
+        }
+        const int x0 = a.anchor[b];
+        const uint64_t m = __ballot(inval);
+        const bool head_bad = a.bar[kTimeoutWord] != 0 || x0 < 0 || x0 >= a.V;
+        if (lane == 0) {
+            xs[0] = x0;
+            first_bad_s = head_bad ? 0 : (m ? __ffsll(static_cast<unsigned long long>(m)) - 1 : a.gamma);
+        }
     }
     __syncthreads();
-    const bool bad = bad_s != 0;
-    const size_t out = static_cast<size_t>(b) * a.gamma + k;
-    // log p_k
-    Stats t = stats_empty();
-    const size_t base = (static_cast<size_t>(k) * a.B + b) * a.nWG;
-    for (int p = threadIdx.x; p < a.nWG; p += blockDim.x)
-        t = stats_merge(t, Stats{a.pm[base + p], a.ps[base + p], a.pkey[base + p], a.pzx[base + p]});
-    for (int o = 32; o > 0; o >>= 1) t = stats_merge(t, shfl_xor_stats(t, o));
-    __shared__ Stats wred[4];
-    if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = t;
+    const int first_bad = first_bad_s;
+    for (int k = wave; k < a.gamma; k += kFinishWaves) {
+        const bool bad = k >= first_bad;
+        Stats t = stats_empty();
+        const size_t base = (static_cast<size_t>(k) * a.B + b) * a.nWG;
+        for (int p = lane; p < a.nWG; p += kWave)
+            t = stats_merge(t, Stats{a.pm[base + p], a.ps[base + p], a.pkey[base + p], a.pzx[base + p]});
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) t = stats_merge(t, shfl_xor_stats(t, o));
+        float part = lane_dot_bf16(a.w_conf, a.h + (static_cast<size_t>(b) * a.gamma + k) * a.d, a.d, lane);
+        if (!bad) part += lane_dot_bf16(a.w_conf + a.d, a.W1 + static_cast<size_t>(xs[k]) * a.r, a.r, lane);
+        const float logit = wave_sum(part);
+        if (lane == 0) {
+            const size_t out = static_cast<size_t>(b) * a.gamma + k;
+            a.tokens[out] = bad ? -1 : xs[k + 1];
+            if (a.logp) a.logp[out] = bad ? NAN : t.zx - (t.m + logf(t.s));
+            cs[k] = bad ? NAN : sigmoidf_(logit);
+        }
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-        Stats m = wred[0];
-        for (int w = 1; w < static_cast<int>(blockDim.x / kWave); ++w) m = stats_merge(m, wred[w]);
-        a.tokens[out] = bad ? -1 : xs[k];
-        if (a.logp) a.logp[out] = bad ? NAN : m.zx - (m.m + logf(m.s));
-        if (bad) a.dead[b] = 1;
-    }
-    // c_1 .. c_k and the survival product
-    float S = a.survival[static_cast<size_t>(b) * a.gamma];  // S_0 = c_0 from prepare
-    float c = S;
-    for (int i = 1; i <= k; ++i) {
-        float part = 0.0f;
-        if (!bad)
-            for (int j = threadIdx.x; j < r; j += blockDim.x)
-                part += bf16_to_f32(a.w_conf[a.d + j]) * bf16_to_f32(a.W1[static_cast<size_t>(xs[i - 1]) * r + j]);
-        const float ae = block_sum(part, red);
-        c = bad ? NAN : sigmoidf_(a.hdot[static_cast<size_t>(b) * a.gamma + i] + ae);
-        S *= c;
-    }
-    if (threadIdx.x == 0 && k > 0) {
-        a.conf[out] = c;
-        a.survival[out] = S;
+        float S = 1.0f;
+        for (int k = 0; k < a.gamma; ++k) {
+            const size_t out = static_cast<size_t>(b) * a.gamma + k;
+            S *= cs[k];
+            a.conf[out] = cs[k];
+            a.survival[out] = S;
+        }
+        a.dead[b] = first_bad < a.gamma ? 1 : 0;
     }
 }
 
@@ -422,8 +506,8 @@ __global__ __launch_bounds__(256) void k_persist_finish(PersistArgs a, int r) {
 
 template <int KC>
 static size_t persist_lds(int Bpad, int B) {
-    return XTile<KC>::kWords * 4 + (persist_stage_e<KC>(Bpad) ? persist_e_bytes<KC>(Bpad) : 0) +
-           align_up(static_cast<size_t>(Bpad) * 4, 16) + sizeof(Stats) * kPWaves * static_cast<size_t>(B);
+    return persist_xfrag_bytes<KC>() + (persist_stage_e<KC>(Bpad) ? persist_e_bytes<KC>(Bpad) : 0) +
+           2 * align_up(static_cast<size_t>(Bpad) * 4, 16) + sizeof(Stats) * kPWaves * static_cast<size_t>(B);
 }
 
 struct PersistPlan {
@@ -440,15 +524,17 @@ static PersistPlan plan_for(const dspark_dims& D) {
     int dev = 0, cus = 0, coop = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return p;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return p;
-    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return p;
+    if (persist_launch_option() == 1 &&
+        (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop))
+        return p;
     void (*fn)(PersistArgs) = k_draft_persistent<KC>;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), 256, lds) !=
         hipSuccess)
         return p;
     if (per_cu < 1) return p;
     const int nWG = std::min(per_cu, 2) * cus;
-    const int T = (D.V + 63) / 64;
-    if (T > kPWaves * nWG + nWG) return p;  // W2 does not fit on chip
+    // columns held on chip: 64 per wave in registers + 16 per wave in LDS
+    if (static_cast<int64_t>(D.V) > static_cast<int64_t>(kPWaves) * nWG * 80) return p;
     if (nWG > draft_persist_max_wg()) return p;
     p.ok = true;
     p.nWG = nWG;
@@ -480,9 +566,8 @@ static hipError_t launch_persist_kc(const DraftArgs& A) {
     p.w_conf = static_cast<const uint16_t*>(A.w_conf);
     p.anchor = A.anchor;
     p.temperature = A.temperature;
-    p.hdot = reinterpret_cast<const float*>(ws + L.hdot);
-    p.V = D.V; p.d = D.d; p.gamma = D.gamma; p.B = D.B; p.Bpad = L.Bpad;
-    p.T = (D.V + 63) / 64;
+    p.h = static_cast<const uint16_t*>(A.h);
+    p.V = D.V; p.r = D.r; p.d = D.d; p.gamma = D.gamma; p.B = D.B; p.Bpad = L.Bpad;
     p.nWG = plan.nWG;
     p.key0 = static_cast<uint32_t>(A.seed);
     p.key1 = static_cast<uint32_t>(A.seed >> 32);
@@ -496,19 +581,23 @@ static hipError_t launch_persist_kc(const DraftArgs& A) {
     p.dead = reinterpret_cast<int32_t*>(ws + L.dead);
     p.tokens = A.tokens; p.logp = A.logp; p.conf = A.conf; p.survival = A.survival;
 
-    hipLaunchKernelGGL(k_persist_prepare, dim3(D.B, D.gamma), dim3(256), 0, A.stream, A.anchor,
-                       p.W1, p.w_conf, static_cast<const uint16_t*>(A.h), D.V, D.r, D.d, D.gamma, D.B,
-                       reinterpret_cast<float*>(ws + L.hdot), p.dead, p.best, p.bar, A.conf, A.survival);
+    hipLaunchKernelGGL(k_persist_prepare, dim3(1), dim3(256), 0, A.stream, D.gamma * D.B * kDraftKeyCopies,
+                       p.best, p.bar);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if ((e = profile_begin(A.stream)) != hipSuccess) return e;
     void* args[] = {&p};
     void (*fn)(PersistArgs) = k_draft_persistent<KC>;
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG),
-                                   dim3(256), args, persist_lds<KC>(L.Bpad, D.B), A.stream);
+    const size_t lds = persist_lds<KC>(L.Bpad, D.B);
+    if (persist_launch_option() == 0)
+        e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG), dim3(256), args, lds,
+                            A.stream);
+    else
+        e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG), dim3(256),
+                                       args, lds, A.stream);
     if (e != hipSuccess) return e;
     if ((e = profile_end(A.stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_persist_finish, dim3(D.B, D.gamma), dim3(256), 0, A.stream, p, D.r);
+    hipLaunchKernelGGL(k_persist_finish, dim3(D.B), dim3(kFinishWaves * kWave), 0, A.stream, p);
     return hipGetLastError();
 }
 

@@ -11,6 +11,13 @@ namespace dspark {
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Single-launch drafting: each argmax key has this many copies (workgroup
+// wg updates copy wg % kDraftKeyCopies), so that no more than 1/8 of the
+// grid contends for one address; the grid barrier uses as many arrival
+// counters for the same reason.
+constexpr int kDraftKeyCopies = 8;
+constexpr int kDraftBarWords = 512;
+
 // Draft-call workspace carve-up.  Every region starts 256-byte aligned.
 struct DraftLayout {
     int Bpad;          // B rounded up to 16 (MFMA column block)
@@ -22,8 +29,8 @@ struct DraftLayout {
     size_t state;      // f32 [Bpad, r]  RNN state s
     size_t gates;      // f32 [Bpad, 3r] RNN joint projection output
     size_t hdot;       // f32 [B, gamma]  h part of the Eq 7 logit, w[0:d] . h_k
-    size_t best;       // u64 [gamma, B, 16]  argmax keys, one line each (single-launch path)
-    size_t bar;        // u32 [64]  grid barrier: arrivals, timeout flag, release flag
+    size_t best;       // u64 [gamma, B, copies, 16]  argmax keys, one line each (single-launch path)
+    size_t bar;        // u32 [512]  grid barrier: arrival counters, release and timeout flags
     size_t qm, qs, qkey, qzx;  // [gamma, B, max workgroups] step partials (single-launch path)
     size_t pm, ps, pkey, pzx;  // partials [B, P]: max, sum, key (u64), z at key
     size_t total;
@@ -90,6 +97,8 @@ hipError_t launch_draft(const DraftArgs& a);
 
 // Per-thread choice of drafting path (see dspark_set_option).
 int draft_path_option();
+// Per-thread launch mode of the single-launch kernel: 0 ordinary, 1 cooperative.
+int persist_launch_option();
 
 // Per-thread event timing of the dominant kernel (see dspark_profile_*).
 bool profiling_enabled();

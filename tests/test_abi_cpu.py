@@ -107,3 +107,55 @@ def test_product_path_never_imports_the_oracle():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"\boracle\b", text.replace("the oracle", "")), fn
+
+
+def test_set_option_validates(lib):
+    for opt, good, bad in ((lib.DSPARK_OPT_DRAFT_PATH, (0, 1, 2), (-1, 3)),
+                           (lib.DSPARK_OPT_PERSIST_LAUNCH, (0, 1), (-1, 2))):
+        for v in good:
+            lib.dspark_set_option(opt, v)
+        for v in bad:
+            with pytest.raises(lib.DsparkError) as e:
+                lib.dspark_set_option(opt, v)
+            assert e.value.status == lib.DSPARK_EINVAL
+    lib.dspark_set_option(lib.DSPARK_OPT_DRAFT_PATH, 0)
+    lib.dspark_set_option(lib.DSPARK_OPT_PERSIST_LAUNCH, 0)
+    with pytest.raises(lib.DsparkError) as e:
+        lib.dspark_set_option(99, 0)
+    assert "unknown option" in str(e.value)
+
+
+def _loss_call(lib, d, ptr=256, **over):
+    args = dict(U=ptr, T_logits=ptr, h=ptr, anchor=ptr, labels=ptr, W1=ptr, W2=ptr, w_conf=ptr,
+                alpha=None, pos_weight=None, loss4=ptr, c_star=ptr, conf=None, dlogits=None,
+                dlogits_dtype="f32", dW2=None, dconf_logit=None, workspace=ptr)
+    args.update(over)
+    wsb = over.pop("workspace_bytes", 1 << 40)
+    args.pop("workspace_bytes", None)
+    lib.dspark_block_loss(d, **args, workspace_bytes=wsb, stream=0)
+
+
+def test_loss_rejects_bad_arguments(lib):
+    d = lib.make_dims(1000, 64, 32, 7, 4)
+    for name in ("U", "T_logits", "h", "anchor", "labels", "W1", "W2", "w_conf", "loss4",
+                 "c_star", "workspace"):
+        with pytest.raises(lib.DsparkError) as e:
+            _loss_call(lib, d, **{name: None})
+        assert e.value.status == lib.DSPARK_EINVAL and name in str(e.value)
+    with pytest.raises(lib.DsparkError) as e:
+        _loss_call(lib, d, dW2=256)
+    assert e.value.status == lib.DSPARK_EINVAL and "dlogits" in str(e.value)
+    with pytest.raises(lib.DsparkError) as e:
+        _loss_call(lib, d, dlogits=256, dlogits_dtype=7)
+    assert e.value.status == lib.DSPARK_EINVAL
+    need = lib.dspark_workspace_size(d, lib.DSPARK_CALL_LOSS)
+    with pytest.raises(lib.DsparkError) as e:
+        _loss_call(lib, d, workspace_bytes=need - 1)
+    assert e.value.status == lib.DSPARK_EWORKSPACE
+    with pytest.raises(lib.DsparkError) as e:
+        _loss_call(lib, lib.make_dims(1000, 64, 32, 7, 4, head="rnn"))
+    assert e.value.status == lib.DSPARK_EUNSUPPORTED
+    # bf16 matrix-core path needs 16-byte aligned streams
+    with pytest.raises(lib.DsparkError) as e:
+        _loss_call(lib, lib.make_dims(1024, 64, 32, 7, 4), U=258)
+    assert e.value.status == lib.DSPARK_EUNSUPPORTED

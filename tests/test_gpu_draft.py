@@ -29,10 +29,11 @@ def ops():
 MULTI, SINGLE = 1, 2  # per-step launches / single-launch kernel
 
 
-def run_gpu(ops, inp, seed=0, offset=0, path=0):
+def run_gpu(ops, inp, seed=0, offset=0, path=0, launch=0):
     import torch
     from semi_autoregressive_draft_markov_amd import binding
     binding.dspark_set_option(binding.DSPARK_OPT_DRAFT_PATH, path)
+    binding.dspark_set_option(binding.DSPARK_OPT_PERSIST_LAUNCH, launch)
     t = synth.to_torch(inp)
     out = ops.draft_block(t["U"], t["h"], t["anchor"], t["W1"], t["W2"], t["w_conf"],
                           t["temperature"], W_rnn=t["W_rnn"], seed=seed, offset=offset)
@@ -127,6 +128,20 @@ def test_paths_agree(ops):
     assert np.array_equal(a["conf"], b["conf"]) or np.allclose(a["conf"], b["conf"], rtol=1e-6)
 
 
+PLAIN, COOP = 0, 1  # launch modes of the single-launch kernel
+
+
+def test_cooperative_launch_matches_plain(ops):
+    # the single-launch kernel started with hipLaunchCooperativeKernel
+    # computes the same bits as with the default ordinary launch
+    inp = small(V=4104, r=256, d=64, gamma=7, B=40, seed=14, temperature=[1.0] * 30 + [0.0] * 10)
+    a = run_gpu(ops, inp, seed=5, path=SINGLE, launch=PLAIN)
+    b = run_gpu(ops, inp, seed=5, path=SINGLE, launch=COOP)
+    for k in ("tokens", "logp", "conf", "survival"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+    check_draft(inp, b, 5, 0, label="cooperative launch")
+
+
 @pytest.mark.parametrize("path", [MULTI, SINGLE])
 def test_out_of_range_anchor_is_flagged(ops, path):
     from semi_autoregressive_draft_markov_amd import binding
@@ -171,11 +186,11 @@ def test_sampler_law_on_gpu(ops, dtype, V, path):
 
 # -------------------------------------------------------------- full sizes
 
-@pytest.mark.parametrize("path", [MULTI, SINGLE])
-def test_qwen3_4b_shape_all_blocks(ops, path):
+@pytest.mark.parametrize("path,launch", [(MULTI, 0), (SINGLE, PLAIN), (SINGLE, COOP)])
+def test_qwen3_4b_shape_all_blocks(ops, path, launch):
     inp = synth.config_inputs(2)
-    note("case: qwen3-4b-shaped V151936 r256 B32 (all blocks) path %d" % path)
-    g = run_gpu(ops, inp, seed=0, path=path)
+    note("case: qwen3-4b-shaped V151936 r256 B32 (all blocks) path %d launch %d" % (path, launch))
+    g = run_gpu(ops, inp, seed=0, path=path, launch=launch)
     info = check_draft(inp, g, 0, 0, label="qwen3-4b shape")
     note("  ties allowed: %d, max |dlogp| %.2e" % (info["ties"], info["logp_err"]))
 
