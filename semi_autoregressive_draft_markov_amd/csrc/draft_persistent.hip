@@ -218,35 +218,45 @@ __device__ __forceinline__ Stats lane_stats(const float (&z)[4 * NQ], const int 
     return Stats{m, s, argmax_key(ybest, ibest), zx};
 }
 
-// U values of the register-tile columns of one unit (two 16-byte loads),
-// loaded one unit ahead of use.  The 4 LDS-fragment columns are loaded at the
-// start of their unit and used last.
+// U values of one unit, loaded one unit ahead of use: 16 columns of the
+// register tile (two 16-byte loads) and the 4 columns of the LDS fragment.
+// They become the initial MFMA accumulators, so z = U + E W2 comes out of
+// the matrix cores directly.
 struct UAhead {
     u32x4 a, b;
+    uint2 x;
 };
 
-// LDS of one workgroup: [4 LDS fragments][E rows (when staged)][prev tokens]
-// [temperatures][per-wave statistics slots].
+// LDS of one workgroup: [4 LDS fragments][E rows][prev tokens]
+// [temperatures][per-wave statistics slots].  The E rows W1[x_{k-1}] are
+// staged either all at once after each barrier, or (GROUPED, when all rows
+// would not fit) 16 at a time in two buffers, the next group's rows loaded
+// while the current group is computed.  Either way the MFMA operand comes
+// from LDS, so its wait never covers the U loads still in flight.
+constexpr size_t kPersistLdsMax = 80 * 1024;  // two workgroups per CU
+
 template <int KC>
 __host__ __device__ constexpr size_t persist_xfrag_bytes() {
     return static_cast<size_t>(kPWaves) * KC * kWave * 16;
 }
 template <int KC>
-__host__ __device__ constexpr size_t persist_e_bytes(int Bpad) {
-    return static_cast<size_t>(Bpad) * (KC * 32 + 8) * 2;
+__host__ __device__ constexpr size_t persist_e_bytes(int rows) {
+    return static_cast<size_t>(rows) * (KC * 32 + 8) * 2;
 }
 template <int KC>
-__host__ __device__ constexpr bool persist_stage_e(int Bpad) {
-    return persist_e_bytes<KC>(Bpad) <= 24 * 1024;
+__host__ __device__ constexpr size_t persist_lds(int Bpad, int B, bool grouped) {
+    return persist_xfrag_bytes<KC>() + persist_e_bytes<KC>(grouped ? 32 : Bpad) +
+           2 * align_up(static_cast<size_t>(Bpad) * 4, 16) + sizeof(Stats) * kPWaves * static_cast<size_t>(B);
 }
 
-template <int KC>
+template <int KC, bool GROUPED>
 __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
     constexpr int r = KC * 32;
     constexpr int ldE = r + 8;  // padded row stride of the staged E rows (bank spread)
+    constexpr int kGroupChunks = 16 * (r / 8);                 // 16-byte pieces of 16 rows
+    constexpr int kStage = (kGroupChunks + 255) / 256;         // per thread
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const bool stage_e = persist_stage_e<KC>(a.Bpad);
-    const size_t e_bytes = stage_e ? persist_e_bytes<KC>(a.Bpad) : 0;
+    const size_t e_bytes = persist_e_bytes<KC>(GROUPED ? 32 : a.Bpad);
     const size_t bp4 = align_up(static_cast<size_t>(a.Bpad) * 4, 16);
     uint16_t* Es = reinterpret_cast<uint16_t*>(smem + persist_xfrag_bytes<KC>());
     int32_t* prev = reinterpret_cast<int32_t*>(smem + persist_xfrag_bytes<KC>() + e_bytes);
@@ -278,21 +288,48 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
         temp_s[b] = b < a.B ? a.temperature[b] : 0.0f;
     }
     __syncthreads();
-    // E rows of the coming step, W1[prev[b]], staged once per workgroup
+    // E rows W1[prev[b]] of the coming step: all rows (or, GROUPED, the
+    // first group into buffer 0), then a workgroup barrier
     auto stage_rows = [&]() {
-        if (!stage_e) return;
-        for (int t = threadIdx.x; t < a.Bpad * (r / 8); t += blockDim.x) {
+        const int chunks = (GROUPED ? 16 : a.Bpad) * (r / 8);
+        for (int t = threadIdx.x; t < chunks; t += blockDim.x) {
             const int row = t / (r / 8), col = t % (r / 8);
             *reinterpret_cast<u32x4*>(&Es[row * ldE + col * 8]) =
                 *reinterpret_cast<const u32x4*>(a.W1 + static_cast<size_t>(prev[row]) * r + col * 8);
         }
         __syncthreads();
     };
+    // GROUPED: rows of block group nb, loaded into registers ...
+    u32x4 staged[kStage];
+    auto load_group = [&](int nb) {
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int t = threadIdx.x + 256 * i;
+            if (t < kGroupChunks) {
+                const int row = t / (r / 8), col = t % (r / 8);
+                staged[i] = *reinterpret_cast<const u32x4*>(a.W1 + static_cast<size_t>(prev[nb * 16 + row]) * r +
+                                                             col * 8);
+            }
+        }
+    };
+    // ... and stored to buffer nb % 2 once the unit before it is done
+    auto store_group = [&](int nb) {
+        uint16_t* buf = Es + (nb & 1) * 16 * ldE;
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int t = threadIdx.x + 256 * i;
+            if (t < kGroupChunks) {
+                const int row = t / (r / 8), col = t % (r / 8);
+                *reinterpret_cast<u32x4*>(&buf[row * ldE + col * 8]) = staged[i];
+            }
+        }
+    };
     // U of unit (step kk, block group nb), issued one unit ahead of its use
     auto fetch_u = [&](int kk, int nb) {
         UAhead p;
         p.a = u32x4{0u, 0u, 0u, 0u};
         p.b = u32x4{0u, 0u, 0u, 0u};
+        p.x = make_uint2(0u, 0u);
         const int b = nb * 16 + n;
         if (b < a.B) {
             const uint16_t* row = a.U + (static_cast<size_t>(b) * a.gamma + kk) * a.V;
@@ -300,6 +337,7 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
                 p.a = *reinterpret_cast<const u32x4*>(row + v0);
                 if (v0 + 8 < a.V) p.b = *reinterpret_cast<const u32x4*>(row + v0 + 8);
             }
+            if (x_live) p.x = *reinterpret_cast<const uint2*>(row + vx);
         }
         return p;
     };
@@ -309,41 +347,42 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
 
     for (int k = 0; k < a.gamma; ++k) {
         for (int b = lane; b < a.B; b += 64) slot[wave * a.B + b] = stats_empty();
-        const int units = active ? NB : 0;
-        for (int nb = 0; nb < units; ++nb) {
-            const UAhead cur = ahead;
+        // every wave runs all NB units (GROUPED stages rows between them);
+        // waves without columns skip the arithmetic
+        for (int nb = 0; nb < NB; ++nb) {
+            if (GROUPED && nb + 1 < NB) load_group(nb + 1);
+            // accumulators start from U (bf16 -> f32 is exact)
+            f32x4 acc[4], accx;
+            {
+                const uint32_t w[8] = {ahead.a[0], ahead.a[1], ahead.a[2], ahead.a[3],
+                                       ahead.b[0], ahead.b[1], ahead.b[2], ahead.b[3]};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int j = 4 * q + c;
+                        acc[c][q] = (j & 1) ? hi_bf16(w[j >> 1]) : lo_bf16(w[j >> 1]);
+                    }
+                accx = f32x4{lo_bf16(ahead.x.x), hi_bf16(ahead.x.x), lo_bf16(ahead.x.y), hi_bf16(ahead.x.y)};
+            }
             if (nb + 1 < NB)
                 ahead = fetch_u(k, nb + 1);
             else if (k + 1 < a.gamma)
                 ahead = fetch_u(k + 1, 0);
             const int b = nb * 16 + n;
-            uint2 ux = make_uint2(0u, 0u);
-            if (x_live && b < a.B)
-                ux = *reinterpret_cast<const uint2*>(a.U + (static_cast<size_t>(b) * a.gamma + k) * a.V + vx);
-            const uint16_t* erow = stage_e ? &Es[b * ldE + 8 * g]
-                                           : a.W1 + static_cast<size_t>(prev[b]) * r + 8 * g;
-            f32x4 acc[4], accx;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            accx = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            unit_mul<KC>(w2, has_reg, xf, has_x, erow, lane, acc, accx);
+            const uint16_t* erow = GROUPED ? &Es[((nb & 1) * 16 + n) * ldE + 8 * g] : &Es[b * ldE + 8 * g];
+            if (active) unit_mul<KC>(w2, has_reg, xf, has_x, erow, lane, acc, accx);
             Stats st = stats_empty();
-            if (b < a.B) {
+            if (active && b < a.B) {
                 const float temp = temp_s[b];
                 const bool sampling = temp > 0.0f;
                 const float invT = sampling ? 1.0f / temp : 1.0f;
                 if (reg_live) {
-                    const uint32_t w[8] = {cur.a[0], cur.a[1], cur.a[2], cur.a[3],
-                                           cur.b[0], cur.b[1], cur.b[2], cur.b[3]};
                     float z[16];
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const int j = 4 * q + c;
-                            const float u = (j & 1) ? hi_bf16(w[j >> 1]) : lo_bf16(w[j >> 1]);
-                            z[j] = u + acc[c][q];
-                        }
+                        for (int c = 0; c < 4; ++c) z[4 * q + c] = acc[c][q];
                     if (v0 + 16 <= a.V) {
                         const int col[4] = {v0, v0 + 4, v0 + 8, v0 + 12};
                         st = lane_stats<4>(z, col, b, k, sampling, invT, a.key0, a.key1, a.ctr3);
@@ -356,8 +395,7 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
                     }
                 }
                 if (x_live) {
-                    const float zx4[4] = {lo_bf16(ux.x) + accx[0], hi_bf16(ux.x) + accx[1],
-                                          lo_bf16(ux.y) + accx[2], hi_bf16(ux.y) + accx[3]};
+                    const float zx4[4] = {accx[0], accx[1], accx[2], accx[3]};
                     const int col[1] = {vx};
                     st = stats_merge(st, lane_stats<1>(zx4, col, b, k, sampling, invT, a.key0, a.key1, a.ctr3));
                 }
@@ -365,6 +403,10 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
             st = stats_merge(st, shfl_xor_stats(st, 16));
             st = stats_merge(st, shfl_xor_stats(st, 32));
             if (g == 0 && b < a.B) slot[wave * a.B + b] = stats_merge(slot[wave * a.B + b], st);
+            if (GROUPED && nb + 1 < NB) {
+                store_group(nb + 1);
+                __syncthreads();
+            }
         }
         __syncthreads();
         // workgroup merge in wave order, then publish
@@ -504,31 +546,36 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
 
 // ---------------------------------------------------------------- launch
 
-template <int KC>
-static size_t persist_lds(int Bpad, int B) {
-    return persist_xfrag_bytes<KC>() + (persist_stage_e<KC>(Bpad) ? persist_e_bytes<KC>(Bpad) : 0) +
-           2 * align_up(static_cast<size_t>(Bpad) * 4, 16) + sizeof(Stats) * kPWaves * static_cast<size_t>(B);
-}
-
 struct PersistPlan {
     bool ok = false;
+    bool grouped = false;
     int nWG = 0;
+    size_t lds = 0;
 };
+
+template <int KC>
+static void (*persist_kernel(bool grouped))(PersistArgs) {
+    return grouped ? k_draft_persistent<KC, true> : k_draft_persistent<KC, false>;
+}
 
 template <int KC>
 static PersistPlan plan_for(const dspark_dims& D) {
     PersistPlan p;
     const int Bpad = (D.B + 15) / 16 * 16;
-    const size_t lds = persist_lds<KC>(Bpad, D.B);
-    if (lds > 64 * 1024) return p;
+    p.grouped = persist_lds<KC>(Bpad, D.B, false) > kPersistLdsMax;
+    p.lds = persist_lds<KC>(Bpad, D.B, p.grouped);
+    if (p.lds > kPersistLdsMax) return p;
     int dev = 0, cus = 0, coop = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return p;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return p;
     if (persist_launch_option() == 1 &&
         (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop))
         return p;
-    void (*fn)(PersistArgs) = k_draft_persistent<KC>;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), 256, lds) !=
+    void (*fn)(PersistArgs) = persist_kernel<KC>(p.grouped);
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(p.lds)) != hipSuccess)
+        return p;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), 256, p.lds) !=
         hipSuccess)
         return p;
     if (per_cu < 1) return p;
@@ -587,8 +634,8 @@ static hipError_t launch_persist_kc(const DraftArgs& A) {
     if (e != hipSuccess) return e;
     if ((e = profile_begin(A.stream)) != hipSuccess) return e;
     void* args[] = {&p};
-    void (*fn)(PersistArgs) = k_draft_persistent<KC>;
-    const size_t lds = persist_lds<KC>(L.Bpad, D.B);
+    void (*fn)(PersistArgs) = persist_kernel<KC>(plan.grouped);
+    const size_t lds = plan.lds;
     if (persist_launch_option() == 0)
         e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG), dim3(256), args, lds,
                             A.stream);
