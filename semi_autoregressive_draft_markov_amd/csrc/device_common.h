@@ -33,16 +33,22 @@ template <> __device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p,
 // ---------------------------------------------------------------- Philox
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
 // Easy as 1, 2, 3", SC'11): ten rounds, each two 32x32 -> 64-bit products,
-// with the key bumped by the Weyl constants between rounds.
+// with the key bumped by the Weyl constants between rounds.  The two
+// three-way xors of a round are single v_bitop3_b32 instructions (truth
+// table 0x96), which gfx950 has and earlier CDNA parts do not.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 x, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
         const uint64_t pa = static_cast<uint64_t>(0xD2511F53u) * x[0];
         const uint64_t pc = static_cast<uint64_t>(0xCD9E8D57u) * x[2];
         const uint32_t b = x[1], d = x[3];
-        x[0] = static_cast<uint32_t>(pc >> 32) ^ b ^ k0;
+        x[0] = xor3(static_cast<uint32_t>(pc >> 32), b, k0);
         x[1] = static_cast<uint32_t>(pc);
-        x[2] = static_cast<uint32_t>(pa >> 32) ^ d ^ k1;
+        x[2] = xor3(static_cast<uint32_t>(pa >> 32), d, k1);
         x[3] = static_cast<uint32_t>(pa);
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;

@@ -180,36 +180,40 @@ __device__ __forceinline__ void unit_mul(const W2Tile<KC>& w2, bool reg, const u
 
 // Statistics of 4 * NQ tempered logits of block b at columns
 // col[q] .. col[q] + 3 (q = 0..NQ-1, increasing, each a multiple of 4, all
-// below V), perturbed with Gumbel noise when sampling.  The perturbed
-// values are not kept: a strict running maximum over increasing columns
-// keeps the lowest column among equal maxima.
+// below V), perturbed with Gumbel noise when sampling.  A strict running
+// maximum over increasing columns keeps the lowest column among equal
+// maxima.
 template <int NQ>
 __device__ __forceinline__ Stats lane_stats(const float (&z)[4 * NQ], const int (&col)[NQ], int b, int k,
                                             bool sampling, float invT, uint32_t key0, uint32_t key1,
                                             uint32_t ctr3) {
-    float zs[4 * NQ];
+    float zs[4 * NQ], y[4 * NQ];
 #pragma unroll
     for (int j = 0; j < 4 * NQ; ++j) zs[j] = z[j] * invT;
-    float m = -INFINITY, ybest = -INFINITY, zx = zs[0];
-    uint32_t ibest = static_cast<uint32_t>(col[0]);
+    // one branch around all the noise of this lane, so the Philox rounds and
+    // logarithms of its columns interleave
+    if (sampling) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (sampling) {
+        for (int q = 0; q < NQ; ++q) {
             const u32x4 ctr = {static_cast<uint32_t>(col[q]) >> 2, static_cast<uint32_t>(k),
                                static_cast<uint32_t>(b), ctr3};
-            w = philox4x32_10(ctr, key0, key1);
-        }
+            const u32x4 w = philox4x32_10(ctr, key0, key1);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float zj = zs[4 * q + c];
-            const float y = sampling ? zj + gumbel_from_word(w[c]) : zj;
-            const bool up = y > ybest;
-            ybest = up ? y : ybest;
-            zx = up ? zj : zx;
-            ibest = up ? static_cast<uint32_t>(col[q] + c) : ibest;
-            m = fmaxf(m, zj);
+            for (int c = 0; c < 4; ++c) y[4 * q + c] = zs[4 * q + c] + gumbel_from_word(w[c]);
         }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4 * NQ; ++j) y[j] = zs[j];
+    }
+    float m = zs[0], ybest = y[0], zx = zs[0];
+    uint32_t ibest = static_cast<uint32_t>(col[0]);
+#pragma unroll
+    for (int j = 1; j < 4 * NQ; ++j) {
+        const bool up = y[j] > ybest;
+        ybest = up ? y[j] : ybest;
+        zx = up ? zs[j] : zx;
+        ibest = up ? static_cast<uint32_t>(col[j >> 2] + (j & 3)) : ibest;
+        m = fmaxf(m, zs[j]);
     }
     const float mb = m * kLog2e;
     float s = 0.0f;
@@ -263,7 +267,8 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
     float* temp_s = reinterpret_cast<float*>(smem + persist_xfrag_bytes<KC>() + e_bytes + bp4);
     Stats* slot = reinterpret_cast<Stats*>(smem + persist_xfrag_bytes<KC>() + e_bytes + 2 * bp4);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: wave-uniform branches
     const int n = lane & 15, g = lane >> 4;
     const int wg = blockIdx.x, nWG = a.nWG;
     const int NB = a.Bpad / 16;
