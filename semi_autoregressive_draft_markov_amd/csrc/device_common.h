@@ -72,6 +72,18 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
     return fmaf(-kLn2, __builtin_amdgcn_logf(L), kNegLnLn2);
 }
 
+// The same draw in base-2 units for a Gumbel-max argmax: with z2 = z log2(e)
+// the perturbed value (z + g) log2(e) - log2(e) (-ln(ln 2)) equals
+// z2 - log2(L), L = -log2(u), a positive multiple of z + g minus a constant,
+// so it has the same argmax.  u is built without a conversion: v_alignbit
+// puts the top 23 bits of w under the exponent of 1.0, giving
+// f = 1 + m 2^-23 in [1, 2), and f - (1 - 2^-24) = (2 m + 1) 2^-24 is exact.
+__device__ __forceinline__ float log2_of_neg_log2_uniform(uint32_t w) {
+    const float f = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w, 9u));
+    const float u = f + -0.99999994039535522461f;  // -(1 - 2^-24)
+    return __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+}
+
 // ------------------------------------------------------- ordered argmax key
 // 64-bit key whose unsigned maximum is the largest value, lowest index on a
 // tie: order-preserving bits of the float (with -0 folded onto +0) in the
@@ -102,6 +114,20 @@ __device__ __forceinline__ Stats stats_merge(const Stats& a, const Stats& b) {
     r.m = fmaxf(a.m, b.m);
     const float sa = (a.s > 0.0f) ? a.s * __expf(a.m - r.m) : 0.0f;
     const float sb = (b.s > 0.0f) ? b.s * __expf(b.m - r.m) : 0.0f;
+    r.s = sa + sb;
+    const bool take_b = b.key > a.key;
+    r.key = take_b ? b.key : a.key;
+    r.zx = take_b ? b.zx : a.zx;
+    return r;
+}
+
+// stats_merge for statistics kept in base-2 units (m and zx multiplied by
+// log2(e), s = sum of 2^(z2 - m2)).
+__device__ __forceinline__ Stats stats_merge2(const Stats& a, const Stats& b) {
+    Stats r;
+    r.m = fmaxf(a.m, b.m);
+    const float sa = (a.s > 0.0f) ? a.s * __builtin_amdgcn_exp2f(a.m - r.m) : 0.0f;
+    const float sb = (b.s > 0.0f) ? b.s * __builtin_amdgcn_exp2f(b.m - r.m) : 0.0f;
     r.s = sa + sb;
     const bool take_b = b.key > a.key;
     r.key = take_b ? b.key : a.key;

@@ -178,18 +178,20 @@ __device__ __forceinline__ void unit_mul(const W2Tile<KC>& w2, bool reg, const u
     }
 }
 
-// Statistics of 4 * NQ tempered logits of block b at columns
-// col[q] .. col[q] + 3 (q = 0..NQ-1, increasing, each a multiple of 4, all
-// below V), perturbed with Gumbel noise when sampling.  A strict running
-// maximum over increasing columns keeps the lowest column among equal
-// maxima.
+// Statistics of 4 * NQ logits of block b at columns col[q] .. col[q] + 3
+// (q = 0..NQ-1, increasing, each a multiple of 4, all below V), in base-2
+// units: z2 = z log2(e) / T, perturbed (when sampling) to z2 - log2(L), the
+// Gumbel-max value up to a positive factor and a constant (see
+// log2_of_neg_log2_uniform).  A strict running maximum over increasing
+// columns keeps the lowest column among equal maxima.  Merge with
+// stats_merge2.
 template <int NQ>
 __device__ __forceinline__ Stats lane_stats(const float (&z)[4 * NQ], const int (&col)[NQ], int b, int k,
-                                            bool sampling, float invT, uint32_t key0, uint32_t key1,
+                                            bool sampling, float scale, uint32_t key0, uint32_t key1,
                                             uint32_t ctr3) {
     float zs[4 * NQ], y[4 * NQ];
 #pragma unroll
-    for (int j = 0; j < 4 * NQ; ++j) zs[j] = z[j] * invT;
+    for (int j = 0; j < 4 * NQ; ++j) zs[j] = z[j] * scale;
     // one branch around all the noise of this lane, so the Philox rounds and
     // logarithms of its columns interleave
     if (sampling) {
@@ -199,7 +201,7 @@ __device__ __forceinline__ Stats lane_stats(const float (&z)[4 * NQ], const int 
                                static_cast<uint32_t>(b), ctr3};
             const u32x4 w = philox4x32_10(ctr, key0, key1);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) y[4 * q + c] = zs[4 * q + c] + gumbel_from_word(w[c]);
+            for (int c = 0; c < 4; ++c) y[4 * q + c] = zs[4 * q + c] - log2_of_neg_log2_uniform(w[c]);
         }
     } else {
 #pragma unroll
@@ -215,10 +217,9 @@ __device__ __forceinline__ Stats lane_stats(const float (&z)[4 * NQ], const int 
         ibest = up ? static_cast<uint32_t>(col[j >> 2] + (j & 3)) : ibest;
         m = fmaxf(m, zs[j]);
     }
-    const float mb = m * kLog2e;
     float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4 * NQ; ++j) s += __builtin_amdgcn_exp2f(fmaf(zs[j], kLog2e, -mb));
+    for (int j = 0; j < 4 * NQ; ++j) s += __builtin_amdgcn_exp2f(zs[j] - m);
     return Stats{m, s, argmax_key(ybest, ibest), zx};
 }
 
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
             if (active && b < a.B) {
                 const float temp = temp_s[b];
                 const bool sampling = temp > 0.0f;
-                const float invT = sampling ? 1.0f / temp : 1.0f;
+                const float scale = sampling ? kLog2e / temp : kLog2e;
                 if (reg_live) {
                     float z[16];
 #pragma unroll
@@ -390,24 +391,24 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
                         for (int c = 0; c < 4; ++c) z[4 * q + c] = acc[c][q];
                     if (v0 + 16 <= a.V) {
                         const int col[4] = {v0, v0 + 4, v0 + 8, v0 + 12};
-                        st = lane_stats<4>(z, col, b, k, sampling, invT, a.key0, a.key1, a.ctr3);
+                        st = lane_stats<4>(z, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3);
                     } else {  // V % 8 == 0: the first 8 columns are in range
                         float zh[8];
                         const int col[2] = {v0, v0 + 4};
 #pragma unroll
                         for (int j = 0; j < 8; ++j) zh[j] = z[j];
-                        st = lane_stats<2>(zh, col, b, k, sampling, invT, a.key0, a.key1, a.ctr3);
+                        st = lane_stats<2>(zh, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3);
                     }
                 }
                 if (x_live) {
                     const float zx4[4] = {accx[0], accx[1], accx[2], accx[3]};
                     const int col[1] = {vx};
-                    st = stats_merge(st, lane_stats<1>(zx4, col, b, k, sampling, invT, a.key0, a.key1, a.ctr3));
+                    st = stats_merge2(st, lane_stats<1>(zx4, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3));
                 }
             }
-            st = stats_merge(st, shfl_xor_stats(st, 16));
-            st = stats_merge(st, shfl_xor_stats(st, 32));
-            if (g == 0 && b < a.B) slot[wave * a.B + b] = stats_merge(slot[wave * a.B + b], st);
+            st = stats_merge2(st, shfl_xor_stats(st, 16));
+            st = stats_merge2(st, shfl_xor_stats(st, 32));
+            if (g == 0 && b < a.B) slot[wave * a.B + b] = stats_merge2(slot[wave * a.B + b], st);
             if (GROUPED && nb + 1 < NB) {
                 store_group(nb + 1);
                 __syncthreads();
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
         for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
             Stats t = slot[b];
 #pragma unroll
-            for (int w = 1; w < kPWaves; ++w) t = stats_merge(t, slot[w * a.B + b]);
+            for (int w = 1; w < kPWaves; ++w) t = stats_merge2(t, slot[w * a.B + b]);
             if (t.key != kKeyNone)
                 __hip_atomic_fetch_max(&a.best[((static_cast<size_t>(k) * a.B + b) * kDraftKeyCopies +
                                                 wg % kDraftKeyCopies) * kKeyStride],
@@ -523,16 +524,16 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
         Stats t = stats_empty();
         const size_t base = (static_cast<size_t>(k) * a.B + b) * a.nWG;
         for (int p = lane; p < a.nWG; p += kWave)
-            t = stats_merge(t, Stats{a.pm[base + p], a.ps[base + p], a.pkey[base + p], a.pzx[base + p]});
+            t = stats_merge2(t, Stats{a.pm[base + p], a.ps[base + p], a.pkey[base + p], a.pzx[base + p]});
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) t = stats_merge(t, shfl_xor_stats(t, o));
+        for (int o = 32; o > 0; o >>= 1) t = stats_merge2(t, shfl_xor_stats(t, o));
         float part = lane_dot_bf16(a.w_conf, a.h + (static_cast<size_t>(b) * a.gamma + k) * a.d, a.d, lane);
         if (!bad) part += lane_dot_bf16(a.w_conf + a.d, a.W1 + static_cast<size_t>(xs[k]) * a.r, a.r, lane);
         const float logit = wave_sum(part);
         if (lane == 0) {
             const size_t out = static_cast<size_t>(b) * a.gamma + k;
             a.tokens[out] = bad ? -1 : xs[k + 1];
-            if (a.logp) a.logp[out] = bad ? NAN : t.zx - (t.m + logf(t.s));
+            if (a.logp) a.logp[out] = bad ? NAN : (t.zx - t.m) * kLn2 - logf(t.s);
             cs[k] = bad ? NAN : sigmoidf_(logit);
         }
     }
