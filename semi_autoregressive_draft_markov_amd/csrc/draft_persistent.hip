@@ -131,25 +131,36 @@ __device__ __forceinline__ T get_shared(const T* p) {
 // LDS area as one extra MFMA A-operand (XFrag): every wave then does the
 // same work per (16-block group), 80 columns of it at full size.
 
-// One 16-column W2 fragment as MFMA A-operands: for chunk kc, lane (g, n)
-// keeps W2[32 kc + 8 g + e][c0 + n], e = 0..7, i.e. row n of A is column
-// c0 + n.  The MFMA result in lane (g, n) is then columns c0 + 4 g + q
-// (q = 0..3) of block row n.  Loaded once per call; columns >= V read 0.
+// The 16-column W2 fragments of a workgroup's 4 waves as MFMA A-operands:
+// wave w's fragment covers columns c0 + 16 w .. c0 + 16 w + 15, and for
+// chunk kc lane (g, n) keeps W2[32 kc + 8 g + e][c0 + 16 w + n], e = 0..7,
+// i.e. row n of A is column c0 + 16 w + n; the MFMA result in lane (g, n) is
+// then columns c0 + 16 w + 4 g + q (q = 0..3) of block row n.  The whole
+// workgroup loads the 64 x r block once per call with 16-byte row loads
+// (two rows per thread and pass) and writes each pair of rows as packed
+// words into the transposed layout.  Columns >= V read 0 (V % 8 == 0).
 template <int KC>
-__device__ __forceinline__ void load_xfrag(const uint16_t* __restrict__ W2, int V, int c0, int g,
-                                           int n, int lane, uint32_t* xf) {
-    const int col = c0 + n;
+__device__ __forceinline__ void load_xfrags(const uint16_t* __restrict__ W2, int V, int c0, uint32_t* xf_all) {
+    constexpr int kPairs = KC * 16;  // row pairs
+    const int cseg = threadIdx.x & 7;
+    const int col = c0 + 8 * cseg;
     const bool ok = col < V;
-    for (int kc = 0; kc < KC; ++kc) {
-        uint32_t w[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const size_t j = static_cast<size_t>(kc * 32 + 8 * g + 2 * p);
-            const uint32_t lo = ok ? W2[j * V + col] : 0u;
-            const uint32_t hi = ok ? W2[(j + 1) * V + col] : 0u;
-            w[p] = lo | (hi << 16);
+    for (int rp = threadIdx.x >> 3; rp < kPairs; rp += 32) {
+        const size_t j0 = static_cast<size_t>(2 * rp);
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (ok) {
+            a = *reinterpret_cast<const u32x4*>(W2 + j0 * V + col);
+            b = *reinterpret_cast<const u32x4*>(W2 + (j0 + 1) * V + col);
         }
-        *reinterpret_cast<u32x4*>(&xf[(kc * kWave + lane) * 4]) = u32x4{w[0], w[1], w[2], w[3]};
+        const int kc = rp >> 4, g = (rp >> 2) & 3, p = rp & 3;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int cc = 8 * cseg + q;  // column within the workgroup's 64
+            const int w = cc >> 4, n = cc & 15;
+            const uint32_t lo = (q & 1) ? (a[q >> 1] >> 16) : (a[q >> 1] & 0xFFFFu);
+            const uint32_t hi = (q & 1) ? (b[q >> 1] & 0xFFFF0000u) : (b[q >> 1] << 16);
+            xf_all[w * (KC * kWave * 4) + (kc * kWave + 16 * g + n) * 4 + p] = lo | hi;
+        }
     }
 }
 
@@ -285,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
 
     W2Tile<KC> w2;
     if (has_reg) w2.load(a.W2, a.V, wv * 64, g, n);
-    if (has_x) load_xfrag<KC>(a.W2, a.V, c0, g, n, lane, xf);
+    load_xfrags<KC>(a.W2, a.V, kPWaves * nWG * 64 + 64 * wg, reinterpret_cast<uint32_t*>(smem));
     // previous tokens of step 0: the anchors (an out-of-range anchor reads
     // row 0; the finish kernel marks its block invalid)
     for (int b = threadIdx.x; b < a.Bpad; b += blockDim.x) {
