@@ -39,6 +39,7 @@ constexpr int kReleaseWord = 288; // barrier release flag
 constexpr int kTimeoutWord = 320; // set when a barrier wait gave up
 static_assert(kTimeoutWord < kDraftBarWords, "barrier words");
 constexpr int kMaxGamma = 64;     // largest gamma the C ABI accepts
+constexpr int kNoiseStride = 256; // noise buffer: [20 columns][256 threads] floats
 
 struct PersistArgs {
     const uint16_t* U;
@@ -196,16 +197,20 @@ __device__ __forceinline__ void unit_mul(const W2Tile<KC>& w2, bool reg, const u
 // log2_of_neg_log2_uniform).  A strict running maximum over increasing
 // columns keeps the lowest column among equal maxima.  Merge with
 // stats_merge2.
-template <int NQ>
+template <int NQ, bool PRE>
 __device__ __forceinline__ Stats lane_stats(const float (&z)[4 * NQ], const int (&col)[NQ], int b, int k,
                                             bool sampling, float scale, uint32_t key0, uint32_t key1,
-                                            uint32_t ctr3) {
+                                            uint32_t ctr3, const float* pre) {
     float zs[4 * NQ], y[4 * NQ];
 #pragma unroll
     for (int j = 0; j < 4 * NQ; ++j) zs[j] = z[j] * scale;
     // one branch around all the noise of this lane, so the Philox rounds and
-    // logarithms of its columns interleave
-    if (sampling) {
+    // logarithms of its columns interleave; PRE: the noise terms were
+    // computed earlier and sit in LDS at pre[256 j]
+    if (PRE && sampling) {
+#pragma unroll
+        for (int j = 0; j < 4 * NQ; ++j) y[j] = zs[j] - pre[kNoiseStride * j];
+    } else if (sampling) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const u32x4 ctr = {static_cast<uint32_t>(col[q]) >> 2, static_cast<uint32_t>(k),
@@ -248,7 +253,11 @@ struct UAhead {
 // staged either all at once after each barrier, or (GROUPED, when all rows
 // would not fit) 16 at a time in two buffers, the next group's rows loaded
 // while the current group is computed.  Either way the MFMA operand comes
-// from LDS, so its wait never covers the U loads still in flight.
+// from LDS, so its wait never covers the U loads still in flight.  AHEAD
+// (small B): the Gumbel terms of the first block group of each step are
+// computed while memory is busy -- under the W2 loads before step 0, under
+// the key and E-row loads after each barrier -- and kept in LDS
+// ([20 columns][256 threads] floats).
 constexpr size_t kPersistLdsMax = 80 * 1024;  // two workgroups per CU
 
 template <int KC>
@@ -259,14 +268,17 @@ template <int KC>
 __host__ __device__ constexpr size_t persist_e_bytes(int rows) {
     return static_cast<size_t>(rows) * (KC * 32 + 8) * 2;
 }
+constexpr size_t kNoiseBytes = 20 * kNoiseStride * 4;
 template <int KC>
-__host__ __device__ constexpr size_t persist_lds(int Bpad, int B, bool grouped) {
+__host__ __device__ constexpr size_t persist_lds(int Bpad, int B, bool grouped, bool ahead) {
     return persist_xfrag_bytes<KC>() + persist_e_bytes<KC>(grouped ? 32 : Bpad) +
-           2 * align_up(static_cast<size_t>(Bpad) * 4, 16) + sizeof(Stats) * kPWaves * static_cast<size_t>(B);
+           2 * align_up(static_cast<size_t>(Bpad) * 4, 16) +
+           align_up(sizeof(Stats) * kPWaves * static_cast<size_t>(B), 16) + (ahead ? kNoiseBytes : 0);
 }
 
-template <int KC, bool GROUPED>
+template <int KC, bool GROUPED, bool AHEAD>
 __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
+    static_assert(!(GROUPED && AHEAD), "noise ahead needs all E rows staged");
     constexpr int r = KC * 32;
     constexpr int ldE = r + 8;  // padded row stride of the staged E rows (bank spread)
     constexpr int kGroupChunks = 16 * (r / 8);                 // 16-byte pieces of 16 rows
@@ -278,6 +290,9 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
     int32_t* prev = reinterpret_cast<int32_t*>(smem + persist_xfrag_bytes<KC>() + e_bytes);
     float* temp_s = reinterpret_cast<float*>(smem + persist_xfrag_bytes<KC>() + e_bytes + bp4);
     Stats* slot = reinterpret_cast<Stats*>(smem + persist_xfrag_bytes<KC>() + e_bytes + 2 * bp4);
+    float* gn = reinterpret_cast<float*>(smem + persist_xfrag_bytes<KC>() + e_bytes + 2 * bp4 +
+                                         align_up(sizeof(Stats) * kPWaves * static_cast<size_t>(a.B), 16)) +
+                threadIdx.x;  // this thread's noise column
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: wave-uniform branches
@@ -294,8 +309,35 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
     const bool has_reg = wv * 64 < a.V, has_x = c0 < a.V;
     const bool reg_live = v0 < a.V, x_live = vx < a.V;
 
+    const bool active = has_reg || has_x;
+    // AHEAD: Gumbel terms of block group 0 at step kk (part 0: the 16
+    // register-tile columns, part 1: the 4 LDS-fragment columns), whether or
+    // not the block samples (the unit only reads them when it does)
+    auto noise_ahead = [&](int kk, int part) {
+        if (!AHEAD || !active || n >= a.B) return;
+        if (part == 0 && reg_live) {
+#pragma unroll 1  // one Philox block at a time: few registers are free here
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(v0 + 4 * q) >> 2, static_cast<uint32_t>(kk),
+                                                    static_cast<uint32_t>(n), a.ctr3},
+                                              a.key0, a.key1);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) gn[kNoiseStride * (4 * q + c)] = log2_of_neg_log2_uniform(w[c]);
+            }
+        }
+        if (part == 1 && x_live) {
+            const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(vx) >> 2, static_cast<uint32_t>(kk),
+                                                static_cast<uint32_t>(n), a.ctr3},
+                                          a.key0, a.key1);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) gn[kNoiseStride * (16 + c)] = log2_of_neg_log2_uniform(w[c]);
+        }
+    };
+
     W2Tile<KC> w2;
     if (has_reg) w2.load(a.W2, a.V, wv * 64, g, n);
+    noise_ahead(0, 0);  // while the tile loads are in flight
+    noise_ahead(0, 1);
     load_xfrags<KC>(a.W2, a.V, kPWaves * nWG * 64 + 64 * wg, reinterpret_cast<uint32_t*>(smem));
     // previous tokens of step 0: the anchors (an out-of-range anchor reads
     // row 0; the finish kernel marks its block invalid)
@@ -313,6 +355,31 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
             const int row = t / (r / 8), col = t % (r / 8);
             *reinterpret_cast<u32x4*>(&Es[row * ldE + col * 8]) =
                 *reinterpret_cast<const u32x4*>(a.W1 + static_cast<size_t>(prev[row]) * r + col * 8);
+        }
+        __syncthreads();
+    };
+    // AHEAD (Bpad <= 32): the same with every load issued first, then the
+    // LDS-fragment noise of step kk, then the stores
+    auto stage_rows_ahead = [&](int kk) {
+        constexpr int kMaxChunks = (32 * (r / 8) + 255) / 256;
+        const int chunks = a.Bpad * (r / 8);
+        u32x4 e[kMaxChunks];
+#pragma unroll
+        for (int i = 0; i < kMaxChunks; ++i) {
+            const int t = threadIdx.x + 256 * i;
+            if (t < chunks) {
+                const int row = t / (r / 8), col = t % (r / 8);
+                e[i] = *reinterpret_cast<const u32x4*>(a.W1 + static_cast<size_t>(prev[row]) * r + col * 8);
+            }
+        }
+        noise_ahead(kk, 1);
+#pragma unroll
+        for (int i = 0; i < kMaxChunks; ++i) {
+            const int t = threadIdx.x + 256 * i;
+            if (t < chunks) {
+                const int row = t / (r / 8), col = t % (r / 8);
+                *reinterpret_cast<u32x4*>(&Es[row * ldE + col * 8]) = e[i];
+            }
         }
         __syncthreads();
     };
@@ -359,7 +426,6 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
         return p;
     };
     stage_rows();
-    const bool active = has_reg || has_x;
     UAhead ahead = fetch_u(0, 0);
 
     for (int k = 0; k < a.gamma; ++k) {
@@ -390,6 +456,7 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
             const uint16_t* erow = GROUPED ? &Es[((nb & 1) * 16 + n) * ldE + 8 * g] : &Es[b * ldE + 8 * g];
             if (active) unit_mul<KC>(w2, has_reg, xf, has_x, erow, lane, acc, accx);
             Stats st = stats_empty();
+            const bool pre = AHEAD && nb == 0;
             if (active && b < a.B) {
                 const float temp = temp_s[b];
                 const bool sampling = temp > 0.0f;
@@ -402,19 +469,23 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
                         for (int c = 0; c < 4; ++c) z[4 * q + c] = acc[c][q];
                     if (v0 + 16 <= a.V) {
                         const int col[4] = {v0, v0 + 4, v0 + 8, v0 + 12};
-                        st = lane_stats<4>(z, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3);
+                        st = pre ? lane_stats<4, true>(z, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gn)
+                                 : lane_stats<4, false>(z, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gn);
                     } else {  // V % 8 == 0: the first 8 columns are in range
                         float zh[8];
                         const int col[2] = {v0, v0 + 4};
 #pragma unroll
                         for (int j = 0; j < 8; ++j) zh[j] = z[j];
-                        st = lane_stats<2>(zh, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3);
+                        st = pre ? lane_stats<2, true>(zh, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gn)
+                                 : lane_stats<2, false>(zh, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gn);
                     }
                 }
                 if (x_live) {
                     const float zx4[4] = {accx[0], accx[1], accx[2], accx[3]};
                     const int col[1] = {vx};
-                    st = stats_merge2(st, lane_stats<1>(zx4, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3));
+                    const float* gx = gn + kNoiseStride * 16;
+                    st = stats_merge2(st, pre ? lane_stats<1, true>(zx4, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gx)
+                                              : lane_stats<1, false>(zx4, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gx));
                 }
             }
             st = stats_merge2(st, shfl_xor_stats(st, 16));
@@ -448,6 +519,7 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
         // copies of a block's key sit in 8 consecutive lanes
         for (int t = threadIdx.x; t < a.B * kDraftKeyCopies; t += blockDim.x) {
             uint64_t key = get_shared(&a.best[(static_cast<size_t>(k) * a.B * kDraftKeyCopies + t) * kKeyStride]);
+            if (AHEAD) noise_ahead(k + 1, 0);  // while the keys are in flight (one pass: B <= 32)
 #pragma unroll
             for (int o = 1; o < kDraftKeyCopies; o <<= 1) {
                 const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o);
@@ -459,8 +531,12 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
             if (t % kDraftKeyCopies == 0)
                 prev[t / kDraftKeyCopies] = (key != kKeyNone && x < static_cast<uint32_t>(a.V)) ? static_cast<int>(x) : 0;
         }
+        if (AHEAD && a.B * kDraftKeyCopies <= static_cast<int>(threadIdx.x)) noise_ahead(k + 1, 0);
         __syncthreads();
-        stage_rows();
+        if (AHEAD)
+            stage_rows_ahead(k + 1);
+        else
+            stage_rows();
     }
 }
 
@@ -566,21 +642,24 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
 struct PersistPlan {
     bool ok = false;
     bool grouped = false;
+    bool ahead = false;
     int nWG = 0;
     size_t lds = 0;
 };
 
 template <int KC>
-static void (*persist_kernel(bool grouped))(PersistArgs) {
-    return grouped ? k_draft_persistent<KC, true> : k_draft_persistent<KC, false>;
+static void (*persist_kernel(bool grouped, bool ahead))(PersistArgs) {
+    if (grouped) return k_draft_persistent<KC, true, false>;
+    return ahead ? k_draft_persistent<KC, false, true> : k_draft_persistent<KC, false, false>;
 }
 
 template <int KC>
 static PersistPlan plan_for(const dspark_dims& D) {
     PersistPlan p;
     const int Bpad = (D.B + 15) / 16 * 16;
-    p.grouped = persist_lds<KC>(Bpad, D.B, false) > kPersistLdsMax;
-    p.lds = persist_lds<KC>(Bpad, D.B, p.grouped);
+    p.grouped = persist_lds<KC>(Bpad, D.B, false, false) > kPersistLdsMax;
+    p.ahead = !p.grouped && Bpad <= 32 && persist_lds<KC>(Bpad, D.B, false, true) <= kPersistLdsMax;
+    p.lds = persist_lds<KC>(Bpad, D.B, p.grouped, p.ahead);
     if (p.lds > kPersistLdsMax) return p;
     int dev = 0, cus = 0, coop = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return p;
@@ -588,7 +667,7 @@ static PersistPlan plan_for(const dspark_dims& D) {
     if (persist_launch_option() == 1 &&
         (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop))
         return p;
-    void (*fn)(PersistArgs) = persist_kernel<KC>(p.grouped);
+    void (*fn)(PersistArgs) = persist_kernel<KC>(p.grouped, p.ahead);
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(p.lds)) != hipSuccess)
         return p;
@@ -651,7 +730,7 @@ static hipError_t launch_persist_kc(const DraftArgs& A) {
     if (e != hipSuccess) return e;
     if ((e = profile_begin(A.stream)) != hipSuccess) return e;
     void* args[] = {&p};
-    void (*fn)(PersistArgs) = persist_kernel<KC>(plan.grouped);
+    void (*fn)(PersistArgs) = persist_kernel<KC>(plan.grouped, plan.ahead);
     const size_t lds = plan.lds;
     if (persist_launch_option() == 0)
         e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG), dim3(256), args, lds,
