@@ -8,9 +8,10 @@ Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Each step uses a new noise offset (offset = step index).
 
 Prints one JSON line: drafted tokens/s over the K timed steps, the roofline
-of the dominant kernel (the V-streaming step kernel, timed with HIP events on
-the library's stream during the timed region) and the CPU oracle's rate on a
-bounded sample of the same workload.
+of the dominant kernel (the single-launch drafting kernel, or the V-streaming
+step kernel of the per-step driver, timed with HIP events on the library's
+stream during the timed region) and the CPU oracle's rate on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -27,9 +28,10 @@ sys.path.insert(0, ROOT)
 METRIC = "drafted block-tokens/s (V=151936, r=256, γ=7) + % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 WORKLOAD_CFG = 2
-COUNTERS = os.path.join(ROOT, "profiles", "stream_kernel_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "draft_persistent_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "semi_autoregressive_draft_markov_amd", "csrc", f)
-                  for f in ("draft.hip", "draft_persistent.hip", "mfma_tile.h", "device_common.h")]
+                  for f in ("draft.hip", "draft_persistent.hip", "mfma_tile.h", "device_common.h",
+                            "internal.h")]
 
 
 def kernel_source_hash() -> str:
@@ -240,7 +242,9 @@ def main() -> int:
     avg_kernel_s = kernel_ms * 1e-3 / launches
     if per_call == 1:
         # single-launch driver: W2 is read once per call, every step's U slice once
-        driver, kname = "single-launch (%s)" % args.launch, "k_draft_persistent<8>"
+        # variant: all E rows staged, Gumbel terms of the first group ahead (B <= 32)
+        driver = "single-launch (%s)" % args.launch
+        kname = "k_draft_persistent<8, false, %s>" % ("true" if B <= 32 else "false")
         alg_bytes = (r + gamma * B) * V * 2
     else:
         # per-step driver: every step streams all of W2 plus its slice of U

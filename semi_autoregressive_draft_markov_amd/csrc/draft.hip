@@ -66,9 +66,7 @@ DraftLayout draft_layout(const dspark_dims& d) {
     L.best = take(sizeof(uint64_t) * 16 * kDraftKeyCopies * static_cast<size_t>(d.B) * d.gamma);
     L.bar = take(sizeof(uint32_t) * kDraftBarWords);
     const size_t nq = static_cast<size_t>(d.gamma) * d.B * draft_persist_max_wg();
-    L.qm = take(sizeof(float) * nq);
-    L.qs = take(sizeof(float) * nq);
-    L.qkey = take(sizeof(uint64_t) * nq);
+    L.qms = take(sizeof(float) * 2 * nq);
     L.qzx = take(sizeof(float) * nq);
     const size_t np = static_cast<size_t>(d.B) * L.P;
     L.pm = take(sizeof(float) * np);

@@ -53,10 +53,8 @@ struct PersistArgs {
     uint32_t key0, key1, ctr3;
     uint64_t* best;      // [gamma, B, copies, 16]  argmax keys, one 128-byte line each (cleared by prepare)
     uint32_t* bar;       // barrier words (cleared by prepare)
-    float* pm;           // [gamma, B, nWG] softmax partials of every step
-    float* ps;
-    uint64_t* pkey;
-    float* pzx;
+    float2* pms;         // [gamma, B, nWG] softmax (max, sum) partials of every step, base 2
+    float* pzx;          // [gamma, B, nWG] base-2 logit at each workgroup's argmax
     int32_t* dead;       // [B]
     int32_t* tokens;
     float* logp;
@@ -116,6 +114,15 @@ __device__ __forceinline__ void grid_barrier(uint32_t* bar, uint32_t step, uint3
         }
     }
     __syncthreads();
+}
+
+// Slot of workgroup wg in the per-step partial arrays.  Workgroups are
+// dealt to the 8 XCDs in turn (wg % 8), so slots are grouped by wg % 8: the
+// partials one XCD writes fill whole cache lines instead of every eighth
+// word of many lines.
+__host__ __device__ __forceinline__ int partial_slot(int wg, int nwg) {
+    const int x = wg % kBarGroups, per = nwg / kBarGroups, extra = nwg % kBarGroups;
+    return x * per + (x < extra ? x : extra) + wg / kBarGroups;
 }
 
 // Device-scope (coherent) load of data other workgroups wrote in this kernel.
@@ -507,10 +514,8 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
                                                 wg % kDraftKeyCopies) * kKeyStride],
                                        t.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // softmax partials are read after the kernel (k_persist_finish)
-            const size_t o = (static_cast<size_t>(k) * a.B + b) * nWG + wg;
-            a.pm[o] = t.m;
-            a.ps[o] = t.s;
-            a.pkey[o] = t.key;
+            const size_t o = (static_cast<size_t>(k) * a.B + b) * nWG + partial_slot(wg, nWG);
+            a.pms[o] = make_float2(t.m, t.s);
             a.pzx[o] = t.zx;
         }
         if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
@@ -573,8 +578,9 @@ __device__ __forceinline__ float lane_dot_bf16(const uint16_t* x, const uint16_t
 }
 
 // Workgroup b, after the loop.  Wave w handles positions k = w, w + 8, ...:
-// x_k from the argmax keys, log p_k from the step's softmax partials (merged
-// lane-strided, then across the wave), c_k = sigma(w[0:d] . h_{b,k} +
+// x_k from the argmax keys, log p_k from the step's (max, sum) partials
+// (merged lane-strided, then across the wave) and the logit of x_k kept by
+// the workgroup that owns that column, c_k = sigma(w[0:d] . h_{b,k} +
 // w[d:d+r] . W1[x_{k-1}]) (Eq 7, x_{-1} = the anchor); then S_k = c_0 ... c_k
 // in position order.  A block is invalid from its first position whose
 // previous token is out of range, or entirely when a grid barrier gave up.
@@ -608,19 +614,36 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
     const int first_bad = first_bad_s;
     for (int k = wave; k < a.gamma; k += kFinishWaves) {
         const bool bad = k >= first_bad;
-        Stats t = stats_empty();
+        // (max, sum) over all workgroups; the logit of x_k from the
+        // workgroup whose columns hold x_k
         const size_t base = (static_cast<size_t>(k) * a.B + b) * a.nWG;
-        for (int p = lane; p < a.nWG; p += kWave)
-            t = stats_merge2(t, Stats{a.pm[base + p], a.ps[base + p], a.pkey[base + p], a.pzx[base + p]});
+        float m = -INFINITY, sum = 0.0f;
+        for (int p = lane; p < a.nWG; p += kWave) {
+            const float2 q = a.pms[base + p];
+            const float mm = fmaxf(m, q.x);
+            sum = (sum > 0.0f ? sum * __builtin_amdgcn_exp2f(m - mm) : 0.0f) +
+                  (q.y > 0.0f ? q.y * __builtin_amdgcn_exp2f(q.x - mm) : 0.0f);
+            m = mm;
+        }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) t = stats_merge2(t, shfl_xor_stats(t, o));
+        for (int o = 32; o > 0; o >>= 1) {
+            const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sum, o);
+            const float mm = fmaxf(m, m2);
+            sum = (sum > 0.0f ? sum * __builtin_amdgcn_exp2f(m - mm) : 0.0f) +
+                  (s2 > 0.0f ? s2 * __builtin_amdgcn_exp2f(m2 - mm) : 0.0f);
+            m = mm;
+        }
+        const int xk = bad ? 0 : xs[k + 1];  // in range unless bad
+        const int c_reg = kPWaves * a.nWG * 64;  // columns below this sit in register tiles
+        const int owner = (xk < c_reg ? xk / 64 : (xk - c_reg) / 16) / kPWaves;
+        const float zx = bad ? 0.0f : a.pzx[base + partial_slot(owner, a.nWG)];
         float part = lane_dot_bf16(a.w_conf, a.h + (static_cast<size_t>(b) * a.gamma + k) * a.d, a.d, lane);
         if (!bad) part += lane_dot_bf16(a.w_conf + a.d, a.W1 + static_cast<size_t>(xs[k]) * a.r, a.r, lane);
         const float logit = wave_sum(part);
         if (lane == 0) {
             const size_t out = static_cast<size_t>(b) * a.gamma + k;
             a.tokens[out] = bad ? -1 : xs[k + 1];
-            if (a.logp) a.logp[out] = bad ? NAN : (t.zx - t.m) * kLn2 - logf(t.s);
+            if (a.logp) a.logp[out] = bad ? NAN : (zx - m) * kLn2 - logf(sum);
             cs[k] = bad ? NAN : sigmoidf_(logit);
         }
     }
@@ -717,9 +740,7 @@ static hipError_t launch_persist_kc(const DraftArgs& A) {
     p.ctr3 = static_cast<uint32_t>(A.offset);
     p.best = reinterpret_cast<uint64_t*>(ws + L.best);
     p.bar = reinterpret_cast<uint32_t*>(ws + L.bar);
-    p.pm = reinterpret_cast<float*>(ws + L.qm);
-    p.ps = reinterpret_cast<float*>(ws + L.qs);
-    p.pkey = reinterpret_cast<uint64_t*>(ws + L.qkey);
+    p.pms = reinterpret_cast<float2*>(ws + L.qms);
     p.pzx = reinterpret_cast<float*>(ws + L.qzx);
     p.dead = reinterpret_cast<int32_t*>(ws + L.dead);
     p.tokens = A.tokens; p.logp = A.logp; p.conf = A.conf; p.survival = A.survival;
