@@ -283,75 +283,108 @@ __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int 
 
 // ----------------------------------------------------- pass kernels (MFMA)
 
+// Inputs of one 16-row block for one lane: its row's E operand chunks and
+// 16 columns of U and T, loaded a block ahead of use so that the HBM latency
+// overlaps the previous block's MFMA and epilogue.
+template <int KC>
+struct BlockIn {
+    u32x4 e[KC];
+    u32x4 u0, u1, t0, t1;
+};
+
 // Work item = (column group cg of 256 columns, row chunk rc).  The
 // workgroup's 4 waves hold the 4 W2 tiles of cg in registers and walk the
-// chunk 16 rows at a time; the 16 E rows of each step are shared through
-// LDS (row stride padded by 16 bytes against bank conflicts).
+// chunk 16 rows at a time.  Each lane reads its own row's E operand from
+// global memory (L2-resident: the 4 waves share it), so the only
+// workgroup barrier left is the cross-wave merge of the row partials
+// (double-buffered, one barrier per block; none in pass 3).
 template <int KC, int PASS>
-__global__ __launch_bounds__(256) void k_loss_mfma(PassArgs a) {
+__global__ __launch_bounds__(256, 1) void k_loss_mfma(PassArgs a) {
     constexpr int r = KC * 32;
-    constexpr int ldE = r + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t Es[16 * ldE];
-    __shared__ RowPart red[kLossWaves][16];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ RowPart red[2][kLossWaves][16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int items = a.P * a.nrc;
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
         const int cg = item % a.P, rc = item / a.P;
         const int vt = cg * kLossColsPerWG + wave * 64;
-        W2Tile<KC> w2;
-        w2.load(a.W2, a.V, vt, g, n);
         const int v0 = vt + 16 * g;
+        const bool cols = v0 < a.V, second = v0 + 8 < a.V;
         const int rb0 = rc * a.rb_per_chunk;
         const int rb1 = min(a.Rpad / 16, rb0 + a.rb_per_chunk);
-        for (int rb = rb0; rb < rb1; ++rb) {
-            __syncthreads();
-            for (int t = threadIdx.x; t < 16 * (r / 8); t += blockDim.x) {
-                const int er = t / (r / 8), ec = t % (r / 8);
-                *reinterpret_cast<u32x4*>(&Es[er * ldE + ec * 8]) =
-                    *reinterpret_cast<const u32x4*>(a.ebf + static_cast<size_t>(rb * 16 + er) * r + ec * 8);
+        auto fetch = [&](int rb) {
+            BlockIn<KC> in;
+            const int row = rb * 16 + n;  // < Rpad: E rows are padded
+            const uint16_t* erow = a.ebf + static_cast<size_t>(row) * r + 8 * g;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) in.e[kc] = *reinterpret_cast<const u32x4*>(erow + 32 * kc);
+            in.u0 = in.u1 = in.t0 = in.t1 = u32x4{0u, 0u, 0u, 0u};
+            if (row < a.R && cols) {
+                const size_t o = static_cast<size_t>(row) * a.V + v0;
+                in.u0 = *reinterpret_cast<const u32x4*>(a.U + o);
+                in.t0 = *reinterpret_cast<const u32x4*>(a.T + o);
+                if (second) {
+                    in.u1 = *reinterpret_cast<const u32x4*>(a.U + o + 8);
+                    in.t1 = *reinterpret_cast<const u32x4*>(a.T + o + 8);
+                }
             }
-            __syncthreads();
+            return in;
+        };
+        W2Tile<KC> w2;
+        w2.load(a.W2, a.V, vt, g, n);
+        BlockIn<KC> nxt = fetch(rb0);
+        for (int rb = rb0; rb < rb1; ++rb) {
+            const BlockIn<KC> cur = nxt;
+            if (rb + 1 < rb1) nxt = fetch(rb + 1);
             f32x4 acc[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            w2.mul(&Es[n * ldE + 8 * g], acc);
-
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const bf16x8 bop = __builtin_bit_cast(bf16x8, cur.e[kc]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 av = {w2.f[kc][c][0], w2.f[kc][c][1], w2.f[kc][c][2], w2.f[kc][c][3]};
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bop,
+                                                                     acc[c], 0, 0, 0);
+                }
+            }
             const int row = rb * 16 + n;
             RowPart p = rowpart_empty(PASS);
-            if (row < a.R && v0 < a.V) {
-                const size_t o = static_cast<size_t>(row) * a.V + v0;
+            if (row < a.R && cols) {
+                const uint32_t uw[8] = {cur.u0[0], cur.u0[1], cur.u0[2], cur.u0[3],
+                                        cur.u1[0], cur.u1[1], cur.u1[2], cur.u1[3]};
+                const uint32_t tw[8] = {cur.t0[0], cur.t0[1], cur.t0[2], cur.t0[3],
+                                        cur.t1[0], cur.t1[1], cur.t1[2], cur.t1[3]};
                 float zd[16], zt[16];
-                load16_bf16(a.U + o, v0 + 8 < a.V, zd);
-                load16_bf16(a.T + o, v0 + 8 < a.V, zt);
                 const int nvalid = a.V - v0;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const int j = 4 * q + c;
-                        zd[j] += acc[c][q];
-                        if (j >= nvalid) {
-                            zd[j] = -INFINITY;
-                            zt[j] = -INFINITY;
-                        }
+                        const bool in = j < nvalid;
+                        zd[j] = in ? ((j & 1) ? hi_bf16(uw[j >> 1]) : lo_bf16(uw[j >> 1])) + acc[c][q] : -INFINITY;
+                        zt[j] = in ? ((j & 1) ? hi_bf16(tw[j >> 1]) : lo_bf16(tw[j >> 1])) : -INFINITY;
                     }
                 p = row_epilogue<PASS, 16>(a, row, v0, zd, zt);
             }
             if (PASS == kPass3) continue;
             p = rowpart_merge(PASS, p, rowpart_shfl(p, 16));
             p = rowpart_merge(PASS, p, rowpart_shfl(p, 32));
-            if (g == 0) red[wave][n] = p;
+            if (g == 0) red[rb & 1][wave][n] = p;
             __syncthreads();
             if (wave == 0 && g == 0 && row < a.R) {
-                RowPart t = red[0][n];
+                RowPart t = red[rb & 1][0][n];
 #pragma unroll
-                for (int w = 1; w < kLossWaves; ++w) t = rowpart_merge(PASS, t, red[w][n]);
+                for (int w = 1; w < kLossWaves; ++w) t = rowpart_merge(PASS, t, red[rb & 1][w][n]);
                 const size_t o = static_cast<size_t>(cg) * a.Rpad + row;
                 const int nv = PASS == kPass1 ? 5 : 3;
                 for (int q = 0; q < nv; ++q) a.part[q][o] = t.v[q];
             }
         }
+        if (PASS != kPass3) __syncthreads();  // red is reused by the next item
     }
 }
 
