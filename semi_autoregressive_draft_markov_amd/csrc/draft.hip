@@ -6,7 +6,8 @@
 // One call runs the whole left-to-right loop on the device:
 //   init                      e = W1[x_0], c_1, S_1
 //   for k = 0 .. gamma-1:
-//     [RNN] gates + update    G = W_rnn [s; e; h_k]; s, o = tanh(G_o)
+//     [RNN] gates + update    G = W_rnn [s; e; h_k] (h columns for all k
+//                             before the loop); s, o = tanh(G_o)
 //     stream                  z = U_k + coef W2 over V tiles -> per-tile
 //                             softmax / Gumbel-argmax partial statistics
 //     combine                 x_k, log p_k; e = W1[x_k]; c_{k+1}, S_{k+1}
@@ -62,6 +63,7 @@ DraftLayout draft_layout(const dspark_dims& d) {
     L.ebf = take(sizeof(uint16_t) * 2 * rows * d.r);
     L.state = take(sizeof(float) * rows * d.r);
     L.gates = take(sizeof(float) * rows * 3 * d.r);
+    L.gh = take(d.head == DSPARK_HEAD_RNN ? sizeof(float) * static_cast<size_t>(d.B) * d.gamma * 3 * d.r : 0);
     L.hdot = take(sizeof(float) * static_cast<size_t>(d.B) * d.gamma);
     L.best = take(sizeof(uint64_t) * 16 * kDraftKeyCopies * static_cast<size_t>(d.B) * d.gamma);
     L.bar = take(sizeof(uint32_t) * kDraftBarWords);
@@ -174,6 +176,158 @@ __global__ __launch_bounds__(256) void k_rnn_gates(
         __syncthreads();
     }
     if (q0 + tq < Q && b0 + tb < B) gates[static_cast<size_t>(b0 + tb) * Q + q0 + tq] = acc;
+}
+
+// Matrix-core form of the same projection (bf16 weights, r % 32 == 0,
+// d % 8 == 0).  The columns of W_rnn that multiply h_k do not depend on the
+// drafted tokens, so their part of G is one GEMM over all B x gamma
+// positions before the loop (k_gate_h); each step then only adds the s and
+// e columns (k_gate_step).  D[q][m] = sum_j W_rnn[q][col(j)] A[m][j] is
+// built from v_mfma_f32_16x16x32_bf16 tiles with A = 16 rows of W_rnn and
+// B = 16 operand rows: lane (g, n) supplies W_rnn row q0 + n and operand row
+// m0 + n at k = 8 g .. 8 g + 7 of the chunk and receives D[q0 + 4 g + i]
+// [m0 + n] in accumulator element i.  A wave computes a 32 (q) x 32 (m)
+// tile.  Products of bf16 values are exact in fp32; the fp32 state s is fed
+// as three bf16 pieces hi + mid + lo, which sum to s exactly, so the step
+// GEMM keeps fp32 accuracy.
+constexpr int kGateTile = 32;
+
+__device__ __forceinline__ u32x4 load8_bf16_or0(const uint16_t* p, bool ok) {
+    return ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// 8 consecutive floats -> 8 bf16 (round to nearest even) packed in pairs.
+__device__ __forceinline__ u32x4 pack8_bf16(const float (&x)[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) r[p] = f32_to_bf16(x[2 * p]) | (f32_to_bf16(x[2 * p + 1]) << 16);
+    return r;
+}
+
+__device__ __forceinline__ void gate_mfma2x2(const u32x4 (&wa)[2], const u32x4 (&ob)[2], f32x4 (&acc)[2][2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[i]),
+                                                                __builtin_bit_cast(bf16x8, ob[j]), acc[i][j], 0, 0, 0);
+}
+
+// Gh[m][q] = sum_{i<d} W_rnn[q][2r + i] h[m][i] for the M = B x gamma rows
+// of h (row m = b gamma + k).
+__global__ __launch_bounds__(256) void k_gate_h(const uint16_t* __restrict__ W_rnn, const uint16_t* __restrict__ h,
+                                                int r, int d, int M, float* __restrict__ Gh) {
+    const int Q = 3 * r, ldw = 2 * r + d;
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+    const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int tq = Q / kGateTile;
+    const int q0 = (tile % tq) * kGateTile, m0 = (tile / tq) * kGateTile;
+    if (m0 >= M) return;
+    const uint16_t* wrow[2] = {W_rnn + static_cast<size_t>(q0 + n) * ldw + 2 * r,
+                               W_rnn + static_cast<size_t>(q0 + 16 + n) * ldw + 2 * r};
+    const bool mok[2] = {m0 + n < M, m0 + 16 + n < M};
+    const uint16_t* hrow[2] = {h + static_cast<size_t>(mok[0] ? m0 + n : 0) * d,
+                               h + static_cast<size_t>(mok[1] ? m0 + 16 + n : 0) * d};
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    u32x4 wa[2], ob[2];
+    auto fetch = [&](int k0) {
+        const int kk = k0 + 8 * g;
+        const bool kin = kk < d;  // d % 8 == 0: a lane's 8 values are all in or all out
+#pragma unroll
+        for (int i = 0; i < 2; ++i) wa[i] = load8_bf16_or0(wrow[i] + kk, kin);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) ob[j] = load8_bf16_or0(hrow[j] + kk, kin && mok[j]);
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < d; k0 += 32) {
+        const u32x4 ca[2] = {wa[0], wa[1]}, cb[2] = {ob[0], ob[1]};
+        if (k0 + 32 < d) fetch(k0 + 32);
+        gate_mfma2x2(ca, cb, acc);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = m0 + 16 * j + n;
+        if (m >= M) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Gh[static_cast<size_t>(m) * Q + q0 + 16 * i + 4 * g + e] = acc[i][j][e];
+    }
+}
+
+// G[b][q] = Gh[b gamma + k][q] + sum_j W_rnn[q][j] s[b][j] + sum_j
+// W_rnn[q][r + j] e[b][j] for the B blocks at step k.
+__global__ __launch_bounds__(256) void k_gate_step(const uint16_t* __restrict__ W_rnn, const float* __restrict__ Gh,
+                                                   const float* __restrict__ state, const float* __restrict__ emb,
+                                                   int r, int d, int gamma, int k, int B, float* __restrict__ gates) {
+    const int Q = 3 * r, ldw = 2 * r + d;
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+    const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int tq = Q / kGateTile;
+    const int q0 = (tile % tq) * kGateTile, m0 = (tile / tq) * kGateTile;
+    if (m0 >= B) return;
+    const uint16_t* wrow[2] = {W_rnn + static_cast<size_t>(q0 + n) * ldw,
+                               W_rnn + static_cast<size_t>(q0 + 16 + n) * ldw};
+    const bool mok[2] = {m0 + n < B, m0 + 16 + n < B};
+    const size_t brow[2] = {static_cast<size_t>(mok[0] ? m0 + n : 0) * r,
+                            static_cast<size_t>(mok[1] ? m0 + 16 + n : 0) * r};
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < r; k0 += 32) {
+        const int kk = k0 + 8 * g;
+        u32x4 ws_[2], we[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            ws_[i] = *reinterpret_cast<const u32x4*>(wrow[i] + kk);
+            we[i] = *reinterpret_cast<const u32x4*>(wrow[i] + r + kk);
+        }
+        u32x4 shi[2], smid[2], slo[2], eb[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float s[8], e[8], t[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                s[q] = mok[j] ? state[brow[j] + kk + q] : 0.0f;
+                e[q] = mok[j] ? emb[brow[j] + kk + q] : 0.0f;
+            }
+            shi[j] = pack8_bf16(s);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) t[q] = s[q] - __uint_as_float((q & 1 ? shi[j][q >> 1] >> 16 : shi[j][q >> 1]) << 16);
+            smid[j] = pack8_bf16(t);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) t[q] -= __uint_as_float((q & 1 ? smid[j][q >> 1] >> 16 : smid[j][q >> 1]) << 16);
+            slo[j] = pack8_bf16(t);
+            eb[j] = pack8_bf16(e);  // exact: e is a bf16 row of W1
+        }
+        gate_mfma2x2(ws_, shi, acc);
+        gate_mfma2x2(ws_, smid, acc);
+        gate_mfma2x2(ws_, slo, acc);
+        gate_mfma2x2(we, eb, acc);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = m0 + 16 * j + n;
+        if (m >= B) continue;
+        const float* gh = Gh + (static_cast<size_t>(m) * gamma + k) * Q;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int q = q0 + 16 * i + 4 * g + e;
+                gates[static_cast<size_t>(m) * Q + q] = gh[q] + acc[i][j][e];
+            }
+    }
+}
+
+bool rnn_gate_mfma_ok(const dspark_dims& d) {
+    return d.dtype == DSPARK_BF16 && d.r % 32 == 0 && d.d % 8 == 0;
 }
 
 // Gated state update of Eq 6 and the bias coefficients o = tanh(W_o z).
@@ -498,10 +652,31 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
     hipLaunchKernelGGL((k_draft_init<T>), dim3(L.Bpad, D.gamma), dim3(256), 0, a.stream, a.anchor, W1, wc, h,
                        D.V, D.r, D.d, D.gamma, D.B, L.Bpad, D.head, dead, emb, coef, ebf, state,
                        reinterpret_cast<float*>(ws + L.hdot), a.conf, a.survival);
+    // RNN on matrix cores: the h columns of the joint projection for every
+    // position at once, before the loop
+    const bool gate_mfma = D.head == DSPARK_HEAD_RNN && rnn_gate_mfma_ok(D) &&
+                           (reinterpret_cast<uintptr_t>(a.W_rnn) & 15) == 0 &&
+                           (reinterpret_cast<uintptr_t>(a.h) & 15) == 0;
+    float* gh = reinterpret_cast<float*>(ws + L.gh);
+    const int gate_tq = 3 * D.r / kGateTile;
+    if (gate_mfma) {
+        const int M = D.B * D.gamma;
+        const int tiles = gate_tq * ((M + kGateTile - 1) / kGateTile);
+        hipLaunchKernelGGL(k_gate_h, dim3((tiles + 3) / 4), dim3(256), 0, a.stream,
+                           reinterpret_cast<const uint16_t*>(Wr), reinterpret_cast<const uint16_t*>(h), D.r, D.d, M,
+                           gh);
+    }
     for (int k = 0; k < D.gamma; ++k) {
         if (D.head == DSPARK_HEAD_RNN) {
-            hipLaunchKernelGGL((k_rnn_gates<T>), dim3((3 * D.r + 15) / 16, (D.B + 15) / 16), dim3(256), 0,
-                               a.stream, Wr, state, emb, h, D.r, D.d, D.gamma, k, D.B, gates);
+            if (gate_mfma) {
+                const int tiles = gate_tq * ((D.B + kGateTile - 1) / kGateTile);
+                hipLaunchKernelGGL(k_gate_step, dim3((tiles + 3) / 4), dim3(256), 0, a.stream,
+                                   reinterpret_cast<const uint16_t*>(Wr), gh, state, emb, D.r, D.d, D.gamma, k, D.B,
+                                   gates);
+            } else {
+                hipLaunchKernelGGL((k_rnn_gates<T>), dim3((3 * D.r + 15) / 16, (D.B + 15) / 16), dim3(256), 0,
+                                   a.stream, Wr, state, emb, h, D.r, D.d, D.gamma, k, D.B, gates);
+            }
             hipLaunchKernelGGL(k_rnn_update, dim3(D.B), dim3(256), 0, a.stream, gates, state, coef, ebf,
                                D.r, L.Bpad);
         }

@@ -28,6 +28,7 @@ struct DraftLayout {
     size_t ebf;        // u16 [2, Bpad, r] bf16 planes of coef (hi, lo)
     size_t state;      // f32 [Bpad, r]  RNN state s
     size_t gates;      // f32 [Bpad, 3r] RNN joint projection output
+    size_t gh;         // f32 [B, gamma, 3r] h columns of the RNN projection (RNN head only)
     size_t hdot;       // f32 [B, gamma]  h part of the Eq 7 logit, w[0:d] . h_k
     size_t best;       // u64 [gamma, B, copies, 16]  argmax keys, one line each (single-launch path)
     size_t bar;        // u32 [512]  grid barrier: arrival counters, release and timeout flags
@@ -38,6 +39,7 @@ struct DraftLayout {
 };
 
 bool mfma_path_ok(const dspark_dims& d);
+bool rnn_gate_mfma_ok(const dspark_dims& d);
 bool persist_path_ok(const dspark_dims& d);
 int draft_persist_max_wg();
 hipError_t launch_draft_persistent(const struct DraftArgs& a);

@@ -81,11 +81,16 @@ def test_bf16_rank256_tail_columns(ops, B, path):
     check_draft(inp, g, 2, 0, label="bf16 r256")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_rnn_head_small(ops, dtype):
-    inp = small(V=512, r=32, d=40, gamma=4, B=10, head="rnn", dtype=dtype, seed=8,
-                wrnn_std=0.3, temperature=[1.0] * 5 + [0.0] * 5)
-    note("case: rnn %s V512 r32 B10" % dtype)
+# bf16 with d % 8 == 0: joint projection on matrix cores (h columns hoisted
+# out of the loop, ragged 32-row tiles, a d tail shorter than 32); f32 and
+# d % 8 != 0: the vector projection
+@pytest.mark.parametrize("dtype,V,r,d,B", [("bf16", 512, 32, 40, 10), ("f32", 512, 32, 40, 10),
+                                           ("bf16", 1000, 64, 72, 37), ("bf16", 512, 32, 20, 5)])
+def test_rnn_head_small(ops, dtype, V, r, d, B):
+    temps = [1.0] * ((B + 1) // 2) + [0.0] * (B // 2)
+    inp = small(V=V, r=r, d=d, gamma=4, B=B, head="rnn", dtype=dtype, seed=8,
+                wrnn_std=0.3, temperature=temps)
+    note("case: rnn %s V%d r%d d%d B%d" % (dtype, V, r, d, B))
     g = run_gpu(ops, inp, seed=6, offset=1)
     check_draft(inp, g, 6, 1, label="rnn " + dtype)
 
