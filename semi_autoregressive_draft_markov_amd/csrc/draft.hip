@@ -185,12 +185,15 @@ __global__ __launch_bounds__(256) void k_rnn_gates(
 // e columns (k_gate_step).  D[q][m] = sum_j W_rnn[q][col(j)] A[m][j] is
 // built from v_mfma_f32_16x16x32_bf16 tiles with A = 16 rows of W_rnn and
 // B = 16 operand rows: lane (g, n) supplies W_rnn row q0 + n and operand row
-// m0 + n at k = 8 g .. 8 g + 7 of the chunk and receives D[q0 + 4 g + i]
-// [m0 + n] in accumulator element i.  A wave computes a 32 (q) x 32 (m)
-// tile.  Products of bf16 values are exact in fp32; the fp32 state s is fed
-// as three bf16 pieces hi + mid + lo, which sum to s exactly, so the step
-// GEMM keeps fp32 accuracy.
+// m0 + n at k = 8 g .. 8 g + 7 of a 32-wide chunk and receives D[q0 + 4 g +
+// i][m0 + n] in accumulator element i.  A workgroup computes one 32 (q) x 32
+// (m) tile; its 4 waves take every 4th chunk of K, so each wave has few
+// dependent loads in flight, and the 4 partial tiles are added in wave order
+// through LDS (deterministic).  Products of bf16 values are exact in fp32;
+// the fp32 state s is fed as three bf16 pieces hi + mid + lo, which sum to s
+// exactly, so the step GEMM keeps fp32 accuracy.
 constexpr int kGateTile = 32;
+constexpr int kGateWaves = 4;
 
 __device__ __forceinline__ u32x4 load8_bf16_or0(const uint16_t* p, bool ok) {
     return ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
@@ -204,6 +207,11 @@ __device__ __forceinline__ u32x4 pack8_bf16(const float (&x)[8]) {
     return r;
 }
 
+// bf16 element q (0..7) of a packed 8-element operand, as float.
+__device__ __forceinline__ float unpack8_at(const u32x4& v, int q) {
+    return (q & 1) ? hi_bf16(v[q >> 1]) : lo_bf16(v[q >> 1]);
+}
+
 __device__ __forceinline__ void gate_mfma2x2(const u32x4 (&wa)[2], const u32x4 (&ob)[2], f32x4 (&acc)[2][2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -213,16 +221,43 @@ __device__ __forceinline__ void gate_mfma2x2(const u32x4 (&wa)[2], const u32x4 (
                                                                 __builtin_bit_cast(bf16x8, ob[j]), acc[i][j], 0, 0, 0);
 }
 
+// Adds the partial tiles of the 4 waves in wave order; wave 0 calls
+// store(i, j, e, value) for every element of the tile.
+template <typename Store>
+__device__ __forceinline__ void gate_reduce(const f32x4 (&acc)[2][2], Store store) {
+    __shared__ f32x4 part[kGateWaves][4][kWave];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) part[wave][2 * i + j][lane] = acc[i][j];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f32x4 t = part[0][2 * i + j][lane];
+#pragma unroll
+            for (int w = 1; w < kGateWaves; ++w) {
+                const f32x4 u = part[w][2 * i + j][lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] += u[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) store(i, j, e, t[e]);
+        }
+}
+
 // Gh[m][q] = sum_{i<d} W_rnn[q][2r + i] h[m][i] for the M = B x gamma rows
-// of h (row m = b gamma + k).
+// of h (row m = b gamma + k).  Grid: one workgroup per 32 x 32 tile.
 __global__ __launch_bounds__(256) void k_gate_h(const uint16_t* __restrict__ W_rnn, const uint16_t* __restrict__ h,
                                                 int r, int d, int M, float* __restrict__ Gh) {
     const int Q = 3 * r, ldw = 2 * r + d;
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-    const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wave = threadIdx.x >> 6;
     const int tq = Q / kGateTile;
-    const int q0 = (tile % tq) * kGateTile, m0 = (tile / tq) * kGateTile;
-    if (m0 >= M) return;
+    const int q0 = (blockIdx.x % tq) * kGateTile, m0 = (blockIdx.x / tq) * kGateTile;
     const uint16_t* wrow[2] = {W_rnn + static_cast<size_t>(q0 + n) * ldw + 2 * r,
                                W_rnn + static_cast<size_t>(q0 + 16 + n) * ldw + 2 * r};
     const bool mok[2] = {m0 + n < M, m0 + 16 + n < M};
@@ -233,43 +268,46 @@ __global__ __launch_bounds__(256) void k_gate_h(const uint16_t* __restrict__ W_r
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    u32x4 wa[2], ob[2];
-    auto fetch = [&](int k0) {
+    // this wave's chunks: k0 = 32 (wave + 4 t); two chunks in flight
+    constexpr int kStride = 32 * kGateWaves;
+    u32x4 wa[2][2], ob[2][2];
+    auto fetch = [&](int slot, int k0) {
         const int kk = k0 + 8 * g;
         const bool kin = kk < d;  // d % 8 == 0: a lane's 8 values are all in or all out
 #pragma unroll
-        for (int i = 0; i < 2; ++i) wa[i] = load8_bf16_or0(wrow[i] + kk, kin);
+        for (int i = 0; i < 2; ++i) wa[slot][i] = load8_bf16_or0(wrow[i] + kk, kin);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) ob[j] = load8_bf16_or0(hrow[j] + kk, kin && mok[j]);
+        for (int j = 0; j < 2; ++j) ob[slot][j] = load8_bf16_or0(hrow[j] + kk, kin && mok[j]);
     };
-    fetch(0);
-    for (int k0 = 0; k0 < d; k0 += 32) {
-        const u32x4 ca[2] = {wa[0], wa[1]}, cb[2] = {ob[0], ob[1]};
-        if (k0 + 32 < d) fetch(k0 + 32);
+    const int kfirst = 32 * wave;
+    fetch(0, kfirst);
+    fetch(1, kfirst + kStride);
+    for (int k0 = kfirst; k0 < d; k0 += 2 * kStride) {
+        const u32x4 ca[2] = {wa[0][0], wa[0][1]}, cb[2] = {ob[0][0], ob[0][1]};
+        if (k0 + 2 * kStride < d) fetch(0, k0 + 2 * kStride);
         gate_mfma2x2(ca, cb, acc);
+        if (k0 + kStride >= d) break;
+        const u32x4 da[2] = {wa[1][0], wa[1][1]}, db[2] = {ob[1][0], ob[1][1]};
+        if (k0 + 3 * kStride < d) fetch(1, k0 + 3 * kStride);
+        gate_mfma2x2(da, db, acc);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    gate_reduce(acc, [&](int i, int j, int e, float v) {
         const int m = m0 + 16 * j + n;
-        if (m >= M) continue;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Gh[static_cast<size_t>(m) * Q + q0 + 16 * i + 4 * g + e] = acc[i][j][e];
-    }
+        if (m < M) Gh[static_cast<size_t>(m) * Q + q0 + 16 * i + 4 * g + e] = v;
+    });
 }
 
 // G[b][q] = Gh[b gamma + k][q] + sum_j W_rnn[q][j] s[b][j] + sum_j
-// W_rnn[q][r + j] e[b][j] for the B blocks at step k.
+// W_rnn[q][r + j] e[b][j] for the B blocks at step k.  Grid: one workgroup
+// per 32 x 32 tile.
 __global__ __launch_bounds__(256) void k_gate_step(const uint16_t* __restrict__ W_rnn, const float* __restrict__ Gh,
                                                    const float* __restrict__ state, const float* __restrict__ emb,
                                                    int r, int d, int gamma, int k, int B, float* __restrict__ gates) {
     const int Q = 3 * r, ldw = 2 * r + d;
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-    const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wave = threadIdx.x >> 6;
     const int tq = Q / kGateTile;
-    const int q0 = (tile % tq) * kGateTile, m0 = (tile / tq) * kGateTile;
-    if (m0 >= B) return;
+    const int q0 = (blockIdx.x % tq) * kGateTile, m0 = (blockIdx.x / tq) * kGateTile;
     const uint16_t* wrow[2] = {W_rnn + static_cast<size_t>(q0 + n) * ldw,
                                W_rnn + static_cast<size_t>(q0 + 16 + n) * ldw};
     const bool mok[2] = {m0 + n < B, m0 + 16 + n < B};
@@ -280,50 +318,52 @@ __global__ __launch_bounds__(256) void k_gate_step(const uint16_t* __restrict__ 
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = 0; k0 < r; k0 += 32) {
+    for (int k0 = 32 * wave; k0 < r; k0 += 32 * kGateWaves) {
         const int kk = k0 + 8 * g;
         u32x4 ws_[2], we[2];
+        f32x4 sv[2][2], ev[2][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             ws_[i] = *reinterpret_cast<const u32x4*>(wrow[i] + kk);
             we[i] = *reinterpret_cast<const u32x4*>(wrow[i] + r + kk);
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                sv[j][h2] = mok[j] ? *reinterpret_cast<const f32x4*>(state + brow[j] + kk + 4 * h2) : z;
+                ev[j][h2] = mok[j] ? *reinterpret_cast<const f32x4*>(emb + brow[j] + kk + 4 * h2) : z;
+            }
         u32x4 shi[2], smid[2], slo[2], eb[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            float s[8], e[8], t[8];
+            float s8[8], e8[8], t[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                s[q] = mok[j] ? state[brow[j] + kk + q] : 0.0f;
-                e[q] = mok[j] ? emb[brow[j] + kk + q] : 0.0f;
+                s8[q] = sv[j][q >> 2][q & 3];
+                e8[q] = ev[j][q >> 2][q & 3];
             }
-            shi[j] = pack8_bf16(s);
+            shi[j] = pack8_bf16(s8);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) t[q] = s[q] - __uint_as_float((q & 1 ? shi[j][q >> 1] >> 16 : shi[j][q >> 1]) << 16);
+            for (int q = 0; q < 8; ++q) t[q] = s8[q] - unpack8_at(shi[j], q);
             smid[j] = pack8_bf16(t);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) t[q] -= __uint_as_float((q & 1 ? smid[j][q >> 1] >> 16 : smid[j][q >> 1]) << 16);
+            for (int q = 0; q < 8; ++q) t[q] -= unpack8_at(smid[j], q);
             slo[j] = pack8_bf16(t);
-            eb[j] = pack8_bf16(e);  // exact: e is a bf16 row of W1
+            eb[j] = pack8_bf16(e8);  // exact: e is a bf16 row of W1
         }
         gate_mfma2x2(ws_, shi, acc);
         gate_mfma2x2(ws_, smid, acc);
         gate_mfma2x2(ws_, slo, acc);
         gate_mfma2x2(we, eb, acc);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    gate_reduce(acc, [&](int i, int j, int e, float v) {
         const int m = m0 + 16 * j + n;
-        if (m >= B) continue;
-        const float* gh = Gh + (static_cast<size_t>(m) * gamma + k) * Q;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int q = q0 + 16 * i + 4 * g + e;
-                gates[static_cast<size_t>(m) * Q + q] = gh[q] + acc[i][j][e];
-            }
-    }
+        if (m >= B) return;
+        const int q = q0 + 16 * i + 4 * g + e;
+        gates[static_cast<size_t>(m) * Q + q] = Gh[(static_cast<size_t>(m) * gamma + k) * Q + q] + v;
+    });
 }
 
 bool rnn_gate_mfma_ok(const dspark_dims& d) {
@@ -662,7 +702,7 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
     if (gate_mfma) {
         const int M = D.B * D.gamma;
         const int tiles = gate_tq * ((M + kGateTile - 1) / kGateTile);
-        hipLaunchKernelGGL(k_gate_h, dim3((tiles + 3) / 4), dim3(256), 0, a.stream,
+        hipLaunchKernelGGL(k_gate_h, dim3(tiles), dim3(kGateWaves * kWave), 0, a.stream,
                            reinterpret_cast<const uint16_t*>(Wr), reinterpret_cast<const uint16_t*>(h), D.r, D.d, M,
                            gh);
     }
@@ -670,7 +710,7 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
         if (D.head == DSPARK_HEAD_RNN) {
             if (gate_mfma) {
                 const int tiles = gate_tq * ((D.B + kGateTile - 1) / kGateTile);
-                hipLaunchKernelGGL(k_gate_step, dim3((tiles + 3) / 4), dim3(256), 0, a.stream,
+                hipLaunchKernelGGL(k_gate_step, dim3(tiles), dim3(kGateWaves * kWave), 0, a.stream,
                                    reinterpret_cast<const uint16_t*>(Wr), gh, state, emb, D.r, D.d, D.gamma, k, D.B,
                                    gates);
             } else {

@@ -6,8 +6,9 @@
 // Rows i = n * gamma + k.  z_d = U + E W2 (E = W1[prev]) is recomputed in
 // each of three sweeps over V rather than stored (storing it in bf16 would
 // break the tolerance, in fp32 it costs more bytes than re-reading U):
-//   prep     prev tokens, E (row-major and transposed), confidence logits
-//   pass 1   per row: log-sum-exp of z_d and z_t, z_d at the label
+//   prep     prev tokens, E (row-major and transposed), confidence logits,
+//            z_d at the label
+//   pass 1   per row: log-sum-exp of z_d and z_t
 //   pass 2   per row: sum |p_d - p_t|, sum min(p_d, p_t), sum p_d sign(p_d - p_t)
 //   finalize c*, CE, BCE, dL/da per row; the four losses (fixed-order sums)
 //   pass 3   dZ = (w_k/N)[a_ce (p_d - onehot) + a_tv p_d (s - S)]  -> dlogits
@@ -79,14 +80,17 @@ struct LossConsts {
 
 // Workgroup = one row i (rows in [R, Rpad) only zero their operand rows).
 // Teacher forcing: prev = anchor[n] at k = 0, labels[n, k-1] after.  The row
-// k = 0 workgroup of block n also checks every token id of the block.
+// k = 0 workgroup of block n also checks every token id of the block.  Also
+// the draft logit at the label, z_d[x*] = U[i, x*] + E_i . W2[:, x*] (Eq 9).
 template <typename T>
 __global__ __launch_bounds__(256) void k_loss_prep(
     const int32_t* __restrict__ anchor, const int32_t* __restrict__ labels,
-    const T* __restrict__ W1, const T* __restrict__ w_conf, const T* __restrict__ h, int V, int r,
+    const T* __restrict__ W1, const T* __restrict__ w_conf, const T* __restrict__ h,
+    const T* __restrict__ U, const T* __restrict__ W2, int V, int r,
     int d, int gamma, int R, int Rpad, LossConsts cst, int32_t* __restrict__ bad,
     uint16_t* __restrict__ ebf, float* __restrict__ ef, uint16_t* __restrict__ et,
-    int32_t* __restrict__ label_out, float* __restrict__ rowc, float* __restrict__ alog) {
+    int32_t* __restrict__ label_out, float* __restrict__ rowc, float* __restrict__ alog,
+    float* __restrict__ zlab) {
     __shared__ float red[16];
     const int i = blockIdx.x;
     if (i >= R) {
@@ -99,6 +103,7 @@ __global__ __launch_bounds__(256) void k_loss_prep(
             label_out[i] = 0;
             rowc[i] = 0.0f;
             alog[i] = 0.0f;
+            zlab[i] = 0.0f;
         }
         return;
     }
@@ -115,7 +120,8 @@ __global__ __launch_bounds__(256) void k_loss_prep(
         }
         bad[n] = all ? 0 : 1;
     }
-    float part = 0.0f;
+    const int lab = ok ? lab_raw : 0;
+    float part = 0.0f, zl = 0.0f;
     for (int j = threadIdx.x; j < r; j += blockDim.x) {
         const float e = load_f(W1, static_cast<int64_t>(prev) * r + j);
         const uint16_t eb = static_cast<uint16_t>(f32_to_bf16(e));
@@ -123,14 +129,17 @@ __global__ __launch_bounds__(256) void k_loss_prep(
         ef[static_cast<size_t>(i) * r + j] = e;
         et[static_cast<size_t>(j) * Rpad + i] = eb;
         part += load_f(w_conf, d + j) * e;
+        zl = fmaf(e, load_f(W2, static_cast<int64_t>(j) * V + lab), zl);
     }
     const int64_t hrow = static_cast<int64_t>(i) * d;
     for (int q = threadIdx.x; q < d; q += blockDim.x) part += load_f(w_conf, q) * load_f(h, hrow + q);
     const float a = block_sum(part, red);
+    zl = block_sum(zl, red);
     if (threadIdx.x == 0) {
-        label_out[i] = ok ? lab_raw : 0;
+        label_out[i] = lab;
         rowc[i] = ok ? cst.pos_weight[k] : 0.0f;  // zero gradient rows for invalid ids
         alog[i] = ok ? a : NAN;
+        zlab[i] = load_f(U, static_cast<int64_t>(i) * V + lab) + zl;
     }
 }
 
@@ -155,6 +164,9 @@ struct PassArgs {
 };
 
 constexpr int kPass1 = 1, kPass2 = 2, kPass3 = 3;
+// partial values per row and column slice: pass 1 (max, sum) of z_d and of
+// z_t; pass 2 sum |p_d - p_t|, sum min(p_d, p_t), sum p_d sign(p_d - p_t)
+constexpr int kPartVals[4] = {0, 4, 3, 0};
 
 // Partial values one pass contributes for one row and one column slice.
 struct RowPart {
@@ -164,15 +176,15 @@ struct RowPart {
 __device__ __forceinline__ RowPart rowpart_empty(int pass) {
     RowPart p;
     if (pass == kPass1) {
-        p.v[0] = -INFINITY; p.v[1] = 0.0f; p.v[2] = -INFINITY; p.v[3] = 0.0f; p.v[4] = -INFINITY;
+        p.v[0] = -INFINITY; p.v[1] = 0.0f; p.v[2] = -INFINITY; p.v[3] = 0.0f; p.v[4] = 0.0f;
     } else {
         p.v[0] = 0.0f; p.v[1] = 0.0f; p.v[2] = 0.0f; p.v[3] = 0.0f; p.v[4] = 0.0f;
     }
     return p;
 }
 
-// (max, sum exp(x - max)) pairs merge with a rescale; the label logit is a
-// max (exactly one slice holds it); pass-2 values are plain sums.
+// (max, sum exp(x - max)) pairs merge with a rescale; pass-2 values are
+// plain sums.
 __device__ __forceinline__ RowPart rowpart_merge(int pass, const RowPart& a, const RowPart& b) {
     RowPart r;
     if (pass == kPass1) {
@@ -184,7 +196,7 @@ __device__ __forceinline__ RowPart rowpart_merge(int pass, const RowPart& a, con
             r.v[2 * h] = m;
             r.v[2 * h + 1] = sa + sb;
         }
-        r.v[4] = fmaxf(a.v[4], b.v[4]);
+        r.v[4] = 0.0f;
     } else {
 #pragma unroll
         for (int q = 0; q < 5; ++q) r.v[q] = a.v[q] + b.v[q];
@@ -199,10 +211,38 @@ __device__ __forceinline__ RowPart rowpart_shfl(const RowPart& a, int mask) {
     return r;
 }
 
+// Per-row values a pass reads (lse of z_d and z_t in base-2 units, w_k / N,
+// the row's S and label), loaded ahead with the row's logits.
+struct RowIn {
+    float ld, lt, rowc, S;
+    int label;
+};
+
+__device__ __forceinline__ RowIn row_in(const PassArgs& a, int pass, int row) {
+    RowIn in{0.0f, 0.0f, 0.0f, 0.0f, -1};
+    if (pass != kPass1) {
+        in.ld = a.lse_d[row] * kLog2e;
+        in.lt = a.lse_t[row] * kLog2e;
+    }
+    if (pass == kPass3) {
+        in.rowc = a.rowc[row];
+        in.S = a.S[row];
+        in.label = a.label[row];
+    }
+    return in;
+}
+
+// float pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+    const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // Per-row work on NC consecutive columns v0 .. v0+NC-1 (zd = U + bias,
 // zt = target logits; columns at or past V hold -inf).
 template <int PASS, int NC>
-__device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int v0,
+__device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int v0, const RowIn& ri,
                                                 const float (&zd)[NC], const float (&zt)[NC]) {
     RowPart p = rowpart_empty(PASS);
     if (PASS == kPass1) {
@@ -219,13 +259,9 @@ __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int 
             sd += __builtin_amdgcn_exp2f(fmaf(zd[j], kLog2e, -mdl));
             st += __builtin_amdgcn_exp2f(fmaf(zt[j], kLog2e, -mtl));
         }
-        const int lab = a.label[row];
-        float zl = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < NC; ++j) zl = (lab == v0 + j) ? zd[j] : zl;
-        p.v[0] = md; p.v[1] = sd; p.v[2] = mt; p.v[3] = st; p.v[4] = zl;
+        p.v[0] = md; p.v[1] = sd; p.v[2] = mt; p.v[3] = st;
     } else {
-        const float ld = a.lse_d[row] * kLog2e, lt = a.lse_t[row] * kLog2e;
+        const float ld = ri.ld, lt = ri.lt;
         if (PASS == kPass2) {
             float tv = 0.0f, cm = 0.0f, S = 0.0f;
 #pragma unroll
@@ -238,8 +274,8 @@ __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int 
             }
             p.v[0] = tv; p.v[1] = cm; p.v[2] = S;
         } else {
-            const float coef = a.rowc[row], S = a.S[row];
-            const int lab = a.label[row];
+            const float coef = ri.rowc, S = ri.S;
+            const int lab = ri.label;
             float dz[NC];
 #pragma unroll
             for (int j = 0; j < NC; ++j) {
@@ -257,8 +293,8 @@ __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int 
                     u32x4 w0, w1;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        w0[q] = f32_to_bf16(dz[2 * q]) | (f32_to_bf16(dz[2 * q + 1]) << 16);
-                        w1[q] = f32_to_bf16(dz[8 + 2 * q]) | (f32_to_bf16(dz[8 + 2 * q + 1]) << 16);
+                        w0[q] = pack2_bf16(dz[2 * q], dz[2 * q + 1]);
+                        w1[q] = pack2_bf16(dz[8 + 2 * q], dz[8 + 2 * q + 1]);
                     }
                     *reinterpret_cast<u32x4*>(dst) = w0;
                     *reinterpret_cast<u32x4*>(dst + 8) = w1;
@@ -283,24 +319,30 @@ __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int 
 
 // ----------------------------------------------------- pass kernels (MFMA)
 
-// Inputs of one 16-row block for one lane: its row's E operand chunks and
-// 16 columns of U and T, loaded a block ahead of use so that the HBM latency
-// overlaps the previous block's MFMA and epilogue.
-template <int KC>
+// Inputs of one 16-row block for one lane, loaded a block ahead of use so
+// that their latency overlaps the previous block's MFMA and epilogue: 16
+// columns of U and T, the per-row values the pass needs, and this thread's
+// share of the block's 16 E rows (staged into LDS for the whole workgroup).
 struct BlockIn {
-    u32x4 e[KC];
     u32x4 u0, u1, t0, t1;
+    RowIn ri;
 };
 
 // Work item = (column group cg of 256 columns, row chunk rc).  The
 // workgroup's 4 waves hold the 4 W2 tiles of cg in registers and walk the
-// chunk 16 rows at a time.  Each lane reads its own row's E operand from
-// global memory (L2-resident: the 4 waves share it), so the only
-// workgroup barrier left is the cross-wave merge of the row partials
-// (double-buffered, one barrier per block; none in pass 3).
+// chunk 16 rows at a time; the 16 E rows of a block are shared through a
+// double-buffered LDS area (row stride padded by 16 bytes against bank
+// conflicts).  One workgroup barrier per block publishes the next block's E
+// rows and, in passes 1 and 2, this block's per-wave row partials, which
+// wave 0 merges.  Two workgroups fit per compute unit (at most 256 VGPRs),
+// so the waves of one can run while the other's wait on memory.
 template <int KC, int PASS>
-__global__ __launch_bounds__(256, 1) void k_loss_mfma(PassArgs a) {
+__global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
     constexpr int r = KC * 32;
+    constexpr int ldE = r + 8;
+    constexpr int kEChunks = 16 * r / 8;  // 16-byte pieces of one block's E rows
+    static_assert(kEChunks <= 2 * 256, "E rows of a block: two 16-byte pieces per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t Es[2][16 * ldE];
     __shared__ RowPart red[2][kLossWaves][16];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -311,45 +353,64 @@ __global__ __launch_bounds__(256, 1) void k_loss_mfma(PassArgs a) {
         const int vt = cg * kLossColsPerWG + wave * 64;
         const int v0 = vt + 16 * g;
         const bool cols = v0 < a.V, second = v0 + 8 < a.V;
+        const bool full = vt + 64 <= a.V;  // wave-uniform: no masked columns
         const int rb0 = rc * a.rb_per_chunk;
         const int rb1 = min(a.Rpad / 16, rb0 + a.rb_per_chunk);
-        auto fetch = [&](int rb) {
-            BlockIn<KC> in;
-            const int row = rb * 16 + n;  // < Rpad: E rows are padded
-            const uint16_t* erow = a.ebf + static_cast<size_t>(row) * r + 8 * g;
+        u32x4 estage[2];  // this thread's pieces of the next block's E rows
+        auto fetch_e = [&](int rb) {
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) in.e[kc] = *reinterpret_cast<const u32x4*>(erow + 32 * kc);
+            for (int h = 0; h < 2; ++h) {
+                const int t = threadIdx.x + 256 * h;
+                estage[h] = u32x4{0u, 0u, 0u, 0u};
+                if (t < kEChunks)  // E rows are padded to Rpad
+                    estage[h] = *reinterpret_cast<const u32x4*>(a.ebf + static_cast<size_t>(rb * 16) * r + 8 * t);
+            }
+        };
+        auto fetch = [&](int rb) {
+            BlockIn in;
+            const int row = rb * 16 + n;
             in.u0 = in.u1 = in.t0 = in.t1 = u32x4{0u, 0u, 0u, 0u};
-            if (row < a.R && cols) {
-                const size_t o = static_cast<size_t>(row) * a.V + v0;
-                in.u0 = *reinterpret_cast<const u32x4*>(a.U + o);
-                in.t0 = *reinterpret_cast<const u32x4*>(a.T + o);
-                if (second) {
-                    in.u1 = *reinterpret_cast<const u32x4*>(a.U + o + 8);
-                    in.t1 = *reinterpret_cast<const u32x4*>(a.T + o + 8);
+            in.ri = RowIn{0.0f, 0.0f, 0.0f, 0.0f, -1};
+            if (row < a.R) {
+                if (cols) {
+                    const size_t o = static_cast<size_t>(row) * a.V + v0;
+                    in.u0 = *reinterpret_cast<const u32x4*>(a.U + o);
+                    in.t0 = *reinterpret_cast<const u32x4*>(a.T + o);
+                    if (second) {
+                        in.u1 = *reinterpret_cast<const u32x4*>(a.U + o + 8);
+                        in.t1 = *reinterpret_cast<const u32x4*>(a.T + o + 8);
+                    }
                 }
+                in.ri = row_in(a, PASS, row);
             }
             return in;
         };
+        auto stage = [&](int buf) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int t = threadIdx.x + 256 * h;
+                if (t < kEChunks) {
+                    const int er = t / (r / 8), ec = t % (r / 8);
+                    *reinterpret_cast<u32x4*>(&Es[buf][er * ldE + ec * 8]) = estage[h];
+                }
+            }
+        };
         W2Tile<KC> w2;
         w2.load(a.W2, a.V, vt, g, n);
-        BlockIn<KC> nxt = fetch(rb0);
+        fetch_e(rb0);
+        BlockIn nxt = fetch(rb0);
+        stage(rb0 & 1);
+        __syncthreads();
         for (int rb = rb0; rb < rb1; ++rb) {
-            const BlockIn<KC> cur = nxt;
-            if (rb + 1 < rb1) nxt = fetch(rb + 1);
+            const BlockIn cur = nxt;
+            if (rb + 1 < rb1) {
+                fetch_e(rb + 1);
+                nxt = fetch(rb + 1);
+            }
             f32x4 acc[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const bf16x8 bop = __builtin_bit_cast(bf16x8, cur.e[kc]);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const u32x4 av = {w2.f[kc][c][0], w2.f[kc][c][1], w2.f[kc][c][2], w2.f[kc][c][3]};
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bop,
-                                                                     acc[c], 0, 0, 0);
-                }
-            }
+            w2.mul(&Es[rb & 1][n * ldE + 8 * g], acc);
             const int row = rb * 16 + n;
             RowPart p = rowpart_empty(PASS);
             if (row < a.R && cols) {
@@ -358,33 +419,46 @@ __global__ __launch_bounds__(256, 1) void k_loss_mfma(PassArgs a) {
                 const uint32_t tw[8] = {cur.t0[0], cur.t0[1], cur.t0[2], cur.t0[3],
                                         cur.t1[0], cur.t1[1], cur.t1[2], cur.t1[3]};
                 float zd[16], zt[16];
-                const int nvalid = a.V - v0;
+                if (full) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                    for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int j = 4 * q + c;
-                        const bool in = j < nvalid;
-                        zd[j] = in ? ((j & 1) ? hi_bf16(uw[j >> 1]) : lo_bf16(uw[j >> 1])) + acc[c][q] : -INFINITY;
-                        zt[j] = in ? ((j & 1) ? hi_bf16(tw[j >> 1]) : lo_bf16(tw[j >> 1])) : -INFINITY;
-                    }
-                p = row_epilogue<PASS, 16>(a, row, v0, zd, zt);
+                        for (int c = 0; c < 4; ++c) {
+                            const int j = 4 * q + c;
+                            zd[j] = ((j & 1) ? hi_bf16(uw[j >> 1]) : lo_bf16(uw[j >> 1])) + acc[c][q];
+                            zt[j] = (j & 1) ? hi_bf16(tw[j >> 1]) : lo_bf16(tw[j >> 1]);
+                        }
+                } else {
+                    const int nvalid = a.V - v0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int j = 4 * q + c;
+                            const bool in = j < nvalid;
+                            zd[j] = in ? ((j & 1) ? hi_bf16(uw[j >> 1]) : lo_bf16(uw[j >> 1])) + acc[c][q] : -INFINITY;
+                            zt[j] = in ? ((j & 1) ? hi_bf16(tw[j >> 1]) : lo_bf16(tw[j >> 1])) : -INFINITY;
+                        }
+                }
+                p = row_epilogue<PASS, 16>(a, row, v0, cur.ri, zd, zt);
             }
-            if (PASS == kPass3) continue;
-            p = rowpart_merge(PASS, p, rowpart_shfl(p, 16));
-            p = rowpart_merge(PASS, p, rowpart_shfl(p, 32));
-            if (g == 0) red[rb & 1][wave][n] = p;
+            if (PASS != kPass3) {
+                p = rowpart_merge(PASS, p, rowpart_shfl(p, 16));
+                p = rowpart_merge(PASS, p, rowpart_shfl(p, 32));
+                if (g == 0) red[rb & 1][wave][n] = p;
+            }
+            if (rb + 1 < rb1) stage((rb + 1) & 1);
             __syncthreads();
-            if (wave == 0 && g == 0 && row < a.R) {
+            if (PASS != kPass3 && wave == 0 && g == 0 && row < a.R) {
                 RowPart t = red[rb & 1][0][n];
 #pragma unroll
                 for (int w = 1; w < kLossWaves; ++w) t = rowpart_merge(PASS, t, red[rb & 1][w][n]);
                 const size_t o = static_cast<size_t>(cg) * a.Rpad + row;
-                const int nv = PASS == kPass1 ? 5 : 3;
-                for (int q = 0; q < nv; ++q) a.part[q][o] = t.v[q];
+#pragma unroll
+                for (int q = 0; q < kPartVals[PASS]; ++q) a.part[q][o] = t.v[q];
             }
         }
-        if (PASS != kPass3) __syncthreads();  // red is reused by the next item
+        __syncthreads();  // Es and red are reused by the next item
     }
 }
 
@@ -422,7 +496,7 @@ __global__ __launch_bounds__(256) void k_loss_generic(PassArgs a) {
                     for (int c = 0; c < 4; ++c)
                         if (v0 + c < a.V) zd[c] = fmaf(e[j], load_f(W2, wrow + c), zd[c]);
                 }
-                p = row_epilogue<PASS, 4>(a, row, v0, zd, zt);
+                p = row_epilogue<PASS, 4>(a, row, v0, row_in(a, PASS, row), zd, zt);
             }
             if (PASS == kPass3) continue;
             for (int o = 32; o > 0; o >>= 1) p = rowpart_merge(PASS, p, rowpart_shfl(p, o));
@@ -432,8 +506,7 @@ __global__ __launch_bounds__(256) void k_loss_generic(PassArgs a) {
                 RowPart t = red[0];
                 for (int w = 1; w < static_cast<int>(blockDim.x / kWave); ++w) t = rowpart_merge(PASS, t, red[w]);
                 const size_t o = static_cast<size_t>(cg) * a.Rpad + row;
-                const int nv = PASS == kPass1 ? 5 : 3;
-                for (int q = 0; q < nv; ++q) a.part[q][o] = t.v[q];
+                for (int q = 0; q < kPartVals[PASS]; ++q) a.part[q][o] = t.v[q];
             }
             __syncthreads();
         }
@@ -449,17 +522,15 @@ __global__ __launch_bounds__(256) void k_loss_rows(const PassArgs a, float* __re
     const int row = blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= a.R) return;
     RowPart t = rowpart_empty(PASS);
-    const int nv = PASS == kPass1 ? 5 : 3;
     for (int p = 0; p < a.P; ++p) {
         RowPart q = rowpart_empty(PASS);
         const size_t o = static_cast<size_t>(p) * a.Rpad + row;
-        for (int k = 0; k < nv; ++k) q.v[k] = a.part[k][o];
+        for (int k = 0; k < kPartVals[PASS]; ++k) q.v[k] = a.part[k][o];
         t = rowpart_merge(PASS, t, q);
     }
     if (PASS == kPass1) {
         out0[row] = t.v[0] + logf(t.v[1]);  // lse_d
         out1[row] = t.v[2] + logf(t.v[3]);  // lse_t
-        out2[row] = t.v[4];                 // z_d at the label
     } else {
         out0[row] = t.v[0];  // sum |p_d - p_t|
         out1[row] = t.v[1];  // sum min(p_d, p_t)
@@ -661,10 +732,11 @@ static hipError_t launch_loss_t(const LossArgs& la) {
 
     hipLaunchKernelGGL((k_loss_prep<T>), dim3(L.Rpad), dim3(256), 0, la.stream, la.anchor, la.labels,
                        static_cast<const T*>(la.W1), static_cast<const T*>(la.w_conf),
-                       static_cast<const T*>(la.h), D.V, D.r, D.d, D.gamma, R, L.Rpad, cst,
+                       static_cast<const T*>(la.h), static_cast<const T*>(la.U), static_cast<const T*>(la.W2),
+                       D.V, D.r, D.d, D.gamma, R, L.Rpad, cst,
                        reinterpret_cast<int32_t*>(ws + L.bad), reinterpret_cast<uint16_t*>(ws + L.ebf),
                        F(L.ef), reinterpret_cast<uint16_t*>(ws + L.et),
-                       reinterpret_cast<int32_t*>(ws + L.label), F(L.rowc), F(L.alog));
+                       reinterpret_cast<int32_t*>(ws + L.label), F(L.rowc), F(L.alog), F(L.zlab));
 
     PassArgs a{};
     a.U = static_cast<const uint16_t*>(la.U);
@@ -691,7 +763,7 @@ static hipError_t launch_loss_t(const LossArgs& la) {
     launch_pass<kPass1>(la, L, a, grid);
     if ((pe = profile_end(la.stream)) != hipSuccess) return pe;
     hipLaunchKernelGGL((k_loss_rows<kPass1>), dim3(rgrid), dim3(256), 0, la.stream, a, F(L.lse_d),
-                       F(L.lse_t), F(L.zlab));
+                       F(L.lse_t), nullptr);
     if ((pe = profile_begin(la.stream)) != hipSuccess) return pe;
     launch_pass<kPass2>(la, L, a, grid);
     if ((pe = profile_end(la.stream)) != hipSuccess) return pe;

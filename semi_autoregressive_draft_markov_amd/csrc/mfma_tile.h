@@ -27,14 +27,16 @@ struct W2Tile {
                                          int n) {
         const int va = vt + 4 * n;
         const bool ok = va < V;
+        // lane base (row 8 g, column va) plus wave-uniform row offsets, so
+        // that no per-row address stays live across calls
+        const uint16_t* base = W2 + static_cast<size_t>(8 * g) * V + va;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
             uint2 raw[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int j = kc * 32 + 8 * g + e;
-                raw[e] = ok ? *reinterpret_cast<const uint2*>(W2 + static_cast<size_t>(j) * V + va)
-                            : make_uint2(0u, 0u);
+                const size_t j = static_cast<size_t>(kc * 32 + e);
+                raw[e] = ok ? *reinterpret_cast<const uint2*>(base + j * V) : make_uint2(0u, 0u);
             }
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
