@@ -241,7 +241,8 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 
 // Per-row work on NC consecutive columns v0 .. v0+NC-1 (zd = U + bias,
 // zt = target logits; columns at or past V hold -inf).
-template <int PASS, int NC>
+// (DZB: pass 3 stores bf16 dZ, else float32)
+template <int PASS, int NC, int DZB>
 __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int v0, const RowIn& ri,
                                                 const float (&zd)[NC], const float (&zt)[NC]) {
     RowPart p = rowpart_empty(PASS);
@@ -276,40 +277,41 @@ __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int 
         } else {
             const float coef = ri.rowc, S = ri.S;
             const int lab = ri.label;
-            float dz[NC];
-#pragma unroll
-            for (int j = 0; j < NC; ++j) {
-                const float pd = __builtin_amdgcn_exp2f(fmaf(zd[j], kLog2e, -ld));
-                const float pt = __builtin_amdgcn_exp2f(fmaf(zt[j], kLog2e, -lt));
-                const float sg = pd > pt ? 1.0f : (pd < pt ? -1.0f : 0.0f);
-                const float onehot = (lab == v0 + j) ? 1.0f : 0.0f;
-                dz[j] = coef * (a.a_ce * (pd - onehot) + a.a_tv * pd * (sg - S));
-            }
             const size_t o = static_cast<size_t>(row) * a.V + v0;
             const int nvalid = a.V - v0;
-            if (a.dz_bf16) {
-                uint16_t* dst = static_cast<uint16_t*>(a.dz) + o;
-                if (NC == 16 && nvalid >= 16 && (o % 8) == 0) {
-                    u32x4 w0, w1;
+            const bool vec = NC % 8 == 0 && nvalid >= NC && (o % 8) == 0;
+            // 8 columns at a time: dZ, then one 16-byte (bf16) or two (f32) stores
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        w0[q] = pack2_bf16(dz[2 * q], dz[2 * q + 1]);
-                        w1[q] = pack2_bf16(dz[8 + 2 * q], dz[8 + 2 * q + 1]);
-                    }
-                    *reinterpret_cast<u32x4*>(dst) = w0;
-                    *reinterpret_cast<u32x4*>(dst + 8) = w1;
-                } else {
-                    for (int j = 0; j < NC && j < nvalid; ++j) dst[j] = static_cast<uint16_t>(f32_to_bf16(dz[j]));
+            for (int h = 0; h < NC; h += 8) {
+                float dz[8];
+#pragma unroll
+                for (int q = 0; q < 8 && h + q < NC; ++q) {
+                    const int j = h + q;
+                    const float pd = __builtin_amdgcn_exp2f(fmaf(zd[j], kLog2e, -ld));
+                    const float pt = __builtin_amdgcn_exp2f(fmaf(zt[j], kLog2e, -lt));
+                    const float sg = pd > pt ? 1.0f : (pd < pt ? -1.0f : 0.0f);
+                    const float onehot = (lab == v0 + j) ? 1.0f : 0.0f;
+                    dz[q] = coef * (a.a_ce * (pd - onehot) + a.a_tv * pd * (sg - S));
                 }
-            } else {
-                float* dst = static_cast<float*>(a.dz) + o;
-                if (NC == 16 && nvalid >= 16 && (o % 4) == 0) {
+                if (DZB) {
+                    uint16_t* dst = static_cast<uint16_t*>(a.dz) + o + h;
+                    if (vec) {
+                        u32x4 w;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<f32x4*>(dst + 4 * q) =
-                            f32x4{dz[4 * q], dz[4 * q + 1], dz[4 * q + 2], dz[4 * q + 3]};
+                        for (int q = 0; q < 4; ++q) w[q] = pack2_bf16(dz[2 * q], dz[2 * q + 1]);
+                        *reinterpret_cast<u32x4*>(dst) = w;
+                    } else {
+                        for (int q = 0; q < 8 && h + q < NC && h + q < nvalid; ++q)
+                            dst[q] = static_cast<uint16_t>(f32_to_bf16(dz[q]));
+                    }
                 } else {
-                    for (int j = 0; j < NC && j < nvalid; ++j) dst[j] = dz[j];
+                    float* dst = static_cast<float*>(a.dz) + o + h;
+                    if (vec) {
+                        *reinterpret_cast<f32x4*>(dst) = f32x4{dz[0], dz[1], dz[2], dz[3]};
+                        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{dz[4], dz[5], dz[6], dz[7]};
+                    } else {
+                        for (int q = 0; q < 8 && h + q < NC && h + q < nvalid; ++q) dst[q] = dz[q];
+                    }
                 }
             }
         }
@@ -336,7 +338,7 @@ struct BlockIn {
 // rows and, in passes 1 and 2, this block's per-wave row partials, which
 // wave 0 merges.  Two workgroups fit per compute unit (at most 256 VGPRs),
 // so the waves of one can run while the other's wait on memory.
-template <int KC, int PASS>
+template <int KC, int PASS, int DZB>
 __global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
     constexpr int r = KC * 32;
     constexpr int ldE = r + 8;
@@ -356,33 +358,28 @@ __global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
         const bool full = vt + 64 <= a.V;  // wave-uniform: no masked columns
         const int rb0 = rc * a.rb_per_chunk;
         const int rb1 = min(a.Rpad / 16, rb0 + a.rb_per_chunk);
+        // All loads below are unconditional, from addresses clamped into
+        // the buffers (values of rows past R or columns past V are never
+        // used), so the compiler can count them and wait only for the ones
+        // a step needs instead of for every load in flight.
         u32x4 estage[2];  // this thread's pieces of the next block's E rows
         auto fetch_e = [&](int rb) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int t = threadIdx.x + 256 * h;
-                estage[h] = u32x4{0u, 0u, 0u, 0u};
-                if (t < kEChunks)  // E rows are padded to Rpad
-                    estage[h] = *reinterpret_cast<const u32x4*>(a.ebf + static_cast<size_t>(rb * 16) * r + 8 * t);
+                const int t = (threadIdx.x + 256 * h) % kEChunks;  // E rows are padded to Rpad
+                estage[h] = *reinterpret_cast<const u32x4*>(a.ebf + static_cast<size_t>(rb * 16) * r + 8 * t);
             }
         };
+        const int vc0 = cols ? v0 : 0, vc1 = second ? v0 + 8 : vc0;
         auto fetch = [&](int rb) {
             BlockIn in;
-            const int row = rb * 16 + n;
-            in.u0 = in.u1 = in.t0 = in.t1 = u32x4{0u, 0u, 0u, 0u};
-            in.ri = RowIn{0.0f, 0.0f, 0.0f, 0.0f, -1};
-            if (row < a.R) {
-                if (cols) {
-                    const size_t o = static_cast<size_t>(row) * a.V + v0;
-                    in.u0 = *reinterpret_cast<const u32x4*>(a.U + o);
-                    in.t0 = *reinterpret_cast<const u32x4*>(a.T + o);
-                    if (second) {
-                        in.u1 = *reinterpret_cast<const u32x4*>(a.U + o + 8);
-                        in.t1 = *reinterpret_cast<const u32x4*>(a.T + o + 8);
-                    }
-                }
-                in.ri = row_in(a, PASS, row);
-            }
+            const int row = rb * 16 + n;  // < Rpad: the per-row arrays are padded
+            const size_t ro = static_cast<size_t>(min(row, a.R - 1)) * a.V;
+            in.u0 = *reinterpret_cast<const u32x4*>(a.U + ro + vc0);
+            in.t0 = *reinterpret_cast<const u32x4*>(a.T + ro + vc0);
+            in.u1 = *reinterpret_cast<const u32x4*>(a.U + ro + vc1);
+            in.t1 = *reinterpret_cast<const u32x4*>(a.T + ro + vc1);
+            in.ri = row_in(a, PASS, row);
             return in;
         };
         auto stage = [&](int buf) {
@@ -440,7 +437,7 @@ __global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
                             zt[j] = in ? ((j & 1) ? hi_bf16(tw[j >> 1]) : lo_bf16(tw[j >> 1])) : -INFINITY;
                         }
                 }
-                p = row_epilogue<PASS, 16>(a, row, v0, cur.ri, zd, zt);
+                p = row_epilogue<PASS, 16, DZB>(a, row, v0, cur.ri, zd, zt);
             }
             if (PASS != kPass3) {
                 p = rowpart_merge(PASS, p, rowpart_shfl(p, 16));
@@ -466,7 +463,7 @@ __global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
 
 // Any dtype / rank: thread = 4 consecutive columns, rows of the item's chunk
 // one at a time, bias as a float dot product with E.
-template <typename T, int PASS>
+template <typename T, int PASS, int DZB>
 __global__ __launch_bounds__(256) void k_loss_generic(PassArgs a) {
     __shared__ RowPart red[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -496,7 +493,7 @@ __global__ __launch_bounds__(256) void k_loss_generic(PassArgs a) {
                     for (int c = 0; c < 4; ++c)
                         if (v0 + c < a.V) zd[c] = fmaf(e[j], load_f(W2, wrow + c), zd[c]);
                 }
-                p = row_epilogue<PASS, 4>(a, row, v0, row_in(a, PASS, row), zd, zt);
+                p = row_epilogue<PASS, 4, DZB>(a, row, v0, row_in(a, PASS, row), zd, zt);
             }
             if (PASS == kPass3) continue;
             for (int o = 32; o > 0; o >>= 1) p = rowpart_merge(PASS, p, rowpart_shfl(p, o));
@@ -515,19 +512,33 @@ __global__ __launch_bounds__(256) void k_loss_generic(PassArgs a) {
 
 // ------------------------------------------------------- row reductions
 
-// Thread = row: merge the P partials of a pass in column order.
+// Merge the P column-group partials of a pass per row.  Workgroup = 16
+// rows x 16 slices: thread (slice sl, row) merges groups sl, sl + 16, ...
+// (16 consecutive rows per quarter wave: 64-byte reads), then slice 0 merges
+// the 16 slice results in slice order through LDS (deterministic).
+constexpr int kRowsPerWG = 16, kRowSlices = 16;
+
 template <int PASS>
 __global__ __launch_bounds__(256) void k_loss_rows(const PassArgs a, float* __restrict__ out0,
                                                    float* __restrict__ out1, float* __restrict__ out2) {
-    const int row = blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= a.R) return;
+    __shared__ RowPart sl_part[kRowSlices][kRowsPerWG];
+    const int rr = threadIdx.x % kRowsPerWG, sl = threadIdx.x / kRowsPerWG;
+    const int row = blockIdx.x * kRowsPerWG + rr;
     RowPart t = rowpart_empty(PASS);
-    for (int p = 0; p < a.P; ++p) {
-        RowPart q = rowpart_empty(PASS);
-        const size_t o = static_cast<size_t>(p) * a.Rpad + row;
-        for (int k = 0; k < kPartVals[PASS]; ++k) q.v[k] = a.part[k][o];
-        t = rowpart_merge(PASS, t, q);
+    if (row < a.R) {
+        for (int p = sl; p < a.P; p += kRowSlices) {
+            RowPart q = rowpart_empty(PASS);
+            const size_t o = static_cast<size_t>(p) * a.Rpad + row;
+#pragma unroll
+            for (int k = 0; k < kPartVals[PASS]; ++k) q.v[k] = a.part[k][o];
+            t = rowpart_merge(PASS, t, q);
+        }
     }
+    sl_part[sl][rr] = t;
+    __syncthreads();
+    if (sl != 0 || row >= a.R) return;
+#pragma unroll 1
+    for (int s2 = 1; s2 < kRowSlices; ++s2) t = rowpart_merge(PASS, t, sl_part[s2][rr]);
     if (PASS == kPass1) {
         out0[row] = t.v[0] + logf(t.v[1]);  // lse_d
         out1[row] = t.v[2] + logf(t.v[3]);  // lse_t
@@ -593,93 +604,159 @@ __global__ __launch_bounds__(256) void k_loss_sum(const float* __restrict__ tce,
 
 // ------------------------------------------------------------------ dW2
 
-// dW2[j, v] = sum_i E[i, j] dZ[i, v].  Workgroup = 64 columns, wave w = rows
-// j in [16w, 16w + 16) of dW2.  Each 32-row slice of dZ is staged in LDS and
-// read back by every wave as B-operand fragments (8 consecutive rows of one
-// column per lane, transposed with v_perm as for W2); A = E^T from its
-// transposed copy.  A float32 dZ is split into bf16 hi + lo, so the product
-// keeps about 16 bits of dZ's mantissa.
+// dW2[j, v] = sum_i E[i, j] dZ[i, v], a GEMM with M = r, N = V, K = R on
+// v_mfma_f32_16x16x32_bf16 (lane (g, n) supplies A[n][8g .. 8g+7] and
+// B[8g .. 8g+7][n] and receives D[4g + q][n] in accumulator element q).
+// Workgroup = 128 columns of V; wave w owns dW2 rows 64 w .. 64 w + 63 of
+// them (4 x 8 tiles, accumulated over all rows of dZ).  K runs in 32-row
+// chunks:
+//   B (dZ) -- K runs along dZ's strided axis, so each chunk is staged
+//     through LDS transposed: thread (row pair p, 8 columns) holds two
+//     16-byte row pieces, pairs the rows of each column with v_perm and
+//     stores column-major words, which lanes read back as 16-byte operand
+//     fragments.  The global loads run kAhead chunks ahead of the LDS
+//     stores (a register ring); the LDS tile is double-buffered with one
+//     workgroup barrier per chunk.  A float32 dZ is split into bf16 hi + lo
+//     planes (two MFMAs per tile), so the product keeps about 16 bits of its
+//     mantissa.
+//   A (E^T) -- from the transposed copy of E, 16 contiguous bytes per lane
+//     and tile, loaded two chunks ahead (E is small and stays in cache).
+constexpr int kDw2Cols = 128;
+constexpr int kDw2Threads = 256;
+constexpr int kDw2Ld = 20;  // words per staged column: 16 row pairs + 4 pad (16-byte aligned)
+
+// Word offset of row pair p of staged column col.  Each group of 8 columns
+// (one staging thread's) is shifted by a further 16 bytes, so the staging
+// threads of a wave, 8 columns apart, spread over the LDS banks instead of
+// meeting in one; a lane's 4 pairs stay one aligned 16-byte piece.
+__device__ __forceinline__ int dw2_word(int col, int p) { return col * kDw2Ld + 4 * (col >> 3) + p; }
+constexpr int kDw2Words = kDw2Cols * kDw2Ld + 4 * (kDw2Cols / 8);
+
+// (float32 dZ: the hi/lo planes need more registers, one workgroup per CU)
 template <int DZF32>
-__global__ __launch_bounds__(1024) void k_dw2_mfma(const void* __restrict__ dz,
-                                                   const uint16_t* __restrict__ et, int V, int r,
-                                                   int R, int Rpad, float* __restrict__ dW2) {
-    constexpr int kEl = DZF32 ? 4 : 2;                 // bytes per dZ element
-    __shared__ __attribute__((aligned(16))) uint8_t S[32 * 64 * kEl];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(kDw2Threads, DZF32 ? 1 : 2) void k_dw2_mfma(const void* __restrict__ dz,
+                                                                         const uint16_t* __restrict__ et, int V,
+                                                                         int r, int R, int Rpad,
+                                                                         float* __restrict__ dW2) {
+    constexpr int kPlanes = DZF32 ? 2 : 1;
+    constexpr int kAhead = DZF32 ? 2 : 4;      // register ring depth of the dZ loads (chunks, even)
+    constexpr int kLdPerRow = DZF32 ? 2 : 1;   // 16-byte pieces per row and thread
+    static_assert(kAhead % 2 == 0, "chunk parity is the unrolled step's parity");
+    __shared__ __attribute__((aligned(16))) uint32_t Bs[2][kPlanes][kDw2Words];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;
-    const int vt = blockIdx.x * 64;
-    const int jb = wave * 16;
-    f32x4 acc[4];
+    const int vt = blockIdx.x * kDw2Cols;
+    const int j0 = 64 * wave;
+    const bool rows_live = j0 < r;
+    const int nchunks = Rpad / 32;
+    // staging role: row pair p (rows 2p, 2p + 1 of the chunk), columns 8 cg .. 8 cg + 7
+    const int sp = threadIdx.x >> 4, scg = threadIdx.x & 15;
+    const int scol = vt + 8 * scg;
+    const bool scol_ok = scol < V;  // V % 8 == 0: a thread's 8 columns are all in or all out
+    u32x4 ring[kAhead][2][kLdPerRow];
+    // Loads are unconditional, from addresses clamped into the buffers
+    // (zeros are substituted when a chunk is staged), so the compiler can
+    // count them and wait only for the chunk being staged.
+    auto load_b = [&](int c, u32x4 (&dst)[2][kLdPerRow]) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const int vbytes = 64 * kEl;
-    for (int i0 = 0; i0 < Rpad; i0 += 32) {
-        __syncthreads();
-        // 32 rows x 64 columns of dZ -> LDS (zero outside R x V)
-        for (int t = threadIdx.x; t < 32 * (vbytes / 16); t += blockDim.x) {
-            const int rr = t / (vbytes / 16), cc = t % (vbytes / 16);
-            const int row = i0 + rr, col = vt + cc * (16 / kEl);
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row < R && col < V) {
-                const uint8_t* src = static_cast<const uint8_t*>(dz) + (static_cast<size_t>(row) * V + col) * kEl;
-                v = *reinterpret_cast<const u32x4*>(src);
-            }
-            *reinterpret_cast<u32x4*>(&S[rr * vbytes + cc * 16]) = v;
+        for (int h = 0; h < 2; ++h) {
+            const int row = min(32 * c + 2 * sp + h, R - 1);
+            const size_t o = static_cast<size_t>(row) * V + (scol_ok ? scol : 0);
+#pragma unroll
+            for (int q = 0; q < kLdPerRow; ++q)
+                dst[h][q] = DZF32 ? *reinterpret_cast<const u32x4*>(static_cast<const float*>(dz) + o + 4 * q)
+                                  : *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(dz) + o);
         }
-        __syncthreads();
-        if (jb >= r) continue;
-        // A: E^T rows jb + n, columns (rows of E) i0 + 8g .. i0 + 8g + 7
-        const u32x4 ev = *reinterpret_cast<const u32x4*>(et + static_cast<size_t>(jb + n) * Rpad + i0 + 8 * g);
-        const bf16x8 aop = __builtin_bit_cast(bf16x8, ev);
-        // B: rows i0 + 8g + e, columns vt + 4n + c
-        uint32_t hi[4][4], lo[4][4];
+    };
+    auto store_b = [&](const u32x4 (&src)[2][kLdPerRow], int buf, int chunk) {
+        // rows past R and columns past V contribute zeros
+        const bool ok0 = scol_ok && 32 * chunk + 2 * sp < R, ok1 = scol_ok && 32 * chunk + 2 * sp + 1 < R;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            float x0[4], x1[4];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int rr = 8 * g + 2 * p + h;
-                float* x = h ? x1 : x0;
-                if (DZF32) {
-                    const f32x4 q = *reinterpret_cast<const f32x4*>(&S[rr * vbytes + 4 * n * 4]);
-                    x[0] = q[0]; x[1] = q[1]; x[2] = q[2]; x[3] = q[3];
-                } else {
-                    const uint2 q = *reinterpret_cast<const uint2*>(&S[rr * vbytes + 4 * n * 2]);
-                    x[0] = lo_bf16(q.x); x[1] = hi_bf16(q.x); x[2] = lo_bf16(q.y); x[3] = hi_bf16(q.y);
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t h0 = f32_to_bf16(x0[c]), h1 = f32_to_bf16(x1[c]);
-                hi[c][p] = h0 | (h1 << 16);
-                if (DZF32) {
-                    const uint32_t l0 = f32_to_bf16(x0[c] - __uint_as_float(h0 << 16));
-                    const uint32_t l1 = f32_to_bf16(x1[c] - __uint_as_float(h1 << 16));
-                    lo[c][p] = l0 | (l1 << 16);
-                }
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 bh = {hi[c][0], hi[c][1], hi[c][2], hi[c][3]};
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bh), acc[c], 0, 0, 0);
+        for (int c = 0; c < 8; ++c) {
+            uint32_t hi, lo = 0u;
             if (DZF32) {
-                const u32x4 bl = {lo[c][0], lo[c][1], lo[c][2], lo[c][3]};
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bl), acc[c], 0, 0, 0);
+                const float x0 = ok0 ? __uint_as_float(src[0][c >> 2][c & 3]) : 0.0f;
+                const float x1 = ok1 ? __uint_as_float(src[1][c >> 2][c & 3]) : 0.0f;
+                hi = pack2_bf16(x0, x1);
+                lo = pack2_bf16(x0 - lo_bf16(hi), x1 - hi_bf16(hi));
+            } else {
+                const uint32_t w0 = ok0 ? src[0][0][c >> 1] : 0u, w1 = ok1 ? src[1][0][c >> 1] : 0u;
+                hi = __builtin_amdgcn_perm(w1, w0, (c & 1) ? 0x07060302u : 0x05040100u);
+            }
+            const int at = dw2_word(8 * scg + c, sp);
+            Bs[buf][0][at] = hi;
+            if (DZF32) Bs[buf][kPlanes - 1][at] = lo;
+        }
+    };
+    // E^T rows past r are never multiplied into a stored row of dW2, and
+    // chunks past the end are never used: clamp, load unconditionally
+    u32x4 afr[2][4];
+    auto load_a = [&](int c, u32x4 (&dst)[4]) {
+        const int cc = min(c, nchunks - 1);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int j = min(j0 + 16 * it + n, r - 1);
+            dst[it] = *reinterpret_cast<const u32x4*>(et + static_cast<size_t>(j) * Rpad + 32 * cc + 8 * g);
+        }
+    };
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) acc[it][jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // prologue: chunk 0 staged, chunks 1 .. kAhead in the ring, A of chunks 0 and 1
+#pragma unroll
+    for (int q = 0; q < kAhead; ++q) load_b(q, ring[q]);
+    load_a(0, afr[0]);
+    load_a(1, afr[1]);
+    store_b(ring[0], 0, 0);
+    load_b(kAhead, ring[0]);
+    __syncthreads();
+    // chunk c: B in Bs[c & 1], A in afr[c & 1]; ring slot (c + 1) % kAhead
+    // holds chunk c + 1, staged at the end of the step, then refilled with
+    // chunk c + 1 + kAhead
+    for (int c0 = 0; c0 < nchunks; c0 += kAhead) {
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) {
+            const int c = c0 + u;
+            if (c >= nchunks) break;
+            if (rows_live) {
+#pragma unroll
+                for (int pl = 0; pl < kPlanes; ++pl)
+#pragma unroll
+                    for (int jt = 0; jt < 8; ++jt) {
+                        const u32x4 bv =
+                            *reinterpret_cast<const u32x4*>(&Bs[u & 1][pl][dw2_word(16 * jt + n, 4 * g)]);
+                        const bf16x8 bop = __builtin_bit_cast(bf16x8, bv);
+#pragma unroll
+                        for (int it = 0; it < 4; ++it)
+                            acc[it][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, afr[u & 1][it]), bop, acc[it][jt], 0, 0, 0);
+                    }
+            }
+            load_a(c + 2, afr[u & 1]);
+            const int slot = (u + 1) % kAhead;
+            if (c + 1 < nchunks) store_b(ring[slot], (u + 1) & 1, c + 1);
+            load_b(c + 1 + kAhead, ring[slot]);
+            __syncthreads();
+        }
+    }
+    if (!rows_live) return;
+    // lane (g, n) of tile (it, jt): dW2 rows j0 + 16 it + 4 g + q, column vt + 16 jt + n
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) {
+            const int v = vt + 16 * jt + n;
+            if (v >= V) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = j0 + 16 * it + 4 * g + q;
+                if (j < r) dW2[static_cast<size_t>(j) * V + v] = acc[it][jt][q];
             }
         }
-    }
-    if (jb >= r) return;
-    // lane (g, n): dW2 rows jb + 4g + q, columns vt + 4n + c
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int j = jb + 4 * g + q;
-        const int v = vt + 4 * n;
-        if (v < V) {
-            float* dst = dW2 + static_cast<size_t>(j) * V + v;
-            *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0][q], acc[1][q], acc[2][q], acc[3][q]};
-        }
-    }
 }
 
 // Vector dW2: thread = (row j of dW2, column v), plain sum over rows.
@@ -697,25 +774,34 @@ __global__ __launch_bounds__(256) void k_dw2_generic(const DZ* __restrict__ dz,
 
 // ---------------------------------------------------------------- launch
 
-template <int PASS>
-static void launch_pass(const LossArgs& la, const LossLayout& L, PassArgs& a, int grid) {
+template <int PASS, int DZB>
+static void launch_pass_t(const LossArgs& la, const LossLayout& L, PassArgs& a, int grid) {
     const int r = la.dims.r;
     if (L.mfma) {
         switch (r / 32) {
-            case 1: hipLaunchKernelGGL((k_loss_mfma<1, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
-            case 2: hipLaunchKernelGGL((k_loss_mfma<2, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
-            case 3: hipLaunchKernelGGL((k_loss_mfma<3, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
-            case 4: hipLaunchKernelGGL((k_loss_mfma<4, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
-            case 5: hipLaunchKernelGGL((k_loss_mfma<5, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
-            case 6: hipLaunchKernelGGL((k_loss_mfma<6, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
-            case 7: hipLaunchKernelGGL((k_loss_mfma<7, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
-            default: hipLaunchKernelGGL((k_loss_mfma<8, PASS>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 1: hipLaunchKernelGGL((k_loss_mfma<1, PASS, DZB>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 2: hipLaunchKernelGGL((k_loss_mfma<2, PASS, DZB>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 3: hipLaunchKernelGGL((k_loss_mfma<3, PASS, DZB>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 4: hipLaunchKernelGGL((k_loss_mfma<4, PASS, DZB>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 5: hipLaunchKernelGGL((k_loss_mfma<5, PASS, DZB>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 6: hipLaunchKernelGGL((k_loss_mfma<6, PASS, DZB>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            case 7: hipLaunchKernelGGL((k_loss_mfma<7, PASS, DZB>), dim3(grid), dim3(256), 0, la.stream, a); break;
+            default: hipLaunchKernelGGL((k_loss_mfma<8, PASS, DZB>), dim3(grid), dim3(256), 0, la.stream, a); break;
         }
     } else if (la.dims.dtype == DSPARK_BF16) {
-        hipLaunchKernelGGL((k_loss_generic<uint16_t, PASS>), dim3(grid), dim3(256), 0, la.stream, a);
+        hipLaunchKernelGGL((k_loss_generic<uint16_t, PASS, DZB>), dim3(grid), dim3(256), 0, la.stream, a);
     } else {
-        hipLaunchKernelGGL((k_loss_generic<float, PASS>), dim3(grid), dim3(256), 0, la.stream, a);
+        hipLaunchKernelGGL((k_loss_generic<float, PASS, DZB>), dim3(grid), dim3(256), 0, la.stream, a);
     }
+}
+
+// Passes 1 and 2 write no dZ; pass 3 is built for both dZ dtypes.
+template <int PASS>
+static void launch_pass(const LossArgs& la, const LossLayout& L, PassArgs& a, int grid) {
+    if (PASS == kPass3 && a.dz_bf16)
+        launch_pass_t<PASS, 1>(la, L, a, grid);
+    else
+        launch_pass_t<PASS, 0>(la, L, a, grid);
 }
 
 template <typename T>
@@ -762,12 +848,13 @@ static hipError_t launch_loss_t(const LossArgs& la) {
     if (pe != hipSuccess) return pe;
     launch_pass<kPass1>(la, L, a, grid);
     if ((pe = profile_end(la.stream)) != hipSuccess) return pe;
-    hipLaunchKernelGGL((k_loss_rows<kPass1>), dim3(rgrid), dim3(256), 0, la.stream, a, F(L.lse_d),
+    const int mgrid = (R + kRowsPerWG - 1) / kRowsPerWG;
+    hipLaunchKernelGGL((k_loss_rows<kPass1>), dim3(mgrid), dim3(256), 0, la.stream, a, F(L.lse_d),
                        F(L.lse_t), nullptr);
     if ((pe = profile_begin(la.stream)) != hipSuccess) return pe;
     launch_pass<kPass2>(la, L, a, grid);
     if ((pe = profile_end(la.stream)) != hipSuccess) return pe;
-    hipLaunchKernelGGL((k_loss_rows<kPass2>), dim3(rgrid), dim3(256), 0, la.stream, a, F(L.tv),
+    hipLaunchKernelGGL((k_loss_rows<kPass2>), dim3(mgrid), dim3(256), 0, la.stream, a, F(L.tv),
                        F(L.cmin), F(L.S));
     hipLaunchKernelGGL(k_loss_finalize, dim3(rgrid), dim3(256), 0, la.stream, F(L.lse_d), F(L.zlab),
                        F(L.tv), F(L.cmin), F(L.alog), F(L.rowc), R, la.alpha[2], la.c_star, la.conf,
@@ -781,14 +868,13 @@ static hipError_t launch_loss_t(const LossArgs& la) {
     }
     if (la.dW2) {
         if (L.mfma) {
+            const dim3 grid((D.V + kDw2Cols - 1) / kDw2Cols);
             if (a.dz_bf16)
-                hipLaunchKernelGGL((k_dw2_mfma<0>), dim3((D.V + 63) / 64), dim3(64 * (D.r / 16)), 0,
-                                   la.stream, la.dlogits, reinterpret_cast<const uint16_t*>(ws + L.et),
-                                   D.V, D.r, R, L.Rpad, la.dW2);
+                hipLaunchKernelGGL((k_dw2_mfma<0>), grid, dim3(kDw2Threads), 0, la.stream, la.dlogits,
+                                   reinterpret_cast<const uint16_t*>(ws + L.et), D.V, D.r, R, L.Rpad, la.dW2);
             else
-                hipLaunchKernelGGL((k_dw2_mfma<1>), dim3((D.V + 63) / 64), dim3(64 * (D.r / 16)), 0,
-                                   la.stream, la.dlogits, reinterpret_cast<const uint16_t*>(ws + L.et),
-                                   D.V, D.r, R, L.Rpad, la.dW2);
+                hipLaunchKernelGGL((k_dw2_mfma<1>), grid, dim3(kDw2Threads), 0, la.stream, la.dlogits,
+                                   reinterpret_cast<const uint16_t*>(ws + L.et), D.V, D.r, R, L.Rpad, la.dW2);
         } else if (a.dz_bf16) {
             hipLaunchKernelGGL((k_dw2_generic<uint16_t>), dim3((D.V + 255) / 256, D.r), dim3(256), 0,
                                la.stream, static_cast<const uint16_t*>(la.dlogits), F(L.ef), D.V, D.r, R,
