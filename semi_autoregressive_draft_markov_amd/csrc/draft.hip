@@ -440,71 +440,6 @@ __device__ __forceinline__ Stats lane_stats16(const float (&z)[16], int v0, int 
     return Stats{m, s, argmax_key(ybest, static_cast<uint32_t>(v0 + idx)), zx};
 }
 
-// One workgroup = 4 waves = 256 columns.  Each wave keeps a 64-column W2
-// tile in registers as MFMA A-fragments (see mfma_tile.h) for the whole step
-// and loops over the blocks 16 at a time; lane (g, n) ends up with the 16
-// consecutive columns vt + 16g .. vt + 16g + 15 of block row b = 16 nb + n,
-// so all of a lane's softmax and argmax work is for one block row.
-template <int KC, int NPLANES>
-__global__ __launch_bounds__(256) void k_stream_mfma(
-    const uint16_t* __restrict__ U, const uint16_t* __restrict__ W2,
-    const uint16_t* __restrict__ ebf, const float* __restrict__ temperature, int V, int B,
-    int Bpad, int gamma, int k, uint32_t key0, uint32_t key1, uint32_t ctr3,
-    float* __restrict__ pm, float* __restrict__ ps, uint64_t* __restrict__ pkey,
-    float* __restrict__ pzx) {
-    constexpr int r = KC * 32;
-    __shared__ Stats red[kWavesPerWG][16];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n = lane & 15, g = lane >> 4;
-    const int vt = (blockIdx.x * kWavesPerWG + wave) * kTileV;
-    const int P = gridDim.x;
-
-    W2Tile<KC> w2;
-    w2.load(W2, V, vt, g, n);
-
-    const int v0 = vt + 16 * g;
-    for (int nb = 0; nb < Bpad / 16; ++nb) {
-        const int b = nb * 16 + n;
-        f32x4 acc[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int pl = 0; pl < NPLANES; ++pl)
-            w2.mul(ebf + (static_cast<size_t>(pl) * Bpad + b) * r + 8 * g, acc);
-
-        Stats st = stats_empty();
-        if (b < B && v0 < V) {
-            const float temp = temperature[b];
-            const bool sampling = temp > 0.0f;
-            const float invT = sampling ? 1.0f / temp : 1.0f;
-            float z[16];
-            load16_bf16(U + (static_cast<size_t>(b) * gamma + k) * V + v0, v0 + 8 < V, z);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) z[4 * q + c] += acc[c][q];
-            if (v0 + 16 <= V)
-                st = lane_stats16<true>(z, v0, V, b, k, sampling, invT, key0, key1, ctr3);
-            else
-                st = lane_stats16<false>(z, v0, V, b, k, sampling, invT, key0, key1, ctr3);
-        }
-        st = stats_merge(st, shfl_xor_stats(st, 16));
-        st = stats_merge(st, shfl_xor_stats(st, 32));
-        if (g == 0) red[wave][n] = st;
-        __syncthreads();
-        if (wave == 0 && g == 0 && b < B) {
-            Stats t = red[0][n];
-#pragma unroll
-            for (int w = 1; w < kWavesPerWG; ++w) t = stats_merge(t, red[w][n]);
-            const size_t o = static_cast<size_t>(b) * P + blockIdx.x;
-            pm[o] = t.m;
-            ps[o] = t.s;
-            pkey[o] = t.key;
-            pzx[o] = t.zx;
-        }
-        __syncthreads();
-    }
-}
 
 // ------------------------------------------------------ stream (generic)
 
@@ -578,6 +513,133 @@ __global__ __launch_bounds__(256) void k_stream_generic(
             pzx[o] = t.zx;
         }
         __syncthreads();
+    }
+}
+
+// One step over V (per-step driver): workgroup = 4 waves = 256 columns, wave
+// = a 64-column W2 tile held in registers as MFMA A-fragments (see
+// mfma_tile.h) for all blocks.  Per 16-block unit: z = U_k + E W2 on the
+// matrix cores (NPL = 2: E as bf16 hi + lo planes); lane (g, n) ends up with
+// the 16 consecutive columns vt + 16g .. vt + 16g + 15 of block row b =
+// 16 nb + n, so all of a lane's softmax and argmax work is for one block
+// row; the per-lane statistics are merged across the 4 lanes of a column
+// group and the 4 waves.  The unit's E rows (all planes) are staged through
+// a double-buffered LDS area, and its U values and temperatures are loaded a
+// unit ahead, unconditionally from clamped addresses so that the loads stay
+// in flight across the previous unit; one workgroup barrier per unit.
+template <int KC, int NPL>
+__global__ __launch_bounds__(256, 2) void k_stream_mfma(
+    const uint16_t* __restrict__ U, const uint16_t* __restrict__ W2,
+    const uint16_t* __restrict__ ebf, const float* __restrict__ temperature, int V, int B,
+    int Bpad, int gamma, int k, uint32_t key0, uint32_t key1, uint32_t ctr3,
+    float* __restrict__ pm, float* __restrict__ ps, uint64_t* __restrict__ pkey,
+    float* __restrict__ pzx) {
+    constexpr int r = KC * 32;
+    constexpr int ldE = r + 8;                        // padded row stride (bank spread)
+    constexpr int kChunks = NPL * 16 * (r / 8);       // 16-byte pieces of one unit's E rows
+    constexpr int kPer = (kChunks + 255) / 256;       // per thread
+    __shared__ __attribute__((aligned(16))) uint16_t Es[2][NPL * 16 * ldE];
+    __shared__ Stats red[2][kWavesPerWG][16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int vt = (blockIdx.x * kWavesPerWG + wave) * kTileV;
+    const int P = gridDim.x;
+    const int NB = Bpad / 16;
+
+    const int v0 = vt + 16 * g;
+    const bool live = v0 < V;
+    const int ua = live ? v0 : 0, ub = (live && v0 + 8 < V) ? v0 + 8 : ua;
+    u32x4 estage[kPer];
+    auto fetch_e = [&](int nb) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int t = (threadIdx.x + 256 * i) % kChunks;
+            const int pl = t / (16 * (r / 8)), rem = t % (16 * (r / 8));
+            const int row = rem / (r / 8), col = rem % (r / 8);
+            estage[i] = *reinterpret_cast<const u32x4*>(ebf + (static_cast<size_t>(pl) * Bpad + nb * 16 + row) * r +
+                                                        col * 8);
+        }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int t = threadIdx.x + 256 * i;
+            if (t < kChunks) {
+                const int pl = t / (16 * (r / 8)), rem = t % (16 * (r / 8));
+                const int row = rem / (r / 8), col = rem % (r / 8);
+                *reinterpret_cast<u32x4*>(&Es[buf][(pl * 16 + row) * ldE + col * 8]) = estage[i];
+            }
+        }
+    };
+    struct UnitIn {
+        u32x4 u0, u1;
+        float temp;
+    };
+    auto fetch = [&](int nb) {
+        UnitIn in;
+        const int b = min(nb * 16 + n, B - 1);
+        const uint16_t* row = U + (static_cast<size_t>(b) * gamma + k) * V;
+        in.u0 = *reinterpret_cast<const u32x4*>(row + ua);
+        in.u1 = *reinterpret_cast<const u32x4*>(row + ub);
+        in.temp = temperature[b];
+        return in;
+    };
+
+    W2Tile<KC> w2;
+    w2.load(W2, V, vt, g, n);
+    fetch_e(0);
+    UnitIn nxt = fetch(0);
+    stage(0);
+    __syncthreads();
+    for (int nb = 0; nb < NB; ++nb) {
+        const UnitIn cur = nxt;
+        if (nb + 1 < NB) {
+            fetch_e(nb + 1);
+            nxt = fetch(nb + 1);
+        }
+        const int b = nb * 16 + n;
+        f32x4 acc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int pl = 0; pl < NPL; ++pl) w2.mul(&Es[nb & 1][(pl * 16 + n) * ldE + 8 * g], acc);
+
+        Stats st = stats_empty();
+        if (b < B && live) {
+            const float temp = cur.temp;
+            const bool sampling = temp > 0.0f;
+            const float invT = sampling ? 1.0f / temp : 1.0f;
+            const uint32_t w[8] = {cur.u0[0], cur.u0[1], cur.u0[2], cur.u0[3],
+                                   cur.u1[0], cur.u1[1], cur.u1[2], cur.u1[3]};
+            float z[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int j = 4 * q + c;
+                    z[j] = ((j & 1) ? hi_bf16(w[j >> 1]) : lo_bf16(w[j >> 1])) + acc[c][q];
+                }
+            if (v0 + 16 <= V)
+                st = lane_stats16<true>(z, v0, V, b, k, sampling, invT, key0, key1, ctr3);
+            else
+                st = lane_stats16<false>(z, v0, V, b, k, sampling, invT, key0, key1, ctr3);
+        }
+        st = stats_merge(st, shfl_xor_stats(st, 16));
+        st = stats_merge(st, shfl_xor_stats(st, 32));
+        if (g == 0) red[nb & 1][wave][n] = st;
+        if (nb + 1 < NB) stage((nb + 1) & 1);
+        __syncthreads();
+        if (wave == 0 && g == 0 && b < B) {
+            Stats t = red[nb & 1][0][n];
+#pragma unroll
+            for (int w = 1; w < kWavesPerWG; ++w) t = stats_merge(t, red[nb & 1][w][n]);
+            const size_t o = static_cast<size_t>(b) * P + blockIdx.x;
+            pm[o] = t.m;
+            ps[o] = t.s;
+            pkey[o] = t.key;
+            pzx[o] = t.zx;
+        }
     }
 }
 

@@ -415,21 +415,19 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
             }
         }
     };
-    // U of unit (step kk, block group nb), issued one unit ahead of its use
+    // U of unit (step kk, block group nb), issued one unit ahead of its use.
+    // The loads are unconditional, from addresses clamped into U (values of
+    // padding blocks and of columns past V are never used), so the compiler
+    // can leave them in flight across the unit instead of waiting at once.
+    const int ua = reg_live ? v0 : 0, ub = (reg_live && v0 + 8 < a.V) ? v0 + 8 : ua;
+    const int ux = x_live ? vx : 0;
     auto fetch_u = [&](int kk, int nb) {
         UAhead p;
-        p.a = u32x4{0u, 0u, 0u, 0u};
-        p.b = u32x4{0u, 0u, 0u, 0u};
-        p.x = make_uint2(0u, 0u);
-        const int b = nb * 16 + n;
-        if (b < a.B) {
-            const uint16_t* row = a.U + (static_cast<size_t>(b) * a.gamma + kk) * a.V;
-            if (reg_live) {
-                p.a = *reinterpret_cast<const u32x4*>(row + v0);
-                if (v0 + 8 < a.V) p.b = *reinterpret_cast<const u32x4*>(row + v0 + 8);
-            }
-            if (x_live) p.x = *reinterpret_cast<const uint2*>(row + vx);
-        }
+        const int b = min(nb * 16 + n, a.B - 1);
+        const uint16_t* row = a.U + (static_cast<size_t>(b) * a.gamma + kk) * a.V;
+        p.a = *reinterpret_cast<const u32x4*>(row + ua);
+        p.b = *reinterpret_cast<const u32x4*>(row + ub);
+        p.x = *reinterpret_cast<const uint2*>(row + ux);
         return p;
     };
     stage_rows();
