@@ -31,7 +31,8 @@
 
 namespace dspark {
 
-constexpr int kPWaves = 4;        // waves per workgroup
+constexpr int kPWaves = 8;        // waves per workgroup (one workgroup per compute unit)
+constexpr int kPThreads = kPWaves * kWave;
 constexpr int kKeyStride = 16;    // uint64 per argmax key copy: one 128-byte line each
 constexpr int kBarGroups = 8;     // arrival counters at bar[32 g]
 constexpr int kBarTop = 256;      // arrivals of the last workgroup of each group
@@ -39,7 +40,7 @@ constexpr int kReleaseWord = 288; // barrier release flag
 constexpr int kTimeoutWord = 320; // set when a barrier wait gave up
 static_assert(kTimeoutWord < kDraftBarWords, "barrier words");
 constexpr int kMaxGamma = 64;     // largest gamma the C ABI accepts
-constexpr int kNoiseStride = 256; // noise buffer: [20 columns][256 threads] floats
+constexpr int kNoiseStride = kPThreads;  // noise buffer: [unit][16 columns][threads] floats
 
 struct PersistArgs {
     const uint16_t* U;
@@ -84,7 +85,8 @@ __global__ __launch_bounds__(256) void k_persist_prepare(int n_keys, uint64_t* _
 // are counted in two levels to spread the contention: workgroup wg adds to
 // counter wg % 8; the workgroup that completes its group's count adds to the
 // top counter, and the one that completes that publishes `step` on a
-// release line, which the others poll about every 0.5 us.  The wait is
+// release line, which the others poll back to back (one device-scope load
+// in flight, a short sleep between).  The wait is
 // bounded: after ~2^20 polls the timeout word is set and the workgroup
 // proceeds, so a broken launch cannot hang the device.
 __device__ __forceinline__ void grid_barrier(uint32_t* bar, uint32_t step, uint32_t nwg, uint32_t wg) {
@@ -105,7 +107,7 @@ __device__ __forceinline__ void grid_barrier(uint32_t* bar, uint32_t step, uint3
         } else {
             uint32_t spins = 0;
             while (__hip_atomic_load(bar + kReleaseWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < step) {
-                __builtin_amdgcn_s_sleep(20);
+                __builtin_amdgcn_s_sleep(2);
                 if (++spins > (1u << 20)) {
                     __hip_atomic_store(bar + kTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
@@ -139,21 +141,22 @@ __device__ __forceinline__ T get_shared(const T* p) {
 // LDS area as one extra MFMA A-operand (XFrag): every wave then does the
 // same work per (16-block group), 80 columns of it at full size.
 
-// The 16-column W2 fragments of a workgroup's 4 waves as MFMA A-operands:
+// The 16-column W2 fragments of a workgroup's waves as MFMA A-operands:
 // wave w's fragment covers columns c0 + 16 w .. c0 + 16 w + 15, and for
 // chunk kc lane (g, n) keeps W2[32 kc + 8 g + e][c0 + 16 w + n], e = 0..7,
 // i.e. row n of A is column c0 + 16 w + n; the MFMA result in lane (g, n) is
 // then columns c0 + 16 w + 4 g + q (q = 0..3) of block row n.  The whole
-// workgroup loads the 64 x r block once per call with 16-byte row loads
-// (two rows per thread and pass) and writes each pair of rows as packed
+// workgroup loads the (16 kPWaves) x r block once per call with 16-byte row
+// loads (two rows per thread and pass) and writes each pair of rows as packed
 // words into the transposed layout.  Columns >= V read 0 (V % 8 == 0).
 template <int KC>
 __device__ __forceinline__ void load_xfrags(const uint16_t* __restrict__ W2, int V, int c0, uint32_t* xf_all) {
-    constexpr int kPairs = KC * 16;  // row pairs
-    const int cseg = threadIdx.x & 7;
+    constexpr int kPairs = KC * 16;             // row pairs
+    constexpr int kSegs = 2 * kPWaves;          // 8-column segments of the workgroup's 16 kPWaves columns
+    const int cseg = threadIdx.x % kSegs;
     const int col = c0 + 8 * cseg;
     const bool ok = col < V;
-    for (int rp = threadIdx.x >> 3; rp < kPairs; rp += 32) {
+    for (int rp = threadIdx.x / kSegs; rp < kPairs; rp += kPThreads / kSegs) {
         const size_t j0 = static_cast<size_t>(2 * rp);
         u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
         if (ok) {
@@ -163,7 +166,7 @@ __device__ __forceinline__ void load_xfrags(const uint16_t* __restrict__ W2, int
         const int kc = rp >> 4, g = (rp >> 2) & 3, p = rp & 3;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const int cc = 8 * cseg + q;  // column within the workgroup's 64
+            const int cc = 8 * cseg + q;  // column within the workgroup's 16 kPWaves
             const int w = cc >> 4, n = cc & 15;
             const uint32_t lo = (q & 1) ? (a[q >> 1] >> 16) : (a[q >> 1] & 0xFFFFu);
             const uint32_t hi = (q & 1) ? (b[q >> 1] & 0xFFFF0000u) : (b[q >> 1] << 16);
@@ -204,7 +207,7 @@ __device__ __forceinline__ void unit_mul(const W2Tile<KC>& w2, bool reg, const u
 // log2_of_neg_log2_uniform).  A strict running maximum over increasing
 // columns keeps the lowest column among equal maxima.  Merge with
 // stats_merge2.
-template <int NQ, bool PRE>
+template <int NQ, bool PRE, int STRIDE = kNoiseStride>
 __device__ __forceinline__ Stats lane_stats(const float (&z)[4 * NQ], const int (&col)[NQ], int b, int k,
                                             bool sampling, float scale, uint32_t key0, uint32_t key1,
                                             uint32_t ctr3, const float* pre) {
@@ -213,10 +216,11 @@ __device__ __forceinline__ Stats lane_stats(const float (&z)[4 * NQ], const int 
     for (int j = 0; j < 4 * NQ; ++j) zs[j] = z[j] * scale;
     // one branch around all the noise of this lane, so the Philox rounds and
     // logarithms of its columns interleave; PRE: the noise terms were
-    // computed earlier and sit in LDS at pre[256 j]
+    // computed earlier and sit at pre[STRIDE j] (LDS, or registers when
+    // STRIDE = 1)
     if (PRE && sampling) {
 #pragma unroll
-        for (int j = 0; j < 4 * NQ; ++j) y[j] = zs[j] - pre[kNoiseStride * j];
+        for (int j = 0; j < 4 * NQ; ++j) y[j] = zs[j] - pre[STRIDE * j];
     } else if (sampling) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
@@ -255,17 +259,19 @@ struct UAhead {
     uint2 x;
 };
 
-// LDS of one workgroup: [4 LDS fragments][E rows][prev tokens]
-// [temperatures][per-wave statistics slots].  The E rows W1[x_{k-1}] are
-// staged either all at once after each barrier, or (GROUPED, when all rows
-// would not fit) 16 at a time in two buffers, the next group's rows loaded
-// while the current group is computed.  Either way the MFMA operand comes
-// from LDS, so its wait never covers the U loads still in flight.  AHEAD
-// (small B): the Gumbel terms of the first block group of each step are
-// computed while memory is busy -- under the W2 loads before step 0, under
-// the key and E-row loads after each barrier -- and kept in LDS
-// ([20 columns][256 threads] floats).
-constexpr size_t kPersistLdsMax = 80 * 1024;  // two workgroups per CU
+// LDS of one workgroup: [kPWaves LDS fragments][E rows][prev tokens]
+// [temperatures][per-wave statistics slots][noise].  The E rows
+// W1[x_{k-1}] are staged either all at once after each barrier, or
+// (GROUPED, when all rows would not fit) 16 at a time in two buffers, the
+// next group's rows loaded while the current group is computed.  Either way
+// the MFMA operand comes from LDS, so its wait never covers the U loads
+// still in flight.  AHEAD (B <= 32, at most two block groups): the Gumbel
+// terms of the register-tile columns of every block group are computed
+// while memory is busy -- under the W2 loads before step 0; after each
+// barrier group 0's under the key loads and group 1's under the E-row
+// loads -- and kept in LDS ([group][16 columns][threads] floats); the 4
+// LDS-fragment columns draw theirs in line.
+constexpr size_t kPersistLdsMax = 160 * 1024;  // one workgroup per CU
 
 template <int KC>
 __host__ __device__ constexpr size_t persist_xfrag_bytes() {
@@ -275,21 +281,22 @@ template <int KC>
 __host__ __device__ constexpr size_t persist_e_bytes(int rows) {
     return static_cast<size_t>(rows) * (KC * 32 + 8) * 2;
 }
-constexpr size_t kNoiseBytes = 20 * kNoiseStride * 4;
+constexpr size_t kNoiseBytesPerGroup = 16 * kNoiseStride * 4;
 template <int KC>
 __host__ __device__ constexpr size_t persist_lds(int Bpad, int B, bool grouped, bool ahead) {
     return persist_xfrag_bytes<KC>() + persist_e_bytes<KC>(grouped ? 32 : Bpad) +
            2 * align_up(static_cast<size_t>(Bpad) * 4, 16) +
-           align_up(sizeof(Stats) * kPWaves * static_cast<size_t>(B), 16) + (ahead ? kNoiseBytes : 0);
+           align_up(sizeof(Stats) * kPWaves * static_cast<size_t>(B), 16) +
+           (ahead ? (Bpad / 16) * kNoiseBytesPerGroup : 0);
 }
 
 template <int KC, bool GROUPED, bool AHEAD>
-__global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
+__global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a) {
     static_assert(!(GROUPED && AHEAD), "noise ahead needs all E rows staged");
     constexpr int r = KC * 32;
     constexpr int ldE = r + 8;  // padded row stride of the staged E rows (bank spread)
-    constexpr int kGroupChunks = 16 * (r / 8);                 // 16-byte pieces of 16 rows
-    constexpr int kStage = (kGroupChunks + 255) / 256;         // per thread
+    constexpr int kGroupChunks = 16 * (r / 8);                       // 16-byte pieces of 16 rows
+    constexpr int kStage = (kGroupChunks + kPThreads - 1) / kPThreads;  // per thread
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const size_t e_bytes = persist_e_bytes<KC>(GROUPED ? 32 : a.Bpad);
     const size_t bp4 = align_up(static_cast<size_t>(a.Bpad) * 4, 16);
@@ -317,27 +324,37 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
     const bool reg_live = v0 < a.V, x_live = vx < a.V;
 
     const bool active = has_reg || has_x;
-    // AHEAD: Gumbel terms of block group 0 at step kk (part 0: the 16
-    // register-tile columns, part 1: the 4 LDS-fragment columns), whether or
-    // not the block samples (the unit only reads them when it does)
-    auto noise_ahead = [&](int kk, int part) {
-        if (!AHEAD || !active || n >= a.B) return;
-        if (part == 0 && reg_live) {
+    // AHEAD: Gumbel terms of block group nb at step kk, whether or not the
+    // block samples (the unit only reads them when it does): the 16
+    // register-tile columns into LDS, the 4 LDS-fragment columns into
+    // registers (nx0 / nx1)
+    float nx0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, nx1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto noise_ahead = [&](int kk, int nb) {
+        const int b = nb * 16 + n;
+        if (!AHEAD || b >= a.B) return;
+        if (reg_live) {
+            float* dst = gn + nb * 16 * kNoiseStride;
 #pragma unroll 1  // one Philox block at a time: few registers are free here
             for (int q = 0; q < 4; ++q) {
                 const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(v0 + 4 * q) >> 2, static_cast<uint32_t>(kk),
-                                                    static_cast<uint32_t>(n), a.ctr3},
+                                                    static_cast<uint32_t>(b), a.ctr3},
                                               a.key0, a.key1);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) gn[kNoiseStride * (4 * q + c)] = log2_of_neg_log2_uniform(w[c]);
+                for (int c = 0; c < 4; ++c) dst[kNoiseStride * (4 * q + c)] = log2_of_neg_log2_uniform(w[c]);
             }
         }
-        if (part == 1 && x_live) {
+        if (x_live) {
             const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(vx) >> 2, static_cast<uint32_t>(kk),
-                                                static_cast<uint32_t>(n), a.ctr3},
+                                                static_cast<uint32_t>(b), a.ctr3},
                                           a.key0, a.key1);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) gn[kNoiseStride * (16 + c)] = log2_of_neg_log2_uniform(w[c]);
+            for (int c = 0; c < 4; ++c) {
+                const float gx = log2_of_neg_log2_uniform(w[c]);
+                if (nb == 0)
+                    nx0[c] = gx;
+                else
+                    nx1[c] = gx;
+            }
         }
     };
 
@@ -345,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
     if (has_reg) w2.load(a.W2, a.V, wv * 64, g, n);
     noise_ahead(0, 0);  // while the tile loads are in flight
     noise_ahead(0, 1);
-    load_xfrags<KC>(a.W2, a.V, kPWaves * nWG * 64 + 64 * wg, reinterpret_cast<uint32_t*>(smem));
+    load_xfrags<KC>(a.W2, a.V, kPWaves * nWG * 64 + 16 * kPWaves * wg, reinterpret_cast<uint32_t*>(smem));
     // previous tokens of step 0: the anchors (an out-of-range anchor reads
     // row 0; the finish kernel marks its block invalid)
     for (int b = threadIdx.x; b < a.Bpad; b += blockDim.x) {
@@ -366,23 +383,21 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
         __syncthreads();
     };
     // AHEAD (Bpad <= 32): the same with every load issued first, then the
-    // LDS-fragment noise of step kk, then the stores
+    // noise of block group 1 at step kk, then the stores
     auto stage_rows_ahead = [&](int kk) {
-        constexpr int kMaxChunks = (32 * (r / 8) + 255) / 256;
+        constexpr int kMaxChunks = (32 * (r / 8) + kPThreads - 1) / kPThreads;
         const int chunks = a.Bpad * (r / 8);
         u32x4 e[kMaxChunks];
 #pragma unroll
         for (int i = 0; i < kMaxChunks; ++i) {
-            const int t = threadIdx.x + 256 * i;
-            if (t < chunks) {
-                const int row = t / (r / 8), col = t % (r / 8);
-                e[i] = *reinterpret_cast<const u32x4*>(a.W1 + static_cast<size_t>(prev[row]) * r + col * 8);
-            }
+            const int t = (threadIdx.x + kPThreads * i) % chunks;  // unconditional: stays in flight
+            const int row = t / (r / 8), col = t % (r / 8);
+            e[i] = *reinterpret_cast<const u32x4*>(a.W1 + static_cast<size_t>(prev[row]) * r + col * 8);
         }
         noise_ahead(kk, 1);
 #pragma unroll
         for (int i = 0; i < kMaxChunks; ++i) {
-            const int t = threadIdx.x + 256 * i;
+            const int t = threadIdx.x + kPThreads * i;
             if (t < chunks) {
                 const int row = t / (r / 8), col = t % (r / 8);
                 *reinterpret_cast<u32x4*>(&Es[row * ldE + col * 8]) = e[i];
@@ -395,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
     auto load_group = [&](int nb) {
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
-            const int t = threadIdx.x + 256 * i;
+            const int t = threadIdx.x + kPThreads * i;
             if (t < kGroupChunks) {
                 const int row = t / (r / 8), col = t % (r / 8);
                 staged[i] = *reinterpret_cast<const u32x4*>(a.W1 + static_cast<size_t>(prev[nb * 16 + row]) * r +
@@ -408,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
         uint16_t* buf = Es + (nb & 1) * 16 * ldE;
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
-            const int t = threadIdx.x + 256 * i;
+            const int t = threadIdx.x + kPThreads * i;
             if (t < kGroupChunks) {
                 const int row = t / (r / 8), col = t % (r / 8);
                 *reinterpret_cast<u32x4*>(&buf[row * ldE + col * 8]) = staged[i];
@@ -461,7 +476,8 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
             const uint16_t* erow = GROUPED ? &Es[((nb & 1) * 16 + n) * ldE + 8 * g] : &Es[b * ldE + 8 * g];
             if (active) unit_mul<KC>(w2, has_reg, xf, has_x, erow, lane, acc, accx);
             Stats st = stats_empty();
-            const bool pre = AHEAD && nb == 0;
+            const bool pre = AHEAD;  // AHEAD: at most two groups, both precomputed
+            const float* gnu = gn + nb * 16 * kNoiseStride;
             if (active && b < a.B) {
                 const float temp = temp_s[b];
                 const bool sampling = temp > 0.0f;
@@ -474,23 +490,29 @@ __global__ __launch_bounds__(256, 2) void k_draft_persistent(PersistArgs a) {
                         for (int c = 0; c < 4; ++c) z[4 * q + c] = acc[c][q];
                     if (v0 + 16 <= a.V) {
                         const int col[4] = {v0, v0 + 4, v0 + 8, v0 + 12};
-                        st = pre ? lane_stats<4, true>(z, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gn)
-                                 : lane_stats<4, false>(z, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gn);
+                        st = pre ? lane_stats<4, true>(z, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gnu)
+                                 : lane_stats<4, false>(z, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gnu);
                     } else {  // V % 8 == 0: the first 8 columns are in range
                         float zh[8];
                         const int col[2] = {v0, v0 + 4};
 #pragma unroll
                         for (int j = 0; j < 8; ++j) zh[j] = z[j];
-                        st = pre ? lane_stats<2, true>(zh, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gn)
-                                 : lane_stats<2, false>(zh, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gn);
+                        st = pre ? lane_stats<2, true>(zh, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gnu)
+                                 : lane_stats<2, false>(zh, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gnu);
                     }
                 }
                 if (x_live) {
                     const float zx4[4] = {accx[0], accx[1], accx[2], accx[3]};
                     const int col[1] = {vx};
-                    const float* gx = gn + kNoiseStride * 16;
-                    st = stats_merge2(st, pre ? lane_stats<1, true>(zx4, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gx)
-                                              : lane_stats<1, false>(zx4, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gx));
+                    if (AHEAD) {
+                        const float nxs[4] = {nb == 0 ? nx0[0] : nx1[0], nb == 0 ? nx0[1] : nx1[1],
+                                              nb == 0 ? nx0[2] : nx1[2], nb == 0 ? nx0[3] : nx1[3]};
+                        st = stats_merge2(st, lane_stats<1, true, 1>(zx4, col, b, k, sampling, scale, a.key0, a.key1,
+                                                                     a.ctr3, nxs));
+                    } else {
+                        st = stats_merge2(st, lane_stats<1, false>(zx4, col, b, k, sampling, scale, a.key0, a.key1,
+                                                                   a.ctr3, gnu));
+                    }
                 }
             }
             st = stats_merge2(st, shfl_xor_stats(st, 16));
@@ -692,11 +714,11 @@ static PersistPlan plan_for(const dspark_dims& D) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(p.lds)) != hipSuccess)
         return p;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), 256, p.lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kPThreads, p.lds) !=
         hipSuccess)
         return p;
     if (per_cu < 1) return p;
-    const int nWG = std::min(per_cu, 2) * cus;
+    const int nWG = std::min(per_cu, 1) * cus;
     // columns held on chip: 64 per wave in registers + 16 per wave in LDS
     if (static_cast<int64_t>(D.V) > static_cast<int64_t>(kPWaves) * nWG * 80) return p;
     if (nWG > draft_persist_max_wg()) return p;
@@ -752,10 +774,10 @@ static hipError_t launch_persist_kc(const DraftArgs& A) {
     void (*fn)(PersistArgs) = persist_kernel<KC>(plan.grouped, plan.ahead);
     const size_t lds = plan.lds;
     if (persist_launch_option() == 0)
-        e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG), dim3(256), args, lds,
+        e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG), dim3(kPThreads), args, lds,
                             A.stream);
     else
-        e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG), dim3(256),
+        e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG), dim3(kPThreads),
                                        args, lds, A.stream);
     if (e != hipSuccess) return e;
     if ((e = profile_end(A.stream)) != hipSuccess) return e;
