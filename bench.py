@@ -240,15 +240,14 @@ def main() -> int:
     ms_per_step = elapsed * 1e3 / args.steps
     value = B * gamma * args.steps / elapsed
     avg_kernel_s = kernel_ms * 1e-3 / launches
+    kname = binding.dspark_draft_kernel_name(dims)
     if per_call == 1:
         # single-launch driver: W2 is read once per call, every step's U slice once
-        # variant: all E rows staged, Gumbel terms of the first group ahead (B <= 32)
         driver = "single-launch (%s)" % args.launch
-        kname = "k_draft_persistent<8, false, %s>" % ("true" if B <= 32 else "false")
         alg_bytes = (r + gamma * B) * V * 2
     else:
         # per-step driver: every step streams all of W2 plus its slice of U
-        driver, kname = "per-step", "k_stream_mfma<8,%d>" % (2 if inp.head == "rnn" else 1)
+        driver = "per-step"
         alg_bytes = (r + B) * V * 2
     names = {"qwen3-4b": "qwen3-4b-shaped markov-head block sampling",
              "qwen3-14b": "qwen3-14b-shaped markov-head block sampling, half greedy",

@@ -196,6 +196,13 @@ dspark_status dspark_set_option(int option, int value);
 dspark_status dspark_profile_enable(int enable);
 dspark_status dspark_profile_read(float* kernel_ms, int32_t* launches);
 
+/* Name of the dominant kernel dspark_draft_block runs for `dims` on the
+ * current device with this thread's options, as a kernel trace lists it
+ * without the namespace (the single-launch variant, or the per-step
+ * V-streaming kernel): for measurement reports.  Host function, no device
+ * work; "" if dims are invalid.  The string is static. */
+const char* dspark_draft_kernel_name(const dspark_dims* dims);
+
 /* Message describing the last failure on this thread ("" if none). */
 const char* dspark_last_error(void);
 

@@ -69,6 +69,8 @@ def load() -> ctypes.CDLL:
     lib.dspark_profile_enable.restype = ctypes.c_int
     lib.dspark_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I32)]
     lib.dspark_profile_read.restype = ctypes.c_int
+    lib.dspark_draft_kernel_name.argtypes = [D]
+    lib.dspark_draft_kernel_name.restype = ctypes.c_char_p
     lib.dspark_last_error.argtypes = []
     lib.dspark_last_error.restype = ctypes.c_char_p
     lib.dspark_version.argtypes = []
@@ -112,6 +114,10 @@ def _check(status: int):
 
 def dspark_version() -> int:
     return load().dspark_version()
+
+
+def dspark_draft_kernel_name(dims: dspark_dims) -> str:
+    return load().dspark_draft_kernel_name(ctypes.byref(dims)).decode()
 
 
 def dspark_last_error() -> str:

@@ -247,6 +247,11 @@ dspark_status dspark_profile_read(float* kernel_ms, int32_t* launches) {
     return ok();
 }
 
+const char* dspark_draft_kernel_name(const dspark_dims* dims) {
+    if (check_dims(dims) != DSPARK_OK) return "";
+    return dspark::draft_kernel_name(*dims);
+}
+
 const char* dspark_last_error(void) { return g_last_error.c_str(); }
 
 int dspark_version(void) { return DSPARK_VERSION; }

@@ -13,6 +13,7 @@
 //     combine                 x_k, log p_k; e = W1[x_k]; c_{k+1}, S_{k+1}
 // The only step-to-step dependency is the reduction over V inside combine.
 #include <math.h>
+#include <stdio.h>
 
 #include "device_common.h"
 #include "internal.h"
@@ -809,6 +810,15 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
                            a.conf, a.survival);
     }
     return hipGetLastError();
+}
+
+const char* draft_kernel_name(const dspark_dims& d) {
+    if (draft_path_option() != 1 && persist_path_ok(d)) return persist_kernel_name(d);
+    if (draft_path_option() == 2) return "";
+    if (!mfma_path_ok(d)) return d.dtype == DSPARK_BF16 ? "k_stream_generic<unsigned short>" : "k_stream_generic<float>";
+    static char buf[64];
+    snprintf(buf, sizeof buf, "k_stream_mfma<%d, %d>", d.r / 32, d.head == DSPARK_HEAD_RNN ? 2 : 1);
+    return buf;
 }
 
 hipError_t launch_draft(const DraftArgs& a) {

@@ -21,6 +21,7 @@
 // The only cross-workgroup dependency per step is the argmax over V; the
 // softmax normaliser and the confidence head are computed after the loop.
 #include <math.h>
+#include <stdio.h>
 
 #include <algorithm>
 #include <mutex>
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         if (!AHEAD || b >= a.B) return;
         if (reg_live) {
             float* dst = gn + nb * 16 * kNoiseStride;
-#pragma unroll 1  // one Philox block at a time: few registers are free here
+#pragma unroll 2  // two independent Philox blocks at a time: their rounds interleave
             for (int q = 0; q < 4; ++q) {
                 const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(v0 + 4 * q) >> 2, static_cast<uint32_t>(kk),
                                                     static_cast<uint32_t>(b), a.ctr3},
@@ -735,6 +736,29 @@ bool persist_path_ok(const dspark_dims& D) {
         case 4: return plan_for<4>(D).ok;
         case 8: return plan_for<8>(D).ok;
         default: return false;
+    }
+}
+
+template <int KC>
+static const char* persist_name_kc(const dspark_dims& D) {
+    static const char* names[3] = {"k_draft_persistent<%d, true, false>", "k_draft_persistent<%d, false, true>",
+                                   "k_draft_persistent<%d, false, false>"};
+    static char buf[3][64];
+    const PersistPlan p = plan_for<KC>(D);
+    if (!p.ok) return "";
+    const int which = p.grouped ? 0 : (p.ahead ? 1 : 2);
+    snprintf(buf[which], sizeof buf[which], names[which], KC);
+    return buf[which];
+}
+
+const char* persist_kernel_name(const dspark_dims& D) {
+    if (D.head != DSPARK_HEAD_MARKOV || !mfma_path_ok(D)) return "";
+    switch (D.r / 32) {
+        case 1: return persist_name_kc<1>(D);
+        case 2: return persist_name_kc<2>(D);
+        case 4: return persist_name_kc<4>(D);
+        case 8: return persist_name_kc<8>(D);
+        default: return "";
     }
 }
 

@@ -41,6 +41,8 @@ struct DraftLayout {
 bool mfma_path_ok(const dspark_dims& d);
 bool rnn_gate_mfma_ok(const dspark_dims& d);
 bool persist_path_ok(const dspark_dims& d);
+const char* persist_kernel_name(const dspark_dims& d);  // "" when the path does not fit
+const char* draft_kernel_name(const dspark_dims& d);
 int draft_persist_max_wg();
 hipError_t launch_draft_persistent(const struct DraftArgs& a);
 int draft_partials(const dspark_dims& d);
