@@ -10,7 +10,7 @@
 //           LDS of workgroup (tile - 4 x grid)
 //     for k = 0 .. gamma-1:
 //       every (tile, 16-block group): bias by MFMA from E = W1[x_{k-1}],
-//         + U_k, Gumbel-max statistics (see lane_stats16p)
+//         + U_k, Gumbel-max statistics (see unit_stats)
 //       workgroup merge -> one 64-bit atomicMax per block on the
 //         (perturbed logit, lowest index) key; softmax partials stored
 //       grid barrier (one monotonic counter, bounded spin, no cache flushes)
@@ -56,7 +56,6 @@ struct PersistArgs {
     uint64_t* best;      // [gamma, B, copies, 16]  argmax keys, one 128-byte line each (cleared by prepare)
     uint32_t* bar;       // barrier words (cleared by prepare)
     float2* pms;         // [gamma, B, nWG] softmax (max, sum) partials of every step, base 2
-    float* pzx;          // [gamma, B, nWG] base-2 logit at each workgroup's argmax
     int32_t* dead;       // [B]
     int32_t* tokens;
     float* logp;
@@ -176,17 +175,27 @@ __device__ __forceinline__ void load_xfrags(const uint16_t* __restrict__ W2, int
     }
 }
 
-// acc[c] += bias from the register tile (when `reg`), accx += bias from the
-// LDS fragment (when `xw`), for the 16 block rows whose E rows start at erow
-// (this lane's row, offset 8 g).  One E operand load per chunk feeds both.
-template <int KC>
-__device__ __forceinline__ void unit_mul(const W2Tile<KC>& w2, bool reg, const uint32_t* xf, bool xw,
-                                         const uint16_t* erow, int lane, f32x4 (&acc)[4], f32x4& accx) {
+// acc[c] += bias from the register tile (when REG), accx += bias from the
+// LDS fragment (when XW), for the 16 block rows whose E rows start at erow
+// (this lane's row, offset 8 g).  The choice is a template parameter so the
+// chunk loop is straight-line code: the LDS reads of two chunks are issued
+// ahead of their matrix-core instructions instead of each waiting behind a
+// branch.
+template <int KC, bool REG, bool XW>
+__device__ __forceinline__ void unit_mul(const W2Tile<KC>& w2, const uint32_t* xf, const uint16_t* erow, int lane,
+                                         f32x4 (&acc)[4], f32x4& accx) {
+    u32x4 ev[2], xv[2];
+    auto fetch = [&](int kc, int slot) {
+        ev[slot] = *reinterpret_cast<const u32x4*>(erow + kc * 32);
+        if (XW) xv[slot] = *reinterpret_cast<const u32x4*>(&xf[(kc * kWave + lane) * 4]);
+    };
+    fetch(0, 0);
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-        const u32x4 ev = *reinterpret_cast<const u32x4*>(erow + kc * 32);
-        const bf16x8 bop = __builtin_bit_cast(bf16x8, ev);
-        if (reg) {
+        const int cur = kc & 1;
+        if (kc + 1 < KC) fetch(kc + 1, cur ^ 1);
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, ev[cur]);
+        if (REG) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const u32x4 av = {w2.f[kc][c][0], w2.f[kc][c][1], w2.f[kc][c][2], w2.f[kc][c][3]};
@@ -194,61 +203,69 @@ __device__ __forceinline__ void unit_mul(const W2Tile<KC>& w2, bool reg, const u
                                                                  acc[c], 0, 0, 0);
             }
         }
-        if (xw) {
-            const u32x4 av = *reinterpret_cast<const u32x4*>(&xf[(kc * kWave + lane) * 4]);
-            accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bop, accx, 0, 0, 0);
-        }
+        if (XW) accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[cur]), bop, accx, 0, 0, 0);
     }
 }
 
-// Statistics of 4 * NQ logits of block b at columns col[q] .. col[q] + 3
-// (q = 0..NQ-1, increasing, each a multiple of 4, all below V), in base-2
-// units: z2 = z log2(e) / T, perturbed (when sampling) to z2 - log2(L), the
-// Gumbel-max value up to a positive factor and a constant (see
-// log2_of_neg_log2_uniform).  A strict running maximum over increasing
-// columns keeps the lowest column among equal maxima.  Merge with
-// stats_merge2.
-template <int NQ, bool PRE, int STRIDE = kNoiseStride>
-__device__ __forceinline__ Stats lane_stats(const float (&z)[4 * NQ], const int (&col)[NQ], int b, int k,
-                                            bool sampling, float scale, uint32_t key0, uint32_t key1,
-                                            uint32_t ctr3, const float* pre) {
-    float zs[4 * NQ], y[4 * NQ];
+// Per-lane statistics of one unit, in base-2 units: the running maximum m
+// of z2 = z log2(e) / T, sum of 2^(z2 - m), and the argmax key of the
+// perturbed values.  The logit at the argmax is not carried: the finish
+// kernel recomputes it from U, W1 and W2.
+struct PStats {
+    float m;
+    float s;
+    uint64_t key;
+};
+
+__device__ __forceinline__ PStats pstats_empty() { return PStats{-INFINITY, 0.0f, kKeyNone}; }
+
+__device__ __forceinline__ PStats pstats_merge(const PStats& a, const PStats& b) {
+    PStats r;
+    r.m = fmaxf(a.m, b.m);
+    const float sa = (a.s > 0.0f) ? a.s * __builtin_amdgcn_exp2f(a.m - r.m) : 0.0f;
+    const float sb = (b.s > 0.0f) ? b.s * __builtin_amdgcn_exp2f(b.m - r.m) : 0.0f;
+    r.s = sa + sb;
+    r.key = b.key > a.key ? b.key : a.key;
+    return r;
+}
+
+__device__ __forceinline__ PStats shfl_xor_pstats(const PStats& a, int mask) {
+    PStats r;
+    r.m = __shfl_xor(a.m, mask);
+    r.s = __shfl_xor(a.s, mask);
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(a.key), mask);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(a.key >> 32), mask);
+    r.key = (static_cast<uint64_t>(hi) << 32) | lo;
+    return r;
+}
+
+// Statistics of the 20 logits z[j] of one lane (columns v0 + j for j < 16,
+// vx + j - 16 after, ascending; a column that does not exist holds -inf).  Sampling: y = z2 -
+// g with g[j] = log2(-log2 u), the Gumbel-max value up to a positive factor
+// and a constant (see log2_of_neg_log2_uniform); greedy: y = z2.  The key
+// takes the maximum y and the lowest column attaining it.
+template <bool SAMPLING>
+__device__ __forceinline__ PStats unit_stats(const float (&z)[20], const float (&g)[20], int v0, int vx,
+                                             float scale) {
+    float y[20];
 #pragma unroll
-    for (int j = 0; j < 4 * NQ; ++j) zs[j] = z[j] * scale;
-    // one branch around all the noise of this lane, so the Philox rounds and
-    // logarithms of its columns interleave; PRE: the noise terms were
-    // computed earlier and sit at pre[STRIDE j] (LDS, or registers when
-    // STRIDE = 1)
-    if (PRE && sampling) {
+    for (int j = 0; j < 20; ++j) y[j] = SAMPLING ? fmaf(z[j], scale, -g[j]) : z[j] * scale;
+    float ybest = y[0], zmax = z[0];
 #pragma unroll
-        for (int j = 0; j < 4 * NQ; ++j) y[j] = zs[j] - pre[STRIDE * j];
-    } else if (sampling) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const u32x4 ctr = {static_cast<uint32_t>(col[q]) >> 2, static_cast<uint32_t>(k),
-                               static_cast<uint32_t>(b), ctr3};
-            const u32x4 w = philox4x32_10(ctr, key0, key1);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) y[4 * q + c] = zs[4 * q + c] - log2_of_neg_log2_uniform(w[c]);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4 * NQ; ++j) y[j] = zs[j];
+    for (int j = 1; j < 20; ++j) {
+        ybest = fmaxf(ybest, y[j]);
+        zmax = fmaxf(zmax, z[j]);
     }
-    float m = zs[0], ybest = y[0], zx = zs[0];
-    uint32_t ibest = static_cast<uint32_t>(col[0]);
+    int idx = 19;
 #pragma unroll
-    for (int j = 1; j < 4 * NQ; ++j) {
-        const bool up = y[j] > ybest;
-        ybest = up ? y[j] : ybest;
-        zx = up ? zs[j] : zx;
-        ibest = up ? static_cast<uint32_t>(col[j >> 2] + (j & 3)) : ibest;
-        m = fmaxf(m, zs[j]);
-    }
+    for (int j = 18; j >= 0; --j) idx = (y[j] == ybest) ? j : idx;
+    if (zmax == -INFINITY) return pstats_empty();  // no column of this lane exists
+    const float m = zmax * scale;
     float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4 * NQ; ++j) s += __builtin_amdgcn_exp2f(zs[j] - m);
-    return Stats{m, s, argmax_key(ybest, ibest), zx};
+    for (int j = 0; j < 20; ++j) s += __builtin_amdgcn_exp2f(fmaf(z[j], scale, -m));
+    const int c = idx < 16 ? v0 + idx : vx + (idx - 16);
+    return PStats{m, s, argmax_key(ybest, static_cast<uint32_t>(c))};
 }
 
 // U values of one unit, loaded one unit ahead of use: 16 columns of the
@@ -287,7 +304,7 @@ template <int KC>
 __host__ __device__ constexpr size_t persist_lds(int Bpad, int B, bool grouped, bool ahead) {
     return persist_xfrag_bytes<KC>() + persist_e_bytes<KC>(grouped ? 32 : Bpad) +
            2 * align_up(static_cast<size_t>(Bpad) * 4, 16) +
-           align_up(sizeof(Stats) * kPWaves * static_cast<size_t>(B), 16) +
+           align_up(sizeof(PStats) * kPWaves * static_cast<size_t>(B), 16) +
            (ahead ? (Bpad / 16) * kNoiseBytesPerGroup : 0);
 }
 
@@ -304,9 +321,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     uint16_t* Es = reinterpret_cast<uint16_t*>(smem + persist_xfrag_bytes<KC>());
     int32_t* prev = reinterpret_cast<int32_t*>(smem + persist_xfrag_bytes<KC>() + e_bytes);
     float* temp_s = reinterpret_cast<float*>(smem + persist_xfrag_bytes<KC>() + e_bytes + bp4);
-    Stats* slot = reinterpret_cast<Stats*>(smem + persist_xfrag_bytes<KC>() + e_bytes + 2 * bp4);
+    PStats* slot = reinterpret_cast<PStats*>(smem + persist_xfrag_bytes<KC>() + e_bytes + 2 * bp4);
     float* gn = reinterpret_cast<float*>(smem + persist_xfrag_bytes<KC>() + e_bytes + 2 * bp4 +
-                                         align_up(sizeof(Stats) * kPWaves * static_cast<size_t>(a.B), 16)) +
+                                         align_up(sizeof(PStats) * kPWaves * static_cast<size_t>(a.B), 16)) +
                 threadIdx.x;  // this thread's noise column
 
     const int lane = threadIdx.x & 63;
@@ -450,7 +467,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     UAhead ahead = fetch_u(0, 0);
 
     for (int k = 0; k < a.gamma; ++k) {
-        for (int b = lane; b < a.B; b += 64) slot[wave * a.B + b] = stats_empty();
+        for (int b = lane; b < a.B; b += 64) slot[wave * a.B + b] = pstats_empty();
         // every wave runs all NB units (GROUPED stages rows between them);
         // waves without columns skip the arithmetic
         for (int nb = 0; nb < NB; ++nb) {
@@ -475,50 +492,60 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
                 ahead = fetch_u(k + 1, 0);
             const int b = nb * 16 + n;
             const uint16_t* erow = GROUPED ? &Es[((nb & 1) * 16 + n) * ldE + 8 * g] : &Es[b * ldE + 8 * g];
-            if (active) unit_mul<KC>(w2, has_reg, xf, has_x, erow, lane, acc, accx);
-            Stats st = stats_empty();
-            const bool pre = AHEAD;  // AHEAD: at most two groups, both precomputed
-            const float* gnu = gn + nb * 16 * kNoiseStride;
+            // (has_x implies has_reg: the fragment columns start past all tiles)
+            if (has_x)
+                unit_mul<KC, true, true>(w2, xf, erow, lane, acc, accx);
+            else if (has_reg)
+                unit_mul<KC, true, false>(w2, xf, erow, lane, acc, accx);
+            PStats st = pstats_empty();
             if (active && b < a.B) {
                 const float temp = temp_s[b];
                 const bool sampling = temp > 0.0f;
                 const float scale = sampling ? kLog2e / temp : kLog2e;
-                if (reg_live) {
-                    float z[16];
+                // the lane's 16 register-tile columns and 4 LDS-fragment
+                // columns; columns past V (V % 8 == 0) and absent parts hold -inf
+                const bool reg_hi = reg_live && v0 + 16 <= a.V;
+                float z[20];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) z[4 * q + c] = acc[c][q];
-                    if (v0 + 16 <= a.V) {
-                        const int col[4] = {v0, v0 + 4, v0 + 8, v0 + 12};
-                        st = pre ? lane_stats<4, true>(z, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gnu)
-                                 : lane_stats<4, false>(z, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gnu);
-                    } else {  // V % 8 == 0: the first 8 columns are in range
-                        float zh[8];
-                        const int col[2] = {v0, v0 + 4};
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) zh[j] = z[j];
-                        st = pre ? lane_stats<2, true>(zh, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gnu)
-                                 : lane_stats<2, false>(zh, col, b, k, sampling, scale, a.key0, a.key1, a.ctr3, gnu);
+                    for (int c = 0; c < 4; ++c) {
+                        const bool ok = q < 2 ? reg_live : reg_hi;
+                        z[4 * q + c] = ok ? acc[c][q] : -INFINITY;
                     }
-                }
-                if (x_live) {
-                    const float zx4[4] = {accx[0], accx[1], accx[2], accx[3]};
-                    const int col[1] = {vx};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) z[16 + c] = x_live ? accx[c] : -INFINITY;
+                if (sampling) {
+                    float gs[20];
                     if (AHEAD) {
-                        const float nxs[4] = {nb == 0 ? nx0[0] : nx1[0], nb == 0 ? nx0[1] : nx1[1],
-                                              nb == 0 ? nx0[2] : nx1[2], nb == 0 ? nx0[3] : nx1[3]};
-                        st = stats_merge2(st, lane_stats<1, true, 1>(zx4, col, b, k, sampling, scale, a.key0, a.key1,
-                                                                     a.ctr3, nxs));
+                        const float* gnu = gn + nb * 16 * kNoiseStride;
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) gs[j] = gnu[kNoiseStride * j];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) gs[16 + c] = nb == 0 ? nx0[c] : nx1[c];
                     } else {
-                        st = stats_merge2(st, lane_stats<1, false>(zx4, col, b, k, sampling, scale, a.key0, a.key1,
-                                                                   a.ctr3, gnu));
+#pragma unroll
+                        for (int q = 0; q < 5; ++q) {
+                            const int cq = q < 4 ? v0 + 4 * q : vx;
+                            const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(cq) >> 2,
+                                                                static_cast<uint32_t>(k), static_cast<uint32_t>(b),
+                                                                a.ctr3},
+                                                          a.key0, a.key1);
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) gs[4 * q + c] = log2_of_neg_log2_uniform(w[c]);
+                        }
                     }
+                    st = unit_stats<true>(z, gs, v0, vx, scale);
+                } else {
+                    float gs[20];
+#pragma unroll
+                    for (int j = 0; j < 20; ++j) gs[j] = 0.0f;
+                    st = unit_stats<false>(z, gs, v0, vx, scale);
                 }
             }
-            st = stats_merge2(st, shfl_xor_stats(st, 16));
-            st = stats_merge2(st, shfl_xor_stats(st, 32));
-            if (g == 0 && b < a.B) slot[wave * a.B + b] = stats_merge2(slot[wave * a.B + b], st);
+            st = pstats_merge(st, shfl_xor_pstats(st, 16));
+            st = pstats_merge(st, shfl_xor_pstats(st, 32));
+            if (g == 0 && b < a.B) slot[wave * a.B + b] = pstats_merge(slot[wave * a.B + b], st);
             if (GROUPED && nb + 1 < NB) {
                 store_group(nb + 1);
                 __syncthreads();
@@ -527,9 +554,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         __syncthreads();
         // workgroup merge in wave order, then publish
         for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
-            Stats t = slot[b];
+            PStats t = slot[b];
 #pragma unroll
-            for (int w = 1; w < kPWaves; ++w) t = stats_merge2(t, slot[w * a.B + b]);
+            for (int w = 1; w < kPWaves; ++w) t = pstats_merge(t, slot[w * a.B + b]);
             if (t.key != kKeyNone)
                 __hip_atomic_fetch_max(&a.best[((static_cast<size_t>(k) * a.B + b) * kDraftKeyCopies +
                                                 wg % kDraftKeyCopies) * kKeyStride],
@@ -537,7 +564,6 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
             // softmax partials are read after the kernel (k_persist_finish)
             const size_t o = (static_cast<size_t>(k) * a.B + b) * nWG + partial_slot(wg, nWG);
             a.pms[o] = make_float2(t.m, t.s);
-            a.pzx[o] = t.zx;
         }
         if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
         grid_barrier(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG), static_cast<uint32_t>(wg));
@@ -600,8 +626,8 @@ __device__ __forceinline__ float lane_dot_bf16(const uint16_t* x, const uint16_t
 
 // Workgroup b, after the loop.  Wave w handles positions k = w, w + 8, ...:
 // x_k from the argmax keys, log p_k from the step's (max, sum) partials
-// (merged lane-strided, then across the wave) and the logit of x_k kept by
-// the workgroup that owns that column, c_k = sigma(w[0:d] . h_{b,k} +
+// (merged lane-strided, then across the wave) and the logit of x_k
+// (recomputed from U, W1 and W2), c_k = sigma(w[0:d] . h_{b,k} +
 // w[d:d+r] . W1[x_{k-1}]) (Eq 7, x_{-1} = the anchor); then S_k = c_0 ... c_k
 // in position order.  A block is invalid from its first position whose
 // previous token is out of range, or entirely when a grid barrier gave up.
@@ -655,9 +681,16 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
             m = mm;
         }
         const int xk = bad ? 0 : xs[k + 1];  // in range unless bad
-        const int c_reg = kPWaves * a.nWG * 64;  // columns below this sit in register tiles
-        const int owner = (xk < c_reg ? xk / 64 : (xk - c_reg) / 16) / kPWaves;
-        const float zx = bad ? 0.0f : a.pzx[base + partial_slot(owner, a.nWG)];
+        // the draft logit at x_k, z = U[b, k, x_k] + W1[x_{k-1}] . W2[:, x_k]
+        // (Eq 4/5), recomputed here in float32
+        const int xp = bad ? 0 : xs[k];
+        float zp = 0.0f;
+        for (int j = lane; j < a.r; j += kWave)
+            zp = fmaf(bf16_to_f32(a.W1[static_cast<size_t>(xp) * a.r + j]),
+                      bf16_to_f32(a.W2[static_cast<size_t>(j) * a.V + xk]), zp);
+        const float zx_raw = wave_sum(zp) + bf16_to_f32(a.U[(static_cast<size_t>(b) * a.gamma + k) * a.V + xk]);
+        const float temp = a.temperature[b];
+        const float zx = zx_raw * (temp > 0.0f ? kLog2e / temp : kLog2e);
         float part = lane_dot_bf16(a.w_conf, a.h + (static_cast<size_t>(b) * a.gamma + k) * a.d, a.d, lane);
         if (!bad) part += lane_dot_bf16(a.w_conf + a.d, a.W1 + static_cast<size_t>(xs[k]) * a.r, a.r, lane);
         const float logit = wave_sum(part);
@@ -785,7 +818,6 @@ static hipError_t launch_persist_kc(const DraftArgs& A) {
     p.best = reinterpret_cast<uint64_t*>(ws + L.best);
     p.bar = reinterpret_cast<uint32_t*>(ws + L.bar);
     p.pms = reinterpret_cast<float2*>(ws + L.qms);
-    p.pzx = reinterpret_cast<float*>(ws + L.qzx);
     p.dead = reinterpret_cast<int32_t*>(ws + L.dead);
     p.tokens = A.tokens; p.logp = A.logp; p.conf = A.conf; p.survival = A.survival;
 
