@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256) void k_persist_prepare(int n_keys, uint64_t* _
 
 // ------------------------------------------------------- grid barrier
 
-// Grid barrier number `step` (1, 2, ...).  Everything one workgroup hands
+// Grid barrier number `step` (1, 2, ...), in two halves (below).
+// Everything one workgroup hands
 // to another inside this kernel is a device-scope atomic (the argmax keys and
 // the barrier words; the softmax partials are only read after the kernel):
 // those are coherent at the device level (sc1), so the barrier needs no L2
@@ -89,15 +90,23 @@ __global__ __launch_bounds__(256) void k_persist_prepare(int n_keys, uint64_t* _
 // in flight, a short sleep between).  The wait is
 // bounded: after ~2^20 polls the timeout word is set and the workgroup
 // proceeds, so a broken launch cannot hang the device.
-__device__ __forceinline__ void grid_barrier(uint32_t* bar, uint32_t step, uint32_t nwg, uint32_t wg) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
+// The barrier in two halves, so that independent work (the next step's
+// Gumbel terms) can run while the arrival's atomic is in flight:
+// barrier_arrive (after the release fence and a workgroup barrier) issues
+// thread 0's add to its group counter; barrier_finish completes the
+// arrival from the returned count and waits for the release.
+__device__ __forceinline__ uint32_t barrier_arrive(uint32_t* bar, uint32_t wg) {
+    if (threadIdx.x != 0) return 0u;
+    return __hip_atomic_fetch_add(bar + 32 * (wg % kBarGroups), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void barrier_finish(uint32_t* bar, uint32_t before, uint32_t step, uint32_t nwg,
+                                               uint32_t wg) {
     if (threadIdx.x == 0) {
         const uint32_t grp = wg % kBarGroups;
         const uint32_t gsize = (nwg - grp + kBarGroups - 1) / kBarGroups;
         const uint32_t ngroups = nwg < kBarGroups ? nwg : kBarGroups;
         bool release = false;
-        const uint32_t before = __hip_atomic_fetch_add(bar + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (before + 1 == step * gsize) {
             const uint32_t top = __hip_atomic_fetch_add(bar + kBarTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             release = top + 1 == step * ngroups;
@@ -284,11 +293,11 @@ struct UAhead {
 // next group's rows loaded while the current group is computed.  Either way
 // the MFMA operand comes from LDS, so its wait never covers the U loads
 // still in flight.  AHEAD (B <= 32, at most two block groups): the Gumbel
-// terms of the register-tile columns of every block group are computed
-// while memory is busy -- under the W2 loads before step 0; after each
-// barrier group 0's under the key loads and group 1's under the E-row
-// loads -- and kept in LDS ([group][16 columns][threads] floats); the 4
-// LDS-fragment columns draw theirs in line.
+// terms of every block group are computed while memory or other workgroups
+// are busy -- under the W2 loads before step 0; at each step end group 0's
+// while the key atomics complete and group 1's while the barrier arrival is
+// in flight -- and kept in LDS ([group][16 columns][threads] floats) for the
+// register-tile columns and in registers for the 4 LDS-fragment columns.
 constexpr size_t kPersistLdsMax = 160 * 1024;  // one workgroup per CU
 
 template <int KC>
@@ -401,8 +410,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         __syncthreads();
     };
     // AHEAD (Bpad <= 32): the same with every load issued first, then the
-    // noise of block group 1 at step kk, then the stores
-    auto stage_rows_ahead = [&](int kk) {
+    // stores
+    auto stage_rows_ahead = [&]() {
         constexpr int kMaxChunks = (32 * (r / 8) + kPThreads - 1) / kPThreads;
         const int chunks = a.Bpad * (r / 8);
         u32x4 e[kMaxChunks];
@@ -412,7 +421,6 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
             const int row = t / (r / 8), col = t % (r / 8);
             e[i] = *reinterpret_cast<const u32x4*>(a.W1 + static_cast<size_t>(prev[row]) * r + col * 8);
         }
-        noise_ahead(kk, 1);
 #pragma unroll
         for (int i = 0; i < kMaxChunks; ++i) {
             const int t = threadIdx.x + kPThreads * i;
@@ -566,12 +574,20 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
             a.pms[o] = make_float2(t.m, t.s);
         }
         if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
-        grid_barrier(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG), static_cast<uint32_t>(wg));
+        // next step's noise of group 0 while the key atomics complete, the
+        // release fence and workgroup barrier, the arrival, group 1's noise
+        // while the arrival is in flight, then the wait for the release
+        noise_ahead(k + 1, 0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        const uint32_t before = barrier_arrive(a.bar, static_cast<uint32_t>(wg));
+        noise_ahead(k + 1, 1);
+        barrier_finish(a.bar, before, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG),
+                       static_cast<uint32_t>(wg));
         // x_k of every block from the keys -> the E rows of step k+1: the
         // copies of a block's key sit in 8 consecutive lanes
         for (int t = threadIdx.x; t < a.B * kDraftKeyCopies; t += blockDim.x) {
             uint64_t key = get_shared(&a.best[(static_cast<size_t>(k) * a.B * kDraftKeyCopies + t) * kKeyStride]);
-            if (AHEAD) noise_ahead(k + 1, 0);  // while the keys are in flight (one pass: B <= 32)
 #pragma unroll
             for (int o = 1; o < kDraftKeyCopies; o <<= 1) {
                 const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o);
@@ -583,10 +599,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
             if (t % kDraftKeyCopies == 0)
                 prev[t / kDraftKeyCopies] = (key != kKeyNone && x < static_cast<uint32_t>(a.V)) ? static_cast<int>(x) : 0;
         }
-        if (AHEAD && a.B * kDraftKeyCopies <= static_cast<int>(threadIdx.x)) noise_ahead(k + 1, 0);
         __syncthreads();
         if (AHEAD)
-            stage_rows_ahead(k + 1);
+            stage_rows_ahead();
         else
             stage_rows();
     }
