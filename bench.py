@@ -137,8 +137,10 @@ def bench_loss(args) -> int:
     el = time.perf_counter() - t0
     pass_ms, launches = binding.dspark_profile_read()
     binding.dspark_profile_enable(False)
-    # three passes: read U and T each; the third also writes bf16 dlogits
-    alg_bytes = 3 * 2 * R * V * 2 + R * V * 2
+    # the three passes' own inputs and outputs: passes 1 and 2 read U and T,
+    # pass 3 reads U and writes bf16 dlogits (its sign bits from pass 2 are
+    # an implementation detail and not counted)
+    alg_bytes = 2 * (2 * R * V * 2) + 2 * R * V * 2
     pass_s = pass_ms * 1e-3 / args.steps
     line = {
         "metric": "teacher-forced rows/s (V=151936, r=256, γ=7, 7168 rows)",

@@ -64,6 +64,7 @@ struct LossLayout {
     size_t alog;       // f32 [Rpad]  confidence logit (NaN for invalid rows)
     size_t lse_d, lse_t, zlab, tv, cmin, S;  // f32 [Rpad] per-row statistics
     size_t part[5];    // f32 [P, Rpad] per-pass partials
+    size_t smask;      // u32 [ceil(V/16), Rpad] sign(p_d - p_t), 2 bits per element (matrix-core path)
     size_t tce, ttv, tbce;  // f32 [Rpad] weighted loss terms
     size_t total;
 };

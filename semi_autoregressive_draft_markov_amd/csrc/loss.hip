@@ -12,6 +12,7 @@
 //   pass 2   per row: sum |p_d - p_t|, sum min(p_d, p_t), sum p_d sign(p_d - p_t)
 //   finalize c*, CE, BCE, dL/da per row; the four losses (fixed-order sums)
 //   pass 3   dZ = (w_k/N)[a_ce (p_d - onehot) + a_tv p_d (s - S)]  -> dlogits
+//            (matrix-core path: s from 2-bit signs pass 2 stored, T not read)
 //   dW2      E^T dZ, MFMA over rows (split-bf16 when dZ is float32)
 #include <math.h>
 
@@ -64,6 +65,8 @@ LossLayout loss_layout(const dspark_dims& d) {
     L.cmin = take(sizeof(float) * rp);
     L.S = take(sizeof(float) * rp);
     for (int q = 0; q < 5; ++q) L.part[q] = take(sizeof(float) * rp * L.P);
+    // one extra column group: the store target of lanes past V
+    L.smask = take(L.mfma ? sizeof(uint32_t) * rp * ((d.V + 15) / 16 + 1) : 0);
     L.tce = take(sizeof(float) * rp);
     L.ttv = take(sizeof(float) * rp);
     L.tbce = take(sizeof(float) * rp);
@@ -158,6 +161,8 @@ struct PassArgs {
     const int32_t* label;
     const float *lse_d, *lse_t, *S, *rowc;
     float* part[5];        // partials [P][Rpad]
+    uint32_t* smask;       // sign(p_d - p_t) as 2 bits per element, [V / 16 + 1][Rpad] (matrix-core path)
+    int mask_groups;       // ceil(V / 16): index of the extra (discard) column group
     void* dz;
     int dz_bf16;
     float a_ce, a_tv;
@@ -241,10 +246,13 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 
 // Per-row work on NC consecutive columns v0 .. v0+NC-1 (zd = U + bias,
 // zt = target logits; columns at or past V hold -inf).
-// (DZB: pass 3 stores bf16 dZ, else float32)
-template <int PASS, int NC, int DZB>
+// (DZB: pass 3 stores bf16 dZ, else float32.  MASK: pass 2 also returns
+// sign(p_d - p_t) of its columns in `bits`, 2 bits per column (bit 2j: p_d >
+// p_t, bit 2j + 1: p_d < p_t), and pass 3 takes the signs from `bits`
+// instead of recomputing p_t, so it never reads the target logits.)
+template <int PASS, int NC, int DZB, bool MASK>
 __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int v0, const RowIn& ri,
-                                                const float (&zd)[NC], const float (&zt)[NC]) {
+                                                const float (&zd)[NC], const float (&zt)[NC], uint32_t& bits) {
     RowPart p = rowpart_empty(PASS);
     if (PASS == kPass1) {
         float md = zd[0], mt = zt[0];
@@ -265,6 +273,7 @@ __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int 
         const float ld = ri.ld, lt = ri.lt;
         if (PASS == kPass2) {
             float tv = 0.0f, cm = 0.0f, S = 0.0f;
+            uint32_t sb = 0u;
 #pragma unroll
             for (int j = 0; j < NC; ++j) {
                 const float pd = __builtin_amdgcn_exp2f(fmaf(zd[j], kLog2e, -ld));
@@ -272,8 +281,10 @@ __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int 
                 tv += fabsf(pd - pt);
                 cm += fminf(pd, pt);
                 S += pd > pt ? pd : (pd < pt ? -pd : 0.0f);
+                if (MASK) sb |= (pd > pt ? 1u : 0u) << (2 * j) | (pd < pt ? 2u : 0u) << (2 * j);
             }
             p.v[0] = tv; p.v[1] = cm; p.v[2] = S;
+            if (MASK) bits = sb;
         } else {
             const float coef = ri.rowc, S = ri.S;
             const int lab = ri.label;
@@ -288,8 +299,14 @@ __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int 
                 for (int q = 0; q < 8 && h + q < NC; ++q) {
                     const int j = h + q;
                     const float pd = __builtin_amdgcn_exp2f(fmaf(zd[j], kLog2e, -ld));
-                    const float pt = __builtin_amdgcn_exp2f(fmaf(zt[j], kLog2e, -lt));
-                    const float sg = pd > pt ? 1.0f : (pd < pt ? -1.0f : 0.0f);
+                    float sg;
+                    if (MASK) {
+                        sg = static_cast<float>(static_cast<int>((bits >> (2 * j)) & 1u) -
+                                                static_cast<int>((bits >> (2 * j + 1)) & 1u));
+                    } else {
+                        const float pt = __builtin_amdgcn_exp2f(fmaf(zt[j], kLog2e, -lt));
+                        sg = pd > pt ? 1.0f : (pd < pt ? -1.0f : 0.0f);
+                    }
                     const float onehot = (lab == v0 + j) ? 1.0f : 0.0f;
                     dz[q] = coef * (a.a_ce * (pd - onehot) + a.a_tv * pd * (sg - S));
                 }
@@ -326,7 +343,8 @@ __device__ __forceinline__ RowPart row_epilogue(const PassArgs& a, int row, int 
 // columns of U and T, the per-row values the pass needs, and this thread's
 // share of the block's 16 E rows (staged into LDS for the whole workgroup).
 struct BlockIn {
-    u32x4 u0, u1, t0, t1;
+    u32x4 u0, u1, t0, t1;  // t: target logits (passes 1, 2)
+    uint32_t sbits;        // pass 3: the sign bits pass 2 stored
     RowIn ri;
 };
 
@@ -376,9 +394,15 @@ __global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
             const int row = rb * 16 + n;  // < Rpad: the per-row arrays are padded
             const size_t ro = static_cast<size_t>(min(row, a.R - 1)) * a.V;
             in.u0 = *reinterpret_cast<const u32x4*>(a.U + ro + vc0);
-            in.t0 = *reinterpret_cast<const u32x4*>(a.T + ro + vc0);
             in.u1 = *reinterpret_cast<const u32x4*>(a.U + ro + vc1);
-            in.t1 = *reinterpret_cast<const u32x4*>(a.T + ro + vc1);
+            if (PASS != kPass3) {
+                in.t0 = *reinterpret_cast<const u32x4*>(a.T + ro + vc0);
+                in.t1 = *reinterpret_cast<const u32x4*>(a.T + ro + vc1);
+                in.sbits = 0u;
+            } else {
+                in.t0 = in.t1 = u32x4{0u, 0u, 0u, 0u};
+                in.sbits = a.smask[static_cast<size_t>(vc0 >> 4) * a.Rpad + row];
+            }
             in.ri = row_in(a, PASS, row);
             return in;
         };
@@ -410,6 +434,7 @@ __global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
             w2.mul(&Es[rb & 1][n * ldE + 8 * g], acc);
             const int row = rb * 16 + n;
             RowPart p = rowpart_empty(PASS);
+            uint32_t bits = cur.sbits;
             if (row < a.R && cols) {
                 const uint32_t uw[8] = {cur.u0[0], cur.u0[1], cur.u0[2], cur.u0[3],
                                         cur.u1[0], cur.u1[1], cur.u1[2], cur.u1[3]};
@@ -437,8 +462,11 @@ __global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
                             zt[j] = in ? ((j & 1) ? hi_bf16(tw[j >> 1]) : lo_bf16(tw[j >> 1])) : -INFINITY;
                         }
                 }
-                p = row_epilogue<PASS, 16, DZB>(a, row, v0, cur.ri, zd, zt);
+                p = row_epilogue<PASS, 16, DZB, true>(a, row, v0, cur.ri, zd, zt, bits);
             }
+            // unconditional (padding rows and the extra column group
+            // absorb the lanes without a row or columns)
+            if (PASS == kPass2) a.smask[static_cast<size_t>(cols ? v0 >> 4 : a.mask_groups) * a.Rpad + row] = bits;
             if (PASS != kPass3) {
                 p = rowpart_merge(PASS, p, rowpart_shfl(p, 16));
                 p = rowpart_merge(PASS, p, rowpart_shfl(p, 32));
@@ -493,7 +521,8 @@ __global__ __launch_bounds__(256) void k_loss_generic(PassArgs a) {
                     for (int c = 0; c < 4; ++c)
                         if (v0 + c < a.V) zd[c] = fmaf(e[j], load_f(W2, wrow + c), zd[c]);
                 }
-                p = row_epilogue<PASS, 4, DZB>(a, row, v0, row_in(a, PASS, row), zd, zt);
+                uint32_t bits = 0u;
+                p = row_epilogue<PASS, 4, DZB, false>(a, row, v0, row_in(a, PASS, row), zd, zt, bits);
             }
             if (PASS == kPass3) continue;
             for (int o = 32; o > 0; o >>= 1) p = rowpart_merge(PASS, p, rowpart_shfl(p, o));
@@ -837,6 +866,8 @@ static hipError_t launch_loss_t(const LossArgs& la) {
     a.label = reinterpret_cast<const int32_t*>(ws + L.label);
     a.lse_d = F(L.lse_d); a.lse_t = F(L.lse_t); a.S = F(L.S); a.rowc = F(L.rowc);
     for (int q = 0; q < 5; ++q) a.part[q] = F(L.part[q]);
+    a.smask = reinterpret_cast<uint32_t*>(ws + L.smask);
+    a.mask_groups = (D.V + 15) / 16;
     a.dz = la.dlogits;
     a.dz_bf16 = la.dlogits_dtype == DSPARK_BF16;
     a.a_ce = la.alpha[0];
