@@ -55,6 +55,8 @@ def _load():
         lib.oracle_block_logprob.restype = I
         lib.oracle_block_loss.argtypes = [I, I, I, I, I, I] + [P] * 10 + [P, ctypes.c_int64] + [P] * 9 + [I]
         lib.oracle_block_loss.restype = I
+        lib.oracle_block_loss_backward.argtypes = [I, I, I, I, I, I] + [P] * 11 + [I]
+        lib.oracle_block_loss_backward.restype = I
         _lib = lib
     return _lib
 
@@ -169,4 +171,28 @@ def block_loss(inp, alpha=(0.1, 0.9, 1.0), pos_weight=None, rows=None,
         _ptr(out["dZ"]), _ptr(out["dW2"]), nthreads)
     if rc != 0:
         raise ValueError("oracle_block_loss rejected its input (rc=%d)" % rc)
+    return out
+
+
+def block_loss_backward(inp, dZ, dA, want_dW1: bool = True, want_dw: bool = True,
+                        want_dh: bool = True, nthreads: int = 0) -> dict:
+    """dW1, dw_conf, dh of the teacher-forced objective from given dZ [R, V]
+    and dA [R] (the loss's gradients w.r.t. the draft logits and the
+    confidence logits), float64."""
+    N, g, V, r, d = inp.B, inp.gamma, inp.V, inp.r, inp.d
+    dt = inp.dtype
+    R = N * g
+    dZ = np.ascontiguousarray(np.asarray(dZ, np.float64).reshape(R, V))
+    dA = np.ascontiguousarray(np.asarray(dA, np.float64).reshape(R))
+    out = dict(dW1=np.zeros((V, r)) if want_dW1 else None,
+               dw=np.zeros(d + r) if want_dw else None,
+               dh=np.zeros((R, d)) if want_dh else None)
+    rc = _load().oracle_block_loss_backward(
+        V, r, d, g, N, _dtype_code(dt), _ptr(_arr(inp.h, dt)),
+        _ptr(np.ascontiguousarray(inp.anchor, np.int32)),
+        _ptr(np.ascontiguousarray(inp.labels, np.int32)),
+        _ptr(_arr(inp.W1, dt)), _ptr(_arr(inp.W2, dt)), _ptr(_arr(inp.w_conf, dt)),
+        _ptr(dZ), _ptr(dA), _ptr(out["dW1"]), _ptr(out["dw"]), _ptr(out["dh"]), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_block_loss_backward rejected its input (rc=%d)" % rc)
     return out

@@ -468,3 +468,67 @@ int oracle_block_loss(int V, int r, int d, int gamma, int N, int dtype,
     if (dZbuf != dZ) free(dZbuf);
     return 0;
 }
+
+/* ------------------------------------------------------------ backward */
+
+/* The rest of the teacher-forced backward (chain rule through z_d = U +
+ * E W2 with E_i = W1[prev_i], Eq 5, and through the Eq 7 logit a_i =
+ * w[0:d] . h_i + w[d:d+r] . E_i), given the loss's own gradients dZ =
+ * dL/dz_d [R, V] and dA = dL/da [R]:
+ *   dE_i[j] = sum_v dZ[i, v] W2[j, v] + dA_i w[d + j]
+ *   dW1[x]  = sum over the rows i fed x (prev_i = x) of dE_i, in row order;
+ *             rows of W1 no position was fed stay 0
+ *   dw[q]   = sum_i dA_i h_i[q]  (q < d),  dw[d + j] = sum_i dA_i E_i[j]
+ *   dh_i    = dA_i w[0:d]
+ * c* is a label (held constant), so it contributes nothing.  Rows whose
+ * previous token is out of range, or whose dA is not finite, are skipped by
+ * the sums (their dh is dA_i w). */
+int oracle_block_loss_backward(int V, int r, int d, int gamma, int N, int dtype,
+                               const void* h, const int32_t* anchor, const int32_t* labels,
+                               const void* W1, const void* W2, const void* w_conf,
+                               const double* dZ, const double* dA,
+                               double* dW1, double* dw, double* dh, int nthreads)
+{
+    if (V < 1 || r < 1 || d < 1 || gamma < 1 || N < 1 || (dtype != 0 && dtype != 1) || !dZ || !dA)
+        return -1;
+    const int64_t R = (int64_t)N * gamma;
+    int32_t* prev = malloc(sizeof(int32_t) * (size_t)R);
+    double* dE = malloc(sizeof(double) * (size_t)R * (size_t)r);
+    if (!prev || !dE) { free(prev); free(dE); return -1; }
+    for (int64_t i = 0; i < R; ++i) {
+        const int n = (int)(i / gamma), k = (int)(i % gamma);
+        const int x = k == 0 ? anchor[n] : labels[i - 1];
+        prev[i] = (x >= 0 && x < V && isfinite(dA[i])) ? x : -1;
+    }
+#pragma omp parallel for schedule(static) num_threads(thread_count(nthreads))
+    for (int64_t i = 0; i < R; ++i) {
+        for (int j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int v = 0; v < V; ++v)
+                acc += dZ[i * V + v] * load_elem(W2, dtype, (int64_t)j * V + v);
+            dE[i * r + j] = acc + dA[i] * load_elem(w_conf, dtype, d + j);
+        }
+    }
+    if (dW1) {
+        for (int64_t t = 0; t < (int64_t)V * r; ++t) dW1[t] = 0.0;
+        for (int64_t i = 0; i < R; ++i) {
+            if (prev[i] < 0) continue;
+            for (int j = 0; j < r; ++j) dW1[(int64_t)prev[i] * r + j] += dE[i * r + j];
+        }
+    }
+    if (dw) {
+        for (int q = 0; q < d + r; ++q) dw[q] = 0.0;
+        for (int64_t i = 0; i < R; ++i) {
+            if (prev[i] < 0) continue;
+            for (int q = 0; q < d; ++q) dw[q] += dA[i] * load_elem(h, dtype, i * d + q);
+            for (int j = 0; j < r; ++j) dw[d + j] += dA[i] * load_elem(W1, dtype, (int64_t)prev[i] * r + j);
+        }
+    }
+    if (dh) {
+        for (int64_t i = 0; i < R; ++i)
+            for (int q = 0; q < d; ++q) dh[i * d + q] = dA[i] * load_elem(w_conf, dtype, q);
+    }
+    free(prev);
+    free(dE);
+    return 0;
+}

@@ -94,6 +94,20 @@ int oracle_block_loss(int V, int r, int d, int gamma, int N, int dtype,
                       double* ce, double* tv, double* bce,
                       double* dZ, double* dW2, int nthreads);
 
+/* Rest of the backward of the teacher-forced objective, from the loss's own
+ * gradients dZ = dL/dz_d [R, V] and dA = dL/d(confidence logit) [R] (float64,
+ * e.g. another implementation's stored outputs widened):
+ *   dW1 [V, r]  sum over the rows fed token x of dZ_i W2^T + dA_i w[d:d+r]
+ *   dw  [d + r] sum_i dA_i [h_i; W1[prev_i]]
+ *   dh  [R, d]  dA_i w[0:d]
+ * (each nullable).  Rows with an out-of-range previous token or a
+ * non-finite dA are left out of the sums.  Returns 0 or -1. */
+int oracle_block_loss_backward(int V, int r, int d, int gamma, int N, int dtype,
+                               const void* h, const int32_t* anchor, const int32_t* labels,
+                               const void* W1, const void* W2, const void* w_conf,
+                               const double* dZ, const double* dA,
+                               double* dW1, double* dw, double* dh, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -276,3 +276,68 @@ def test_rejects_out_of_range_label(oracle_lib):
     inp.labels[0, 1] = 10
     with pytest.raises(ValueError):
         oracle_lib.block_loss(inp)
+
+
+# --------------------------------------------------------- rest of the backward
+# dW1, dw and dh from the loss's own dZ and dA, each against central finite
+# differences of the oracle's loss.  c* is a label (held constant), so each
+# check picks inputs where c* does not move with the perturbed parameter:
+# alpha_conf = 0 for the path through z_d, W2 = 0 (z_d independent of W1)
+# for the confidence path of dW1, and h (which never enters z_d).
+
+def _backward(oracle_lib, inp, alpha):
+    out = oracle_lib.block_loss(inp, alpha=alpha)
+    return oracle_lib.block_loss_backward(inp, out["dZ"], out["dA"])
+
+
+def test_dw1_through_the_bias_matches_finite_differences(oracle_lib):
+    alpha = (0.1, 0.9, 0.0)
+    inp = train_inputs(V=8, r=4, N=2, gamma=3, seed=21)
+    assert _away_from_kinks(oracle_lib, inp)
+    g = _backward(oracle_lib, inp, alpha)["dW1"]
+    fed = sorted(set(prev_tokens(inp).reshape(-1).tolist()))
+    for x in fed[:3]:
+        for j in (0, 3):
+            fd = _fd(oracle_lib, inp, "W1", (x, j), alpha)
+            assert abs(fd - g[x, j]) < 1e-6 + 1e-5 * abs(g[x, j]), (x, j, fd, g[x, j])
+
+
+def test_dw1_through_the_confidence_matches_finite_differences(oracle_lib):
+    alpha = (0.1, 0.9, 1.0)
+    inp = train_inputs(V=8, r=4, N=2, gamma=3, seed=22, w2_std=0.0)
+    assert not np.any(inp.W2)
+    g = _backward(oracle_lib, inp, alpha)["dW1"]
+    fed = sorted(set(prev_tokens(inp).reshape(-1).tolist()))
+    for x in fed[:3]:
+        for j in (1, 2):
+            fd = _fd(oracle_lib, inp, "W1", (x, j), alpha)
+            assert abs(fd - g[x, j]) < 1e-7 + 1e-5 * abs(g[x, j]), (x, j, fd, g[x, j])
+
+
+def test_dw1_rows_of_tokens_never_fed_are_zero(oracle_lib):
+    inp = train_inputs(V=16, r=4, N=2, gamma=3, seed=23)
+    g = _backward(oracle_lib, inp, (0.1, 0.9, 1.0))["dW1"]
+    fed = set(prev_tokens(inp).reshape(-1).tolist())
+    for x in range(inp.V):
+        if x not in fed:
+            assert not np.any(g[x])
+        else:
+            assert np.any(g[x])
+
+
+def test_dh_matches_finite_differences(oracle_lib):
+    alpha = (0.1, 0.9, 1.0)
+    inp = train_inputs(V=8, r=4, d=5, N=2, gamma=3, seed=24)
+    dh = _backward(oracle_lib, inp, alpha)["dh"].reshape(inp.B, inp.gamma, inp.d)
+    for idx in [(0, 0, 0), (1, 2, 4), (0, 1, 2)]:
+        fd = _fd(oracle_lib, inp, "h", idx, alpha)
+        assert abs(fd - dh[idx]) < 1e-7 + 1e-5 * abs(dh[idx]), (idx, fd, dh[idx])
+
+
+def test_dw_conf_matches_finite_differences(oracle_lib):
+    alpha = (0.1, 0.9, 1.0)
+    inp = train_inputs(V=8, r=4, d=5, N=2, gamma=3, seed=25)
+    dw = _backward(oracle_lib, inp, alpha)["dw"]
+    for m in (0, 2, inp.d, inp.d + 3):
+        fd = _fd(oracle_lib, inp, "w_conf", (m,), alpha)
+        assert abs(fd - dw[m]) < 1e-7 + 1e-5 * abs(dw[m]), (m, fd, dw[m])
