@@ -71,9 +71,11 @@ typedef struct dspark_dims {
 
 #define DSPARK_CALL_DRAFT 0
 #define DSPARK_CALL_LOSS 1
+#define DSPARK_CALL_LOSS_BACKWARD 2
 
-/* Bytes of device workspace `which` (DSPARK_CALL_DRAFT or DSPARK_CALL_LOSS)
- * needs for `dims`; 0 if dims are invalid.  Host function, no device work. */
+/* Bytes of device workspace `which` (DSPARK_CALL_DRAFT, DSPARK_CALL_LOSS or
+ * DSPARK_CALL_LOSS_BACKWARD) needs for `dims`; 0 if dims are invalid or
+ * `which` is unknown.  Host function, no device work. */
 size_t dspark_workspace_size(const dspark_dims* dims, int which);
 
 /* Semi-autoregressive block drafting: Eq 4 with the Eq 5 (Markov) or Eq 6
@@ -154,6 +156,45 @@ dspark_status dspark_block_loss(const dspark_dims* dims, const void* U, const vo
                                 float* dconf_logit,
                                 void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* The rest of the backward pass of the teacher-forced objective, Markov
+ * head: from dZ = dL/dz_d and dA = dL/d(confidence logit), as
+ * dspark_block_loss returns them, to the gradients of the Markov table, the
+ * confidence weights and the hidden states.  Training updates the
+ * sequential block and the confidence head (dormouse page, section 2, delta
+ * table row D16); row i = n * gamma + k is fed prev_i (anchor[n] at k = 0,
+ * labels[n, k-1] after), and e_i = W1[prev_i] enters both the bias (Eq 5)
+ * and the confidence logit a_i = w . [h_i; e_i] (Eq 7), so
+ *   dE_i     = dZ_i W2^T + dA_i w[d : d+r]
+ *   dW1[x]   = sum of dE_i over the rows i with prev_i = x (0 for tokens
+ *              never fed)
+ *   dw_conf  = sum_i dA_i [h_i; e_i]
+ *   dh_i     = dA_i w[0 : d]
+ * Rows whose prev is outside [0, V) or whose dA is not finite (the loss
+ * call returns NaN for a block with a bad token id) are left out of dW1
+ * and dw_conf; such a block's flag is raised as for the other calls.
+ *
+ * Inputs (device): dlogits [N, gamma, V] float32 or bfloat16 per
+ *   dlogits_dtype (required when dW1 is wanted, else nullable);
+ *   dconf_logit [N, gamma] float (nullable only when dw_conf and dh are
+ *   NULL: dW1 then has no confidence term); h, anchor, labels, W1, W2,
+ *   w_conf as for dspark_block_loss (h is only read for dw_conf).
+ * Outputs (device, float32, each nullable, overwritten):
+ *   dW1 [V, r], dw_conf [d + r] (h part first), dh [N, gamma, d].
+ * The dW1 sums run in row order per token, the others in fixed row order:
+ * results are bitwise reproducible.  bf16 data on the matrix-core shapes
+ * (r a multiple of 32 up to 256, V a multiple of 8) multiply dZ by W2^T
+ * on the matrix cores (float32 dZ as a hi + lo pair of bf16 values, so dZ
+ * is carried to 2^-16 relative); other shapes use the vector units.
+ * workspace: at least dspark_workspace_size(dims, DSPARK_CALL_LOSS_BACKWARD)
+ *   bytes, 256-byte aligned. */
+dspark_status dspark_block_loss_backward(const dspark_dims* dims, const void* dlogits,
+                                         int32_t dlogits_dtype, const float* dconf_logit,
+                                         const void* h, const int32_t* anchor,
+                                         const int32_t* labels, const void* W1, const void* W2,
+                                         const void* w_conf, float* dW1, float* dw_conf, float* dh,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* hip_stream);
+
 /* Synchronises `hip_stream`, then reads the per-block error flags the last
  * call with these dims left at the start of `workspace`: *code (HOST
  * pointer) = the number of blocks that met a token id outside [0, V) (0
@@ -185,10 +226,11 @@ dspark_status dspark_read_device_error(const dspark_dims* dims, const void* work
 dspark_status dspark_set_option(int option, int value);
 
 /* Kernel timing for measurement.  While enabled on the calling thread, each
- * dspark_draft_block / dspark_block_loss call also records a pair of HIP
- * events on `hip_stream` around every launch of its dominant kernel (the
- * V-streaming step kernel when drafting, the V-streaming passes of the
- * loss).  dspark_profile_read() waits for those events and returns (HOST
+ * dspark_draft_block / dspark_block_loss / dspark_block_loss_backward call
+ * also records a pair of HIP events on `hip_stream` around every launch of
+ * its dominant kernel (the V-streaming step kernel when drafting, the
+ * V-streaming passes of the loss, the matrix-core dZ W2^T kernel of the
+ * backward).  dspark_profile_read() waits for those events and returns (HOST
  * out-pointers) the summed milliseconds and the number of timed launches
  * since the previous read, then forgets them.  Events are created on first
  * use and reused; enable = 0 stops recording.  Returns DSPARK_EDEVICE if a

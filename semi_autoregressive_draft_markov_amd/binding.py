@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 DSPARK_OK, DSPARK_EINVAL, DSPARK_EUNSUPPORTED, DSPARK_EWORKSPACE, DSPARK_EDEVICE = range(5)
 DSPARK_F32, DSPARK_BF16 = 0, 1
 DSPARK_HEAD_MARKOV, DSPARK_HEAD_RNN = 0, 1
-DSPARK_CALL_DRAFT, DSPARK_CALL_LOSS = 0, 1
+DSPARK_CALL_DRAFT, DSPARK_CALL_LOSS, DSPARK_CALL_LOSS_BACKWARD = 0, 1, 2
 DSPARK_OPT_DRAFT_PATH = 1
 DSPARK_OPT_PERSIST_LAUNCH = 2
 
@@ -61,6 +61,8 @@ def load() -> ctypes.CDLL:
     lib.dspark_draft_block.restype = ctypes.c_int
     lib.dspark_block_loss.argtypes = [D] + [P] * 13 + [P, I32, P, P, P, SZ, P]
     lib.dspark_block_loss.restype = ctypes.c_int
+    lib.dspark_block_loss_backward.argtypes = [D, P, I32] + [P] * 11 + [SZ, P]
+    lib.dspark_block_loss_backward.restype = ctypes.c_int
     lib.dspark_read_device_error.argtypes = [D, P, ctypes.POINTER(I32), P]
     lib.dspark_read_device_error.restype = ctypes.c_int
     lib.dspark_set_option.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -150,6 +152,17 @@ def dspark_block_loss(dims, U, T_logits, h, anchor, labels, W1, W2, w_conf, alph
         _p(w_conf), _p(a), _p(pw), _p(loss4), _p(c_star), _p(conf), _p(dlogits),
         {"f32": DSPARK_F32, "bf16": DSPARK_BF16}.get(dlogits_dtype, dlogits_dtype),
         _p(dW2), _p(dconf_logit), _p(workspace), nbytes, _stream(stream)))
+
+
+def dspark_block_loss_backward(dims, dlogits, dlogits_dtype, dconf_logit, h, anchor, labels, W1,
+                               W2, w_conf, dW1, dw_conf, dh, workspace, workspace_bytes=None,
+                               stream=None):
+    nbytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(load().dspark_block_loss_backward(
+        ctypes.byref(dims), _p(dlogits),
+        {"f32": DSPARK_F32, "bf16": DSPARK_BF16}.get(dlogits_dtype, dlogits_dtype),
+        _p(dconf_logit), _p(h), _p(anchor), _p(labels), _p(W1), _p(W2), _p(w_conf), _p(dW1),
+        _p(dw_conf), _p(dh), _p(workspace), nbytes, _stream(stream)))
 
 
 def dspark_read_device_error(dims, workspace, stream=None) -> int:

@@ -92,6 +92,7 @@ size_t dspark_workspace_size(const dspark_dims* dims, int which) {
     if (check_dims(dims) != DSPARK_OK) return 0;
     if (which == DSPARK_CALL_DRAFT) return dspark::draft_layout(*dims).total;
     if (which == DSPARK_CALL_LOSS) return dspark::loss_layout(*dims).total;
+    if (which == DSPARK_CALL_LOSS_BACKWARD) return dspark::bwd_layout(*dims).total;
     return 0;
 }
 
@@ -181,6 +182,50 @@ dspark_status dspark_block_loss(const dspark_dims* dims, const void* U, const vo
     a.ws = static_cast<char*>(workspace);
     a.stream = static_cast<hipStream_t>(hip_stream);
     const hipError_t e = dspark::launch_loss(a);
+    if (e != hipSuccess) return fail(DSPARK_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+dspark_status dspark_block_loss_backward(const dspark_dims* dims, const void* dlogits,
+                                         int32_t dlogits_dtype, const float* dconf_logit,
+                                         const void* h, const int32_t* anchor,
+                                         const int32_t* labels, const void* W1, const void* W2,
+                                         const void* w_conf, float* dW1, float* dw_conf, float* dh,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* hip_stream) {
+    dspark_status s = check_dims(dims);
+    if (s != DSPARK_OK) return s;
+    if (dims->head != DSPARK_HEAD_MARKOV)
+        return fail(DSPARK_EUNSUPPORTED, "the training objective is built for the Markov head only");
+    const char* missing = !anchor ? "anchor" : !labels ? "labels" : !W1 ? "W1" : !W2 ? "W2"
+                        : !w_conf ? "w_conf" : !workspace ? "workspace"
+                        : (dW1 && !dlogits) ? "dlogits (needed for dW1)"
+                        : ((dw_conf || dh) && !dconf_logit) ? "dconf_logit (needed for dw_conf and dh)"
+                        : (dw_conf && !h) ? "h (needed for dw_conf)" : nullptr;
+    if (missing) return fail(DSPARK_EINVAL, "required pointer %s is NULL", missing);
+    if (dlogits && dlogits_dtype != DSPARK_F32 && dlogits_dtype != DSPARK_BF16)
+        return fail(DSPARK_EINVAL, "dlogits_dtype = %d is neither DSPARK_F32 nor DSPARK_BF16", dlogits_dtype);
+    if (!aligned(workspace, 256)) return fail(DSPARK_EINVAL, "workspace is not 256-byte aligned");
+    const dspark::BwdLayout L = dspark::bwd_layout(*dims);
+    if (workspace_bytes < L.total)
+        return fail(DSPARK_EWORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, L.total);
+    const size_t esz = dims->dtype == DSPARK_BF16 ? 2 : 4;
+    const size_t dzsz = dlogits_dtype == DSPARK_BF16 ? 2 : 4;
+    if ((h && !aligned(h, esz)) || !aligned(W1, esz) || !aligned(W2, esz) || !aligned(w_conf, esz) ||
+        (dlogits && !aligned(dlogits, dzsz)) || (dconf_logit && !aligned(dconf_logit, 4)) ||
+        (dW1 && !aligned(dW1, 4)) || (dw_conf && !aligned(dw_conf, 4)) || (dh && !aligned(dh, 4)))
+        return fail(DSPARK_EINVAL, "a tensor is not aligned to its element size");
+    if (L.mfma && dW1 && (!aligned(W2, 16) || !aligned(dlogits, 16)))
+        return fail(DSPARK_EUNSUPPORTED, "bf16 W2 and dlogits must be 16-byte aligned");
+
+    dspark::BwdArgs a{};
+    a.dims = *dims;
+    a.dz = dlogits; a.dz_dtype = dlogits_dtype; a.dA = dconf_logit;
+    a.h = h; a.W1 = W1; a.W2 = W2; a.w_conf = w_conf; a.anchor = anchor; a.labels = labels;
+    a.dW1 = dW1; a.dw_conf = dw_conf; a.dh = dh;
+    a.ws = static_cast<char*>(workspace);
+    a.stream = static_cast<hipStream_t>(hip_stream);
+    const hipError_t e = dspark::launch_loss_backward(a);
     if (e != hipSuccess) return fail(DSPARK_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

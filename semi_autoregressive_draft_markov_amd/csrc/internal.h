@@ -86,6 +86,39 @@ struct LossArgs {
 
 hipError_t launch_loss(const LossArgs& a);
 
+// Workspace of the backward call past the logits.  Rows i = n * gamma + k.
+struct BwdLayout {
+    int R;             // rows
+    bool mfma;         // matrix-core dE (the loss call's matrix-core shapes)
+    int T;             // 256-row tiles of dE
+    int S;             // vocabulary slices of dE (bf16 dZ; fp32 dZ picks its own)
+    int RS;            // row splits of the dw_conf sums
+    size_t bad;        // int32 [N]  1 if a token fed to the block is out of range
+    size_t prev;       // i32 [R]  token fed to row i, -1 when left out
+    size_t srow, sprev, slo, shi;  // i32 [R]  rows sorted by prev: row, prev, segment bounds
+    size_t de;         // f32 [R, r]  dL/dE
+    size_t seg;        // f32 [R, r]  chunk sums of dE over sorted rows
+    size_t part;       // f32 [T * S, 256 * r]  split-vocabulary partial tiles
+    size_t dwp;        // f32 [RS, d + r]  dw_conf partial sums
+    size_t total;
+};
+BwdLayout bwd_layout(const dspark_dims& d);
+bool bwd_mfma_ok(const dspark_dims& d);
+
+struct BwdArgs {
+    dspark_dims dims;
+    const void* dz;
+    int32_t dz_dtype;
+    const float* dA;
+    const void *h, *W1, *W2, *w_conf;
+    const int32_t *anchor, *labels;
+    float *dW1, *dw_conf, *dh;
+    char* ws;
+    hipStream_t stream;
+};
+
+hipError_t launch_loss_backward(const BwdArgs& a);
+
 struct DraftArgs {
     dspark_dims dims;
     const void *U, *h, *W1, *W2, *w_conf, *W_rnn;

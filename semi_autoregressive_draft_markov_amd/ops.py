@@ -78,3 +78,26 @@ def block_loss(U, T_logits, h, anchor, labels, W1, W2, w_conf, *, alpha=None, po
     out["_ws"] = ws
     out["_dims"] = dims
     return out
+
+
+def block_loss_backward(dlogits, dconf_logit, h, anchor, labels, W1, W2, w_conf, *,
+                        want_dW1: bool = True, want_dw_conf: bool = True, want_dh: bool = True,
+                        ws: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """dW1, dw_conf and dh from the loss call's dlogits and dconf_logit
+    (see dspark_block_loss_backward)."""
+    N, gamma, d = h.shape
+    V, r = W1.shape
+    dims = _b.make_dims(V, r, d, gamma, N, _dtype_of(W1), "markov")
+    dev = W1.device
+    out = dict(
+        dW1=torch.empty((V, r), dtype=torch.float32, device=dev) if want_dW1 else None,
+        dw_conf=torch.empty(d + r, dtype=torch.float32, device=dev) if want_dw_conf else None,
+        dh=torch.empty((N, gamma, d), dtype=torch.float32, device=dev) if want_dh else None)
+    if ws is None:
+        ws = workspace(dims, _b.DSPARK_CALL_LOSS_BACKWARD, dev)
+    dz_dtype = "f32" if dlogits is None else _dtype_of(dlogits)
+    _b.dspark_block_loss_backward(dims, dlogits, dz_dtype, dconf_logit, h, anchor, labels, W1, W2,
+                                  w_conf, out["dW1"], out["dw_conf"], out["dh"], ws, stream=stream)
+    out["_ws"] = ws
+    out["_dims"] = dims
+    return out

@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for need in ("dspark_draft_block", "dspark_block_loss", "dspark_workspace_size",
+    for need in ("dspark_draft_block", "dspark_block_loss", "dspark_block_loss_backward",
+                 "dspark_workspace_size",
                  "dspark_read_device_error", "dspark_last_error", "dspark_version"):
         assert need in names
 
@@ -49,6 +50,9 @@ def test_version_and_workspace_sizes(lib):
     assert ws > 0 and ws % 256 == 0
     assert lib.dspark_workspace_size(lib.make_dims(1, 256, 2560, 7, 32), 0) == 0
     assert lib.dspark_workspace_size(d, 7) == 0
+    wb = lib.dspark_workspace_size(lib.make_dims(151936, 256, 4096, 7, 1024),
+                                   lib.DSPARK_CALL_LOSS_BACKWARD)
+    assert wb > 0 and wb % 256 == 0
 
 
 BAD_DIMS = [
@@ -159,3 +163,41 @@ def test_loss_rejects_bad_arguments(lib):
     with pytest.raises(lib.DsparkError) as e:
         _loss_call(lib, lib.make_dims(1024, 64, 32, 7, 4), U=258)
     assert e.value.status == lib.DSPARK_EUNSUPPORTED
+
+
+def _bwd_call(lib, d, ptr=256, **over):
+    args = dict(dlogits=ptr, dlogits_dtype="bf16", dconf_logit=ptr, h=ptr, anchor=ptr, labels=ptr,
+                W1=ptr, W2=ptr, w_conf=ptr, dW1=ptr, dw_conf=ptr, dh=ptr, workspace=ptr)
+    wsb = over.pop("workspace_bytes", 1 << 40)
+    args.update(over)
+    lib.dspark_block_loss_backward(d, **args, workspace_bytes=wsb, stream=0)
+
+
+def test_loss_backward_rejects_bad_arguments(lib):
+    d = lib.make_dims(1000, 64, 32, 7, 4)
+    for name in ("anchor", "labels", "W1", "W2", "w_conf", "workspace"):
+        with pytest.raises(lib.DsparkError) as e:
+            _bwd_call(lib, d, **{name: None})
+        assert e.value.status == lib.DSPARK_EINVAL and name in str(e.value)
+    # each output names the input it needs
+    for over, word in ((dict(dlogits=None), "dlogits"), (dict(dconf_logit=None), "dconf_logit"),
+                       (dict(h=None), "h (needed")):
+        with pytest.raises(lib.DsparkError) as e:
+            _bwd_call(lib, d, **over)
+        assert e.value.status == lib.DSPARK_EINVAL and word in str(e.value)
+    with pytest.raises(lib.DsparkError) as e:
+        _bwd_call(lib, d, dlogits_dtype=7)
+    assert e.value.status == lib.DSPARK_EINVAL
+    need = lib.dspark_workspace_size(d, lib.DSPARK_CALL_LOSS_BACKWARD)
+    with pytest.raises(lib.DsparkError) as e:
+        _bwd_call(lib, d, workspace_bytes=need - 1)
+    assert e.value.status == lib.DSPARK_EWORKSPACE
+    with pytest.raises(lib.DsparkError) as e:
+        _bwd_call(lib, lib.make_dims(1000, 64, 32, 7, 4, head="rnn"))
+    assert e.value.status == lib.DSPARK_EUNSUPPORTED
+    with pytest.raises(lib.DsparkError) as e:
+        _bwd_call(lib, d, dlogits=258)
+    assert e.value.status == lib.DSPARK_EUNSUPPORTED
+    with pytest.raises(lib.DsparkError) as e:
+        _bwd_call(lib, d, dW1=258)
+    assert e.value.status == lib.DSPARK_EINVAL
