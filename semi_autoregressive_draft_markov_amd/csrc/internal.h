@@ -91,9 +91,10 @@ struct BwdLayout {
     int R;             // rows
     bool mfma;         // matrix-core dE (the loss call's matrix-core shapes)
     int T;             // 256-row tiles of dE
-    int S;             // vocabulary slices of dE (bf16 dZ; fp32 dZ picks its own)
+    int S;             // vocabulary slices of dE
     int RS;            // row splits of the dw_conf sums
     size_t bad;        // int32 [N]  1 if a token fed to the block is out of range
+    size_t zpage;      // 16 zero bytes, the source of vocabulary entries past V
     size_t prev;       // i32 [R]  token fed to row i, -1 when left out
     size_t srow, sprev, slo, shi;  // i32 [R]  rows sorted by prev: row, prev, segment bounds
     size_t de;         // f32 [R, r]  dL/dE

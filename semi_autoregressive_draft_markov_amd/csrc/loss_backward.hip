@@ -38,9 +38,10 @@ namespace dspark {
 constexpr int kBwdTileRows = 256;   // rows of one dE tile (matrix-core path)
 constexpr int kBwdChunk = 64;       // sorted rows per dW1 chunk sum
 constexpr int kBwdCus = 256;        // workgroups the split-K grid aims at
-constexpr int kBwdDwSplits = 64;    // row splits of the dw_conf sums
-constexpr int kRankRows = 64;       // rows per k_bwd_rank workgroup
-constexpr int kRankTile = 2048;     // prev entries per LDS tile
+constexpr int kBwdDwSplits = 128;   // row splits of the dw_conf sums
+constexpr int kRankRows = 16;       // rows per k_bwd_rank workgroup
+constexpr int kRankSplits = 16;     // splits of each prev tile per row
+constexpr int kRankTile = 4096;     // prev entries per LDS tile
 
 bool bwd_mfma_ok(const dspark_dims& d) { return loss_mfma_ok(d); }
 
@@ -50,8 +51,7 @@ BwdLayout bwd_layout(const dspark_dims& d) {
     L.R = static_cast<int>(R);
     L.mfma = bwd_mfma_ok(d);
     L.T = static_cast<int>((R + kBwdTileRows - 1) / kBwdTileRows);
-    const int ks = 64;  // vocabulary entries per stage (bf16 dZ; fp32 dZ uses 32)
-    const int stages = (d.V + ks - 1) / ks;
+    const int stages = (d.V + 31) / 32;  // fp32 dZ: 32 entries per stage (bf16: 64)
     L.S = L.mfma ? std::max(1, std::min(kBwdCus / L.T, stages)) : 0;
     L.RS = static_cast<int>(std::min<int64_t>(R, kBwdDwSplits));
     size_t off = 0;
@@ -62,6 +62,7 @@ BwdLayout bwd_layout(const dspark_dims& d) {
     };
     const size_t rr = static_cast<size_t>(R);
     L.bad = take(sizeof(int32_t) * d.B);
+    L.zpage = take(16);
     L.prev = take(sizeof(int32_t) * rr);
     L.srow = take(sizeof(int32_t) * rr);
     L.sprev = take(sizeof(int32_t) * rr);
@@ -69,10 +70,7 @@ BwdLayout bwd_layout(const dspark_dims& d) {
     L.shi = take(sizeof(int32_t) * rr);
     L.de = take(sizeof(float) * rr * d.r);
     L.seg = take(sizeof(float) * rr * d.r);
-    // the fp32-dZ variant uses 32-entry stages and up to twice the slices,
-    // so size the partials for the larger count
-    const int s_max = L.mfma ? std::max(1, std::min(kBwdCus / L.T, 2 * stages)) : 0;
-    L.part = take(sizeof(float) * static_cast<size_t>(L.T) * s_max * kBwdTileRows * d.r);
+    L.part = take(sizeof(float) * static_cast<size_t>(L.T) * L.S * kBwdTileRows * d.r);
     L.dwp = take(sizeof(float) * static_cast<size_t>(L.RS) * (d.d + d.r));
     L.total = off;
     return L;
@@ -81,13 +79,16 @@ BwdLayout bwd_layout(const dspark_dims& d) {
 // ------------------------------------------------------------ prev tokens
 
 // Thread per block n: prev of its gamma rows and its error flag (one writer
-// per flag, so no clearing pass is needed).
+// per flag, so no clearing pass is needed).  Also zeroes the 16-byte page
+// that the dE kernel loads for vocabulary entries past V.
 __global__ __launch_bounds__(256) void k_bwd_prev(const int32_t* __restrict__ anchor,
                                                   const int32_t* __restrict__ labels,
                                                   const float* __restrict__ dA, int N, int gamma,
                                                   int V, int32_t* __restrict__ bad,
-                                                  int32_t* __restrict__ prev) {
+                                                  int32_t* __restrict__ prev,
+                                                  uint32_t* __restrict__ zpage) {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n < 4) zpage[n] = 0u;
     if (n >= N) return;
     int flag = 0;
     for (int k = 0; k < gamma; ++k) {
@@ -102,14 +103,16 @@ __global__ __launch_bounds__(256) void k_bwd_prev(const int32_t* __restrict__ an
 }
 
 // Stable counting sort by prev: position = #(prev_j < prev_i) + #(j < i,
-// prev_j == prev_i).  Workgroup = 64 rows x 4 quarters of every LDS tile.
+// prev_j == prev_i).  Workgroup = 16 rows x 16 splits of each LDS tile of
+// prev (read 4 entries at a time); the 16 partial counts of a row are added
+// through LDS.
 __global__ __launch_bounds__(256) void k_bwd_rank(const int32_t* __restrict__ prev, int R,
                                                   int32_t* __restrict__ srow,
                                                   int32_t* __restrict__ sprev,
                                                   int32_t* __restrict__ slo,
                                                   int32_t* __restrict__ shi) {
-    __shared__ int32_t tile[kRankTile];
-    __shared__ int32_t red[3][4][kRankRows];
+    __shared__ __attribute__((aligned(16))) int32_t tile[kRankTile];
+    __shared__ int32_t red[3][kRankSplits][kRankRows];
     const int t = threadIdx.x;
     const int rl = t % kRankRows, qt = t / kRankRows;
     const int i = blockIdx.x * kRankRows + rl;
@@ -118,16 +121,19 @@ __global__ __launch_bounds__(256) void k_bwd_rank(const int32_t* __restrict__ pr
     for (int j0 = 0; j0 < R; j0 += kRankTile) {
         const int m = min(kRankTile, R - j0);
         __syncthreads();
-        for (int q = t; q < m; q += 256) tile[q] = prev[j0 + q];
+        // entries past R hold INT32_MAX: never below or equal to a real prev
+        for (int q = t; q < kRankTile; q += 256) tile[q] = q < m ? prev[j0 + q] : INT32_MAX;
         __syncthreads();
-        const int per = (m + 3) / 4;
-        const int qa = qt * per, qb = min(m, qa + per);
-        for (int q = qa; q < qb; ++q) {
-            const int x = tile[q];
-            lt += x < p;
-            const int e = x == p;
-            eq += e;
-            eqb += e & (j0 + q < i);
+        constexpr int per = kRankTile / kRankSplits;  // multiple of 4
+        const int qa = qt * per;
+#pragma unroll 4
+        for (int q = qa; q < qa + per; q += 4) {
+            const int4 x = *reinterpret_cast<const int4*>(tile + q);
+            const int jj = j0 + q;
+            lt += (x.x < p) + (x.y < p) + (x.z < p) + (x.w < p);
+            const int e0 = x.x == p, e1 = x.y == p, e2 = x.z == p, e3 = x.w == p;
+            eq += e0 + e1 + e2 + e3;
+            eqb += (e0 & (jj < i)) + (e1 & (jj + 1 < i)) + (e2 & (jj + 2 < i)) + (e3 & (jj + 3 < i));
         }
     }
     red[0][qt][rl] = lt;
@@ -135,9 +141,12 @@ __global__ __launch_bounds__(256) void k_bwd_rank(const int32_t* __restrict__ pr
     red[2][qt][rl] = eq;
     __syncthreads();
     if (qt == 0 && i < R) {
-        lt = red[0][0][rl] + red[0][1][rl] + red[0][2][rl] + red[0][3][rl];
-        eqb = red[1][0][rl] + red[1][1][rl] + red[1][2][rl] + red[1][3][rl];
-        eq = red[2][0][rl] + red[2][1][rl] + red[2][2][rl] + red[2][3][rl];
+        lt = eqb = eq = 0;
+        for (int u = 0; u < kRankSplits; ++u) {
+            lt += red[0][u][rl];
+            eqb += red[1][u][rl];
+            eq += red[2][u][rl];
+        }
         const int pos = lt + eqb;
         srow[pos] = i;
         sprev[pos] = p;
@@ -156,129 +165,121 @@ __global__ __launch_bounds__(256) void k_bwd_rank(const int32_t* __restrict__ pr
 //
 // Workgroup: 256 rows x all r columns, 4 WN waves, wave (wm, wn) owns rows
 // 64 wm .. 64 wm + 63 and columns wn r / WN .. (JF = r / (16 WN) column
-// fragments).  Stages of KS vocabulary entries go through two LDS buffers:
-//   A tile [256][64] bf16, 128-byte rows.  bf16 dZ: entries 0..63 of the
-//     stage.  fp32 dZ (KS = 32): hi(dZ) in 0..31, lo(dZ) = bf16(dZ - hi) in
-//     32..63, so hi x W2 + lo x W2 carries dZ to 2^-16 of itself with exact
-//     products.
-//   B tile [r][KS] bf16 (W2 rows), 128-byte rows (KS = 64) or 64-byte rows.
-// 16-byte segments are XOR-swizzled by row so that the 8 lanes of one LDS
-// cycle hit 8 distinct bank groups.  Stage s + 2 is fetched into registers
-// while stage s is multiplied; the vocabulary range of each slice is split
-// in stages, entries at or past V load as zero.
+// fragments).  The vocabulary range of a slice goes through LDS in stages of
+// KS entries: A tile [256][KS] of dZ as stored (bf16, KS = 64; fp32,
+// KS = 32: 128-byte rows either way) and B tile [r][KS] of bf16 W2 rows.
+// Both stream straight from memory into LDS with global_load_lds_dwordx4
+// (each wave instruction fills 1 KB, lane l the 16 bytes at 16 l), without
+// staging registers: A through a ring of NA buffers (3 for bf16, 4 for
+// fp32), B through 2, which fills the 160 KB of LDS at r = 256.  16-byte
+// segments are XOR-swizzled by row (the lane that fills physical segment p
+// of a row loads logical segment p ^ swizzle(row)), so the 8 lanes of one
+// LDS read cycle hit 8 distinct bank groups.  Entries at or past V load from
+// a zeroed 16-byte page.  fp32 dZ is split on the LDS read into
+// hi = bf16(dZ) and lo = bf16(dZ - hi), both multiplied by the exact bf16
+// W2: dZ is carried to 2^-18 of itself with exact products.
+//
+// The compiler does not order LDS reads after these loads, so the rings are
+// synchronised by hand: every wave issues the same numbers DA and DB of
+// loads per stage (chunk indices past the last are clamped, which rewrites
+// the same bytes with the same data), loads complete in issue order, stage s
+// issues B(s + 1) then A(s + NA - 1), and before stage s is read each wave
+// waits until at most DA of its loads are outstanding (then A(s) and B(s)
+// are in), then the workgroup meets at a barrier.
 struct DeArgs {
     const void* dz;
     const uint16_t* W2;
+    const uint32_t* zpage;  // 16 zero bytes (device)
     float* part;
     int R, V, T, S, stages;
+    int per_xcd;  // work items (tile, slice) per XCD, ceil(T S / 8)
 };
+
+// 16 bytes per lane from global memory into LDS at lds + 16 lane (lds is
+// wave-uniform).  The builtin exists for the device pass only; the host pass
+// just needs the kernel's launch stub.
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+#if __HIP_DEVICE_COMPILE__
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+#endif
+}
 
 __device__ __forceinline__ int sw128(int row, int seg) { return (seg ^ (row & 7)) << 4; }
 __device__ __forceinline__ int sw64(int row, int seg) { return (seg ^ ((row >> 1) & 3)) << 4; }
 
 template <int JF, int WN, bool F32Z>
 __global__ __launch_bounds__(256 * WN, 1) void k_de_mfma(DeArgs a) {
-    constexpr int NT = 256 * WN;
+    constexpr int NW = 4 * WN;
     constexpr int RJ = JF * 16 * WN;           // r
-    constexpr int KS = F32Z ? 32 : 64;          // vocabulary entries per stage
-    constexpr int BRB = KS * 2;                 // B row bytes
-    constexpr int BSEG = BRB / 16;              // 16-byte segments per B row
-    constexpr int ABYTES = kBwdTileRows * 128;  // A tile bytes
+    constexpr int KS = F32Z ? 32 : 64;         // vocabulary entries per stage
+    constexpr int BRB = KS * 2;                // B row bytes (A rows are 128 bytes)
+    constexpr int ABYTES = kBwdTileRows * 128;
     constexpr int BBYTES = RJ * BRB;
-    constexpr int LA = kBwdTileRows * 8 / NT;           // A segments per thread
-    constexpr int LB = (RJ * BSEG + NT - 1) / NT;      // B segments per thread
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * (ABYTES + BBYTES)];
+    constexpr int NA = F32Z ? 4 : 3, NB = 2;   // ring depths of the A and B tiles
+    constexpr int ACH = ABYTES / 1024, BCH = BBYTES / 1024;
+    constexpr int DA = (ACH + NW - 1) / NW;   // A loads per wave per stage
+    constexpr int DB = (BCH + NW - 1) / NW;   // B loads per wave per stage
+    static_assert(BBYTES % 1024 == 0 && DA < 64, "ring accounting");
+    static_assert(NA * ABYTES + NB * BBYTES <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NA * ABYTES + NB * BBYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w & 3, wn = w >> 2;
     const int g = lane >> 4, n = lane & 15;
-    const int tile = blockIdx.x % a.T, slice = blockIdx.x / a.T;
+    // Workgroups go round-robin to the 8 XCDs (blockIdx % 8); XCD x takes
+    // work items [x per_xcd, (x + 1) per_xcd) in slice-major order, so that
+    // the tiles sharing a W2 slice share an L2 (a slice spans at most two
+    // XCDs when per_xcd >= T).
+    const int item = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
+    if (item >= a.T * a.S) return;
+    const int tile = item % a.T, slice = item / a.T;
     const int s_begin = static_cast<int>(static_cast<int64_t>(slice) * a.stages / a.S);
     const int s_end = static_cast<int>(static_cast<int64_t>(slice + 1) * a.stages / a.S);
     const int ns = s_end - s_begin;
     const int64_t V = a.V;
 
-    // per-thread global sources: A rows (clamped into [0, R)), B rows
-    const int seg8 = tid & 7;
-    int arow[LA];
+    // per load q: this lane's source row start and vocabulary offset in the stage
+    const unsigned char* srcA[DA];
+    int voffA[DA];
 #pragma unroll
-    for (int q = 0; q < LA; ++q) arow[q] = q * (NT / 8) + (tid >> 3);
-    const int bseg = tid % BSEG;
-    int brow[LB];
+    for (int q = 0; q < DA; ++q) {
+        const int byte = min(w + q * NW, ACH - 1) * 1024 + lane * 16;
+        const int row = byte >> 7, lseg = ((byte & 127) >> 4) ^ (row & 7);
+        const int64_t gr = min(static_cast<int64_t>(tile) * kBwdTileRows + row,
+                               static_cast<int64_t>(a.R - 1));
+        srcA[q] = static_cast<const unsigned char*>(a.dz) + gr * V * (F32Z ? 4 : 2);
+        voffA[q] = lseg * (F32Z ? 4 : 8);
+    }
+    const unsigned char* srcB[DB];
+    int voffB[DB];
 #pragma unroll
-    for (int q = 0; q < LB; ++q) brow[q] = q * (NT / BSEG) + tid / BSEG;
+    for (int q = 0; q < DB; ++q) {
+        const int byte = min(w + q * NW, BCH - 1) * 1024 + lane * 16;
+        const int j = byte / BRB, pseg = (byte % BRB) >> 4;
+        srcB[q] = reinterpret_cast<const unsigned char*>(a.W2 + static_cast<int64_t>(j) * V);
+        voffB[q] = (BRB == 128 ? (pseg ^ (j & 7)) : (pseg ^ ((j >> 1) & 3))) * 8;
+    }
+    unsigned char* const Aring = smem;
+    unsigned char* const Bring = smem + NA * ABYTES;
 
-    u32x4 ra[LA];
-    u32x4 rb[LB];
-
-    auto gload = [&](int stage) {
+    auto issueA = [&](int stage, int buf) {
         const int64_t v0 = static_cast<int64_t>(stage) * KS;
 #pragma unroll
-        for (int q = 0; q < LA; ++q) {
-            const int64_t gr = min(static_cast<int64_t>(tile) * kBwdTileRows + arow[q],
-                                   static_cast<int64_t>(a.R - 1));
-            const int64_t v = v0 + (F32Z ? 4 : 8) * seg8;
-            const bool ok = v < V;
-            const int64_t vc = ok ? v : V - 8;
-            u32x4 x;
-            if (F32Z)
-                x = *reinterpret_cast<const u32x4*>(static_cast<const float*>(a.dz) + gr * V + vc);
-            else
-                x = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dz) + gr * V + vc);
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            ra[q] = ok ? x : zero;
-        }
-#pragma unroll
-        for (int q = 0; q < LB; ++q) {
-            const int j = min(brow[q], RJ - 1);
-            const int64_t v = v0 + 8 * bseg;
-            const bool ok = v < V;
-            const int64_t vc = ok ? v : V - 8;
-            const u32x4 x = *reinterpret_cast<const u32x4*>(a.W2 + static_cast<int64_t>(j) * V + vc);
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            rb[q] = ok ? x : zero;
+        for (int q = 0; q < DA; ++q) {
+            const int64_t v = v0 + voffA[q];
+            const void* p = v < V ? static_cast<const void*>(srcA[q] + v * (F32Z ? 4 : 2))
+                                  : static_cast<const void*>(a.zpage);
+            dma16(p, Aring + buf * ABYTES + min(w + q * NW, ACH - 1) * 1024);
         }
     };
-
-    auto lstore = [&](int buf) {
-        unsigned char* As = smem + buf * (ABYTES + BBYTES);
-        unsigned char* Bs = As + ABYTES;
+    auto issueB = [&](int stage, int buf) {
+        const int64_t v0 = static_cast<int64_t>(stage) * KS;
 #pragma unroll
-        for (int q = 0; q < LA; ++q) {
-            const int row = arow[q];
-            if (F32Z) {
-                // 4 fp32 entries 4 seg8 .. 4 seg8 + 3 -> hi at k, lo at 32 + k
-                float f[4], hf[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(ra[q][e]);
-                typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-                uint32_t hw[2], lw[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const bf16x2 hb = {static_cast<__bf16>(f[2 * e]), static_cast<__bf16>(f[2 * e + 1])};
-                    hw[e] = __builtin_bit_cast(uint32_t, hb);
-                    hf[2 * e] = static_cast<float>(hb[0]);
-                    hf[2 * e + 1] = static_cast<float>(hb[1]);
-                    const bf16x2 lb = {static_cast<__bf16>(f[2 * e] - hf[2 * e]),
-                                       static_cast<__bf16>(f[2 * e + 1] - hf[2 * e + 1])};
-                    lw[e] = __builtin_bit_cast(uint32_t, lb);
-                }
-                const int half = (seg8 & 1) * 8;
-                *reinterpret_cast<uint2*>(As + row * 128 + sw128(row, seg8 >> 1) + half) =
-                    make_uint2(hw[0], hw[1]);
-                *reinterpret_cast<uint2*>(As + row * 128 + sw128(row, 4 + (seg8 >> 1)) + half) =
-                    make_uint2(lw[0], lw[1]);
-            } else {
-                *reinterpret_cast<u32x4*>(As + row * 128 + sw128(row, seg8)) = ra[q];
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < LB; ++q) {
-            const int j = brow[q];
-            if (j < RJ) {
-                const int off = BRB == 128 ? j * 128 + sw128(j, bseg) : j * 64 + sw64(j, bseg);
-                *reinterpret_cast<u32x4*>(Bs + off) = rb[q];
-            }
+        for (int q = 0; q < DB; ++q) {
+            const int64_t v = v0 + voffB[q];
+            const void* p = v < V ? static_cast<const void*>(srcB[q] + v * 2)
+                                  : static_cast<const void*>(a.zpage);
+            dma16(p, Bring + buf * BBYTES + min(w + q * NW, BCH - 1) * 1024);
         }
     };
 
@@ -288,43 +289,70 @@ __global__ __launch_bounds__(256 * WN, 1) void k_de_mfma(DeArgs a) {
 #pragma unroll
         for (int f = 0; f < JF; ++f) acc[m][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    if (ns > 0) {
-        gload(s_begin);
-        lstore(0);
-        gload(s_begin + min(1, ns - 1));
-        __syncthreads();
-        for (int s = 0; s < ns; ++s) {
-            const unsigned char* As = smem + (s & 1) * (ABYTES + BBYTES);
-            const unsigned char* Bs = As + ABYTES;
+    // Issue order B(s + 1), A(s + NA - 1) per stage: loads complete in
+    // order, so once at most DA loads are outstanding, A(s) and B(s) are in.
+    issueB(s_begin, 0);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                bf16x8 af[4];
+    for (int q = 0; q < NA - 1; ++q) issueA(s_begin + min(q, ns - 1), q);
+    for (int s = 0; s < ns; ++s) {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(DA) : "memory");
+        issueB(s_begin + min(s + 1, ns - 1), (s + 1) & 1);
+        issueA(s_begin + min(s + NA - 1, ns - 1), (s + NA - 1) % NA);
+        const unsigned char* As = Aring + (s % NA) * ABYTES;
+        const unsigned char* Bs = Bring + (s & 1) * BBYTES;
+        // operand fragments: A for sub-step kk (32 entries), B for (kk, f);
+        // B is fetched one step ahead and A of kk = 1 early, so that LDS
+        // latency hides behind the matrix-core work of the step before
+        auto ldA = [&](int kk, bf16x8 (&ah)[4], bf16x8 (&al)[4]) {
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int row = wm * 64 + m * 16 + n;
-                    af[m] = __builtin_bit_cast(
+            for (int m = 0; m < 4; ++m) {
+                const int row = wm * 64 + m * 16 + n;
+                if (F32Z) {
+                    const f32x4 x0 = *reinterpret_cast<const f32x4*>(As + row * 128 + sw128(row, 2 * g));
+                    const f32x4 x1 = *reinterpret_cast<const f32x4*>(As + row * 128 + sw128(row, 2 * g + 1));
+                    const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        ah[m][e] = static_cast<__bf16>(x[e]);
+                        al[m][e] = static_cast<__bf16>(x[e] - static_cast<float>(ah[m][e]));
+                    }
+                } else {
+                    ah[m] = __builtin_bit_cast(
                         bf16x8, *reinterpret_cast<const u32x4*>(As + row * 128 + sw128(row, kk * 4 + g)));
                 }
-#pragma unroll
-                for (int f = 0; f < JF; ++f) {
-                    const int j = wn * (JF * 16) + f * 16 + n;
-                    const int off = BRB == 128 ? j * 128 + sw128(j, kk * 4 + g) : j * 64 + sw64(j, g);
-                    const bf16x8 bf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bs + off));
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bf, acc[m][f], 0, 0, 0);
-                }
             }
-            // stage s + 1 (already in registers) to the other buffer, then
-            // fetch stage s + 2; past the end both repeat the last stage
-            lstore((s + 1) & 1);
-            gload(s_begin + min(s + 2, ns - 1));
-            __syncthreads();
+        };
+        auto ldB = [&](int kk, int f) {
+            const int j = wn * (JF * 16) + f * 16 + n;
+            const int boff = BRB == 128 ? j * 128 + sw128(j, kk * 4 + g) : j * 64 + sw64(j, g);
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bs + boff));
+        };
+        constexpr int KK = F32Z ? 1 : 2;
+        bf16x8 ah0[4], al0[4], ah1[4], al1[4];
+        ldA(0, ah0, al0);
+        bf16x8 bcur = ldB(0, 0);
+#pragma unroll
+        for (int step = 0; step < KK * JF; ++step) {
+            const int kk = step / JF, f = step % JF;
+            bf16x8 bnext = bcur;
+            if (step + 1 < KK * JF) bnext = ldB((step + 1) / JF, (step + 1) % JF);
+            if (KK == 2 && step == 1) ldA(1, ah1, al1);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const bf16x8 ah = kk == 0 ? ah0[m] : ah1[m];
+                acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bcur, acc[m][f], 0, 0, 0);
+                if (F32Z) acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al0[m], bcur, acc[m][f], 0, 0, 0);
+            }
+            bcur = bnext;
+            // keep the fetch-ahead order: the scheduler would otherwise sink
+            // each LDS read next to its first use
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // raw accumulator dump: [slot][wave][m][f][lane] f32x4, coalesced
-    float* out = a.part + static_cast<int64_t>(blockIdx.x) * (kBwdTileRows * RJ);
+    // raw accumulator dump: [item][wave][m][f][lane] f32x4, coalesced
+    float* out = a.part + static_cast<int64_t>(item) * (kBwdTileRows * RJ);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -415,7 +443,9 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_
 
 // Wave per sorted position p that starts a chunk (its segment's first
 // position, or 64, 128, ... after it): the dE rows at positions p .. up to
-// 63 after it, summed in position (= row) order.
+// 63 after it, summed in position (= row) order.  Lane l holds columns
+// 4 l + 256 t (r % 4 == 0) or l + 64 t; rows are fetched 8 at a time.
+template <bool VEC4>
 __global__ __launch_bounds__(256) void k_seg_chunk(const float* __restrict__ dE,
                                                    const int32_t* __restrict__ srow,
                                                    const int32_t* __restrict__ sprev,
@@ -429,13 +459,37 @@ __global__ __launch_bounds__(256) void k_seg_chunk(const float* __restrict__ dE,
     if (sprev[p] < 0 || (p - lo) % kBwdChunk != 0) return;
     const int cnt = min(kBwdChunk, shi[p] - p);
     const int myrow = lane < cnt ? srow[p + lane] : 0;
-    for (int j = lane; j < r; j += 64) {
-        float acc = 0.0f;
-        for (int q = 0; q < cnt; ++q) {
-            const int row = __builtin_amdgcn_readlane(myrow, q);
-            acc += dE[static_cast<int64_t>(row) * r + j];
+    constexpr int W = VEC4 ? 4 : 1;
+    for (int j = lane * W; j < r; j += 64 * W) {
+        float acc[W];
+#pragma unroll
+        for (int e = 0; e < W; ++e) acc[e] = 0.0f;
+        for (int q0 = 0; q0 < cnt; q0 += 8) {
+            float x[8][W];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int row = __builtin_amdgcn_readlane(myrow, min(q0 + u, cnt - 1));
+                const float* src = dE + static_cast<int64_t>(row) * r + j;
+                if (VEC4) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+                    for (int e = 0; e < W; ++e) x[u][e] = v[e];
+                } else {
+                    x[u][0] = *src;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (q0 + u < cnt)
+#pragma unroll
+                    for (int e = 0; e < W; ++e) acc[e] += x[u][e];
         }
-        seg[static_cast<int64_t>(p) * r + j] = acc;
+        float* dst = seg + static_cast<int64_t>(p) * r + j;
+        if (VEC4) {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[W > 1 ? 1 : 0], acc[W > 2 ? 2 : 0], acc[W > 3 ? 3 : 0]};
+        } else {
+            dst[0] = acc[0];
+        }
     }
 }
 
@@ -460,7 +514,9 @@ __global__ __launch_bounds__(256) void k_seg_final(const float* __restrict__ seg
 
 // ------------------------------------------------------------ dw_conf, dh
 
-// Thread per column q of [h; e], rows of split blockIdx.y in row order.
+// Thread per column q of [h; e] (h part first), rows of split blockIdx.y in
+// row order.  Rows are fetched 8 at a time; a row left out contributes
+// fma(0, 0, acc) = acc exactly.
 template <typename T>
 __global__ __launch_bounds__(256) void k_dw_part(const T* __restrict__ h, const T* __restrict__ W1,
                                                  const int32_t* __restrict__ prev,
@@ -473,35 +529,53 @@ __global__ __launch_bounds__(256) void k_dw_part(const T* __restrict__ h, const 
     const int i0 = static_cast<int>(static_cast<int64_t>(rs) * R / RS);
     const int i1 = static_cast<int>(static_cast<int64_t>(rs + 1) * R / RS);
     float acc = 0.0f;
-    for (int i = i0; i < i1; ++i) {
-        const int p = prev[i];
-        if (p < 0) continue;
-        const float x = q < d ? load_f(h, static_cast<int64_t>(i) * d + q)
-                              : load_f(W1, static_cast<int64_t>(p) * r + (q - d));
-        acc = fmaf(dA[i], x, acc);
+    for (int b = i0; b < i1; b += 8) {
+        float x[8], c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = min(b + u, i1 - 1);
+            const int p = prev[i];
+            const bool use = p >= 0 && b + u < i1;
+            const float v = q < d ? load_f(h, static_cast<int64_t>(i) * d + q)
+                                  : load_f(W1, static_cast<int64_t>(max(p, 0)) * r + (q - d));
+            x[u] = use ? v : 0.0f;
+            c[u] = use ? dA[i] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = fmaf(c[u], x[u], acc);
     }
     dwp[static_cast<int64_t>(rs) * cols + q] = acc;
 }
 
+// Workgroup per 64 columns: 4 threads per column add every 4th split, then
+// the 4 sums are added in order.
 __global__ __launch_bounds__(256) void k_dw_final(const float* __restrict__ dwp, int cols, int RS,
                                                   float* __restrict__ dw) {
-    const int q = blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= cols) return;
+    __shared__ float red[4][64];
+    const int c = threadIdx.x & 63, u = threadIdx.x >> 6;
+    const int q = blockIdx.x * 64 + c;
     float acc = 0.0f;
-    for (int rs = 0; rs < RS; ++rs) acc += dwp[static_cast<int64_t>(rs) * cols + q];
-    dw[q] = acc;
+    if (q < cols)
+        for (int rs = u; rs < RS; rs += 4) acc += dwp[static_cast<int64_t>(rs) * cols + q];
+    red[u][c] = acc;
+    __syncthreads();
+    if (u == 0 && q < cols) dw[q] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
 }
 
 // dh[i, q] = dA_i w[q] for every row (a row with a non-finite dA gets it).
-template <typename T>
+// Workgroup per row; 4 columns per thread when the rows are 16-byte aligned.
+template <typename T, bool VEC4>
 __global__ __launch_bounds__(256) void k_dh(const float* __restrict__ dA, const T* __restrict__ w_conf,
-                                            int64_t R, int d, float* __restrict__ dh) {
-    const int64_t n = R * d;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) {
-        const int64_t i = e / d;
-        const int q = static_cast<int>(e - i * d);
-        dh[e] = dA[i] * load_f(w_conf, q);
+                                            int R, int d, float* __restrict__ dh) {
+    const int i = blockIdx.x;
+    const float c = dA[i];
+    float* out = dh + static_cast<int64_t>(i) * d;
+    if (VEC4) {
+        for (int q = threadIdx.x * 4; q < d; q += 1024)
+            *reinterpret_cast<f32x4*>(out + q) = f32x4{c * load_f(w_conf, q), c * load_f(w_conf, q + 1),
+                                                       c * load_f(w_conf, q + 2), c * load_f(w_conf, q + 3)};
+    } else {
+        for (int q = threadIdx.x; q < d; q += 256) out[q] = c * load_f(w_conf, q);
     }
 }
 
@@ -509,7 +583,7 @@ __global__ __launch_bounds__(256) void k_dh(const float* __restrict__ dA, const 
 
 template <int JF, int WN, bool F32Z>
 static void launch_de_t(const DeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((k_de_mfma<JF, WN, F32Z>), dim3(a.T * a.S), dim3(256 * WN), 0, st, a);
+    hipLaunchKernelGGL((k_de_mfma<JF, WN, F32Z>), dim3(8 * a.per_xcd), dim3(256 * WN), 0, st, a);
 }
 
 template <bool F32Z>
@@ -553,8 +627,8 @@ static hipError_t launch_bwd_t(const BwdArgs& ba) {
     const T* w = static_cast<const T*>(ba.w_conf);
     const int R = L.R, r = D.r, d = D.d, V = D.V;
 
-    hipLaunchKernelGGL(k_bwd_prev, dim3(grid_for(D.B, 256)), dim3(256), 0, st, ba.anchor, ba.labels,
-                       ba.dA, D.B, D.gamma, V, bad, prev);
+    hipLaunchKernelGGL(k_bwd_prev, dim3(grid_for(std::max(D.B, 4), 256)), dim3(256), 0, st, ba.anchor, ba.labels,
+                       ba.dA, D.B, D.gamma, V, bad, prev, reinterpret_cast<uint32_t*>(ws + L.zpage));
     if (ba.dW1) {
         hipLaunchKernelGGL(k_bwd_rank, dim3((R + kRankRows - 1) / kRankRows), dim3(256), 0, st, prev, R,
                            srow, sprev, slo, shi);
@@ -567,9 +641,10 @@ static hipError_t launch_bwd_t(const BwdArgs& ba) {
             a.R = R;
             a.V = V;
             a.T = L.T;
-            const int ks = f32z ? 32 : 64;
-            a.stages = (V + ks - 1) / ks;
-            a.S = std::max(1, std::min(kBwdCus / L.T, a.stages));
+            a.zpage = reinterpret_cast<const uint32_t*>(ws + L.zpage);
+            a.stages = f32z ? (V + 31) / 32 : (V + 63) / 64;
+            a.S = std::min(L.S, a.stages);
+            a.per_xcd = (L.T * a.S + 7) / 8;
             hipError_t pe = profile_begin(st);
             if (pe != hipSuccess) return pe;
             const bool ok = f32z ? launch_de<true>(r, a, st) : launch_de<false>(r, a, st);
@@ -589,8 +664,12 @@ static hipError_t launch_bwd_t(const BwdArgs& ba) {
         }
         const int64_t nW1 = static_cast<int64_t>(V) * r;
         hipLaunchKernelGGL(k_fill_zero, dim3(grid_for(nW1 / 4 + 1, 256 * 8)), dim3(256), 0, st, ba.dW1, nW1);
-        hipLaunchKernelGGL(k_seg_chunk, dim3((R + 3) / 4), dim3(256), 0, st, dE, srow, sprev, slo, shi, R, r,
-                           seg);
+        if (r % 4 == 0)
+            hipLaunchKernelGGL(k_seg_chunk<true>, dim3((R + 3) / 4), dim3(256), 0, st, dE, srow, sprev, slo, shi,
+                               R, r, seg);
+        else
+            hipLaunchKernelGGL(k_seg_chunk<false>, dim3((R + 3) / 4), dim3(256), 0, st, dE, srow, sprev, slo, shi,
+                               R, r, seg);
         hipLaunchKernelGGL(k_seg_final, dim3((R + 3) / 4), dim3(256), 0, st, seg, sprev, slo, shi, R, r,
                            ba.dW1);
     }
@@ -598,13 +677,13 @@ static hipError_t launch_bwd_t(const BwdArgs& ba) {
         const int cols = d + r;
         hipLaunchKernelGGL((k_dw_part<T>), dim3((cols + 255) / 256, L.RS), dim3(256), 0, st, h, W1, prev,
                            ba.dA, R, r, d, L.RS, dwp);
-        hipLaunchKernelGGL(k_dw_final, dim3((cols + 255) / 256), dim3(256), 0, st, dwp, cols, L.RS,
-                           ba.dw_conf);
+        hipLaunchKernelGGL(k_dw_final, dim3((cols + 63) / 64), dim3(256), 0, st, dwp, cols, L.RS, ba.dw_conf);
     }
     if (ba.dh) {
-        const int64_t n = static_cast<int64_t>(R) * d;
-        hipLaunchKernelGGL((k_dh<T>), dim3(grid_for(n, 256 * 8)), dim3(256), 0, st, ba.dA, w,
-                           static_cast<int64_t>(R), d, ba.dh);
+        if (d % 4 == 0 && (reinterpret_cast<uintptr_t>(ba.dh) & 15) == 0)
+            hipLaunchKernelGGL((k_dh<T, true>), dim3(R), dim3(256), 0, st, ba.dA, w, R, d, ba.dh);
+        else
+            hipLaunchKernelGGL((k_dh<T, false>), dim3(R), dim3(256), 0, st, ba.dA, w, R, d, ba.dh);
     }
     return hipGetLastError();
 }
