@@ -160,6 +160,69 @@ def bench_loss(args) -> int:
     return 0
 
 
+def bench_backward(args) -> int:
+    """Backward past the logits over the Qwen3-8B-shaped workload (7168 rows,
+    V = 151936, r = 256, d = 4096): one dspark_block_loss call makes bf16
+    dlogits and dconf_logit, then a step is one dspark_block_loss_backward
+    call (dW1, dw_conf, dh).  Roofline of its dZ W2^T kernel: the dZ stream
+    plus one pass over W2 per launch, against HBM."""
+    import torch
+
+    import synth
+    from semi_autoregressive_draft_markov_amd import binding, ops
+
+    binding.load()
+    dev = torch.device("cuda:0")
+    inp = synth.config_inputs(3)
+    t = synth.to_torch(inp, dev)
+    R, V, r, d = inp.B * inp.gamma, inp.V, inp.r, inp.d
+    lo = ops.block_loss(t["U"], t["target"], t["h"], t["anchor"], t["labels"], t["W1"], t["W2"],
+                        t["w_conf"], dlogits_dtype="bf16", want_dW2=False)
+    out = ops.block_loss_backward(lo["dlogits"], lo["dconf_logit"], t["h"], t["anchor"],
+                                  t["labels"], t["W1"], t["W2"], t["w_conf"])
+    dims, ws = out["_dims"], out["_ws"]
+    del t["U"], t["target"]
+
+    def step():
+        binding.dspark_block_loss_backward(dims, lo["dlogits"], "bf16", lo["dconf_logit"], t["h"],
+                                           t["anchor"], t["labels"], t["W1"], t["W2"],
+                                           t["w_conf"], out["dW1"], out["dw_conf"], out["dh"], ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    binding.dspark_profile_enable(True)
+    binding.dspark_profile_read()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    de_ms, launches = binding.dspark_profile_read()
+    binding.dspark_profile_enable(False)
+    de_s = de_ms * 1e-3 / max(launches, 1)
+    alg_bytes = R * V * 2 + r * V * 2
+    flops = 2.0 * R * V * r
+    line = {
+        "metric": "teacher-forced rows/s through the backward past the logits (V=151936, r=256, "
+                  "d=4096, 7168 rows)",
+        "value": round(R * args.steps / el, 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(el * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-8b-shaped backward past the logits", "V": V, "r": r,
+                   "d": d, "gamma": inp.gamma, "N": inp.B, "dlogits": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(alg_bytes / de_s / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg_bytes / de_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_de_mfma<8, 2, false>", "kernel_ms": round(de_s * 1e3, 4),
+                     "mfma_tflops": round(flops / de_s / 1e12, 1)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def synth_subset(inp, idx):
     import synth
     return synth.subset(inp, idx)
@@ -173,7 +236,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time of the CPU oracle sample (0 skips it)")
     ap.add_argument("--workload", default="qwen3-4b",
-                    choices=["qwen3-4b", "qwen3-14b", "gemma4-rnn", "qwen3-8b-loss"],
+                    choices=["qwen3-4b", "qwen3-14b", "gemma4-rnn", "qwen3-8b-loss",
+                             "qwen3-8b-backward"],
                     help="qwen3-4b (default) is the reported workload; the others are "
                          "extra measurements of the same kernels at the other shapes")
     ap.add_argument("--launch", default="plain", choices=["plain", "cooperative"],
@@ -193,6 +257,8 @@ def main() -> int:
 
     if args.workload == "qwen3-8b-loss":
         return bench_loss(args)
+    if args.workload == "qwen3-8b-backward":
+        return bench_backward(args)
 
     import numpy as np
     import torch
