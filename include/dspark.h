@@ -160,7 +160,7 @@ dspark_status dspark_block_loss(const dspark_dims* dims, const void* U, const vo
  * head: from dZ = dL/dz_d and dA = dL/d(confidence logit), as
  * dspark_block_loss returns them, to the gradients of the Markov table, the
  * confidence weights and the hidden states.  Training updates the
- * sequential block and the confidence head (dormouse page, section 2, delta
+ * sequential block and the confidence head (dormouse page, section 4, delta
  * table row D16); row i = n * gamma + k is fed prev_i (anchor[n] at k = 0,
  * labels[n, k-1] after), and e_i = W1[prev_i] enters both the bias (Eq 5)
  * and the confidence logit a_i = w . [h_i; e_i] (Eq 7), so

@@ -6,7 +6,7 @@
 // after; the alignment the dormouse "DSpark - paper verification" page calls
 // correct in its off-by-one discussion, section 2).  e_i = W1[prev_i] enters
 // the bias z_d = U + e W2 (Eq 5) and the confidence logit a = w . [h; e]
-// (Eq 7), and the same page's delta table (section 2, row D16) has training
+// (Eq 7), and the same page's delta table (section 4, row D16) has training
 // update the sequential block and the confidence head, so the chain rule
 // gives
 //   dE_i  = dZ_i W2^T + dA_i w[d : d + r]
