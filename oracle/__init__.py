@@ -57,6 +57,13 @@ def _load():
         lib.oracle_block_loss.restype = I
         lib.oracle_block_loss_backward.argtypes = [I, I, I, I, I, I] + [P] * 11 + [I]
         lib.oracle_block_loss_backward.restype = I
+        D = ctypes.c_double
+        lib.oracle_verify_uniform.argtypes = [U64, U64, I, I]
+        lib.oracle_verify_uniform.restype = D
+        lib.oracle_verify_gumbel.argtypes = [U64, U64, I, I, I]
+        lib.oracle_verify_gumbel.restype = D
+        lib.oracle_verify_block.argtypes = [I, I, I, I, I] + [P] * 9 + [D, U64, U64] + [P] * 6 + [I]
+        lib.oracle_verify_block.restype = I
         _lib = lib
     return _lib
 
@@ -195,4 +202,37 @@ def block_loss_backward(inp, dZ, dA, want_dW1: bool = True, want_dw: bool = True
         _ptr(dZ), _ptr(dA), _ptr(out["dW1"]), _ptr(out["dw"]), _ptr(out["dh"]), nthreads)
     if rc != 0:
         raise ValueError("oracle_block_loss_backward rejected its input (rc=%d)" % rc)
+    return out
+
+
+def verify_uniform(seed: int, offset: int, b: int, k: int) -> float:
+    return _load().oracle_verify_uniform(seed, offset, b, k)
+
+
+def verify_gumbel(seed: int, offset: int, b: int, j: int, v: int) -> float:
+    return _load().oracle_verify_gumbel(seed, offset, b, j, v)
+
+
+def verify_block(inp, tokens, logp, surv, target, tau: float, seed: int = 0, offset: int = 0,
+                 temperature=None, nthreads: int = 0) -> dict:
+    """Trim by survival >= tau, accept/reject the drafted `tokens` [B, gamma]
+    against `target` logits [B, gamma + 1, V] (stored like inp.U), then draw
+    the next token (see oracle_verify_block)."""
+    B, g, V = inp.B, inp.gamma, inp.V
+    dt = inp.dtype
+    temp = np.ascontiguousarray(inp.temperature if temperature is None else temperature,
+                                dtype=np.float32)
+    out = dict(keep=np.zeros(B, np.int32), accept=np.zeros(B, np.int32),
+               next=np.zeros(B, np.int32), margin=np.zeros(B), gap=np.zeros(B),
+               accept_prob=np.zeros((B, g)))
+    rc = _load().oracle_verify_block(
+        V, inp.r, g, B, _dtype_code(dt), _ptr(_arr(inp.U, dt)),
+        _ptr(np.ascontiguousarray(inp.anchor, np.int32)), _ptr(_arr(inp.W1, dt)),
+        _ptr(_arr(inp.W2, dt)), _ptr(np.ascontiguousarray(tokens, np.int32)),
+        _ptr(np.ascontiguousarray(logp, np.float64)), _ptr(np.ascontiguousarray(surv, np.float64)),
+        _ptr(temp), _ptr(_arr(target, dt)), float(tau), seed, offset,
+        _ptr(out["keep"]), _ptr(out["accept"]), _ptr(out["next"]), _ptr(out["margin"]),
+        _ptr(out["gap"]), _ptr(out["accept_prob"]), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_verify_block rejected its input (rc=%d)" % rc)
     return out

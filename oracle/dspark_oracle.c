@@ -532,3 +532,174 @@ int oracle_block_loss_backward(int V, int r, int d, int gamma, int N, int dtype,
     free(dE);
     return 0;
 }
+
+/* ----------------------------------------------------------- verification */
+
+/* Reading (the pages fix no random numbers for verification): the uniform
+ * of the accept test at 0-based position k of block b is word 0 of
+ * Philox4x32-10 at counter (0xFFFFFFFF, k, b, offset low 32 bits), and the
+ * Gumbel variate of element v of the final draw (made at 0-based position j)
+ * is word v mod 4 at counter (v / 4, 0x80000000 | j, b, offset low 32 bits),
+ * both with the sampling key and the same word -> u map.  Neither counter can
+ * equal one the drafting noise uses (its first word is v / 4 < 2^30 and its
+ * second word a step index below 64). */
+static double verify_u(uint64_t seed, uint64_t offset, uint32_t c0, uint32_t c1, int b, int word)
+{
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t ctr[4] = {c0, c1, (uint32_t)b, (uint32_t)offset};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    return (2.0 * (double)(out[word] >> 9) + 1.0) / 16777216.0;
+}
+
+double oracle_verify_uniform(uint64_t seed, uint64_t offset, int b, int k)
+{
+    return verify_u(seed, offset, 0xFFFFFFFFu, (uint32_t)k, b, 0);
+}
+
+double oracle_verify_gumbel(uint64_t seed, uint64_t offset, int b, int j, int v)
+{
+    double u = verify_u(seed, offset, (uint32_t)(v / 4), 0x80000000u | (uint32_t)j, b, v % 4);
+    return -log(-log(u));
+}
+
+/* Index of the largest y (lowest index on a tie) and the gap to the runner-up. */
+static int argmax_gap(const double* y, int V, double* gap)
+{
+    int best = -1;
+    double b1 = -INFINITY, b2 = -INFINITY;
+    for (int v = 0; v < V; ++v) {
+        if (y[v] > b1) {
+            b2 = b1;
+            b1 = y[v];
+            best = v;
+        } else if (y[v] > b2) {
+            b2 = y[v];
+        }
+    }
+    *gap = b1 - b2;
+    return best;
+}
+
+/* One block: trim, accept/reject left to right, then the final draw. */
+static int verify_one_block(int V, int r, int gamma, int b, int dtype, const void* U,
+                            const int32_t* anchor, const void* W1, const void* W2,
+                            const int32_t* tokens, const double* logp, const double* surv,
+                            const float* temperature, const void* T_logits, double tau,
+                            uint64_t seed, uint64_t offset, int32_t* keep, int32_t* accept,
+                            int32_t* next, double* margin, double* gap, double* accept_prob,
+                            double* zt, double* zd, double* y, double* e)
+{
+    const double T = (double)temperature[b];
+    const int greedy = !(T > 0.0);
+    /* Static threshold pruning ([bowenzhou] "Results", static-threshold
+     * diagnostic; [meridian] section 3: the survival is the product of the
+     * c_k): keep the leading positions whose survival is at least tau. */
+    int m = 0;
+    while (m < gamma && surv[(int64_t)b * gamma + m] >= tau) ++m;
+    for (int k = 0; k < gamma; ++k) accept_prob[(int64_t)b * gamma + k] = NAN;
+    /* Standard speculative accept/reject ([bowenzhou] "Why DSpark?": the
+     * target checks the block and keeps the leading tokens up to the first
+     * rejection; [meridian] section 3: c* is the single-step acceptance
+     * probability of that rule): accept x_k with probability
+     * min(1, p_t(x_k) / p_d(x_k)); greedy accepts x_k iff it is the target's
+     * argmax. */
+    int n = 0;
+    double mg = INFINITY;
+    for (; n < m; ++n) {
+        const int x = tokens[(int64_t)b * gamma + n];
+        if (x < 0 || x >= V) return -1;
+        for (int v = 0; v < V; ++v)
+            zt[v] = load_elem(T_logits, dtype, ((int64_t)b * (gamma + 1) + n) * V + v);
+        int ok;
+        if (greedy) {
+            double g_unused;
+            ok = argmax_gap(zt, V, &g_unused) == x;
+            accept_prob[(int64_t)b * gamma + n] = ok ? 1.0 : 0.0;
+        } else {
+            for (int v = 0; v < V; ++v) zt[v] /= T;
+            const double pt = exp(zt[x] - log_sum_exp(zt, V));
+            const double pd = exp(logp[(int64_t)b * gamma + n]);
+            const double u = oracle_verify_uniform(seed, offset, b, n);
+            accept_prob[(int64_t)b * gamma + n] = pt >= pd ? 1.0 : pt / pd;
+            ok = u * pd < pt;
+            const double rel = fabs(u * pd - pt) / fmax(pt, u * pd);
+            if (rel < mg) mg = rel;
+        }
+        if (!ok) break;
+    }
+    /* The final draw at 0-based position j = n: after a rejection, from the
+     * residual max(0, p_t - p_d) normalised (drawn as the argmax of
+     * ln(residual) + Gumbel); after m acceptances, the target's own next
+     * token.  Greedy takes the target's argmax either way. */
+    const int j = n;
+    for (int v = 0; v < V; ++v)
+        zt[v] = load_elem(T_logits, dtype, ((int64_t)b * (gamma + 1) + j) * V + v);
+    double gp;
+    int out;
+    if (greedy) {
+        out = argmax_gap(zt, V, &gp);
+    } else {
+        for (int v = 0; v < V; ++v) zt[v] /= T;
+        const double lse_t = log_sum_exp(zt, V);
+        int residual = n < m;
+        if (residual) {
+            /* the draft distribution at position j (Eq 4 with the Eq 5 bias
+             * of the token before it) */
+            const int prev = j == 0 ? anchor[b] : tokens[(int64_t)b * gamma + j - 1];
+            if (prev < 0 || prev >= V) return -1;
+            for (int q = 0; q < r; ++q) e[q] = load_elem(W1, dtype, (int64_t)prev * r + q);
+            for (int v = 0; v < V; ++v) {
+                double acc = load_elem(U, dtype, ((int64_t)b * gamma + j) * V + v);
+                for (int q = 0; q < r; ++q) acc += e[q] * load_elem(W2, dtype, (int64_t)q * V + v);
+                zd[v] = acc / T;
+            }
+            const double lse_d = log_sum_exp(zd, V);
+            int any = 0;
+            for (int v = 0; v < V; ++v) {
+                const double res = exp(zt[v] - lse_t) - exp(zd[v] - lse_d);
+                y[v] = res > 0.0 ? log(res) + oracle_verify_gumbel(seed, offset, b, j, v) : -INFINITY;
+                any |= res > 0.0;
+            }
+            /* Reading: a residual with no positive entry (p_t = p_d exactly)
+             * falls back to the target distribution. */
+            residual = any;
+        }
+        if (!residual)
+            for (int v = 0; v < V; ++v) y[v] = zt[v] + oracle_verify_gumbel(seed, offset, b, j, v);
+        out = argmax_gap(y, V, &gp);
+    }
+    keep[b] = m;
+    accept[b] = n;
+    next[b] = out;
+    margin[b] = mg;
+    gap[b] = gp;
+    return 0;
+}
+
+int oracle_verify_block(int V, int r, int gamma, int B, int dtype, const void* U,
+                        const int32_t* anchor, const void* W1, const void* W2,
+                        const int32_t* tokens, const double* logp, const double* surv,
+                        const float* temperature, const void* T_logits, double tau,
+                        uint64_t seed, uint64_t offset, int32_t* keep, int32_t* accept,
+                        int32_t* next, double* margin, double* gap, double* accept_prob,
+                        int nthreads)
+{
+    if (V < 1 || r < 1 || gamma < 1 || B < 0 || (dtype != 0 && dtype != 1))
+        return -1;
+    int failed = 0;
+#pragma omp parallel num_threads(thread_count(nthreads)) reduction(| : failed)
+    {
+        double* zt = malloc(sizeof(double) * (size_t)V);
+        double* zd = malloc(sizeof(double) * (size_t)V);
+        double* y = malloc(sizeof(double) * (size_t)V);
+        double* e = malloc(sizeof(double) * (size_t)r);
+#pragma omp for schedule(static)
+        for (int b = 0; b < B; ++b)
+            failed |= verify_one_block(V, r, gamma, b, dtype, U, anchor, W1, W2, tokens, logp, surv,
+                                       temperature, T_logits, tau, seed, offset, keep, accept, next,
+                                       margin, gap, accept_prob, zt, zd, y, e) != 0;
+        free(zt); free(zd); free(y); free(e);
+    }
+    return failed ? -1 : 0;
+}

@@ -108,6 +108,29 @@ int oracle_block_loss_backward(int V, int r, int d, int gamma, int N, int dtype,
                                const double* dZ, const double* dA,
                                double* dW1, double* dw, double* dh, int nthreads);
 
+/* Verification of drafted blocks, Markov head: confidence-driven prefix
+ * trimming, the standard speculative accept/reject rule, and the final draw
+ * (residual after a rejection, the target's next token after full
+ * acceptance).  Inputs: U [B,gamma,V], anchor [B], W1, W2 as for sampling;
+ * tokens [B,gamma] drafted; logp [B,gamma] their draft log-probabilities
+ * (under softmax(z/T)); surv [B,gamma] prefix survival; temperature [B]
+ * (<= 0: greedy); T_logits [B,gamma+1,V] target logits for positions
+ * 1..gamma+1; tau the survival threshold.  Outputs [B]: keep (m, positions
+ * kept), accept (n <= m, positions accepted), next (the token emitted after
+ * them); margin (smallest relative distance |u p_d - p_t| / max of the two
+ * over the accept tests, inf if none), gap (top-two gap of the final draw);
+ * accept_prob [B,gamma] min(1, p_t/p_d) at the tested positions, NaN
+ * elsewhere.  Returns 0, or -1 on a bad argument / token id. */
+double oracle_verify_uniform(uint64_t seed, uint64_t offset, int b, int k);
+double oracle_verify_gumbel(uint64_t seed, uint64_t offset, int b, int j, int v);
+int oracle_verify_block(int V, int r, int gamma, int B, int dtype, const void* U,
+                        const int32_t* anchor, const void* W1, const void* W2,
+                        const int32_t* tokens, const double* logp, const double* surv,
+                        const float* temperature, const void* T_logits, double tau,
+                        uint64_t seed, uint64_t offset, int32_t* keep, int32_t* accept,
+                        int32_t* next, double* margin, double* gap, double* accept_prob,
+                        int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
