@@ -72,10 +72,11 @@ typedef struct dspark_dims {
 #define DSPARK_CALL_DRAFT 0
 #define DSPARK_CALL_LOSS 1
 #define DSPARK_CALL_LOSS_BACKWARD 2
+#define DSPARK_CALL_VERIFY 3
 
-/* Bytes of device workspace `which` (DSPARK_CALL_DRAFT, DSPARK_CALL_LOSS or
- * DSPARK_CALL_LOSS_BACKWARD) needs for `dims`; 0 if dims are invalid or
- * `which` is unknown.  Host function, no device work. */
+/* Bytes of device workspace `which` (DSPARK_CALL_DRAFT, DSPARK_CALL_LOSS,
+ * DSPARK_CALL_LOSS_BACKWARD or DSPARK_CALL_VERIFY) needs for `dims`; 0 if
+ * dims are invalid or `which` is unknown.  Host function, no device work. */
 size_t dspark_workspace_size(const dspark_dims* dims, int which);
 
 /* Semi-autoregressive block drafting: Eq 4 with the Eq 5 (Markov) or Eq 6
@@ -195,6 +196,51 @@ dspark_status dspark_block_loss_backward(const dspark_dims* dims, const void* dl
                                          void* workspace, size_t workspace_bytes,
                                          void* hip_stream);
 
+/* Verification of drafted blocks against the target, Markov head: prefix
+ * trimming by confidence, the standard speculative accept/reject rule and
+ * the token emitted after the accepted prefix.  The target checks the block
+ * and keeps the leading tokens up to the first rejection, so the output
+ * follows the target's distribution (bowenzhou page, "Why DSpark?");
+ * c* = 1 - TV(p_d, p_t) is the single-step acceptance probability of that
+ * rule (Meridian page, section 3); confidence pruning only cuts a suffix of
+ * the proposal (bowenzhou page, "设计" and "Results").  Per block b, with
+ * T = temperature[b]:
+ *   m = number of leading positions k with survival[b,k] >= threshold;
+ *   for k < m, left to right: accept x_k iff u p_d(x_k) < p_t(x_k), where
+ *     p_d(x_k) = exp(logp[b,k]), p_t = softmax(T_logits[b,k] / T) and u is
+ *     word 0 of Philox4x32-10 at counter (0xFFFFFFFF, k, b, offset mod 2^32)
+ *     mapped as for drafting; greedy (T <= 0): accept iff x_k is the argmax
+ *     of T_logits[b,k] (lowest id on a tie); stop at the first rejection;
+ *   n = number accepted;
+ *   next token: after a rejection at position j = n, a draw from the residual
+ *     max(0, p_t - p_d) at j, with p_d = softmax((U[b,j] + W1[x_{j-1}] W2) / T)
+ *     (x_{-1} = anchor) recomputed here, as argmax_v ln(residual) + g_v;
+ *     after m acceptances, argmax_v T_logits[b,m,v] / T + g_v (a residual
+ *     with no positive entry also takes this draw); greedy: the argmax of
+ *     T_logits[b,j].  g_v is the standard Gumbel draw from word v mod 4 of
+ *     Philox4x32-10 at counter (v / 4, 0x80000000 | j, b, offset mod 2^32),
+ *     key (seed mod 2^32, seed >> 32).
+ * Inputs (device): U [B,gamma,V], anchor [B], W1, W2 as for drafting;
+ *   T_logits [B, gamma+1, V] target logits for positions 1..gamma+1 (same
+ *   dtype as U); tokens [B,gamma] int32, logp [B,gamma] float, survival
+ *   [B,gamma] float as dspark_draft_block returns them (logp required, it
+ *   is p_d at the drafted tokens); temperature [B] float.  threshold, seed,
+ *   offset are values (a threshold <= 0 keeps every position).
+ * Outputs (device): n_keep [B], n_accept [B], next_token [B] int32;
+ *   accept_prob [B,gamma] float (nullable): min(1, p_t/p_d) (greedy 0 or 1)
+ *   at the tested positions, NaN elsewhere.  A block whose anchor or drafted
+ *   tokens hold an id outside [0, V) gets n_keep = n_accept = 0,
+ *   next_token = -1 and its flag raised (dspark_read_device_error).
+ * workspace: at least dspark_workspace_size(dims, DSPARK_CALL_VERIFY) bytes,
+ *   256-byte aligned.  dims->d is not used; dims->head must be Markov. */
+dspark_status dspark_verify_block(const dspark_dims* dims, const void* U, const int32_t* anchor,
+                                  const void* W1, const void* W2, const void* T_logits,
+                                  const int32_t* tokens, const float* logp, const float* survival,
+                                  const float* temperature, float threshold, uint64_t seed,
+                                  uint64_t offset, int32_t* n_keep, int32_t* n_accept,
+                                  int32_t* next_token, float* accept_prob, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream);
+
 /* Synchronises `hip_stream`, then reads the per-block error flags the last
  * call with these dims left at the start of `workspace`: *code (HOST
  * pointer) = the number of blocks that met a token id outside [0, V) (0
@@ -226,11 +272,11 @@ dspark_status dspark_read_device_error(const dspark_dims* dims, const void* work
 dspark_status dspark_set_option(int option, int value);
 
 /* Kernel timing for measurement.  While enabled on the calling thread, each
- * dspark_draft_block / dspark_block_loss / dspark_block_loss_backward call
- * also records a pair of HIP events on `hip_stream` around every launch of
- * its dominant kernel (the V-streaming step kernel when drafting, the
- * V-streaming passes of the loss, the matrix-core dZ W2^T kernel of the
- * backward).  dspark_profile_read() waits for those events and returns (HOST
+ * dspark_draft_block / dspark_block_loss / dspark_block_loss_backward /
+ * dspark_verify_block call also records a pair of HIP events on `hip_stream`
+ * around every launch of its dominant kernel (the V-streaming step kernel
+ * when drafting, the V-streaming passes of the loss, the matrix-core dZ W2^T
+ * kernel of the backward, the draft-row kernel of the verification).  dspark_profile_read() waits for those events and returns (HOST
  * out-pointers) the summed milliseconds and the number of timed launches
  * since the previous read, then forgets them.  Events are created on first
  * use and reused; enable = 0 stops recording.  Returns DSPARK_EDEVICE if a

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 DSPARK_OK, DSPARK_EINVAL, DSPARK_EUNSUPPORTED, DSPARK_EWORKSPACE, DSPARK_EDEVICE = range(5)
 DSPARK_F32, DSPARK_BF16 = 0, 1
 DSPARK_HEAD_MARKOV, DSPARK_HEAD_RNN = 0, 1
-DSPARK_CALL_DRAFT, DSPARK_CALL_LOSS, DSPARK_CALL_LOSS_BACKWARD = 0, 1, 2
+DSPARK_CALL_DRAFT, DSPARK_CALL_LOSS, DSPARK_CALL_LOSS_BACKWARD, DSPARK_CALL_VERIFY = 0, 1, 2, 3
 DSPARK_OPT_DRAFT_PATH = 1
 DSPARK_OPT_PERSIST_LAUNCH = 2
 
@@ -63,6 +63,8 @@ def load() -> ctypes.CDLL:
     lib.dspark_block_loss.restype = ctypes.c_int
     lib.dspark_block_loss_backward.argtypes = [D, P, I32] + [P] * 11 + [SZ, P]
     lib.dspark_block_loss_backward.restype = ctypes.c_int
+    lib.dspark_verify_block.argtypes = [D] + [P] * 9 + [ctypes.c_float, U64, U64] + [P] * 5 + [SZ, P]
+    lib.dspark_verify_block.restype = ctypes.c_int
     lib.dspark_read_device_error.argtypes = [D, P, ctypes.POINTER(I32), P]
     lib.dspark_read_device_error.restype = ctypes.c_int
     lib.dspark_set_option.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -163,6 +165,16 @@ def dspark_block_loss_backward(dims, dlogits, dlogits_dtype, dconf_logit, h, anc
         {"f32": DSPARK_F32, "bf16": DSPARK_BF16}.get(dlogits_dtype, dlogits_dtype),
         _p(dconf_logit), _p(h), _p(anchor), _p(labels), _p(W1), _p(W2), _p(w_conf), _p(dW1),
         _p(dw_conf), _p(dh), _p(workspace), nbytes, _stream(stream)))
+
+
+def dspark_verify_block(dims, U, anchor, W1, W2, T_logits, tokens, logp, survival, temperature,
+                        threshold, seed, offset, n_keep, n_accept, next_token, accept_prob,
+                        workspace, workspace_bytes=None, stream=None):
+    nbytes = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(load().dspark_verify_block(
+        ctypes.byref(dims), _p(U), _p(anchor), _p(W1), _p(W2), _p(T_logits), _p(tokens), _p(logp),
+        _p(survival), _p(temperature), float(threshold), seed, offset, _p(n_keep), _p(n_accept),
+        _p(next_token), _p(accept_prob), _p(workspace), nbytes, _stream(stream)))
 
 
 def dspark_read_device_error(dims, workspace, stream=None) -> int:

@@ -93,6 +93,7 @@ size_t dspark_workspace_size(const dspark_dims* dims, int which) {
     if (which == DSPARK_CALL_DRAFT) return dspark::draft_layout(*dims).total;
     if (which == DSPARK_CALL_LOSS) return dspark::loss_layout(*dims).total;
     if (which == DSPARK_CALL_LOSS_BACKWARD) return dspark::bwd_layout(*dims).total;
+    if (which == DSPARK_CALL_VERIFY) return dspark::verify_layout(*dims).total;
     return 0;
 }
 
@@ -226,6 +227,49 @@ dspark_status dspark_block_loss_backward(const dspark_dims* dims, const void* dl
     a.ws = static_cast<char*>(workspace);
     a.stream = static_cast<hipStream_t>(hip_stream);
     const hipError_t e = dspark::launch_loss_backward(a);
+    if (e != hipSuccess) return fail(DSPARK_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+dspark_status dspark_verify_block(const dspark_dims* dims, const void* U, const int32_t* anchor,
+                                  const void* W1, const void* W2, const void* T_logits,
+                                  const int32_t* tokens, const float* logp, const float* survival,
+                                  const float* temperature, float threshold, uint64_t seed,
+                                  uint64_t offset, int32_t* n_keep, int32_t* n_accept,
+                                  int32_t* next_token, float* accept_prob, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream) {
+    dspark_status s = check_dims(dims);
+    if (s != DSPARK_OK) return s;
+    if (dims->head != DSPARK_HEAD_MARKOV)
+        return fail(DSPARK_EUNSUPPORTED, "verification is built for the Markov head only");
+    const char* missing = !U ? "U" : !anchor ? "anchor" : !W1 ? "W1" : !W2 ? "W2"
+                        : !T_logits ? "T_logits" : !tokens ? "tokens" : !logp ? "logp"
+                        : !survival ? "survival" : !temperature ? "temperature"
+                        : !n_keep ? "n_keep" : !n_accept ? "n_accept" : !next_token ? "next_token"
+                        : !workspace ? "workspace" : nullptr;
+    if (missing) return fail(DSPARK_EINVAL, "required pointer %s is NULL", missing);
+    if (isnan(threshold)) return fail(DSPARK_EINVAL, "threshold is NaN");
+    if (!aligned(workspace, 256)) return fail(DSPARK_EINVAL, "workspace is not 256-byte aligned");
+    const dspark::VerifyLayout L = dspark::verify_layout(*dims);
+    if (workspace_bytes < L.total)
+        return fail(DSPARK_EWORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, L.total);
+    const size_t esz = dims->dtype == DSPARK_BF16 ? 2 : 4;
+    if (!aligned(U, esz) || !aligned(W1, esz) || !aligned(W2, esz) || !aligned(T_logits, esz) ||
+        !aligned(logp, 4) || !aligned(survival, 4) || !aligned(temperature, 4) ||
+        (accept_prob && !aligned(accept_prob, 4)))
+        return fail(DSPARK_EINVAL, "a tensor is not aligned to its element size");
+    if (L.mfma && (!aligned(U, 16) || !aligned(W2, 16)))
+        return fail(DSPARK_EUNSUPPORTED, "bf16 U and W2 must be 16-byte aligned");
+
+    dspark::VerifyArgs a{};
+    a.dims = *dims;
+    a.U = U; a.W1 = W1; a.W2 = W2; a.T_logits = T_logits;
+    a.anchor = anchor; a.tokens = tokens; a.logp = logp; a.survival = survival;
+    a.temperature = temperature; a.threshold = threshold; a.seed = seed; a.offset = offset;
+    a.n_keep = n_keep; a.n_accept = n_accept; a.next_token = next_token; a.accept_prob = accept_prob;
+    a.ws = static_cast<char*>(workspace);
+    a.stream = static_cast<hipStream_t>(hip_stream);
+    const hipError_t e = dspark::launch_verify(a);
     if (e != hipSuccess) return fail(DSPARK_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -120,6 +120,42 @@ struct BwdArgs {
 
 hipError_t launch_loss_backward(const BwdArgs& a);
 
+// Workspace of the verification call.
+struct VerifyLayout {
+    bool mfma;         // matrix-core draft row (bf16, r % 32 == 0, r <= 256, V % 8 == 0)
+    int Bpad;          // B rounded up to 16
+    int P;             // 256-column groups of the draft row
+    int C;             // 4096-column chunks of the final draw
+    size_t bad;        // int32 [B]  1 if the block holds a token id out of range
+    size_t lse_t;      // f32 [B, gamma+1]  lse of z_t / T
+    size_t amax;       // i32 [B, gamma+1]  argmax of z_t
+    size_t mode, jpos; // i32 [B]  final-draw mode and position
+    size_t invT;       // f32 [B]  1 / T (1 when greedy)
+    size_t ebf;        // u16 [Bpad, r]  E row of the residual position (bf16)
+    size_t ef;         // f32 [B, r]     same, fp32
+    size_t zd;         // f32 [B, V]  z_d / T at the residual position
+    size_t pmx, psm;   // f32 [B, P]  (max, sum) partials of z_d / T
+    size_t lse_d;      // f32 [B]
+    size_t keys;       // u64 [B, C, 2]  residual and target argmax keys per chunk
+    size_t total;
+};
+VerifyLayout verify_layout(const dspark_dims& d);
+
+struct VerifyArgs {
+    dspark_dims dims;
+    const void *U, *W1, *W2, *T_logits;
+    const int32_t *anchor, *tokens;
+    const float *logp, *survival, *temperature;
+    float threshold;
+    uint64_t seed, offset;
+    int32_t *n_keep, *n_accept, *next_token;
+    float* accept_prob;
+    char* ws;
+    hipStream_t stream;
+};
+
+hipError_t launch_verify(const VerifyArgs& a);
+
 struct DraftArgs {
     dspark_dims dims;
     const void *U, *h, *W1, *W2, *w_conf, *W_rnn;

@@ -101,3 +101,26 @@ def block_loss_backward(dlogits, dconf_logit, h, anchor, labels, W1, W2, w_conf,
     out["_ws"] = ws
     out["_dims"] = dims
     return out
+
+
+def verify_block(U, anchor, W1, W2, T_logits, tokens, logp, survival, temperature, *,
+                 threshold: float = 0.0, seed: int = 0, offset: int = 0, want_accept_prob=True,
+                 ws: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Trim, accept/reject and the next token for drafted blocks (see
+    dspark_verify_block)."""
+    B, gamma, V = U.shape
+    dims = _b.make_dims(V, W1.shape[1], 1, gamma, B, _dtype_of(U), "markov")
+    dev = U.device
+    out = dict(n_keep=torch.empty(B, dtype=torch.int32, device=dev),
+               n_accept=torch.empty(B, dtype=torch.int32, device=dev),
+               next_token=torch.empty(B, dtype=torch.int32, device=dev),
+               accept_prob=torch.empty((B, gamma), dtype=torch.float32, device=dev)
+               if want_accept_prob else None)
+    if ws is None:
+        ws = workspace(dims, _b.DSPARK_CALL_VERIFY, dev)
+    _b.dspark_verify_block(dims, U, anchor, W1, W2, T_logits, tokens, logp, survival, temperature,
+                           threshold, seed, offset, out["n_keep"], out["n_accept"],
+                           out["next_token"], out["accept_prob"], ws, stream=stream)
+    out["_ws"] = ws
+    out["_dims"] = dims
+    return out

@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for need in ("dspark_draft_block", "dspark_block_loss", "dspark_block_loss_backward",
-                 "dspark_workspace_size",
+                 "dspark_verify_block", "dspark_workspace_size",
                  "dspark_read_device_error", "dspark_last_error", "dspark_version"):
         assert need in names
 
@@ -53,6 +53,8 @@ def test_version_and_workspace_sizes(lib):
     wb = lib.dspark_workspace_size(lib.make_dims(151936, 256, 4096, 7, 1024),
                                    lib.DSPARK_CALL_LOSS_BACKWARD)
     assert wb > 0 and wb % 256 == 0
+    wv = lib.dspark_workspace_size(d, lib.DSPARK_CALL_VERIFY)
+    assert wv > 0 and wv % 256 == 0
 
 
 BAD_DIMS = [
@@ -200,4 +202,38 @@ def test_loss_backward_rejects_bad_arguments(lib):
     assert e.value.status == lib.DSPARK_EUNSUPPORTED
     with pytest.raises(lib.DsparkError) as e:
         _bwd_call(lib, d, dW1=258)
+    assert e.value.status == lib.DSPARK_EINVAL
+
+
+def _verify_call(lib, d, ptr=256, **over):
+    args = dict(U=ptr, anchor=ptr, W1=ptr, W2=ptr, T_logits=ptr, tokens=ptr, logp=ptr,
+                survival=ptr, temperature=ptr, threshold=0.5, seed=0, offset=0, n_keep=ptr,
+                n_accept=ptr, next_token=ptr, accept_prob=None, workspace=ptr)
+    wsb = over.pop("workspace_bytes", 1 << 40)
+    args.update(over)
+    lib.dspark_verify_block(d, **args, workspace_bytes=wsb, stream=0)
+
+
+def test_verify_rejects_bad_arguments(lib):
+    d = lib.make_dims(1000, 64, 1, 7, 4)
+    for name in ("U", "anchor", "W1", "W2", "T_logits", "tokens", "logp", "survival",
+                 "temperature", "n_keep", "n_accept", "next_token", "workspace"):
+        with pytest.raises(lib.DsparkError) as e:
+            _verify_call(lib, d, **{name: None})
+        assert e.value.status == lib.DSPARK_EINVAL and name in str(e.value)
+    with pytest.raises(lib.DsparkError) as e:
+        _verify_call(lib, d, threshold=float("nan"))
+    assert e.value.status == lib.DSPARK_EINVAL
+    need = lib.dspark_workspace_size(d, lib.DSPARK_CALL_VERIFY)
+    with pytest.raises(lib.DsparkError) as e:
+        _verify_call(lib, d, workspace_bytes=need - 1)
+    assert e.value.status == lib.DSPARK_EWORKSPACE
+    with pytest.raises(lib.DsparkError) as e:
+        _verify_call(lib, lib.make_dims(1000, 64, 1, 7, 4, head="rnn"))
+    assert e.value.status == lib.DSPARK_EUNSUPPORTED
+    with pytest.raises(lib.DsparkError) as e:
+        _verify_call(lib, d, U=258)
+    assert e.value.status == lib.DSPARK_EUNSUPPORTED
+    with pytest.raises(lib.DsparkError) as e:
+        _verify_call(lib, d, logp=258)
     assert e.value.status == lib.DSPARK_EINVAL
