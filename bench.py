@@ -223,6 +223,75 @@ def bench_backward(args) -> int:
     return 0
 
 
+def bench_verify(args) -> int:
+    """Verification of Qwen3-4B-shaped drafted blocks (B = 32, gamma = 7,
+    V = 151936, r = 256, bf16): one dspark_draft_block call drafts the
+    blocks, synthetic target logits [B, gamma + 1, V] (the base logits plus
+    N(0, 0.3^2) at the drafted positions) stand in for the target model;
+    a step is one dspark_verify_block call (threshold 0.25).  Roofline of its
+    draft-row kernel: W2 once, the U rows of the residual positions and the
+    float32 draft rows it writes."""
+    import numpy as np
+    import torch
+
+    import synth
+    from semi_autoregressive_draft_markov_amd import binding, ops
+
+    binding.load()
+    dev = torch.device("cuda:0")
+    inp = synth.config_inputs(WORKLOAD_CFG)
+    t = synth.to_torch(inp, dev)
+    B, gamma, V, r = inp.B, inp.gamma, inp.V, inp.r
+    d = ops.draft_block(t["U"], t["h"], t["anchor"], t["W1"], t["W2"], t["w_conf"], t["temperature"])
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    tgt = torch.empty((B, gamma + 1, V), dtype=torch.bfloat16, device=dev)
+    tgt[:, :gamma] = (t["U"].float() + 0.3 * torch.randn((B, gamma, V), generator=g, device=dev)).bfloat16()
+    tgt[:, gamma] = (2.0 * torch.randn((B, V), generator=g, device=dev)).bfloat16()
+    out = ops.verify_block(t["U"], t["anchor"], t["W1"], t["W2"], tgt, d["tokens"], d["logp"],
+                           d["survival"], t["temperature"], threshold=0.25)
+    dims, ws = out["_dims"], out["_ws"]
+
+    def step(i):
+        binding.dspark_verify_block(dims, t["U"], t["anchor"], t["W1"], t["W2"], tgt, d["tokens"],
+                                    d["logp"], d["survival"], t["temperature"], 0.25, 0, i,
+                                    out["n_keep"], out["n_accept"], out["next_token"],
+                                    out["accept_prob"], ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    binding.dspark_profile_enable(True)
+    binding.dspark_profile_read()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    k_ms, launches = binding.dspark_profile_read()
+    binding.dspark_profile_enable(False)
+    k_s = k_ms * 1e-3 / max(launches, 1)
+    alg_bytes = r * V * 2 + B * V * 2 + B * V * 4
+    acc = out["n_accept"].float().mean().item()
+    line = {
+        "metric": "verified blocks/s (V=151936, r=256, γ=7, B=32)",
+        "value": round(B * args.steps / el, 1), "unit": "blocks/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(el * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-4b-shaped verification of drafted blocks", "V": V, "r": r,
+                   "gamma": gamma, "B": B, "threshold": 0.25,
+                   "mean_accepted": round(acc, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(alg_bytes / k_s / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg_bytes / k_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_v_bias_mfma<8>", "kernel_us": round(k_s * 1e6, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def synth_subset(inp, idx):
     import synth
     return synth.subset(inp, idx)
@@ -237,7 +306,7 @@ def main() -> int:
                     help="wall time of the CPU oracle sample (0 skips it)")
     ap.add_argument("--workload", default="qwen3-4b",
                     choices=["qwen3-4b", "qwen3-14b", "gemma4-rnn", "qwen3-8b-loss",
-                             "qwen3-8b-backward"],
+                             "qwen3-8b-backward", "qwen3-4b-verify"],
                     help="qwen3-4b (default) is the reported workload; the others are "
                          "extra measurements of the same kernels at the other shapes")
     ap.add_argument("--launch", default="plain", choices=["plain", "cooperative"],
@@ -259,6 +328,8 @@ def main() -> int:
         return bench_loss(args)
     if args.workload == "qwen3-8b-backward":
         return bench_backward(args)
+    if args.workload == "qwen3-4b-verify":
+        return bench_verify(args)
 
     import numpy as np
     import torch

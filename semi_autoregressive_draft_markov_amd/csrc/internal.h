@@ -126,9 +126,11 @@ struct VerifyLayout {
     int Bpad;          // B rounded up to 16
     int P;             // 256-column groups of the draft row
     int C;             // 4096-column chunks of the final draw
+    int CT;            // 8192-column chunks of the target-row statistics
     size_t bad;        // int32 [B]  1 if the block holds a token id out of range
     size_t lse_t;      // f32 [B, gamma+1]  lse of z_t / T
     size_t amax;       // i32 [B, gamma+1]  argmax of z_t
+    size_t tmx, tsm, tkey;  // [B, gamma+1, CT] chunk max / sum / argmax key of the target rows
     size_t mode, jpos; // i32 [B]  final-draw mode and position
     size_t invT;       // f32 [B]  1 / T (1 when greedy)
     size_t ebf;        // u16 [Bpad, r]  E row of the residual position (bf16)
@@ -136,7 +138,7 @@ struct VerifyLayout {
     size_t zd;         // f32 [B, V]  z_d / T at the residual position
     size_t pmx, psm;   // f32 [B, P]  (max, sum) partials of z_d / T
     size_t lse_d;      // f32 [B]
-    size_t keys;       // u64 [B, C, 2]  residual and target argmax keys per chunk
+    size_t keys;       // u64 [B, 2]  residual and target argmax keys (atomic maxima)
     size_t total;
 };
 VerifyLayout verify_layout(const dspark_dims& d);

@@ -23,9 +23,11 @@
 // (v / 4, 0x80000000 | j, b, offset); the key and the word -> u map are the
 // drafting ones, and no counter coincides with a drafting counter.
 //
-// Kernels: k_vt_stats (target row statistics: softmax normaliser of z_t / T
-// and argmax, per (block, position)), k_v_decide (thread per block: trim,
-// accept loop, the mode of the final draw, E row of the residual position),
+// Kernels: k_vt_stats (chunk statistics of the target rows: max, sum of
+// exp((z_t - max) / T), argmax), k_v_decide (wave per block: row
+// normalisers, the accept tests of all positions at once, trim and first
+// rejection by ballot, the mode of the final draw, E row of the residual
+// position),
 // k_v_bias_mfma / k_v_bias_vec (z_d / T at the residual position for every
 // block, and per-column-group softmax partials), k_v_lse, k_v_sample
 // (partial argmax keys of the residual and the target draw), k_v_final.
@@ -39,6 +41,7 @@ namespace dspark {
 
 constexpr int kVCols = 256;      // columns per bias workgroup (4 waves x 64)
 constexpr int kVChunk = 4096;    // columns per sampling workgroup (256 threads x 16)
+constexpr int kVTChunk = 8192;   // columns per target-statistics workgroup (256 threads x 32)
 constexpr uint32_t kVerifyAcceptCtr0 = 0xFFFFFFFFu;
 constexpr uint32_t kVerifyDrawCtr1 = 0x80000000u;
 
@@ -54,6 +57,7 @@ VerifyLayout verify_layout(const dspark_dims& d) {
     L.Bpad = (d.B + 15) / 16 * 16;
     L.P = (d.V + kVCols - 1) / kVCols;
     L.C = (d.V + kVChunk - 1) / kVChunk;
+    L.CT = (d.V + kVTChunk - 1) / kVTChunk;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -64,6 +68,9 @@ VerifyLayout verify_layout(const dspark_dims& d) {
     L.bad = take(sizeof(int32_t) * B);
     L.lse_t = take(sizeof(float) * rows);
     L.amax = take(sizeof(int32_t) * rows);
+    L.tmx = take(sizeof(float) * rows * L.CT);
+    L.tsm = take(sizeof(float) * rows * L.CT);
+    L.tkey = take(sizeof(uint64_t) * rows * L.CT);
     L.mode = take(sizeof(int32_t) * B);
     L.jpos = take(sizeof(int32_t) * B);
     L.invT = take(sizeof(float) * B);
@@ -73,7 +80,7 @@ VerifyLayout verify_layout(const dspark_dims& d) {
     L.pmx = take(sizeof(float) * B * L.P);
     L.psm = take(sizeof(float) * B * L.P);
     L.lse_d = take(sizeof(float) * B);
-    L.keys = take(sizeof(uint64_t) * B * L.C * 2);
+    L.keys = take(sizeof(uint64_t) * B * 2);
     L.total = off;
     return L;
 }
@@ -95,29 +102,57 @@ __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2)
 
 // ------------------------------------------------------------ target rows
 
-// Workgroup per target row (b, position k in 0..gamma): lse of z_t / T
-// (T > 0) and the argmax of z_t (lowest index on a tie).
-template <typename T>
+// Workgroup per (target row, 8192-column chunk), row = (b, position k in
+// 0..gamma), thread per 32 strided columns: the chunk's max of z_t (and its
+// argmax key, lowest index on a tie) and sum of exp((z_t - max) / T).
+template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void k_vt_stats(const T* __restrict__ Tl,
                                                   const float* __restrict__ temperature, int V,
-                                                  int gamma, float* __restrict__ lse_t,
-                                                  int32_t* __restrict__ amax) {
+                                                  int gamma, int CT, float* __restrict__ tmx,
+                                                  float* __restrict__ tsm, uint64_t* __restrict__ tkey) {
     __shared__ float sm[256], ss[256];
     __shared__ uint64_t sk[256];
     const int64_t row = blockIdx.x;
+    const int chunk = blockIdx.y;
     const int b = static_cast<int>(row / (gamma + 1));
     const float Tb = temperature[b];
     const float invT = Tb > 0.0f ? 1.0f / Tb : 1.0f;
     const T* z = Tl + row * V;
-    float m = -INFINITY, s = 0.0f;
+    float x[kVTChunk / 256];
+    float m = -INFINITY;
     uint64_t key = kKeyNone;
-    for (int v = threadIdx.x; v < V; v += 256) {
-        const float x = load_f(z, v);
-        const uint64_t kk = argmax_key(x, static_cast<uint32_t>(v));
-        key = kk > key ? kk : key;
-        ms_merge(m, s, x * invT, 1.0f);
+    if (VEC) {
+        // 4 runs of 8 consecutive columns per thread, 16-byte loads
+#pragma unroll
+        for (int i = 0; i < kVTChunk / 2048; ++i) {
+            const int v = chunk * kVTChunk + 2048 * i + 8 * threadIdx.x;
+            const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(z) + min(v, V - 8));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xv = v < V ? ((e & 1) ? hi_bf16(w[e >> 1]) : lo_bf16(w[e >> 1])) : -INFINITY;
+                x[8 * i + e] = xv;
+                if (xv > m) {  // strict: the lowest column wins a tie
+                    m = xv;
+                    key = argmax_key(xv, static_cast<uint32_t>(v + e));
+                }
+            }
+        }
+    } else {
+        const int v0 = chunk * kVTChunk + threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < kVTChunk / 256; ++i) {
+            const int v = v0 + 256 * i;
+            x[i] = v < V ? load_f(z, min(v, V - 1)) : -INFINITY;
+            if (x[i] > m) {
+                m = x[i];
+                key = argmax_key(x[i], static_cast<uint32_t>(v));
+            }
+        }
     }
-    sm[threadIdx.x] = m;
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kVTChunk / 256; ++i) s += x[i] > -INFINITY ? __expf((x[i] - m) * invT) : 0.0f;
+    sm[threadIdx.x] = m * invT;
     ss[threadIdx.x] = s;
     sk[threadIdx.x] = key;
     __syncthreads();
@@ -132,78 +167,108 @@ __global__ __launch_bounds__(256) void k_vt_stats(const T* __restrict__ Tl,
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        lse_t[row] = sm[0] + __logf(ss[0]);
-        amax[row] = static_cast<int32_t>(key_index(sk[0]));
+        tmx[row * CT + chunk] = sm[0];
+        tsm[row * CT + chunk] = ss[0];
+        tkey[row * CT + chunk] = sk[0];
     }
 }
 
 // ----------------------------------------------------------------- decide
 
-// Thread per block: trim, accept loop, mode and position of the final draw,
-// the E row (W1[token before the residual position]) in bf16 and fp32.
+// Wave per block.  Lane k <= gamma merges the chunk statistics of target row
+// k (lse of z_t / T, argmax); lane k < gamma runs the accept test of
+// position k (independent of the others; the first failure ends the run);
+// lane 0 then takes m, n, the mode and position of the final draw, and the
+// wave copies the E row (W1[token before the residual position]) in bf16
+// and fp32.
 template <typename T>
-__global__ __launch_bounds__(256) void k_v_decide(
+__global__ __launch_bounds__(64) void k_v_decide(
     const T* __restrict__ Tl, const T* __restrict__ W1, const int32_t* __restrict__ anchor,
     const int32_t* __restrict__ tokens, const float* __restrict__ logp,
     const float* __restrict__ survival, const float* __restrict__ temperature,
-    const float* __restrict__ lse_t, const int32_t* __restrict__ amax, int V, int r, int gamma,
-    int B, float tau, uint32_t key0, uint32_t key1, uint32_t ctr3, int32_t* __restrict__ bad,
+    const float* __restrict__ tmx, const float* __restrict__ tsm, const uint64_t* __restrict__ tkey,
+    int CT, int V, int r, int gamma, float tau, uint32_t key0, uint32_t key1, uint32_t ctr3,
+    float* __restrict__ lse_t, int32_t* __restrict__ amax, uint64_t* __restrict__ keys,
+    int32_t* __restrict__ bad,
     int32_t* __restrict__ mode, int32_t* __restrict__ jpos, float* __restrict__ invTo,
     uint16_t* __restrict__ ebf, float* __restrict__ ef, int32_t* __restrict__ n_keep,
     int32_t* __restrict__ n_accept, int32_t* __restrict__ next_token,
     float* __restrict__ accept_prob) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= B) return;
+    __shared__ int s_prev;
+    __shared__ float s_lt[65];
+    __shared__ int s_am[65];
+    const int b = blockIdx.x, lane = threadIdx.x;
     const float Tb = temperature[b];
     const bool greedy = !(Tb > 0.0f);
     const float invT = greedy ? 1.0f : 1.0f / Tb;
-    int flag = anchor[b] < 0 || anchor[b] >= V;
-    for (int k = 0; k < gamma; ++k) {
-        const int x = tokens[static_cast<int64_t>(b) * gamma + k];
-        flag |= x < 0 || x >= V;
+    const int64_t i0 = static_cast<int64_t>(b) * gamma;
+    // target row statistics (rows 0..gamma, gamma <= 64)
+    for (int k = lane; k <= gamma; k += 64) {
+        const int64_t row = static_cast<int64_t>(b) * (gamma + 1) + k;
+        float m = -INFINITY, s = 0.0f;
+        uint64_t key = kKeyNone;
+        for (int c = 0; c < CT; ++c) {
+            ms_merge(m, s, tmx[row * CT + c], tsm[row * CT + c]);
+            const uint64_t k2 = tkey[row * CT + c];
+            key = k2 > key ? k2 : key;
+        }
+        s_lt[k] = m + __logf(s);
+        s_am[k] = static_cast<int32_t>(key_index(key));
+        lse_t[row] = s_lt[k];
+        amax[row] = s_am[k];
     }
-    int m = 0;
-    while (m < gamma && survival[static_cast<int64_t>(b) * gamma + m] >= tau) ++m;
-    int n = 0;
-    if (!flag) {
-        for (; n < m; ++n) {
-            const int64_t i = static_cast<int64_t>(b) * gamma + n;
-            const int64_t row = static_cast<int64_t>(b) * (gamma + 1) + n;
-            const int x = tokens[i];
-            bool ok;
-            float ap;
-            if (greedy) {
-                ok = x == amax[row];
-                ap = ok ? 1.0f : 0.0f;
-            } else {
-                const float pt = __expf(load_f(Tl, row * V + x) * invT - lse_t[row]);
-                const float pd = __expf(logp[i]);
-                const uint32_t w = philox_word(kVerifyAcceptCtr0, static_cast<uint32_t>(n),
-                                               static_cast<uint32_t>(b), ctr3, key0, key1, 0);
-                const float u = static_cast<float>((w >> 8) | 1u) * 5.9604644775390625e-8f;
-                ok = u * pd < pt;
-                ap = pt >= pd ? 1.0f : pt / pd;
-            }
-            if (accept_prob) accept_prob[i] = ap;
-            if (!ok) break;
+    __syncthreads();
+    const float lt = lane <= gamma ? s_lt[lane] : 0.0f;
+    const int am = lane <= gamma ? s_am[lane] : 0;
+    // per-position accept tests
+    const int x = lane < gamma ? tokens[i0 + lane] : 0;
+    const bool xbad = lane < gamma && (x < 0 || x >= V);
+    const bool in_keep = lane < gamma && survival[i0 + lane] >= tau;
+    bool ok = false;
+    float ap = 0.0f;
+    if (lane < gamma && !xbad) {
+        if (greedy) {
+            ok = x == am;
+            ap = ok ? 1.0f : 0.0f;
+        } else {
+            const int64_t row = static_cast<int64_t>(b) * (gamma + 1) + lane;
+            const float pt = __expf(load_f(Tl, row * V + x) * invT - lt);
+            const float pd = __expf(logp[i0 + lane]);
+            const uint32_t w = philox_word(kVerifyAcceptCtr0, static_cast<uint32_t>(lane),
+                                           static_cast<uint32_t>(b), ctr3, key0, key1, 0);
+            const float u = static_cast<float>((w >> 8) | 1u) * 5.9604644775390625e-8f;
+            ok = u * pd < pt;
+            ap = pt >= pd ? 1.0f : pt / pd;
         }
     }
-    if (accept_prob)
-        for (int k = flag ? 0 : min(n + 1, m); k < gamma; ++k)
-            accept_prob[static_cast<int64_t>(b) * gamma + k] = NAN;
+    const uint64_t badmask = __ballot(xbad);
+    const int flag = badmask != 0 || anchor[b] < 0 || anchor[b] >= V;
+    // m = leading kept positions, n = leading accepted positions among them
+    const uint64_t past = gamma < 64 ? (~0ull << gamma) : 0ull;
+    const uint64_t notkeep = __ballot(lane < gamma && !in_keep) | past;
+    const int m = notkeep ? __builtin_ctzll(notkeep) : 64;
+    const uint64_t notok = __ballot(lane < gamma && !ok) | past;
+    const int n = flag ? 0 : min(m, notok ? static_cast<int>(__builtin_ctzll(notok)) : 64);
+    // tested positions: 0..n (the rejected one included) within the kept ones
+    if (accept_prob && lane < gamma)
+        accept_prob[i0 + lane] = (!flag && lane < m && lane <= n) ? ap : NAN;
     const int j = n;
     const int md = greedy ? kModeGreedy : (n < m ? kModeResidual : kModeTarget);
-    bad[b] = flag;
-    mode[b] = flag ? -1 : md;
-    jpos[b] = j;
-    invTo[b] = invT;
-    n_keep[b] = flag ? 0 : m;
-    n_accept[b] = flag ? 0 : n;
-    next_token[b] = flag ? -1 : (greedy ? amax[static_cast<int64_t>(b) * (gamma + 1) + j] : -1);
-    // E row of the residual position (zero for the other modes)
-    const int prev = (md == kModeResidual && !flag) ? (j == 0 ? anchor[b] : tokens[static_cast<int64_t>(b) * gamma + j - 1])
-                                                     : -1;
-    for (int q = 0; q < r; ++q) {
+    if (lane < 2) keys[2 * b + lane] = kKeyNone;
+    if (lane == 0) {
+        bad[b] = flag;
+        mode[b] = flag ? -1 : md;
+        jpos[b] = j;
+        invTo[b] = invT;
+        n_keep[b] = flag ? 0 : m;
+        n_accept[b] = n;
+        s_prev = (md == kModeResidual && !flag) ? (j == 0 ? anchor[b] : tokens[i0 + j - 1]) : -1;
+    }
+    // the greedy emission is the target's argmax at j
+    if (lane == 0) next_token[b] = flag ? -1 : (greedy ? s_am[j] : -1);
+    __syncthreads();
+    const int prev = s_prev;
+    for (int q = lane; q < r; q += 64) {
         const float e = prev >= 0 ? load_f(W1, static_cast<int64_t>(prev) * r + q) : 0.0f;
         ef[static_cast<int64_t>(b) * r + q] = e;
         ebf[static_cast<int64_t>(b) * r + q] = static_cast<uint16_t>(__float_as_uint(e) >> 16);  // exact: bf16 data
@@ -362,14 +427,14 @@ __global__ __launch_bounds__(64) void k_v_lse(const float* __restrict__ pmx, con
 // Workgroup per (block, 4096-column chunk), thread per 16 columns: partial
 // argmax keys of the residual draw (entries with p_t > p_d only) and of the
 // target draw.  Greedy blocks are skipped.
-template <typename T>
+template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void k_v_sample(const T* __restrict__ Tl, const float* __restrict__ zd,
                                                   const float* __restrict__ lse_t,
                                                   const float* __restrict__ lse_d,
                                                   const int32_t* __restrict__ mode,
                                                   const int32_t* __restrict__ jpos,
                                                   const float* __restrict__ invT, int V, int gamma,
-                                                  int C, uint32_t key0, uint32_t key1, uint32_t ctr3,
+                                                  uint32_t key0, uint32_t key1, uint32_t ctr3,
                                                   uint64_t* __restrict__ keys) {
     __shared__ uint64_t kr[256], kt[256];
     const int b = blockIdx.y, chunk = blockIdx.x;
@@ -384,24 +449,54 @@ __global__ __launch_bounds__(256) void k_v_sample(const T* __restrict__ Tl, cons
     const float* zr = zd + static_cast<int64_t>(b) * V;
     uint64_t bres = kKeyNone, btgt = kKeyNone;
     const int v0 = chunk * kVChunk + threadIdx.x * 16;
+    float xt[16], xd[16];
+    if (VEC) {
+        // 16 consecutive columns: two 16-byte loads of the target row, four
+        // of the draft row (residual mode only); clamped past V
+        const int va = min(v0, V - 8), vb = min(v0 + 8, V - 8);
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(zt) + va);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(zt) + vb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            xt[e] = (e & 1) ? hi_bf16(w0[e >> 1]) : lo_bf16(w0[e >> 1]);
+            xt[8 + e] = (e & 1) ? hi_bf16(w1[e >> 1]) : lo_bf16(w1[e >> 1]);
+        }
+        if (md == kModeResidual) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(zr + min(v0 + 4 * q, V - 4));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xd[4 * q + e] = d4[e];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int v = min(v0 + e, V - 1);
+            xt[e] = load_f(zt, v);
+            xd[e] = md == kModeResidual ? zr[v] : 0.0f;
+        }
+    }
+#pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int vb = v0 + 4 * q;
-        if (vb >= V) break;
         const u32x4 wd = philox4x32_10(u32x4{static_cast<uint32_t>(vb >> 2), kVerifyDrawCtr1 | static_cast<uint32_t>(j),
                                              static_cast<uint32_t>(b), ctr3},
                                        key0, key1);
+#pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int v = vb + e;
-            if (v >= V) break;
-            const float g = gumbel_from_word(wd[e]);
-            const float zl = load_f(zt, v) * it;
-            const uint64_t k2 = argmax_key(zl + g, static_cast<uint32_t>(v));
-            btgt = k2 > btgt ? k2 : btgt;
-            if (md == kModeResidual) {
-                const float res = __expf(zl - lt) - __expf(zr[v] - ld);
-                if (res > 0.0f) {
-                    const uint64_t k1 = argmax_key(__logf(res) + g, static_cast<uint32_t>(v));
-                    bres = k1 > bres ? k1 : bres;
+            if (v < V) {
+                const float g = gumbel_from_word(wd[e]);
+                const float zl = xt[4 * q + e] * it;
+                const uint64_t k2 = argmax_key(zl + g, static_cast<uint32_t>(v));
+                btgt = k2 > btgt ? k2 : btgt;
+                if (md == kModeResidual) {
+                    const float res = __expf(zl - lt) - __expf(xd[4 * q + e] - ld);
+                    if (res > 0.0f) {
+                        const uint64_t k1 = argmax_key(__logf(res) + g, static_cast<uint32_t>(v));
+                        bres = k1 > bres ? k1 : bres;
+                    }
                 }
             }
         }
@@ -416,28 +511,23 @@ __global__ __launch_bounds__(256) void k_v_sample(const T* __restrict__ Tl, cons
         }
         __syncthreads();
     }
+    // a maximum does not depend on the order of the updates
     if (threadIdx.x == 0) {
-        keys[(static_cast<int64_t>(b) * C + chunk) * 2] = kr[0];
-        keys[(static_cast<int64_t>(b) * C + chunk) * 2 + 1] = kt[0];
+        if (kr[0] != kKeyNone) atomicMax(reinterpret_cast<unsigned long long*>(keys + 2 * b), kr[0]);
+        atomicMax(reinterpret_cast<unsigned long long*>(keys + 2 * b + 1), kt[0]);
     }
 }
 
-// Thread per block: the chunk keys in order -> the next token (the residual
-// draw, or the target draw when no entry of the residual is positive).
+// Thread per block: the next token from the two keys (the residual draw, or
+// the target draw when no entry of the residual is positive).
 __global__ __launch_bounds__(256) void k_v_final(const uint64_t* __restrict__ keys,
-                                                 const int32_t* __restrict__ mode, int B, int C,
+                                                 const int32_t* __restrict__ mode, int B,
                                                  int32_t* __restrict__ next_token) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
     const int md = mode[b];
     if (md != kModeResidual && md != kModeTarget) return;
-    uint64_t kr = kKeyNone, kt = kKeyNone;
-    for (int c = 0; c < C; ++c) {
-        const uint64_t a = keys[(static_cast<int64_t>(b) * C + c) * 2];
-        const uint64_t t = keys[(static_cast<int64_t>(b) * C + c) * 2 + 1];
-        kr = a > kr ? a : kr;
-        kt = t > kt ? t : kt;
-    }
+    const uint64_t kr = keys[2 * b], kt = keys[2 * b + 1];
     const uint64_t k = (md == kModeResidual && kr != kKeyNone) ? kr : kt;
     next_token[b] = static_cast<int32_t>(key_index(k));
 }
@@ -468,12 +558,21 @@ static hipError_t launch_verify_t(const VerifyArgs& va) {
     const uint32_t ctr3 = static_cast<uint32_t>(va.offset);
     const int B = D.B, V = D.V, r = D.r, g = D.gamma;
 
-    hipLaunchKernelGGL((k_vt_stats<T>), dim3(B * (g + 1)), dim3(256), 0, st, Tl, va.temperature, V, g,
-                       lse_t, amax);
-    hipLaunchKernelGGL((k_v_decide<T>), dim3((B + 255) / 256), dim3(256), 0, st, Tl,
-                       static_cast<const T*>(va.W1), va.anchor, va.tokens, va.logp, va.survival,
-                       va.temperature, lse_t, amax, V, r, g, B, va.threshold, key0, key1, ctr3, bad,
-                       mode, jpos, invT, ebf, ef, va.n_keep, va.n_accept, va.next_token, va.accept_prob);
+    float* tmx = reinterpret_cast<float*>(ws + L.tmx);
+    float* tsm = reinterpret_cast<float*>(ws + L.tsm);
+    uint64_t* tkey = reinterpret_cast<uint64_t*>(ws + L.tkey);
+    // 16-byte loads for bf16 rows (V % 8 == 0 keeps every row 16-byte aligned)
+    const bool vec = sizeof(T) == 2 && V % 8 == 0 && (reinterpret_cast<uintptr_t>(Tl) & 15) == 0;
+    if (vec)
+        hipLaunchKernelGGL((k_vt_stats<T, true>), dim3(B * (g + 1), L.CT), dim3(256), 0, st, Tl, va.temperature,
+                           V, g, L.CT, tmx, tsm, tkey);
+    else
+        hipLaunchKernelGGL((k_vt_stats<T, false>), dim3(B * (g + 1), L.CT), dim3(256), 0, st, Tl, va.temperature,
+                           V, g, L.CT, tmx, tsm, tkey);
+    hipLaunchKernelGGL((k_v_decide<T>), dim3(B), dim3(64), 0, st, Tl, static_cast<const T*>(va.W1),
+                       va.anchor, va.tokens, va.logp, va.survival, va.temperature, tmx, tsm, tkey, L.CT,
+                       V, r, g, va.threshold, key0, key1, ctr3, lse_t, amax, keys, bad, mode, jpos, invT, ebf,
+                       ef, va.n_keep, va.n_accept, va.next_token, va.accept_prob);
     if (L.Bpad > B) {
         // padding E rows of the last 16-block unit (read by the MFMA, never used)
         hipLaunchKernelGGL(k_v_zero_u16, dim3(1), dim3(256), 0, st, ebf + static_cast<size_t>(B) * r,
@@ -500,9 +599,13 @@ static hipError_t launch_verify_t(const VerifyArgs& va) {
     }
     if ((pe = profile_end(st)) != hipSuccess) return pe;
     hipLaunchKernelGGL(k_v_lse, dim3(B), dim3(64), 0, st, pmx, psm, L.P, lse_d);
-    hipLaunchKernelGGL((k_v_sample<T>), dim3(L.C, B), dim3(256), 0, st, Tl, zd, lse_t, lse_d, mode, jpos, invT, V,
-                       g, L.C, key0, key1, ctr3, keys);
-    hipLaunchKernelGGL(k_v_final, dim3((B + 255) / 256), dim3(256), 0, st, keys, mode, B, L.C, va.next_token);
+    if (vec)
+        hipLaunchKernelGGL((k_v_sample<T, true>), dim3(L.C, B), dim3(256), 0, st, Tl, zd, lse_t, lse_d, mode, jpos,
+                           invT, V, g, key0, key1, ctr3, keys);
+    else
+        hipLaunchKernelGGL((k_v_sample<T, false>), dim3(L.C, B), dim3(256), 0, st, Tl, zd, lse_t, lse_d, mode, jpos,
+                           invT, V, g, key0, key1, ctr3, keys);
+    hipLaunchKernelGGL(k_v_final, dim3((B + 255) / 256), dim3(256), 0, st, keys, mode, B, va.next_token);
     return hipGetLastError();
 }
 

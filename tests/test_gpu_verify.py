@@ -158,3 +158,15 @@ def test_qwen3_4b_shape_every_block(ops):
     note("case: verify qwen3-4b-shaped V151936 r256 B32")
     ref = check(inp, target, run(ops, inp, target, 0.0), 0.0, label="qwen3-4b")
     assert (ref["accept"] < ref["keep"]).any() and (ref["accept"] > 0).any()
+
+
+def test_longest_block(ops):
+    # gamma = 64: every lane of the decision wave holds a position, the
+    # bonus row is the 65th; the target equals the base logits closely so
+    # long accepted runs occur
+    inp = small(V=520, r=32, gamma=64, B=6, seed=46, w1_std=0.05, w2_std=0.05,
+                temperature=[1.0] * 4 + [0.0] * 2)
+    target = make_target(inp, noise=0.05, seed=83)
+    note("case: verify gamma 64")
+    ref = check(inp, target, run(ops, inp, target, 0.0), 0.0, label="gamma 64")
+    assert ref["accept"].max() >= 8
