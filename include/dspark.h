@@ -241,6 +241,55 @@ dspark_status dspark_verify_block(const dspark_dims* dims, const void* U, const 
                                   int32_t* next_token, float* accept_prob, void* workspace,
                                   size_t workspace_bytes, void* hip_stream);
 
+/* ---- Host-side post-draft stages.  HOST pointers, no device work, no
+ * stream; results are deterministic. ---- */
+
+/* Sequential Temperature Scaling of the confidence head (dormouse page,
+ * section 1, the post-hoc calibration paragraph; bowenzhou page, "设计"):
+ * the survival of a (k+1)-token prefix is prod_{i<=k} c_i, and STS fits one
+ * temperature per position, left to right, by a 1-D grid search minimising
+ * the expected calibration error of that product with the earlier positions
+ * held at their fitted temperatures.  Position k's calibrated confidence is
+ * sigmoid(conf_logit / temperature[k]).
+ *   conf_logit [N, gamma] raw confidence logits a = w . [h; e] (Eq 7);
+ *   accepted [N] int32: accepted prefix length of each block (0..gamma), so
+ *     the outcome at position k is accepted > k;
+ *   grid [G] candidate temperatures (> 0); NULL uses 201 geometric points
+ *     from 0.05 to 20 (the middle one exactly 1); bins: equal-width ECE
+ *     bins over [0, 1] (<= 0 means 15);
+ *   temperature [gamma] out; ece_before / ece_after [gamma] (nullable): ECE
+ *     of the uncalibrated and the calibrated product at each position.
+ * The first grid point wins a tie.  EINVAL for a bad size or pointer or a
+ * non-positive grid entry. */
+dspark_status dspark_sts_calibrate(int32_t N, int32_t gamma, const float* conf_logit,
+                                   const int32_t* accepted, const float* grid, int32_t G,
+                                   int32_t bins, float* temperature, float* ece_before,
+                                   float* ece_after);
+
+/* Hardware-aware prefix scheduler (bowenzhou page, "设计"; Meridian page,
+ * section 3): choose each request's verified prefix length l_r in 0..gamma
+ * to maximise Theta = (R + sum_r sum_{k<l_r} survival[r,k]) * sps[B] with
+ * B = R + sum_r l_r tokens in the verification batch (each request also
+ * verifies its bonus position, which always yields one token).  Tokens are
+ * added in order of survival (ties: lower request first), each only as the
+ * next position of its request, and the best count is kept (the first on a
+ * tie); for survivals that do not increase along each request this is the
+ * exact optimum.  survival [R, gamma]; sps [T + 1] steps per second at a
+ * batch of t tokens, T >= R (gamma + 1); length [R] out; theta (nullable)
+ * out.  The engine's measured capacity (the production system estimates it
+ * two steps late) is the caller's sps table. */
+dspark_status dspark_schedule_prefixes(int32_t R, int32_t gamma, const float* survival,
+                                       const float* sps, int32_t T, int32_t* length,
+                                       float* theta);
+
+/* Depth planner for i.i.d. acceptance (Meridian page, section 6): the depth
+ * g in 0..gamma_max maximising tau(a, g) / (draft_us g + verify_fixed_us +
+ * verify_token_us g), tau(a, g) = (1 - a^(g+1)) / (1 - a) (1 + g at a = 1);
+ * the smallest g wins a tie.  a in [0, 1], costs >= 0 with a positive
+ * cycle cost; gamma_out and theta (nullable) out. */
+dspark_status dspark_plan_depth(float a, int32_t gamma_max, float draft_us, float verify_fixed_us,
+                                float verify_token_us, int32_t* gamma_out, float* theta);
+
 /* Synchronises `hip_stream`, then reads the per-block error flags the last
  * call with these dims left at the start of `workspace`: *code (HOST
  * pointer) = the number of blocks that met a token id outside [0, V) (0

@@ -65,6 +65,13 @@ def load() -> ctypes.CDLL:
     lib.dspark_block_loss_backward.restype = ctypes.c_int
     lib.dspark_verify_block.argtypes = [D] + [P] * 9 + [ctypes.c_float, U64, U64] + [P] * 5 + [SZ, P]
     lib.dspark_verify_block.restype = ctypes.c_int
+    F = ctypes.c_float
+    lib.dspark_sts_calibrate.argtypes = [I32, I32, P, P, P, I32, I32, P, P, P]
+    lib.dspark_sts_calibrate.restype = ctypes.c_int
+    lib.dspark_schedule_prefixes.argtypes = [I32, I32, P, P, I32, P, P]
+    lib.dspark_schedule_prefixes.restype = ctypes.c_int
+    lib.dspark_plan_depth.argtypes = [F, I32, F, F, F, P, P]
+    lib.dspark_plan_depth.restype = ctypes.c_int
     lib.dspark_read_device_error.argtypes = [D, P, ctypes.POINTER(I32), P]
     lib.dspark_read_device_error.restype = ctypes.c_int
     lib.dspark_set_option.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -175,6 +182,51 @@ def dspark_verify_block(dims, U, anchor, W1, W2, T_logits, tokens, logp, surviva
         ctypes.byref(dims), _p(U), _p(anchor), _p(W1), _p(W2), _p(T_logits), _p(tokens), _p(logp),
         _p(survival), _p(temperature), float(threshold), seed, offset, _p(n_keep), _p(n_accept),
         _p(next_token), _p(accept_prob), _p(workspace), nbytes, _stream(stream)))
+
+
+def _host(a, dtype):
+    import numpy as np
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def dspark_sts_calibrate(conf_logit, accepted, grid=None, bins: int = 15):
+    """HOST arrays: conf_logit [N, gamma], accepted [N]; returns (temperature,
+    ece_before, ece_after) as float32 numpy arrays of length gamma."""
+    import numpy as np
+    a = _host(conf_logit, np.float32)
+    acc = _host(accepted, np.int32)
+    N, gamma = a.shape
+    g = None if grid is None else _host(grid, np.float32)
+    t = np.zeros(gamma, np.float32)
+    eb = np.zeros(gamma, np.float32)
+    ea = np.zeros(gamma, np.float32)
+    _check(load().dspark_sts_calibrate(N, gamma, a.ctypes.data, acc.ctypes.data,
+                                       None if g is None else g.ctypes.data,
+                                       0 if g is None else len(g), bins, t.ctypes.data,
+                                       eb.ctypes.data, ea.ctypes.data))
+    return t, eb, ea
+
+
+def dspark_schedule_prefixes(survival, sps):
+    """HOST arrays: survival [R, gamma], sps [T + 1]; returns (length [R], theta)."""
+    import numpy as np
+    s = _host(survival, np.float32)
+    sp = _host(sps, np.float32)
+    R, gamma = s.shape
+    length = np.zeros(R, np.int32)
+    th = ctypes.c_float(0)
+    _check(load().dspark_schedule_prefixes(R, gamma, s.ctypes.data, sp.ctypes.data, len(sp) - 1,
+                                           length.ctypes.data, ctypes.addressof(th)))
+    return length, th.value
+
+
+def dspark_plan_depth(a, gamma_max, draft_us, verify_fixed_us, verify_token_us):
+    """Returns (depth, theta)."""
+    g = ctypes.c_int32(0)
+    th = ctypes.c_float(0)
+    _check(load().dspark_plan_depth(a, gamma_max, draft_us, verify_fixed_us, verify_token_us,
+                                    ctypes.addressof(g), ctypes.addressof(th)))
+    return g.value, th.value
 
 
 def dspark_read_device_error(dims, workspace, stream=None) -> int:

@@ -28,11 +28,12 @@ def hipcc() -> str:
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip into libdspark.so (always recompiles)."""
+    """Compile every csrc/*.hip (and the host-only csrc/*.cpp) into libdspark.so
+    (always recompiles)."""
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc()] + HIPCC_FLAGS + sources() + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -274,6 +274,60 @@ dspark_status dspark_verify_block(const dspark_dims* dims, const void* U, const 
     return ok();
 }
 
+dspark_status dspark_sts_calibrate(int32_t N, int32_t gamma, const float* conf_logit,
+                                   const int32_t* accepted, const float* grid, int32_t G,
+                                   int32_t bins, float* temperature, float* ece_before,
+                                   float* ece_after) {
+    if (N < 1 || gamma < 1) return fail(DSPARK_EINVAL, "N = %d, gamma = %d: both must be >= 1", N, gamma);
+    if (!conf_logit || !accepted || !temperature)
+        return fail(DSPARK_EINVAL, "conf_logit, accepted and temperature must not be NULL");
+    std::vector<double> g;
+    if (grid) {
+        if (G < 1) return fail(DSPARK_EINVAL, "grid has %d entries", G);
+        for (int i = 0; i < G; ++i) {
+            if (!(grid[i] > 0.0f)) return fail(DSPARK_EINVAL, "grid[%d] = %g is not positive", i, grid[i]);
+            g.push_back(static_cast<double>(grid[i]));
+        }
+    } else {
+        g = dspark::sts_default_grid();
+    }
+    for (int n = 0; n < N; ++n)
+        if (accepted[n] < 0 || accepted[n] > gamma)
+            return fail(DSPARK_EINVAL, "accepted[%d] = %d is outside 0..gamma", n, accepted[n]);
+    dspark::sts_calibrate(N, gamma, conf_logit, accepted, g, bins > 0 ? bins : 15, temperature, ece_before,
+                          ece_after);
+    return ok();
+}
+
+dspark_status dspark_schedule_prefixes(int32_t R, int32_t gamma, const float* survival,
+                                       const float* sps, int32_t T, int32_t* length,
+                                       float* theta) {
+    if (R < 1 || gamma < 0) return fail(DSPARK_EINVAL, "R = %d, gamma = %d", R, gamma);
+    if ((gamma > 0 && !survival) || !sps || !length)
+        return fail(DSPARK_EINVAL, "survival, sps and length must not be NULL");
+    if (static_cast<int64_t>(T) < static_cast<int64_t>(R) * (gamma + 1))
+        return fail(DSPARK_EINVAL, "sps covers %d tokens, a full batch is %lld", T,
+                    static_cast<long long>(R) * (gamma + 1));
+    const double t = dspark::schedule_prefixes(R, gamma, survival, sps, length);
+    if (theta) *theta = static_cast<float>(t);
+    return ok();
+}
+
+dspark_status dspark_plan_depth(float a, int32_t gamma_max, float draft_us, float verify_fixed_us,
+                                float verify_token_us, int32_t* gamma_out, float* theta) {
+    if (!(a >= 0.0f && a <= 1.0f)) return fail(DSPARK_EINVAL, "a = %g is outside [0, 1]", a);
+    if (gamma_max < 0 || !gamma_out) return fail(DSPARK_EINVAL, "gamma_max < 0 or gamma_out is NULL");
+    if (!(draft_us >= 0.0f) || !(verify_fixed_us >= 0.0f) || !(verify_token_us >= 0.0f) ||
+        !(verify_fixed_us > 0.0f || (gamma_max > 0 && draft_us + verify_token_us > 0.0f)))
+        return fail(DSPARK_EINVAL, "costs must be >= 0 with a positive cycle cost");
+    if (!(verify_fixed_us > 0.0f))
+        return fail(DSPARK_EINVAL, "verify_fixed_us must be positive (the g = 0 cycle)");
+    double t = 0.0;
+    *gamma_out = dspark::plan_depth(a, gamma_max, draft_us, verify_fixed_us, verify_token_us, &t);
+    if (theta) *theta = static_cast<float>(t);
+    return ok();
+}
+
 dspark_status dspark_read_device_error(const dspark_dims* dims, const void* workspace,
                                        int32_t* code, void* hip_stream) {
     dspark_status s = check_dims(dims);

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/dspark.h"
 
 namespace dspark {
@@ -172,6 +174,15 @@ struct DraftArgs {
 
 // Enqueue the whole draft call.  Returns hipSuccess or the first launch error.
 hipError_t launch_draft(const DraftArgs& a);
+
+// Host-side post-draft stages (schedule.cpp).
+std::vector<double> sts_default_grid();
+void sts_calibrate(int N, int gamma, const float* logit, const int32_t* accepted,
+                   const std::vector<double>& grid, int bins, float* temperature, float* ece_before,
+                   float* ece_after);
+double schedule_prefixes(int R, int gamma, const float* survival, const float* sps, int32_t* length);
+int plan_depth(double a, int gamma_max, double draft_us, double verify_fixed_us,
+               double verify_token_us, double* theta);
 
 // Per-thread choice of drafting path (see dspark_set_option).
 int draft_path_option();
