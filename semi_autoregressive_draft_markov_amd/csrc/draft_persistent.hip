@@ -474,120 +474,106 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     stage_rows();
     UAhead ahead = fetch_u(0, 0);
 
-    for (int k = 0; k < a.gamma; ++k) {
-        for (int b = lane; b < a.B; b += 64) slot[wave * a.B + b] = pstats_empty();
-        // every wave runs all NB units (GROUPED stages rows between them);
-        // waves without columns skip the arithmetic
-        for (int nb = 0; nb < NB; ++nb) {
-            if (GROUPED && nb + 1 < NB) load_group(nb + 1);
-            // accumulators start from U (bf16 -> f32 is exact)
-            f32x4 acc[4], accx;
-            {
-                const uint32_t w[8] = {ahead.a[0], ahead.a[1], ahead.a[2], ahead.a[3],
-                                       ahead.b[0], ahead.b[1], ahead.b[2], ahead.b[3]};
+    // One unit: step kk, block group nb (16 blocks): accumulators from U,
+    // bias on the matrix cores, lane statistics, merged into this wave's
+    // slots.  The U of the next unit is fetched here.
+    auto run_unit = [&](int kk, int nb) {
+        // accumulators start from U (bf16 -> f32 is exact)
+        f32x4 acc[4], accx;
+        {
+            const uint32_t w[8] = {ahead.a[0], ahead.a[1], ahead.a[2], ahead.a[3],
+                                   ahead.b[0], ahead.b[1], ahead.b[2], ahead.b[3]};
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int j = 4 * q + c;
-                        acc[c][q] = (j & 1) ? hi_bf16(w[j >> 1]) : lo_bf16(w[j >> 1]);
-                    }
-                accx = f32x4{lo_bf16(ahead.x.x), hi_bf16(ahead.x.x), lo_bf16(ahead.x.y), hi_bf16(ahead.x.y)};
-            }
-            if (nb + 1 < NB)
-                ahead = fetch_u(k, nb + 1);
-            else if (k + 1 < a.gamma)
-                ahead = fetch_u(k + 1, 0);
-            const int b = nb * 16 + n;
-            const uint16_t* erow = GROUPED ? &Es[((nb & 1) * 16 + n) * ldE + 8 * g] : &Es[b * ldE + 8 * g];
-            // (has_x implies has_reg: the fragment columns start past all tiles)
-            if (has_x)
-                unit_mul<KC, true, true>(w2, xf, erow, lane, acc, accx);
-            else if (has_reg)
-                unit_mul<KC, true, false>(w2, xf, erow, lane, acc, accx);
-            PStats st = pstats_empty();
-            if (active && b < a.B) {
-                const float temp = temp_s[b];
-                const bool sampling = temp > 0.0f;
-                const float scale = sampling ? kLog2e / temp : kLog2e;
-                // the lane's 16 register-tile columns and 4 LDS-fragment
-                // columns; columns past V (V % 8 == 0) and absent parts hold -inf
-                const bool reg_hi = reg_live && v0 + 16 <= a.V;
-                float z[20];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const bool ok = q < 2 ? reg_live : reg_hi;
-                        z[4 * q + c] = ok ? acc[c][q] : -INFINITY;
-                    }
-#pragma unroll
-                for (int c = 0; c < 4; ++c) z[16 + c] = x_live ? accx[c] : -INFINITY;
-                if (sampling) {
-                    float gs[20];
-                    if (AHEAD) {
-                        const float* gnu = gn + nb * 16 * kNoiseStride;
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) gs[j] = gnu[kNoiseStride * j];
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) gs[16 + c] = nb == 0 ? nx0[c] : nx1[c];
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < 5; ++q) {
-                            const int cq = q < 4 ? v0 + 4 * q : vx;
-                            const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(cq) >> 2,
-                                                                static_cast<uint32_t>(k), static_cast<uint32_t>(b),
-                                                                a.ctr3},
-                                                          a.key0, a.key1);
-#pragma unroll
-                            for (int c = 0; c < 4; ++c) gs[4 * q + c] = log2_of_neg_log2_uniform(w[c]);
-                        }
-                    }
-                    st = unit_stats<true>(z, gs, v0, vx, scale);
-                } else {
-                    float gs[20];
-#pragma unroll
-                    for (int j = 0; j < 20; ++j) gs[j] = 0.0f;
-                    st = unit_stats<false>(z, gs, v0, vx, scale);
+                for (int c = 0; c < 4; ++c) {
+                    const int j = 4 * q + c;
+                    acc[c][q] = (j & 1) ? hi_bf16(w[j >> 1]) : lo_bf16(w[j >> 1]);
                 }
-            }
-            st = pstats_merge(st, shfl_xor_pstats(st, 16));
-            st = pstats_merge(st, shfl_xor_pstats(st, 32));
-            if (g == 0 && b < a.B) slot[wave * a.B + b] = pstats_merge(slot[wave * a.B + b], st);
-            if (GROUPED && nb + 1 < NB) {
-                store_group(nb + 1);
-                __syncthreads();
+            accx = f32x4{lo_bf16(ahead.x.x), hi_bf16(ahead.x.x), lo_bf16(ahead.x.y), hi_bf16(ahead.x.y)};
+        }
+        if (nb + 1 < NB)
+            ahead = fetch_u(kk, nb + 1);
+        else if (kk + 1 < a.gamma)
+            ahead = fetch_u(kk + 1, 0);
+        const int b = nb * 16 + n;
+        const uint16_t* erow = GROUPED ? &Es[((nb & 1) * 16 + n) * ldE + 8 * g] : &Es[b * ldE + 8 * g];
+        // (has_x implies has_reg: the fragment columns start past all tiles)
+        if (has_x)
+            unit_mul<KC, true, true>(w2, xf, erow, lane, acc, accx);
+        else if (has_reg)
+            unit_mul<KC, true, false>(w2, xf, erow, lane, acc, accx);
+        PStats st = pstats_empty();
+        if (active && b < a.B) {
+            const float temp = temp_s[b];
+            const bool sampling = temp > 0.0f;
+            const float scale = sampling ? kLog2e / temp : kLog2e;
+            // the lane's 16 register-tile columns and 4 LDS-fragment
+            // columns; columns past V (V % 8 == 0) and absent parts hold -inf
+            const bool reg_hi = reg_live && v0 + 16 <= a.V;
+            float z[20];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const bool ok = q < 2 ? reg_live : reg_hi;
+                    z[4 * q + c] = ok ? acc[c][q] : -INFINITY;
+                }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) z[16 + c] = x_live ? accx[c] : -INFINITY;
+            if (sampling) {
+                float gs[20];
+                if (AHEAD) {
+                    const float* gnu = gn + nb * 16 * kNoiseStride;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) gs[j] = gnu[kNoiseStride * j];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) gs[16 + c] = nb == 0 ? nx0[c] : nx1[c];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 5; ++q) {
+                        const int cq = q < 4 ? v0 + 4 * q : vx;
+                        const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(cq) >> 2,
+                                                            static_cast<uint32_t>(kk), static_cast<uint32_t>(b),
+                                                            a.ctr3},
+                                                      a.key0, a.key1);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) gs[4 * q + c] = log2_of_neg_log2_uniform(w[c]);
+                    }
+                }
+                st = unit_stats<true>(z, gs, v0, vx, scale);
+            } else {
+                float gs[20];
+#pragma unroll
+                for (int j = 0; j < 20; ++j) gs[j] = 0.0f;
+                st = unit_stats<false>(z, gs, v0, vx, scale);
             }
         }
+        st = pstats_merge(st, shfl_xor_pstats(st, 16));
+        st = pstats_merge(st, shfl_xor_pstats(st, 32));
+        if (g == 0 && b < a.B) slot[wave * a.B + b] = pstats_merge(slot[wave * a.B + b], st);
+    };
+    // Workgroup merge of blocks [b0, b1) in wave order, then publish: the
+    // argmax key atomics and the softmax partials (read after the kernel).
+    auto publish = [&](int kk, int b0, int b1) {
         __syncthreads();
-        // workgroup merge in wave order, then publish
-        for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
+        for (int b = b0 + static_cast<int>(threadIdx.x); b < b1; b += blockDim.x) {
             PStats t = slot[b];
 #pragma unroll
             for (int w = 1; w < kPWaves; ++w) t = pstats_merge(t, slot[w * a.B + b]);
             if (t.key != kKeyNone)
-                __hip_atomic_fetch_max(&a.best[((static_cast<size_t>(k) * a.B + b) * kDraftKeyCopies +
+                __hip_atomic_fetch_max(&a.best[((static_cast<size_t>(kk) * a.B + b) * kDraftKeyCopies +
                                                 wg % kDraftKeyCopies) * kKeyStride],
                                        t.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // softmax partials are read after the kernel (k_persist_finish)
-            const size_t o = (static_cast<size_t>(k) * a.B + b) * nWG + partial_slot(wg, nWG);
+            const size_t o = (static_cast<size_t>(kk) * a.B + b) * nWG + partial_slot(wg, nWG);
             a.pms[o] = make_float2(t.m, t.s);
         }
-        if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
-        // next step's noise of group 0 while the key atomics complete, the
-        // release fence and workgroup barrier, the arrival, group 1's noise
-        // while the arrival is in flight, then the wait for the release
-        noise_ahead(k + 1, 0);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __syncthreads();
-        const uint32_t before = barrier_arrive(a.bar, static_cast<uint32_t>(wg));
-        noise_ahead(k + 1, 1);
-        barrier_finish(a.bar, before, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG),
-                       static_cast<uint32_t>(wg));
-        // x_k of every block from the keys -> the E rows of step k+1: the
-        // copies of a block's key sit in 8 consecutive lanes
-        for (int t = threadIdx.x; t < a.B * kDraftKeyCopies; t += blockDim.x) {
-            uint64_t key = get_shared(&a.best[(static_cast<size_t>(k) * a.B * kDraftKeyCopies + t) * kKeyStride]);
+    };
+    // x_kk of blocks [b0, b1) from the keys: the copies of a block's key sit
+    // in 8 consecutive lanes (b0 is a multiple of 16)
+    auto read_keys = [&](int kk, int b0, int b1) {
+        for (int t = b0 * kDraftKeyCopies + static_cast<int>(threadIdx.x); t < b1 * kDraftKeyCopies; t += blockDim.x) {
+            uint64_t key = get_shared(&a.best[(static_cast<size_t>(kk) * a.B * kDraftKeyCopies + t) * kKeyStride]);
 #pragma unroll
             for (int o = 1; o < kDraftKeyCopies; o <<= 1) {
                 const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o);
@@ -600,6 +586,33 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
                 prev[t / kDraftKeyCopies] = (key != kKeyNone && x < static_cast<uint32_t>(a.V)) ? static_cast<int>(x) : 0;
         }
         __syncthreads();
+    };
+
+    for (int k = 0; k < a.gamma; ++k) {
+        for (int b = lane; b < a.B; b += 64) slot[wave * a.B + b] = pstats_empty();
+        // every wave runs all NB units (GROUPED stages rows between them);
+        // waves without columns skip the arithmetic
+        for (int nb = 0; nb < NB; ++nb) {
+            if (GROUPED && nb + 1 < NB) load_group(nb + 1);
+            run_unit(k, nb);
+            if (GROUPED && nb + 1 < NB) {
+                store_group(nb + 1);
+                __syncthreads();
+            }
+        }
+        publish(k, 0, a.B);
+        if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
+        // next step's noise of group 0 while the key atomics complete, the
+        // release fence and workgroup barrier, the arrival, group 1's noise
+        // while the arrival is in flight, then the wait for the release
+        noise_ahead(k + 1, 0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        const uint32_t before = barrier_arrive(a.bar, static_cast<uint32_t>(wg));
+        noise_ahead(k + 1, 1);
+        barrier_finish(a.bar, before, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG),
+                       static_cast<uint32_t>(wg));
+        read_keys(k, 0, a.B);
         if (AHEAD)
             stage_rows_ahead();
         else

@@ -72,6 +72,17 @@ def test_bf16_matrix_core_ragged_mixed_temperature(ops, path):
     check_draft(inp, g, 11, 5, label="bf16 mfma ragged")
 
 
+@pytest.mark.parametrize("gamma", [1, 2, 3])
+def test_single_launch_short_blocks(ops, gamma):
+    # the first and last steps of the single-launch loop (no grid barrier at
+    # gamma = 1, one at gamma = 2) with two 16-block groups
+    inp = small(V=1000, r=64, d=48, gamma=gamma, B=21, seed=30 + gamma,
+                temperature=[1.0] * 15 + [0.0] * 6)
+    note("case: bf16 single-launch short blocks gamma %d" % gamma)
+    g = run_gpu(ops, inp, seed=6, offset=2, path=SINGLE)
+    check_draft(inp, g, 6, 2, label="short blocks gamma %d" % gamma)
+
+
 @pytest.mark.parametrize("path", [MULTI, SINGLE])
 @pytest.mark.parametrize("B", [1, 33])
 def test_bf16_rank256_tail_columns(ops, B, path):
