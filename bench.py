@@ -311,6 +311,10 @@ def main() -> int:
                          "extra measurements of the same kernels at the other shapes")
     ap.add_argument("--launch", default="plain", choices=["plain", "cooperative"],
                     help="how the single-launch drafting kernel is started (same kernel and grid)")
+    ap.add_argument("--flush", action="store_true",
+                    help="write a 1 GiB buffer before every timed drafting call (untimed) so that "
+                         "W2 and U come from HBM, not from the 256 MB memory-side cache; the "
+                         "value is then B*gamma*steps over the summed per-call event times")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the benchmark, run a plain device copy of 1 GiB "
                          "(reference for HBM byte counters)")
@@ -364,11 +368,23 @@ def main() -> int:
     binding.dspark_profile_enable(True)
     binding.dspark_profile_read()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    if args.flush:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            scratch.zero_()
+            evs[i][0].record(stream)
+            step(args.warmup + i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        elapsed = sum(a.elapsed_time(b) for a, b in evs) * 1e-3
+    else:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     kernel_ms, launches = binding.dspark_profile_read()
     binding.dspark_profile_enable(False)
     per_call = launches // args.steps
@@ -409,7 +425,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": names[args.workload],
                    "V": V, "r": r, "d": d, "gamma": gamma, "B": B,
-                   "head": inp.head, "parallelism": "single-gpu"},
+                   "head": inp.head, "parallelism": "single-gpu",
+                   **({"caches": "flushed before every call"} if args.flush else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic if args.workload == "qwen3-4b" else None,
