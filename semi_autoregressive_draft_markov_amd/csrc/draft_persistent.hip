@@ -196,6 +196,7 @@ __device__ __forceinline__ void unit_mul(const W2Tile<KC>& w2, const uint32_t* x
         if (XW) xv[slot] = *reinterpret_cast<const u32x4*>(&xf[(kc * kWave + lane) * 4]);
     };
     fetch(0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, XW ? 2 : 1, 0);
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
         const int cur = kc & 1;
@@ -210,6 +211,10 @@ __device__ __forceinline__ void unit_mul(const W2Tile<KC>& w2, const uint32_t* x
             }
         }
         if (XW) accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[cur]), bop, accx, 0, 0, 0);
+        // keep the order: the next chunk's LDS reads, then this chunk's
+        // products (the reads then have the products' duration to land)
+        if (kc + 1 < KC) __builtin_amdgcn_sched_group_barrier(0x100, XW ? 2 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, (REG ? 4 : 0) + (XW ? 1 : 0), 0);
     }
 }
 
@@ -274,6 +279,43 @@ __device__ __forceinline__ PStats unit_stats(const float (&z)[20], const float (
     return PStats{m, s, argmax_key(ybest, static_cast<uint32_t>(c))};
 }
 
+// The same statistics when the Gumbel terms are precomputed (g = 0 for a
+// greedy block, so that y = z2 - g covers both cases without a branch), for
+// the 20 accumulator values of a lane (absent columns already -inf).  The
+// softmax reference is the lane's largest perturbed value ybest instead of
+// the largest z2: z2 - ybest <= g <= log2(24) for every column, so no term
+// of the sum overflows, and the largest term is at least 2^-24, so none of
+// the mass is lost.  This saves the second maximum and keeps the code
+// branch-free.
+__device__ __forceinline__ PStats unit_stats_pre(const f32x4 (&acc)[4], const f32x4& accx, const float* gnu,
+                                                 const float (&nx)[4], float scale, int v0, int vx) {
+    float z[20], y[20];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            z[4 * q + c] = acc[c][q];
+            y[4 * q + c] = fmaf(acc[c][q], scale, -gnu[kNoiseStride * (4 * q + c)]);
+        }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        z[16 + c] = accx[c];
+        y[16 + c] = fmaf(accx[c], scale, -nx[c]);
+    }
+    float ybest = y[0];
+#pragma unroll
+    for (int j = 1; j < 20; ++j) ybest = fmaxf(ybest, y[j]);
+    int idx = 19;
+#pragma unroll
+    for (int j = 18; j >= 0; --j) idx = (y[j] == ybest) ? j : idx;
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 20; ++j) s += __builtin_amdgcn_exp2f(fmaf(z[j], scale, -ybest));
+    const int c = idx < 16 ? v0 + idx : vx + (idx - 16);
+    if (ybest == -INFINITY) return pstats_empty();  // no column of this lane exists
+    return PStats{ybest, s, argmax_key(ybest, static_cast<uint32_t>(c))};
+}
+
 // U values of one unit, loaded one unit ahead of use: 16 columns of the
 // register tile (two 16-byte loads) and the 4 columns of the LDS fragment.
 // They become the initial MFMA accumulators, so z = U + E W2 comes out of
@@ -326,7 +368,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     const size_t bp4 = align_up(static_cast<size_t>(a.Bpad) * 4, 16);
     uint16_t* Es = reinterpret_cast<uint16_t*>(smem + persist_xfrag_bytes<KC>());
     int32_t* prev = reinterpret_cast<int32_t*>(smem + persist_xfrag_bytes<KC>() + e_bytes);
-    float* temp_s = reinterpret_cast<float*>(smem + persist_xfrag_bytes<KC>() + e_bytes + bp4);
+    // per block: log2(e) / T when the block samples (T > 0), -log2(e) when greedy
+    float* scale_s = reinterpret_cast<float*>(smem + persist_xfrag_bytes<KC>() + e_bytes + bp4);
     PStats* slot = reinterpret_cast<PStats*>(smem + persist_xfrag_bytes<KC>() + e_bytes + 2 * bp4);
     float* gn = reinterpret_cast<float*>(smem + persist_xfrag_bytes<KC>() + e_bytes + 2 * bp4 +
                                          align_up(sizeof(PStats) * kPWaves * static_cast<size_t>(a.B), 16)) +
@@ -348,12 +391,11 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     const bool reg_live = v0 < a.V, x_live = vx < a.V;
 
     const bool active = has_reg || has_x;
-    // AHEAD: Gumbel terms of block group nb at step kk, whether or not the
-    // block samples (the unit only reads them when it does): the 16
-    // register-tile columns into LDS, the 4 LDS-fragment columns into
-    // registers (nx0 / nx1)
+    // AHEAD: Gumbel terms of block group nb at step kk (zero when the
+    // block is greedy, on = false): the 16 register-tile columns into LDS,
+    // the 4 LDS-fragment columns into registers (nx0 / nx1)
     float nx0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, nx1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto noise_ahead = [&](int kk, int nb) {
+    auto noise_ahead = [&](int kk, int nb, bool on) {
         const int b = nb * 16 + n;
         if (!AHEAD || b >= a.B) return;
         if (reg_live) {
@@ -364,7 +406,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
                                                     static_cast<uint32_t>(b), a.ctr3},
                                               a.key0, a.key1);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) dst[kNoiseStride * (4 * q + c)] = log2_of_neg_log2_uniform(w[c]);
+                for (int c = 0; c < 4; ++c) dst[kNoiseStride * (4 * q + c)] = on ? log2_of_neg_log2_uniform(w[c]) : 0.0f;
             }
         }
         if (x_live) {
@@ -373,7 +415,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
                                           a.key0, a.key1);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float gx = log2_of_neg_log2_uniform(w[c]);
+                const float gx = on ? log2_of_neg_log2_uniform(w[c]) : 0.0f;
                 if (nb == 0)
                     nx0[c] = gx;
                 else
@@ -384,15 +426,17 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
 
     W2Tile<KC> w2;
     if (has_reg) w2.load(a.W2, a.V, wv * 64, g, n);
-    noise_ahead(0, 0);  // while the tile loads are in flight
-    noise_ahead(0, 1);
+    // while the tile loads are in flight
+    noise_ahead(0, 0, AHEAD && n < a.B && a.temperature[n] > 0.0f);
+    noise_ahead(0, 1, AHEAD && 16 + n < a.B && a.temperature[16 + n] > 0.0f);
     load_xfrags<KC>(a.W2, a.V, kPWaves * nWG * 64 + 16 * kPWaves * wg, reinterpret_cast<uint32_t*>(smem));
     // previous tokens of step 0: the anchors (an out-of-range anchor reads
     // row 0; the finish kernel marks its block invalid)
     for (int b = threadIdx.x; b < a.Bpad; b += blockDim.x) {
         const int x = b < a.B ? a.anchor[b] : 0;
         prev[b] = (x >= 0 && x < a.V) ? x : 0;
-        temp_s[b] = b < a.B ? a.temperature[b] : 0.0f;
+        const float t = b < a.B ? a.temperature[b] : 0.0f;
+        scale_s[b] = t > 0.0f ? kLog2e / t : -kLog2e;
     }
     __syncthreads();
     // E rows W1[prev[b]] of the coming step: all rows (or, GROUPED, the
@@ -471,40 +515,38 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     stage_rows();
     UAhead ahead = fetch_u(0, 0);
 
-    // One unit: step kk, block group nb (16 blocks): accumulators from U,
-    // bias on the matrix cores, lane statistics, merged into this wave's
-    // slots.  The U of the next unit is fetched here.
-    auto run_unit = [&](int kk, int nb) {
-        // accumulators start from U (bf16 -> f32 is exact)
-        f32x4 acc[4], accx;
-        {
-            const uint32_t w[8] = {ahead.a[0], ahead.a[1], ahead.a[2], ahead.a[3],
-                                   ahead.b[0], ahead.b[1], ahead.b[2], ahead.b[3]};
+    // accumulators start from U (bf16 -> f32 is exact)
+    auto acc_from = [&](const UAhead& u, f32x4 (&acc)[4], f32x4& accx) {
+        const uint32_t w[8] = {u.a[0], u.a[1], u.a[2], u.a[3], u.b[0], u.b[1], u.b[2], u.b[3]};
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int j = 4 * q + c;
-                    acc[c][q] = (j & 1) ? hi_bf16(w[j >> 1]) : lo_bf16(w[j >> 1]);
-                }
-            accx = f32x4{lo_bf16(ahead.x.x), hi_bf16(ahead.x.x), lo_bf16(ahead.x.y), hi_bf16(ahead.x.y)};
-        }
-        if (nb + 1 < NB)
-            ahead = fetch_u(kk, nb + 1);
-        else if (kk + 1 < a.gamma)
-            ahead = fetch_u(kk + 1, 0);
-        const int b = nb * 16 + n;
-        const uint16_t* erow = GROUPED ? &Es[((nb & 1) * 16 + n) * ldE + 8 * g] : &Es[b * ldE + 8 * g];
-        // (has_x implies has_reg: the fragment columns start past all tiles)
+            for (int c = 0; c < 4; ++c) {
+                const int j = 4 * q + c;
+                acc[c][q] = (j & 1) ? hi_bf16(w[j >> 1]) : lo_bf16(w[j >> 1]);
+            }
+        accx = f32x4{lo_bf16(u.x.x), hi_bf16(u.x.x), lo_bf16(u.x.y), hi_bf16(u.x.y)};
+    };
+    auto erow_of = [&](int nb) -> const uint16_t* {
+        return GROUPED ? &Es[((nb & 1) * 16 + n) * ldE + 8 * g] : &Es[(nb * 16 + n) * ldE + 8 * g];
+    };
+    // bias of one unit on the matrix cores, for whichever column parts the
+    // wave has (has_x implies has_reg: the fragment columns start past all
+    // tiles)
+    auto mul_any = [&](int nb, f32x4 (&acc)[4], f32x4& accx) {
         if (has_x)
-            unit_mul<KC, true, true>(w2, xf, erow, lane, acc, accx);
+            unit_mul<KC, true, true>(w2, xf, erow_of(nb), lane, acc, accx);
         else if (has_reg)
-            unit_mul<KC, true, false>(w2, xf, erow, lane, acc, accx);
+            unit_mul<KC, true, false>(w2, xf, erow_of(nb), lane, acc, accx);
+    };
+    // lane statistics of a unit for any wave: absent columns hold -inf
+    auto any_stats = [&](int kk, int nb, const f32x4 (&acc)[4], const f32x4& accx) {
+        const int b = nb * 16 + n;
         PStats st = pstats_empty();
         if (active && b < a.B) {
-            const float temp = temp_s[b];
-            const bool sampling = temp > 0.0f;
-            const float scale = sampling ? kLog2e / temp : kLog2e;
+            const float sc = scale_s[b];
+            const bool sampling = sc > 0.0f;
+            const float scale = fabsf(sc);
             // the lane's 16 register-tile columns and 4 LDS-fragment
             // columns; columns past V (V % 8 == 0) and absent parts hold -inf
             const bool reg_hi = reg_live && v0 + 16 <= a.V;
@@ -520,23 +562,14 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
             for (int c = 0; c < 4; ++c) z[16 + c] = x_live ? accx[c] : -INFINITY;
             if (sampling) {
                 float gs[20];
-                if (AHEAD) {
-                    const float* gnu = gn + nb * 16 * kNoiseStride;
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) gs[j] = gnu[kNoiseStride * j];
+                for (int q = 0; q < 5; ++q) {
+                    const int cq = q < 4 ? v0 + 4 * q : vx;
+                    const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(cq) >> 2, static_cast<uint32_t>(kk),
+                                                        static_cast<uint32_t>(b), a.ctr3},
+                                                  a.key0, a.key1);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) gs[16 + c] = nb == 0 ? nx0[c] : nx1[c];
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 5; ++q) {
-                        const int cq = q < 4 ? v0 + 4 * q : vx;
-                        const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(cq) >> 2,
-                                                            static_cast<uint32_t>(kk), static_cast<uint32_t>(b),
-                                                            a.ctr3},
-                                                      a.key0, a.key1);
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) gs[4 * q + c] = log2_of_neg_log2_uniform(w[c]);
-                    }
+                    for (int c = 0; c < 4; ++c) gs[4 * q + c] = log2_of_neg_log2_uniform(w[c]);
                 }
                 st = unit_stats<true>(z, gs, v0, vx, scale);
             } else {
@@ -546,9 +579,59 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
                 st = unit_stats<false>(z, gs, v0, vx, scale);
             }
         }
+        return st;
+    };
+    // the unit's statistics over the 4 lanes of each block row, into this
+    // wave's slots
+    auto to_slot = [&](PStats st, int nb) {
+        const int b = nb * 16 + n;
         st = pstats_merge(st, shfl_xor_pstats(st, 16));
         st = pstats_merge(st, shfl_xor_pstats(st, 32));
         if (g == 0 && b < a.B) slot[wave * a.B + b] = pstats_merge(slot[wave * a.B + b], st);
+    };
+
+    // wave-uniform: every column of the wave's register tile and LDS
+    // fragment exists
+    const bool full = has_x && c0 + 16 <= a.V;
+
+    // One unit: step kk, block group nb (16 blocks): accumulators from U,
+    // bias on the matrix cores, lane statistics, merged into this wave's
+    // slots.  The U of the next unit is fetched here.
+    auto run_unit = [&](int kk, int nb) {
+        f32x4 acc[4], accx;
+        acc_from(ahead, acc, accx);
+        if (nb + 1 < NB)
+            ahead = fetch_u(kk, nb + 1);
+        else if (kk + 1 < a.gamma)
+            ahead = fetch_u(kk + 1, 0);
+        mul_any(nb, acc, accx);
+        PStats st;
+        if (AHEAD) {
+            if (active) {
+                // (the noise reads stay after the products: hoisted into
+                // them they would hold registers the tile needs)
+                __builtin_amdgcn_sched_barrier(0);
+                if (!full) {
+                    // columns past V (V % 8 == 0) and absent parts: -inf
+                    const bool reg_hi = reg_live && v0 + 16 <= a.V;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            if (!(q < 2 ? reg_live : reg_hi)) acc[c][q] = -INFINITY;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (!x_live) accx[c] = -INFINITY;
+                }
+                st = unit_stats_pre(acc, accx, gn + nb * 16 * kNoiseStride, nb == 0 ? nx0 : nx1,
+                                    fabsf(scale_s[nb * 16 + n]), v0, vx);
+            } else {
+                st = pstats_empty();
+            }
+        } else {
+            st = any_stats(kk, nb, acc, accx);
+        }
+        to_slot(st, nb);
     };
     // Workgroup merge of blocks [b0, b1) in wave order, then publish: the
     // argmax key atomics and the softmax partials (read after the kernel).
@@ -587,8 +670,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
 
     for (int k = 0; k < a.gamma; ++k) {
         for (int b = lane; b < a.B; b += 64) slot[wave * a.B + b] = pstats_empty();
-        // every wave runs all NB units (GROUPED stages rows between them);
-        // waves without columns skip the arithmetic
+        // every wave runs all NB units (GROUPED stages rows between
+        // them); waves without columns skip the arithmetic
         for (int nb = 0; nb < NB; ++nb) {
             if (GROUPED && nb + 1 < NB) load_group(nb + 1);
             run_unit(k, nb);
@@ -599,14 +682,15 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         }
         publish(k, 0, a.B);
         if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
-        // next step's noise of group 0 while the key atomics complete, the
-        // release fence and workgroup barrier, the arrival, group 1's noise
-        // while the arrival is in flight, then the wait for the release
-        noise_ahead(k + 1, 0);
+        // next step's noise of group 0 while the key atomics complete,
+        // the release fence and workgroup barrier, the arrival, group
+        // 1's noise while the arrival is in flight, then the wait for
+        // the other workgroups
+        noise_ahead(k + 1, 0, scale_s[n] > 0.0f);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __syncthreads();
         barrier_arrive(a.bar, static_cast<uint32_t>(wg));
-        noise_ahead(k + 1, 1);
+        noise_ahead(k + 1, 1, 16 + n < a.B && scale_s[16 + n] > 0.0f);
         barrier_finish(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG));
         read_keys(k, 0, a.B);
         if (AHEAD)
