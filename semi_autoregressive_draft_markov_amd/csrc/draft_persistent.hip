@@ -398,21 +398,25 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     auto noise_ahead = [&](int kk, int nb, bool on) {
         const int b = nb * 16 + n;
         if (!AHEAD || b >= a.B) return;
+        // the counter words are opaque here, so that the compiler does not
+        // keep products of the first Philox round (which do not depend on
+        // the step) live across the whole loop
+        uint32_t cb = static_cast<uint32_t>(b), cv = static_cast<uint32_t>(v0) >> 2;
+        asm volatile("" : "+v"(cb), "+v"(cv));
         if (reg_live) {
             float* dst = gn + nb * 16 * kNoiseStride;
 #pragma unroll 2  // two independent Philox blocks at a time: their rounds interleave
             for (int q = 0; q < 4; ++q) {
-                const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(v0 + 4 * q) >> 2, static_cast<uint32_t>(kk),
-                                                    static_cast<uint32_t>(b), a.ctr3},
+                const u32x4 w = philox4x32_10(u32x4{cv + static_cast<uint32_t>(q), static_cast<uint32_t>(kk), cb, a.ctr3},
                                               a.key0, a.key1);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) dst[kNoiseStride * (4 * q + c)] = on ? log2_of_neg_log2_uniform(w[c]) : 0.0f;
             }
         }
         if (x_live) {
-            const u32x4 w = philox4x32_10(u32x4{static_cast<uint32_t>(vx) >> 2, static_cast<uint32_t>(kk),
-                                                static_cast<uint32_t>(b), a.ctr3},
-                                          a.key0, a.key1);
+            uint32_t cx = static_cast<uint32_t>(vx) >> 2;
+            asm volatile("" : "+v"(cx));
+            const u32x4 w = philox4x32_10(u32x4{cx, static_cast<uint32_t>(kk), cb, a.ctr3}, a.key0, a.key1);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const float gx = on ? log2_of_neg_log2_uniform(w[c]) : 0.0f;
@@ -633,27 +637,35 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         }
         to_slot(st, nb);
     };
-    // Workgroup merge of blocks [b0, b1) in wave order, then publish: the
-    // argmax key atomics and the softmax partials (read after the kernel).
+    // Workgroup merge of blocks [b0, b1), then publish: the argmax key
+    // atomics and the softmax partials (read after the kernel).  Each wave
+    // takes 8 blocks at a time: lane l reads wave l / 8's slot of block
+    // l % 8 (consecutive lanes, consecutive slots), and three exchange
+    // steps (lane distance 8, 16, 32) merge the 8 waves' slots in a fixed
+    // tree order.
     auto publish = [&](int kk, int b0, int b1) {
         __syncthreads();
-        for (int b = b0 + static_cast<int>(threadIdx.x); b < b1; b += blockDim.x) {
-            PStats t = slot[b];
-#pragma unroll
-            for (int w = 1; w < kPWaves; ++w) t = pstats_merge(t, slot[w * a.B + b]);
-            if (t.key != kKeyNone)
-                __hip_atomic_fetch_max(&a.best[((static_cast<size_t>(kk) * a.B + b) * kDraftKeyCopies +
-                                                wg % kDraftKeyCopies) * kKeyStride],
-                                       t.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const size_t o = (static_cast<size_t>(kk) * a.B + b) * nWG + partial_slot(wg, nWG);
-            a.pms[o] = make_float2(t.m, t.s);
+        const int groups = (b1 - b0 + 7) / 8;
+        for (int q = wave; q < groups; q += kPWaves) {  // wave-uniform trip count
+            const int b = b0 + 8 * q + (lane & 7), w = lane >> 3;
+            PStats t = b < b1 ? slot[w * a.B + b] : pstats_empty();
+            t = pstats_merge(t, shfl_xor_pstats(t, 8));
+            t = pstats_merge(t, shfl_xor_pstats(t, 16));
+            t = pstats_merge(t, shfl_xor_pstats(t, 32));
+            if (w == 0 && b < b1) {
+                if (t.key != kKeyNone)
+                    __hip_atomic_fetch_max(&a.best[((static_cast<size_t>(kk) * a.B + b) * kDraftKeyCopies +
+                                                    wg % kDraftKeyCopies) * kKeyStride],
+                                           t.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const size_t o = (static_cast<size_t>(kk) * a.B + b) * nWG + partial_slot(wg, nWG);
+                a.pms[o] = make_float2(t.m, t.s);
+            }
         }
     };
     // x_kk of blocks [b0, b1) from the keys: the copies of a block's key sit
     // in 8 consecutive lanes (b0 is a multiple of 16)
     auto read_keys = [&](int kk, int b0, int b1) {
-        for (int t = b0 * kDraftKeyCopies + static_cast<int>(threadIdx.x); t < b1 * kDraftKeyCopies; t += blockDim.x) {
-            uint64_t key = get_shared(&a.best[(static_cast<size_t>(kk) * a.B * kDraftKeyCopies + t) * kKeyStride]);
+        auto finish_key = [&](int t, uint64_t key) {
 #pragma unroll
             for (int o = 1; o < kDraftKeyCopies; o <<= 1) {
                 const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o);
@@ -662,9 +674,12 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
                 key = other > key ? other : key;
             }
             const uint32_t x = key_index(key);
-            if (t % kDraftKeyCopies == 0)
+            if (t < b1 * kDraftKeyCopies && t % kDraftKeyCopies == 0)
                 prev[t / kDraftKeyCopies] = (key != kKeyNone && x < static_cast<uint32_t>(a.V)) ? static_cast<int>(x) : 0;
-        }
+        };
+        const size_t base = static_cast<size_t>(kk) * a.B * kDraftKeyCopies;
+        for (int t = b0 * kDraftKeyCopies + static_cast<int>(threadIdx.x); t < b1 * kDraftKeyCopies; t += blockDim.x)
+            finish_key(t, get_shared(&a.best[(base + t) * kKeyStride]));
         __syncthreads();
     };
 
@@ -683,9 +698,10 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         publish(k, 0, a.B);
         if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
         // next step's noise of group 0 while the key atomics complete,
-        // the release fence and workgroup barrier, the arrival, group
-        // 1's noise while the arrival is in flight, then the wait for
-        // the other workgroups
+        // the release fence and workgroup barrier, the arrival and the
+        // wait for the other workgroups, with group 1's noise computed while
+        // the arrival is in flight (the barrier's latency, about as long,
+        // is hidden behind it)
         noise_ahead(k + 1, 0, scale_s[n] > 0.0f);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __syncthreads();
