@@ -68,6 +68,7 @@ DraftLayout draft_layout(const dspark_dims& d) {
     L.hdot = take(sizeof(float) * static_cast<size_t>(d.B) * d.gamma);
     L.best = take(sizeof(uint64_t) * 16 * kDraftKeyCopies * static_cast<size_t>(d.B) * d.gamma);
     L.bar = take(sizeof(uint32_t) * kDraftBarWords);
+    L.flags = take(sizeof(uint64_t) * (static_cast<size_t>(draft_persist_max_wg()) + 1));
     const size_t nq = static_cast<size_t>(d.gamma) * d.B * draft_persist_max_wg();
     L.qms = take(sizeof(float) * 2 * nq);
     L.qzx = take(sizeof(float) * nq);

@@ -3,8 +3,10 @@
 // dormouse "DSpark - paper verification" page, section 1) in one persistent
 // kernel, with W2 loaded from HBM once per call instead of once per step.
 //
-//   prepare (one workgroup)  clears the argmax keys and the barrier words
 //   persistent kernel, grid = every workgroup that can be resident:
+//     start: the workgroups clear the argmax keys and the barrier words and
+//           raise a per-call flag; before step 0 publishes anything, every
+//           workgroup waits for all flags (see start_barrier_*)
 //     load: wave w keeps W2 tile w (64 columns) in registers as MFMA
 //           A-fragments; tiles beyond 4 x grid live, pre-transposed, in the
 //           LDS of workgroup (tile - 4 x grid)
@@ -24,7 +26,11 @@
 #include <math.h>
 #include <stdio.h>
 
+#include <unistd.h>
+
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <mutex>
 
 #include "device_common.h"
@@ -52,8 +58,10 @@ struct PersistArgs {
     const uint16_t* h;   // [B, gamma, d]
     int V, r, d, gamma, B, Bpad, nWG;
     uint32_t key0, key1, ctr3;
-    uint64_t* best;      // [gamma, B, copies, 16]  argmax keys, one 128-byte line each (cleared by prepare)
-    uint32_t* bar;       // barrier words (cleared by prepare)
+    uint64_t* best;      // [gamma, B, copies, 16]  argmax keys, one 128-byte line each (cleared at the start)
+    uint32_t* bar;       // barrier words (cleared at the kernel's start)
+    uint64_t* flags;     // [nWG + 1] start-barrier flags, then the start barrier's time-out slot
+    uint64_t epoch;      // this call's flag value (never repeats within a process)
     float2* pms;         // [gamma, B, nWG] softmax (max, sum) partials of every step, base 2
     int32_t* dead;       // [B]
     int32_t* tokens;
@@ -62,13 +70,50 @@ struct PersistArgs {
     float* survival;
 };
 
-// -------------------------------------------------------------- prepare
+// ---------------------------------------------------------- start barrier
 
-// One workgroup: clears the argmax key copies and the barrier words.
-__global__ __launch_bounds__(256) void k_persist_prepare(int n_keys, uint64_t* __restrict__ best,
-                                                         uint32_t* __restrict__ bar) {
-    for (int i = threadIdx.x; i < n_keys; i += blockDim.x) best[static_cast<size_t>(i) * kKeyStride] = kKeyNone;
-    for (int i = threadIdx.x; i < kDraftBarWords; i += blockDim.x) bar[i] = 0u;
+// The workspace arrives with arbitrary contents, so the argmax keys and the
+// barrier words are cleared inside the kernel, and one more barrier makes
+// the clearing visible before anything uses them.  That barrier cannot use
+// counters (they would need clearing first): each workgroup stores the
+// call's epoch -- a value no earlier call in the process used -- in its own
+// flag word, and waits until every flag holds it.  Stale flags hold older
+// epochs, so they never pass.  All of it is device-scope atomics, like the
+// step barrier below.
+__device__ __forceinline__ void start_barrier_arrive(const PersistArgs& a, int n_keys) {
+    const int wg = blockIdx.x;
+    for (int i = wg * static_cast<int>(blockDim.x) + static_cast<int>(threadIdx.x); i < n_keys;
+         i += a.nWG * static_cast<int>(blockDim.x))
+        __hip_atomic_store(a.best + static_cast<size_t>(i) * kKeyStride, kKeyNone, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (wg == 0)
+        for (int i = threadIdx.x; i < kDraftBarWords; i += blockDim.x)
+            __hip_atomic_store(a.bar + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(a.flags + wg, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait (first wave, each lane a few flags) until every workgroup's flag
+// holds this call's epoch; bounded like the step barrier, with the time-out
+// recorded in slot nWG (the finish kernel then marks every block invalid).
+__device__ __forceinline__ void start_barrier_wait(const PersistArgs& a) {
+    if (threadIdx.x < kWave) {
+        uint32_t spins = 0;
+        while (true) {
+            bool late = false;
+            for (int i = threadIdx.x; i < a.nWG; i += kWave)
+                late |= __hip_atomic_load(a.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch;
+            if (__ballot(late) == 0) break;
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > (1u << 20)) {
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(a.flags + a.nWG, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
 }
 
 // ------------------------------------------------------- grid barrier
@@ -428,6 +473,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         }
     };
 
+    start_barrier_arrive(a, a.gamma * a.B * kDraftKeyCopies);
     W2Tile<KC> w2;
     if (has_reg) w2.load(a.W2, a.V, wv * 64, g, n);
     // while the tile loads are in flight
@@ -518,6 +564,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     };
     stage_rows();
     UAhead ahead = fetch_u(0, 0);
+    // the keys and barrier words are cleared everywhere before step 0
+    // publishes (the W2 loads above took far longer than the clearing)
+    start_barrier_wait(a);
 
     // accumulators start from U (bf16 -> f32 is exact)
     auto acc_from = [&](const UAhead& u, f32x4 (&acc)[4], f32x4& accx) {
@@ -775,7 +824,7 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
         }
         const int x0 = a.anchor[b];
         const uint64_t m = __ballot(inval);
-        const bool head_bad = a.bar[kTimeoutWord] != 0 || x0 < 0 || x0 >= a.V;
+        const bool head_bad = a.bar[kTimeoutWord] != 0 || a.flags[a.nWG] == a.epoch || x0 < 0 || x0 >= a.V;
         if (lane == 0) {
             xs[0] = x0;
             first_bad_s = head_bad ? 0 : (m ? __ffsll(static_cast<unsigned long long>(m)) - 1 : a.gamma);
@@ -919,6 +968,17 @@ const char* persist_kernel_name(const dspark_dims& D) {
     }
 }
 
+// Epochs of the start barrier: a process-wide counter, started from the
+// clock and the process id so that memory left by another process is
+// unlikely to hold a value it will produce.
+static uint64_t next_epoch() {
+    static std::atomic<uint64_t> counter{(static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count()) *
+                                          0x9E3779B97F4A7C15ull) ^
+                                         (static_cast<uint64_t>(getpid()) << 40)};
+    uint64_t e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+    return e != 0 ? e : counter.fetch_add(1, std::memory_order_relaxed) + 1;
+}
+
 template <int KC>
 static hipError_t launch_persist_kc(const DraftArgs& A) {
     const dspark_dims& D = A.dims;
@@ -945,11 +1005,10 @@ static hipError_t launch_persist_kc(const DraftArgs& A) {
     p.dead = reinterpret_cast<int32_t*>(ws + L.dead);
     p.tokens = A.tokens; p.logp = A.logp; p.conf = A.conf; p.survival = A.survival;
 
-    hipLaunchKernelGGL(k_persist_prepare, dim3(1), dim3(256), 0, A.stream, D.gamma * D.B * kDraftKeyCopies,
-                       p.best, p.bar);
-    hipError_t e = hipGetLastError();
+    p.flags = reinterpret_cast<uint64_t*>(ws + L.flags);
+    p.epoch = next_epoch();
+    hipError_t e = profile_begin(A.stream);
     if (e != hipSuccess) return e;
-    if ((e = profile_begin(A.stream)) != hipSuccess) return e;
     void* args[] = {&p};
     void (*fn)(PersistArgs) = persist_kernel<KC>(plan.grouped, plan.ahead);
     const size_t lds = plan.lds;
