@@ -354,7 +354,7 @@ struct BlockIn {
 // double-buffered LDS area (row stride padded by 16 bytes against bank
 // conflicts).  One workgroup barrier per block publishes the next block's E
 // rows and, in passes 1 and 2, this block's per-wave row partials, which
-// wave 0 merges.  Two workgroups fit per compute unit (at most 256 VGPRs),
+// one wave merges (wave rb mod 4 for block rb).  Two workgroups fit per compute unit (at most 256 VGPRs),
 // so the waves of one can run while the other's wait on memory.
 template <int KC, int PASS, int DZB>
 __global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
@@ -474,13 +474,20 @@ __global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
             }
             if (rb + 1 < rb1) stage((rb + 1) & 1);
             __syncthreads();
-            if (PASS != kPass3 && wave == 0 && g == 0 && row < a.R) {
-                RowPart t = red[rb & 1][0][n];
+            // the 4 waves' partials of this block's 16 rows, merged by one
+            // wave (a different one each block, so that no wave falls
+            // behind): lane (w, n) takes wave w's partial of row n, two
+            // exchange steps merge the 4 in a fixed tree order
+            if (PASS != kPass3 && wave == (rb & (kLossWaves - 1))) {
+                static_assert(kLossWaves == 4, "one lane per (wave, row)");
+                RowPart t = red[rb & 1][g][n];
+                t = rowpart_merge(PASS, t, rowpart_shfl(t, 16));
+                t = rowpart_merge(PASS, t, rowpart_shfl(t, 32));
+                if (g == 0 && row < a.R) {
+                    const size_t o = static_cast<size_t>(cg) * a.Rpad + row;
 #pragma unroll
-                for (int w = 1; w < kLossWaves; ++w) t = rowpart_merge(PASS, t, red[rb & 1][w][n]);
-                const size_t o = static_cast<size_t>(cg) * a.Rpad + row;
-#pragma unroll
-                for (int q = 0; q < kPartVals[PASS]; ++q) a.part[q][o] = t.v[q];
+                    for (int q = 0; q < kPartVals[PASS]; ++q) a.part[q][o] = t.v[q];
+                }
             }
         }
         __syncthreads();  // Es and red are reused by the next item
