@@ -211,6 +211,49 @@ def test_qwen3_4b_shape_all_blocks(ops, path, launch):
     note("  ties allowed: %d, max |dlogp| %.2e" % (info["ties"], info["logp_err"]))
 
 
+def test_qwen3_4b_shape_mixed_temperature_single_launch(ops):
+    # V = 151936: every wave of the single-launch kernel has its full
+    # register tile and LDS fragment, so the branch-free statistics run;
+    # sampled, greedy (zero noise) and tempered blocks in both 16-block
+    # groups
+    temps = ([1.0, 0.0, 0.7] * 8)[:24]
+    inp = synth.config_inputs(2, B=24, temperature=temps, seed=1102)
+    note("case: qwen3-4b-shaped V151936 r256 B24 mixed T single launch")
+    g = run_gpu(ops, inp, seed=3, offset=1, path=SINGLE)
+    info = check_draft(inp, g, 3, 1, label="qwen3-4b shape mixed T")
+    note("  ties allowed: %d, max |dlogp| %.2e" % (info["ties"], info["logp_err"]))
+
+
+def test_single_launch_dirty_reused_workspace(ops):
+    # the workspace arrives with arbitrary contents (all bits set: argmax
+    # keys that would beat every real key, barrier counters far past any
+    # target) and is then reused by a call with fewer blocks and positions;
+    # the kernel clears what it uses itself
+    import torch
+    from semi_autoregressive_draft_markov_amd import binding
+    binding.dspark_set_option(binding.DSPARK_OPT_DRAFT_PATH, SINGLE)
+    binding.dspark_set_option(binding.DSPARK_OPT_PERSIST_LAUNCH, 0)
+    big = small(V=4104, r=256, d=64, gamma=6, B=28, seed=51, temperature=[1.0] * 20 + [0.0] * 8)
+    tb = synth.to_torch(big)
+    dims = ops.draft_dims(tb["U"], tb["h"], tb["W1"])
+    ws = ops.workspace(dims, binding.DSPARK_CALL_DRAFT, tb["U"].device)
+    ws.fill_(0xFF)
+    note("case: single launch, workspace filled with 0xFF, V4104 B28 gamma6")
+    out = ops.draft_block(tb["U"], tb["h"], tb["anchor"], tb["W1"], tb["W2"], tb["w_conf"], tb["temperature"],
+                          seed=4, offset=2, ws=ws)
+    torch.cuda.synchronize()
+    check_draft(big, {k: out[k].cpu().numpy() for k in ("tokens", "logp", "conf", "survival")}, 4, 2,
+                label="dirty workspace")
+    sm = small(V=4104, r=256, d=64, gamma=3, B=9, seed=52)
+    ts = synth.to_torch(sm)
+    note("case: the same workspace again, V4104 B9 gamma3")
+    out = ops.draft_block(ts["U"], ts["h"], ts["anchor"], ts["W1"], ts["W2"], ts["w_conf"], ts["temperature"],
+                          seed=5, ws=ws)
+    torch.cuda.synchronize()
+    check_draft(sm, {k: out[k].cpu().numpy() for k in ("tokens", "logp", "conf", "survival")}, 5, 0,
+                label="reused workspace")
+
+
 @pytest.mark.parametrize("path", [MULTI, SINGLE])
 def test_qwen3_14b_shape_sampled_blocks(ops, path):
     inp = synth.config_inputs(4)
