@@ -140,8 +140,8 @@ struct VerifyLayout {
     size_t ef;         // f32 [B, r]     same, fp32
     size_t zd;         // f32 [B, V]  z_d / T at the residual position
     size_t pmx, psm;   // f32 [B, P]  (max, sum) partials of z_d / T
-    size_t lse_d;      // f32 [B]
     size_t keys;       // u64 [B, 2]  residual and target argmax keys (atomic maxima)
+    size_t done;       // u32 [B]  finished sampling workgroups of each block (the last one picks the token)
     size_t total;
 };
 VerifyLayout verify_layout(const dspark_dims& d);

@@ -29,8 +29,10 @@
 // rejection by ballot, the mode of the final draw, E row of the residual
 // position),
 // k_v_bias_mfma / k_v_bias_vec (z_d / T at the residual position for every
-// block, and per-column-group softmax partials), k_v_lse, k_v_sample
-// (partial argmax keys of the residual and the target draw), k_v_final.
+// block, and per-column-group softmax partials), k_v_sample (the draft
+// row's normaliser from those partials, partial argmax keys of the
+// residual and the target draw, and in the block's last workgroup the
+// next token).
 #include <algorithm>
 
 #include "device_common.h"
@@ -79,8 +81,8 @@ VerifyLayout verify_layout(const dspark_dims& d) {
     L.zd = take(sizeof(float) * B * d.V);
     L.pmx = take(sizeof(float) * B * L.P);
     L.psm = take(sizeof(float) * B * L.P);
-    L.lse_d = take(sizeof(float) * B);
     L.keys = take(sizeof(uint64_t) * B * 2);
+    L.done = take(sizeof(uint32_t) * B);
     L.total = off;
     return L;
 }
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(64) void k_v_decide(
     const float* __restrict__ tmx, const float* __restrict__ tsm, const uint64_t* __restrict__ tkey,
     int CT, int V, int r, int gamma, float tau, uint32_t key0, uint32_t key1, uint32_t ctr3,
     float* __restrict__ lse_t, int32_t* __restrict__ amax, uint64_t* __restrict__ keys,
-    int32_t* __restrict__ bad,
+    uint32_t* __restrict__ done, int32_t* __restrict__ bad,
     int32_t* __restrict__ mode, int32_t* __restrict__ jpos, float* __restrict__ invTo,
     uint16_t* __restrict__ ebf, float* __restrict__ ef, int32_t* __restrict__ n_keep,
     int32_t* __restrict__ n_accept, int32_t* __restrict__ next_token,
@@ -255,6 +257,7 @@ __global__ __launch_bounds__(64) void k_v_decide(
     const int j = n;
     const int md = greedy ? kModeGreedy : (n < m ? kModeResidual : kModeTarget);
     if (lane < 2) keys[2 * b + lane] = kKeyNone;
+    if (lane == 2) done[b] = 0u;
     if (lane == 0) {
         bad[b] = flag;
         mode[b] = flag ? -1 : md;
@@ -410,18 +413,6 @@ __global__ __launch_bounds__(256) void k_v_bias_vec(const T* __restrict__ U, con
 }
 
 // Wave per block: lse of z_d / T from the P partials, in order.
-__global__ __launch_bounds__(64) void k_v_lse(const float* __restrict__ pmx, const float* __restrict__ psm,
-                                              int P, float* __restrict__ lse_d) {
-    const int b = blockIdx.x, lane = threadIdx.x;
-    float m = -INFINITY, s = 0.0f;
-    for (int p = lane; p < P; p += 64) ms_merge(m, s, pmx[static_cast<int64_t>(b) * P + p], psm[static_cast<int64_t>(b) * P + p]);
-    for (int o = 1; o < 64; o <<= 1) {
-        const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-        ms_merge(m, s, m2, s2);
-    }
-    if (lane == 0) lse_d[b] = m + __logf(s);
-}
-
 // ------------------------------------------------------------ final draw
 
 // Workgroup per (block, 4096-column chunk), thread per 16 columns: partial
@@ -430,13 +421,16 @@ __global__ __launch_bounds__(64) void k_v_lse(const float* __restrict__ pmx, con
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void k_v_sample(const T* __restrict__ Tl, const float* __restrict__ zd,
                                                   const float* __restrict__ lse_t,
-                                                  const float* __restrict__ lse_d,
-                                                  const int32_t* __restrict__ mode,
+                                                  const float* __restrict__ pmx, const float* __restrict__ psm,
+                                                  int P, const int32_t* __restrict__ mode,
                                                   const int32_t* __restrict__ jpos,
                                                   const float* __restrict__ invT, int V, int gamma,
                                                   uint32_t key0, uint32_t key1, uint32_t ctr3,
-                                                  uint64_t* __restrict__ keys) {
+                                                  uint64_t* __restrict__ keys, uint32_t* __restrict__ done,
+                                                  int32_t* __restrict__ next_token) {
     __shared__ uint64_t kr[256], kt[256];
+    __shared__ float sm[256 / kWave], ss[256 / kWave];
+    __shared__ bool last;
     const int b = blockIdx.y, chunk = blockIdx.x;
     const int md = mode[b];
     if (md != kModeResidual && md != kModeTarget) return;
@@ -444,7 +438,27 @@ __global__ __launch_bounds__(256) void k_v_sample(const T* __restrict__ Tl, cons
     const float it = invT[b];
     const int64_t row = static_cast<int64_t>(b) * (gamma + 1) + j;
     const float lt = lse_t[row];
-    const float ld = md == kModeResidual ? lse_d[b] : 0.0f;
+    // log-normaliser of the draft row from the bias kernel's P partials,
+    // merged in the same fixed order by every workgroup of the block
+    float ld = 0.0f;
+    if (md == kModeResidual) {
+        float m = -INFINITY, s = 0.0f;
+        for (int p = threadIdx.x; p < P; p += blockDim.x)
+            ms_merge(m, s, pmx[static_cast<int64_t>(b) * P + p], psm[static_cast<int64_t>(b) * P + p]);
+        for (int o = 1; o < kWave; o <<= 1) {
+            const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+            ms_merge(m, s, m2, s2);
+        }
+        if ((threadIdx.x & (kWave - 1)) == 0) {
+            sm[threadIdx.x / kWave] = m;
+            ss[threadIdx.x / kWave] = s;
+        }
+        __syncthreads();
+        m = sm[0];
+        s = ss[0];
+        for (int w = 1; w < static_cast<int>(blockDim.x) / kWave; ++w) ms_merge(m, s, sm[w], ss[w]);
+        ld = m + __logf(s);
+    }
     const T* zt = Tl + row * V;
     const float* zr = zd + static_cast<int64_t>(b) * V;
     uint64_t bres = kKeyNone, btgt = kKeyNone;
@@ -511,25 +525,25 @@ __global__ __launch_bounds__(256) void k_v_sample(const T* __restrict__ Tl, cons
         }
         __syncthreads();
     }
-    // a maximum does not depend on the order of the updates
+    // a maximum does not depend on the order of the updates; the block's
+    // last workgroup to finish (counted after its own keys are complete)
+    // picks the token: the residual draw, or the target draw when no entry
+    // of the residual is positive
     if (threadIdx.x == 0) {
         if (kr[0] != kKeyNone) atomicMax(reinterpret_cast<unsigned long long*>(keys + 2 * b), kr[0]);
         atomicMax(reinterpret_cast<unsigned long long*>(keys + 2 * b + 1), kt[0]);
+        // the key atomics are device-coherent: waiting for their completion
+        // (no cache write-back) orders them before the count
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        last = __hip_atomic_fetch_add(done + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
     }
-}
-
-// Thread per block: the next token from the two keys (the residual draw, or
-// the target draw when no entry of the residual is positive).
-__global__ __launch_bounds__(256) void k_v_final(const uint64_t* __restrict__ keys,
-                                                 const int32_t* __restrict__ mode, int B,
-                                                 int32_t* __restrict__ next_token) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= B) return;
-    const int md = mode[b];
-    if (md != kModeResidual && md != kModeTarget) return;
-    const uint64_t kr = keys[2 * b], kt = keys[2 * b + 1];
-    const uint64_t k = (md == kModeResidual && kr != kKeyNone) ? kr : kt;
-    next_token[b] = static_cast<int32_t>(key_index(k));
+    __syncthreads();
+    if (last && threadIdx.x == 0) {
+        const uint64_t fr = __hip_atomic_load(keys + 2 * b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t ft = __hip_atomic_load(keys + 2 * b + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t k = (md == kModeResidual && fr != kKeyNone) ? fr : ft;
+        next_token[b] = static_cast<int32_t>(key_index(k));
+    }
 }
 
 // ------------------------------------------------------------------ launch
@@ -551,8 +565,8 @@ static hipError_t launch_verify_t(const VerifyArgs& va) {
     float* zd = reinterpret_cast<float*>(ws + L.zd);
     float* pmx = reinterpret_cast<float*>(ws + L.pmx);
     float* psm = reinterpret_cast<float*>(ws + L.psm);
-    float* lse_d = reinterpret_cast<float*>(ws + L.lse_d);
     uint64_t* keys = reinterpret_cast<uint64_t*>(ws + L.keys);
+    uint32_t* done = reinterpret_cast<uint32_t*>(ws + L.done);
     const T* Tl = static_cast<const T*>(va.T_logits);
     const uint32_t key0 = static_cast<uint32_t>(va.seed), key1 = static_cast<uint32_t>(va.seed >> 32);
     const uint32_t ctr3 = static_cast<uint32_t>(va.offset);
@@ -571,7 +585,7 @@ static hipError_t launch_verify_t(const VerifyArgs& va) {
                            V, g, L.CT, tmx, tsm, tkey);
     hipLaunchKernelGGL((k_v_decide<T>), dim3(B), dim3(64), 0, st, Tl, static_cast<const T*>(va.W1),
                        va.anchor, va.tokens, va.logp, va.survival, va.temperature, tmx, tsm, tkey, L.CT,
-                       V, r, g, va.threshold, key0, key1, ctr3, lse_t, amax, keys, bad, mode, jpos, invT, ebf,
+                       V, r, g, va.threshold, key0, key1, ctr3, lse_t, amax, keys, done, bad, mode, jpos, invT, ebf,
                        ef, va.n_keep, va.n_accept, va.next_token, va.accept_prob);
     if (L.Bpad > B) {
         // padding E rows of the last 16-block unit (read by the MFMA, never used)
@@ -598,14 +612,12 @@ static hipError_t launch_verify_t(const VerifyArgs& va) {
                            static_cast<const T*>(va.W2), ef, jpos, invT, V, r, B, g, zd, pmx, psm);
     }
     if ((pe = profile_end(st)) != hipSuccess) return pe;
-    hipLaunchKernelGGL(k_v_lse, dim3(B), dim3(64), 0, st, pmx, psm, L.P, lse_d);
     if (vec)
-        hipLaunchKernelGGL((k_v_sample<T, true>), dim3(L.C, B), dim3(256), 0, st, Tl, zd, lse_t, lse_d, mode, jpos,
-                           invT, V, g, key0, key1, ctr3, keys);
+        hipLaunchKernelGGL((k_v_sample<T, true>), dim3(L.C, B), dim3(256), 0, st, Tl, zd, lse_t, pmx, psm, L.P, mode,
+                           jpos, invT, V, g, key0, key1, ctr3, keys, done, va.next_token);
     else
-        hipLaunchKernelGGL((k_v_sample<T, false>), dim3(L.C, B), dim3(256), 0, st, Tl, zd, lse_t, lse_d, mode, jpos,
-                           invT, V, g, key0, key1, ctr3, keys);
-    hipLaunchKernelGGL(k_v_final, dim3((B + 255) / 256), dim3(256), 0, st, keys, mode, B, va.next_token);
+        hipLaunchKernelGGL((k_v_sample<T, false>), dim3(L.C, B), dim3(256), 0, st, Tl, zd, lse_t, pmx, psm, L.P, mode,
+                           jpos, invT, V, g, key0, key1, ctr3, keys, done, va.next_token);
     return hipGetLastError();
 }
 
