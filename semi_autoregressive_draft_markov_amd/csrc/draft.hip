@@ -71,7 +71,6 @@ DraftLayout draft_layout(const dspark_dims& d) {
     L.flags = take(sizeof(uint64_t) * (static_cast<size_t>(draft_persist_max_wg()) + 1));
     const size_t nq = static_cast<size_t>(d.gamma) * d.B * draft_persist_max_wg();
     L.qms = take(sizeof(float) * 2 * nq);
-    L.qzx = take(sizeof(float) * nq);
     const size_t np = static_cast<size_t>(d.B) * L.P;
     L.pm = take(sizeof(float) * np);
     L.ps = take(sizeof(float) * np);

@@ -33,10 +33,9 @@ struct DraftLayout {
     size_t gh;         // f32 [B, gamma, 3r] h columns of the RNN projection (RNN head only)
     size_t hdot;       // f32 [B, gamma]  h part of the Eq 7 logit, w[0:d] . h_k
     size_t best;       // u64 [gamma, B, copies, 16]  argmax keys, one line each (single-launch path)
-    size_t bar;        // u32 [512]  grid barrier: arrival counters, release and timeout flags
+    size_t bar;        // u32 [512]  grid barrier: arrival counters and the time-out flag
     size_t flags;      // u64 [max workgroups + 1]  start-barrier flags of the single-launch kernel, then its time-out slot
     size_t qms;        // f32x2 [gamma, B, max workgroups] (max, sum) step partials (single-launch path)
-    size_t qzx;        // f32 [gamma, B, max workgroups] logit at each workgroup's argmax (single-launch path)
     size_t pm, ps, pkey, pzx;  // partials [B, P]: max, sum, key (u64), z at key
     size_t total;
 };
