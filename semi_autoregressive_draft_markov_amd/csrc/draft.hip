@@ -631,15 +631,22 @@ __global__ __launch_bounds__(256, 2) void k_stream_mfma(
         if (g == 0) red[nb & 1][wave][n] = st;
         if (nb + 1 < NB) stage((nb + 1) & 1);
         __syncthreads();
-        if (wave == 0 && g == 0 && b < B) {
-            Stats t = red[nb & 1][0][n];
-#pragma unroll
-            for (int w = 1; w < kWavesPerWG; ++w) t = stats_merge(t, red[nb & 1][w][n]);
-            const size_t o = static_cast<size_t>(b) * P + blockIdx.x;
-            pm[o] = t.m;
-            ps[o] = t.s;
-            pkey[o] = t.key;
-            pzx[o] = t.zx;
+        // the 4 waves' statistics of this unit's 16 blocks, merged by one
+        // wave (a different one each unit, so that no wave falls behind):
+        // lane (w, n) takes wave w's statistics of block n, two exchange
+        // steps merge the 4 in a fixed tree order
+        if (wave == (nb & (kWavesPerWG - 1))) {
+            static_assert(kWavesPerWG == 4, "one lane per (wave, block)");
+            Stats t = red[nb & 1][g][n];
+            t = stats_merge(t, shfl_xor_stats(t, 16));
+            t = stats_merge(t, shfl_xor_stats(t, 32));
+            if (g == 0 && b < B) {
+                const size_t o = static_cast<size_t>(b) * P + blockIdx.x;
+                pm[o] = t.m;
+                ps[o] = t.s;
+                pkey[o] = t.key;
+                pzx[o] = t.zx;
+            }
         }
     }
 }
