@@ -661,12 +661,14 @@ constexpr int kDw2Cols = 128;
 constexpr int kDw2Threads = 256;
 constexpr int kDw2Ld = 20;  // words per staged column: 16 row pairs + 4 pad (16-byte aligned)
 
-// Word offset of row pair p of staged column col.  Each group of 8 columns
-// (one staging thread's) is shifted by a further 16 bytes, so the staging
-// threads of a wave, 8 columns apart, spread over the LDS banks instead of
-// meeting in one; a lane's 4 pairs stay one aligned 16-byte piece.
-__device__ __forceinline__ int dw2_word(int col, int p) { return col * kDw2Ld + 4 * (col >> 3) + p; }
-constexpr int kDw2Words = kDw2Cols * kDw2Ld + 4 * (kDw2Cols / 8);
+// Word offset of row pair p of staged column col.  Each group of 16 columns
+// is shifted by a further 16 bytes: with the 20-word column stride, the
+// staging stores of a wave (threads 8 columns apart) and the operand reads
+// (16 lanes on 16 consecutive columns, 16 bytes each) then both fall on
+// distinct banks of a 64-bank LDS; a lane's 4 pairs stay one aligned
+// 16-byte piece.
+__device__ __forceinline__ int dw2_word(int col, int p) { return col * kDw2Ld + 4 * (col >> 4) + p; }
+constexpr int kDw2Words = kDw2Cols * kDw2Ld + 4 * (kDw2Cols / 16);
 
 // (float32 dZ: the hi/lo planes need more registers, one workgroup per CU)
 template <int DZF32>
