@@ -28,6 +28,9 @@
  *    temperature and all outputs are float32).  Accumulation is float32.
  *  - Results are deterministic: the same inputs, seed and offset give
  *    bitwise-identical outputs (no floating-point atomics).
+ *  - A workspace serves one call at a time: calls that may run at the same
+ *    time (on different streams) need workspaces of their own.  Entry
+ *    points are otherwise reentrant.
  *  - No exceptions cross the ABI.  On failure the status says why and
  *    dspark_last_error() (thread-local) holds a message.  Token ids out of
  *    [0, V) are found on the device: the block's outputs become token -1 and
