@@ -105,73 +105,85 @@ __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2)
 // ------------------------------------------------------------ target rows
 
 // Workgroup per (target row, 8192-column chunk), row = (b, position k in
-// 0..gamma), thread per 32 strided columns: the chunk's max of z_t (and its
-// argmax key, lowest index on a tie) and sum of exp((z_t - max) / T).
+// 0..gamma), thread per 32 columns: the chunk's max of z_t (and its argmax
+// key, lowest index on a tie) and sum of exp((z_t - max) / T).  A thread
+// takes its maximum first and the lowest of its columns attaining it after
+// (one key per thread), then the workgroup merges across lanes (exchange
+// steps) and across its 4 waves (in wave order).
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void k_vt_stats(const T* __restrict__ Tl,
                                                   const float* __restrict__ temperature, int V,
                                                   int gamma, int CT, float* __restrict__ tmx,
                                                   float* __restrict__ tsm, uint64_t* __restrict__ tkey) {
-    __shared__ float sm[256], ss[256];
-    __shared__ uint64_t sk[256];
+    constexpr int NX = kVTChunk / 256;
+    __shared__ float sm[4], ss[4];
+    __shared__ uint64_t sk[4];
     const int64_t row = blockIdx.x;
     const int chunk = blockIdx.y;
     const int b = static_cast<int>(row / (gamma + 1));
     const float Tb = temperature[b];
     const float invT = Tb > 0.0f ? 1.0f / Tb : 1.0f;
     const T* z = Tl + row * V;
-    float x[kVTChunk / 256];
-    float m = -INFINITY;
-    uint64_t key = kKeyNone;
+    float x[NX];
+    // column of element j of this thread (increasing in j)
+    auto col = [&](int j) {
+        return VEC ? chunk * kVTChunk + 2048 * (j / 8) + 8 * static_cast<int>(threadIdx.x) + (j % 8)
+                   : chunk * kVTChunk + static_cast<int>(threadIdx.x) + 256 * j;
+    };
     if (VEC) {
         // 4 runs of 8 consecutive columns per thread, 16-byte loads
 #pragma unroll
-        for (int i = 0; i < kVTChunk / 2048; ++i) {
-            const int v = chunk * kVTChunk + 2048 * i + 8 * threadIdx.x;
+        for (int i = 0; i < NX / 8; ++i) {
+            const int v = col(8 * i);
             const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(z) + min(v, V - 8));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float xv = v < V ? ((e & 1) ? hi_bf16(w[e >> 1]) : lo_bf16(w[e >> 1])) : -INFINITY;
-                x[8 * i + e] = xv;
-                if (xv > m) {  // strict: the lowest column wins a tie
-                    m = xv;
-                    key = argmax_key(xv, static_cast<uint32_t>(v + e));
-                }
-            }
+            for (int e = 0; e < 8; ++e) x[8 * i + e] = v < V ? ((e & 1) ? hi_bf16(w[e >> 1]) : lo_bf16(w[e >> 1])) : -INFINITY;
         }
     } else {
-        const int v0 = chunk * kVTChunk + threadIdx.x;
 #pragma unroll
-        for (int i = 0; i < kVTChunk / 256; ++i) {
-            const int v = v0 + 256 * i;
+        for (int i = 0; i < NX; ++i) {
+            const int v = col(i);
             x[i] = v < V ? load_f(z, min(v, V - 1)) : -INFINITY;
-            if (x[i] > m) {
-                m = x[i];
-                key = argmax_key(x[i], static_cast<uint32_t>(v));
-            }
         }
     }
+    float m = x[0];
+#pragma unroll
+    for (int i = 1; i < NX; ++i) m = fmaxf(m, x[i]);
+    int jb = NX - 1;
+#pragma unroll
+    for (int i = NX - 2; i >= 0; --i) jb = x[i] == m ? i : jb;
+    uint64_t key = m > -INFINITY ? argmax_key(m, static_cast<uint32_t>(col(jb))) : kKeyNone;
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kVTChunk / 256; ++i) s += x[i] > -INFINITY ? __expf((x[i] - m) * invT) : 0.0f;
-    sm[threadIdx.x] = m * invT;
-    ss[threadIdx.x] = s;
-    sk[threadIdx.x] = key;
-    __syncthreads();
-    for (int h = 128; h > 0; h >>= 1) {
-        if (threadIdx.x < h) {
-            float m1 = sm[threadIdx.x], s1 = ss[threadIdx.x];
-            ms_merge(m1, s1, sm[threadIdx.x + h], ss[threadIdx.x + h]);
-            sm[threadIdx.x] = m1;
-            ss[threadIdx.x] = s1;
-            sk[threadIdx.x] = sk[threadIdx.x + h] > sk[threadIdx.x] ? sk[threadIdx.x + h] : sk[threadIdx.x];
-        }
-        __syncthreads();
+    for (int i = 0; i < NX; ++i) s += x[i] > -INFINITY ? __expf((x[i] - m) * invT) : 0.0f;
+    float ms = m * invT;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const float m2 = __shfl_xor(ms, o), s2 = __shfl_xor(s, o);
+        ms_merge(ms, s, m2, s2);
+        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o);
+        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key >> 32), o);
+        const uint64_t k2 = (static_cast<uint64_t>(hi) << 32) | lo;
+        key = k2 > key ? k2 : key;
     }
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        sm[wave] = ms;
+        ss[wave] = s;
+        sk[wave] = key;
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
-        tmx[row * CT + chunk] = sm[0];
-        tsm[row * CT + chunk] = ss[0];
-        tkey[row * CT + chunk] = sk[0];
+        float m1 = sm[0], s1 = ss[0];
+        uint64_t k1 = sk[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            ms_merge(m1, s1, sm[w], ss[w]);
+            k1 = sk[w] > k1 ? sk[w] : k1;
+        }
+        tmx[row * CT + chunk] = m1;
+        tsm[row * CT + chunk] = s1;
+        tkey[row * CT + chunk] = k1;
     }
 }
 
