@@ -18,8 +18,8 @@
  *  - Meridian "Phase-Conditioned Speculative Decoding", section 3: the prefix
  *    survival is the cumulative product of the c_k.
  * Readings where the pages are silent (RNG, tie-break, temperature, batch
- * reduction, stop-gradient through c*) are listed in the design doc; each is
- * restated at its point of use in dspark_oracle.c.
+ * reduction, stop-gradient through c*) are each stated at their point of
+ * use in dspark_oracle.c.
  *
  * Parity status: every function here is pinned by tests/test_oracle_*.py
  * except the points the pages leave open (overall loss scale, the logp

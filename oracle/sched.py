@@ -13,8 +13,10 @@ Plain Python and numpy, float64, written from the pages:
     cycle times steps/s at the resulting batch, every request's choice a
     prefix.
   - depth planner: Meridian section 6, Theta(g) = tau(a, g) / cycle cost.
-Readings (ECE bins, default grid, batch size counting the bonus position)
-are listed in the design doc.
+Readings where the pages leave a detail open: the ECE uses 15 equal-width
+bins over [0, 1]; the default temperature grid is 201 geometric points in
+[0.05, 20] with 1 in the middle; the scheduler's batch size counts every
+request's bonus position.
 """
 from __future__ import annotations
 

@@ -8,7 +8,7 @@ consume what it returns, so the two sides always see the same bytes.
 Shapes and value laws follow the workloads the DSpark pages describe: the
 Qwen3-4B/8B/14B and Gemma4-12B drafters (block size 7, Markov rank 256,
 DSpark paper section 4.1 as transcribed on the dormouse verification note,
-section 1), with the distributions fixed by the workload table in the design doc.
+section 1), with the distributions of the CONFIGS table below.
 
 Layouts (all C-contiguous):
   anchor [B] int32, U [B, gamma, V], h [B, gamma, d], W1 [V, r], W2 [r, V],
