@@ -160,6 +160,16 @@ def test_qwen3_4b_shape_every_block(ops):
     assert (ref["accept"] < ref["keep"]).any() and (ref["accept"] > 0).any()
 
 
+def test_many_blocks(ops):
+    # 130 blocks: several 16-block units in the draft-row kernel and one
+    # final-draw workgroup per (block, chunk), each block's last one picking
+    # its token
+    inp = small(V=9000, r=64, gamma=4, B=130, seed=47, temperature=[1.0] * 90 + [0.0] * 40)
+    target = make_target(inp, noise=0.3, seed=84)
+    note("case: verify V9000 r64 B130")
+    check(inp, target, run(ops, inp, target, 0.125), 0.125, label="many blocks")
+
+
 def test_longest_block(ops):
     # gamma = 64: every lane of the decision wave holds a position, the
     # bonus row is the 65th; the target equals the base logits closely so
