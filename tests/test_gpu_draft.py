@@ -83,6 +83,16 @@ def test_single_launch_short_blocks(ops, gamma):
     check_draft(inp, g, 6, 2, label="short blocks gamma %d" % gamma)
 
 
+def test_single_launch_longest_block(ops):
+    # gamma = 64, the largest the C ABI accepts: 63 grid barriers, the
+    # finish kernel's waves each take 8 positions
+    inp = small(V=2048, r=64, d=48, gamma=64, B=5, seed=33, w1_std=0.05, w2_std=0.05,
+                temperature=[1.0, 0.0, 1.0, 0.5, 1.0])
+    note("case: bf16 single-launch gamma 64")
+    g = run_gpu(ops, inp, seed=7, offset=3, path=SINGLE)
+    check_draft(inp, g, 7, 3, label="single launch gamma 64")
+
+
 @pytest.mark.parametrize("path", [MULTI, SINGLE])
 @pytest.mark.parametrize("B", [1, 33])
 def test_bf16_rank256_tail_columns(ops, B, path):
