@@ -83,6 +83,19 @@ def test_single_launch_short_blocks(ops, gamma):
     check_draft(inp, g, 6, 2, label="short blocks gamma %d" % gamma)
 
 
+def test_single_launch_many_blocks(ops):
+    # B = 300: E rows staged 16 blocks at a time (19 block groups, the last
+    # one partial), the workgroup merge loops over 38 groups of 8 blocks
+    temps = [1.0] * 150 + [0.0] * 100 + [0.8] * 50
+    inp = small(V=4104, r=256, d=64, gamma=3, B=300, seed=34, temperature=temps)
+    note("case: bf16 single-launch V4104 r256 B300")
+    g = run_gpu(ops, inp, seed=8, offset=1, path=SINGLE)
+    pick = np.array([0, 1, 15, 16, 149, 150, 255, 256, 287, 288, 298, 299])
+    sub = synth.subset(inp, pick)
+    check_draft(sub, {k: g[k][pick] for k in ("tokens", "logp", "conf", "survival")}, 8, 1,
+                block_ids=pick, label="single launch B300")
+
+
 def test_single_launch_longest_block(ops):
     # gamma = 64, the largest the C ABI accepts: 63 grid barriers, the
     # finish kernel's waves each take 8 positions
