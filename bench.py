@@ -309,8 +309,6 @@ def main() -> int:
                              "qwen3-8b-backward", "qwen3-4b-verify"],
                     help="qwen3-4b (default) is the reported workload; the others are "
                          "extra measurements of the same kernels at the other shapes")
-    ap.add_argument("--launch", default="plain", choices=["plain", "cooperative"],
-                    help="how the single-launch drafting kernel is started (same kernel and grid)")
     ap.add_argument("--flush", action="store_true",
                     help="write a 1 GiB buffer before every timed drafting call (untimed) so that "
                          "W2 and U come from HBM, not from the 256 MB memory-side cache; the "
@@ -343,7 +341,6 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
-    binding.dspark_set_option(binding.DSPARK_OPT_PERSIST_LAUNCH, 1 if args.launch == "cooperative" else 0)
     dev = torch.device("cuda:0")
     cfg = {"qwen3-4b": 2, "qwen3-14b": 4, "gemma4-rnn": 5}[args.workload]
     inp = synth.config_inputs(cfg)
@@ -398,7 +395,7 @@ def main() -> int:
     kname = binding.dspark_draft_kernel_name(dims)
     if per_call == 1:
         # single-launch driver: W2 is read once per call, every step's U slice once
-        driver = "single-launch (%s)" % args.launch
+        driver = "single-launch"
         alg_bytes = (r + gamma * B) * V * 2
     else:
         # per-step driver: every step streams all of W2 plus its slice of U

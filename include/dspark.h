@@ -285,13 +285,25 @@ dspark_status dspark_schedule_prefixes(int32_t R, int32_t gamma, const float* su
                                        const float* sps, int32_t T, int32_t* length,
                                        float* theta);
 
-/* Depth planner for i.i.d. acceptance (Meridian page, section 6): the depth
- * g in 0..gamma_max maximising tau(a, g) / (draft_us g + verify_fixed_us +
- * verify_token_us g), tau(a, g) = (1 - a^(g+1)) / (1 - a) (1 + g at a = 1);
- * the smallest g wins a tie.  a in [0, 1], costs >= 0 with a positive
- * cycle cost; gamma_out and theta (nullable) out. */
-dspark_status dspark_plan_depth(float a, int32_t gamma_max, float draft_us, float verify_fixed_us,
-                                float verify_token_us, int32_t* gamma_out, float* theta);
+/* The random numbers the kernels draw, for checking them against an
+ * independent Philox4x32-10 (Salmon et al., SC'11; the pages name no
+ * generator).  For i < n and v = v0 + i (v0 >= 0, n >= 0, v0 + n <= 2^31):
+ *   words[i]  = word (v mod 4) of Philox4x32-10 at counter (v / 4, c1, c2,
+ *               offset mod 2^32), key (seed mod 2^32, seed >> 32) -- the word
+ *               dspark_draft_block uses for element v of block b at 0-based
+ *               step k when c1 = k, c2 = b (the verification's final draw at
+ *               position j uses c1 = 0x80000000 | j) -- or words_in[i] when
+ *               words_in is not NULL;
+ *   gumbel[i]      = -ln(-ln u) and
+ *   gumbel_log2[i] = log2(-log2 u), both as the kernels evaluate them in
+ *               float32, u = (2 m + 1) / 2^24 with m the top 23 bits of the
+ *               word (gumbel_log2 is the form the single-launch drafting
+ *               kernel subtracts from z log2(e) / T: same argmax).
+ * DEVICE pointers; every output is nullable; asynchronous on hip_stream.
+ * EINVAL for n < 0, v0 < 0 or a range past 2^31. */
+dspark_status dspark_noise(uint64_t seed, uint64_t offset, uint32_t c1, uint32_t c2, int32_t v0, int32_t n,
+                           const uint32_t* words_in, uint32_t* words, float* gumbel, float* gumbel_log2,
+                           void* hip_stream);
 
 /* Synchronises `hip_stream`, then reads the per-block error flags the last
  * call with these dims left at the start of `workspace`: *code (HOST
@@ -309,18 +321,6 @@ dspark_status dspark_read_device_error(const dspark_dims* dims, const void* work
  * (DSPARK_EUNSUPPORTED when the problem does not fit it).  Both paths give
  * the same results.  Returns DSPARK_EINVAL for an unknown option or value. */
 #define DSPARK_OPT_DRAFT_PATH 1
-/* DSPARK_OPT_PERSIST_LAUNCH selects how the single-launch kernel is started:
- * 0 (default) = an ordinary launch of a grid with one workgroup per free
- * slot that the occupancy query reports for the device; 1 =
- * hipLaunchCooperativeKernel with the same grid (the runtime re-checks that
- * the grid can be resident; on this hardware it is measurably slower).  The
- * workgroups meet at grid barriers, so mode 0 assumes that kernels running
- * concurrently on other streams do not hold the compute units for long: a
- * workgroup that cannot become resident only delays the call, but if the
- * barrier wait exceeds about half a second per step the call gives up and
- * reports every block invalid (tokens -1, counted by
- * dspark_read_device_error) instead of hanging. */
-#define DSPARK_OPT_PERSIST_LAUNCH 2
 dspark_status dspark_set_option(int option, int value);
 
 /* Kernel timing for measurement.  While enabled on the calling thread, each

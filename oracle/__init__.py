@@ -53,7 +53,8 @@ def _load():
         lib.oracle_draft_block.restype = I
         lib.oracle_block_logprob.argtypes = [I, I, I, I, I, I, I] + [P] * 8 + [P, I]
         lib.oracle_block_logprob.restype = I
-        lib.oracle_block_loss.argtypes = [I, I, I, I, I, I] + [P] * 10 + [P, ctypes.c_int64] + [P] * 9 + [I]
+        lib.oracle_block_loss.argtypes = ([I, I, I, I, I, I] + [P] * 10 + [P, ctypes.c_int64]
+                                          + [P, ctypes.c_int32] + [P] * 9 + [I])
         lib.oracle_block_loss.restype = I
         lib.oracle_block_loss_backward.argtypes = [I, I, I, I, I, I] + [P] * 11 + [I]
         lib.oracle_block_loss_backward.restype = I
@@ -153,19 +154,23 @@ def position_weights(gamma: int) -> np.ndarray:
     return np.exp(-np.arange(gamma, dtype=np.float64) / gamma)
 
 
-def block_loss(inp, alpha=(0.1, 0.9, 1.0), pos_weight=None, rows=None,
+def block_loss(inp, alpha=(0.1, 0.9, 1.0), pos_weight=None, rows=None, cols=None,
                want_dZ: bool = True, want_dW2: bool = True, nthreads: int = 0) -> dict:
-    """Teacher-forced loss over the N = inp.B blocks of `inp` (needs target, labels)."""
+    """Teacher-forced loss over the N = inp.B blocks of `inp` (needs target, labels).
+    `rows` restricts the per-row outputs to those rows; `cols` returns dZ and
+    dW2 only at those vocabulary columns ([rows, len(cols)], [r, len(cols)])."""
     N, g, V = inp.B, inp.gamma, inp.V
     dt = inp.dtype
     a = np.ascontiguousarray(alpha, dtype=np.float64)
     pw = position_weights(g) if pos_weight is None else np.ascontiguousarray(pos_weight, np.float64)
     rws = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    cls = None if cols is None else np.ascontiguousarray(cols, dtype=np.int32)
     count = N * g if rws is None else len(rws)
+    W = V if cls is None else len(cls)
     out = dict(loss4=np.zeros(4), c_star=np.zeros(count), conf=np.zeros(count),
                dA=np.zeros(count), ce=np.zeros(count), tv=np.zeros(count), bce=np.zeros(count))
-    out["dZ"] = np.zeros((count, V)) if want_dZ else None
-    out["dW2"] = np.zeros((inp.r, V)) if (want_dW2 and rws is None) else None
+    out["dZ"] = np.zeros((count, W)) if want_dZ else None
+    out["dW2"] = np.zeros((inp.r, W)) if (want_dW2 and rws is None) else None
     rc = _load().oracle_block_loss(
         V, inp.r, inp.d, g, N, _dtype_code(dt),
         _ptr(_arr(inp.U, dt)), _ptr(_arr(inp.target, dt)), _ptr(_arr(inp.h, dt)),
@@ -173,6 +178,7 @@ def block_loss(inp, alpha=(0.1, 0.9, 1.0), pos_weight=None, rows=None,
         _ptr(np.ascontiguousarray(inp.labels, np.int32)),
         _ptr(_arr(inp.W1, dt)), _ptr(_arr(inp.W2, dt)), _ptr(_arr(inp.w_conf, dt)),
         _ptr(a), _ptr(pw), _ptr(rws), 0 if rws is None else len(rws),
+        _ptr(cls), 0 if cls is None else len(cls),
         _ptr(out["loss4"]), _ptr(out["c_star"]), _ptr(out["conf"]), _ptr(out["dA"]),
         _ptr(out["ce"]), _ptr(out["tv"]), _ptr(out["bce"]),
         _ptr(out["dZ"]), _ptr(out["dW2"]), nthreads)
@@ -185,11 +191,14 @@ def block_loss_backward(inp, dZ, dA, want_dW1: bool = True, want_dw: bool = True
                         want_dh: bool = True, nthreads: int = 0) -> dict:
     """dW1, dw_conf, dh of the teacher-forced objective from given dZ [R, V]
     and dA [R] (the loss's gradients w.r.t. the draft logits and the
-    confidence logits), float64."""
+    confidence logits), float64.  dZ may be None when dW1 is not wanted."""
     N, g, V, r, d = inp.B, inp.gamma, inp.V, inp.r, inp.d
     dt = inp.dtype
     R = N * g
-    dZ = np.ascontiguousarray(np.asarray(dZ, np.float64).reshape(R, V))
+    if dZ is not None:
+        dZ = np.ascontiguousarray(np.asarray(dZ, np.float64).reshape(R, V))
+    elif want_dW1:
+        raise ValueError("dW1 needs dZ")
     dA = np.ascontiguousarray(np.asarray(dA, np.float64).reshape(R))
     out = dict(dW1=np.zeros((V, r)) if want_dW1 else None,
                dw=np.zeros(d + r) if want_dw else None,

@@ -389,25 +389,35 @@ static int loss_one_row(int V, int r, int d, int gamma, int N, int dtype, int64_
     return 0;
 }
 
+/* cols (optional, n_cols entries in [0, V)): dZ and dW2 are returned only
+ * at these vocabulary columns -- dZ as [count, n_cols], dW2 as [r, n_cols]
+ * -- so that every row can be checked without holding R x V values.  Each
+ * row is still computed in full; only the stored columns change. */
 int oracle_block_loss(int V, int r, int d, int gamma, int N, int dtype,
                       const void* U, const void* T_logits, const void* h,
                       const int32_t* anchor, const int32_t* labels,
                       const void* W1, const void* W2, const void* w_conf,
                       const double* alpha, const double* pos_weight,
                       const int64_t* rows, int64_t n_rows,
+                      const int32_t* cols, int32_t n_cols,
                       double* loss4, double* c_star, double* conf, double* dA,
                       double* ce, double* tv, double* bce,
                       double* dZ, double* dW2, int nthreads)
 {
     if (V < 1 || r < 1 || d < 1 || gamma < 1 || N < 1 || (dtype != 0 && dtype != 1))
         return -1;
+    if (cols && n_cols < 1)
+        return -1;
+    for (int32_t c = 0; cols && c < n_cols; ++c)
+        if (cols[c] < 0 || cols[c] >= V) return -1;
     const int64_t R = (int64_t)N * gamma;
     const int64_t count = rows ? n_rows : R;
+    const int64_t W = cols ? n_cols : V; /* stored columns per dZ row */
     if (dW2 && rows)
         return -1; /* dW2 needs every row */
     double* dZbuf = dZ;
     if (dW2 && !dZ) {
-        dZbuf = malloc(sizeof(double) * (size_t)R * (size_t)V);
+        dZbuf = malloc(sizeof(double) * (size_t)R * (size_t)W);
         if (!dZbuf) return -1;
     }
     int failed = 0;
@@ -416,16 +426,20 @@ int oracle_block_loss(int V, int r, int d, int gamma, int N, int dtype,
         double* zd = malloc(sizeof(double) * (size_t)V);
         double* zt = malloc(sizeof(double) * (size_t)V);
         double* e = malloc(sizeof(double) * (size_t)r);
+        double* full = (cols && dZbuf) ? malloc(sizeof(double) * (size_t)V) : NULL;
 #pragma omp for schedule(static)
         for (int64_t t = 0; t < count; ++t) {
             const int64_t i = rows ? rows[t] : t;
             if (i < 0 || i >= R) { failed = 1; continue; }
+            double* row_out = dZbuf ? (cols ? full : dZbuf + t * W) : NULL;
             failed |= loss_one_row(V, r, d, gamma, N, dtype, i, U, T_logits, h, anchor, labels,
                                    W1, W2, w_conf, alpha, pos_weight,
                                    c_star + t, conf + t, dA + t, ce + t, tv + t, bce + t,
-                                   dZbuf ? dZbuf + t * (int64_t)V : NULL, zd, zt, e) != 0;
+                                   row_out, zd, zt, e) != 0;
+            if (cols && dZbuf)
+                for (int32_t c = 0; c < n_cols; ++c) dZbuf[t * W + c] = full[cols[c]];
         }
-        free(zd); free(zt); free(e);
+        free(zd); free(zt); free(e); free(full);
     }
     if (failed) {
         if (dZbuf != dZ) free(dZbuf);
@@ -454,14 +468,14 @@ int oracle_block_loss(int V, int r, int d, int gamma, int N, int dtype,
          * over i in order. */
 #pragma omp parallel for schedule(static) num_threads(thread_count(nthreads))
         for (int j = 0; j < r; ++j) {
-            double* out = dW2 + (int64_t)j * V;
-            for (int v = 0; v < V; ++v) out[v] = 0.0;
+            double* out = dW2 + (int64_t)j * W;
+            for (int64_t v = 0; v < W; ++v) out[v] = 0.0;
             for (int64_t i = 0; i < R; ++i) {
                 const int k = (int)(i % gamma), n = (int)(i / gamma);
                 const int prev = k == 0 ? anchor[n] : labels[i - 1];
                 const double ej = load_elem(W1, dtype, (int64_t)prev * r + j);
-                const double* dz = dZbuf + i * (int64_t)V;
-                for (int v = 0; v < V; ++v) out[v] += ej * dz[v];
+                const double* dz = dZbuf + i * W;
+                for (int64_t v = 0; v < W; ++v) out[v] += ej * dz[v];
             }
         }
     }
@@ -489,19 +503,21 @@ int oracle_block_loss_backward(int V, int r, int d, int gamma, int N, int dtype,
                                const double* dZ, const double* dA,
                                double* dW1, double* dw, double* dh, int nthreads)
 {
-    if (V < 1 || r < 1 || d < 1 || gamma < 1 || N < 1 || (dtype != 0 && dtype != 1) || !dZ || !dA)
+    if (V < 1 || r < 1 || d < 1 || gamma < 1 || N < 1 || (dtype != 0 && dtype != 1) || !dA)
         return -1;
+    if (dW1 && !dZ)
+        return -1; /* dZ is only read for dW1 */
     const int64_t R = (int64_t)N * gamma;
     int32_t* prev = malloc(sizeof(int32_t) * (size_t)R);
-    double* dE = malloc(sizeof(double) * (size_t)R * (size_t)r);
-    if (!prev || !dE) { free(prev); free(dE); return -1; }
+    double* dE = dW1 ? malloc(sizeof(double) * (size_t)R * (size_t)r) : NULL;
+    if (!prev || (dW1 && !dE)) { free(prev); free(dE); return -1; }
     for (int64_t i = 0; i < R; ++i) {
         const int n = (int)(i / gamma), k = (int)(i % gamma);
         const int x = k == 0 ? anchor[n] : labels[i - 1];
         prev[i] = (x >= 0 && x < V && isfinite(dA[i])) ? x : -1;
     }
 #pragma omp parallel for schedule(static) num_threads(thread_count(nthreads))
-    for (int64_t i = 0; i < R; ++i) {
+    for (int64_t i = 0; i < (dW1 ? R : 0); ++i) {
         for (int j = 0; j < r; ++j) {
             double acc = 0.0;
             for (int v = 0; v < V; ++v)

@@ -83,13 +83,16 @@ int oracle_block_logprob(int V, int r, int d, int gamma, int B, int dtype, int h
  * Outputs: loss4 [4] = (L, L_ce, L_tv, L_conf) over the evaluated rows;
  * per evaluated row t (t = position in `rows`, t = i when rows is NULL):
  * c_star, conf, dA (dL/d confidence logit), ce, tv, bce, and dZ [t, V]
- * (nullable); dW2 [r, V] (nullable, all rows only).  Returns 0 or -1. */
+ * (nullable); dW2 [r, V] (nullable, all rows only).  With `cols` (n_cols
+ * ids in [0, V)), dZ is [t, n_cols] and dW2 [r, n_cols]: the same values at
+ * those columns only.  Returns 0 or -1. */
 int oracle_block_loss(int V, int r, int d, int gamma, int N, int dtype,
                       const void* U, const void* T_logits, const void* h,
                       const int32_t* anchor, const int32_t* labels,
                       const void* W1, const void* W2, const void* w_conf,
                       const double* alpha, const double* pos_weight,
                       const int64_t* rows, int64_t n_rows,
+                      const int32_t* cols, int32_t n_cols,
                       double* loss4, double* c_star, double* conf, double* dA,
                       double* ce, double* tv, double* bce,
                       double* dZ, double* dW2, int nthreads);
@@ -100,8 +103,9 @@ int oracle_block_loss(int V, int r, int d, int gamma, int N, int dtype,
  *   dW1 [V, r]  sum over the rows fed token x of dZ_i W2^T + dA_i w[d:d+r]
  *   dw  [d + r] sum_i dA_i [h_i; W1[prev_i]]
  *   dh  [R, d]  dA_i w[0:d]
- * (each nullable).  Rows with an out-of-range previous token or a
- * non-finite dA are left out of the sums.  Returns 0 or -1. */
+ * (each nullable; dZ may be NULL when dW1 is).  Rows with an out-of-range
+ * previous token or a non-finite dA are left out of the sums.  Returns 0 or
+ * -1. */
 int oracle_block_loss_backward(int V, int r, int d, int gamma, int N, int dtype,
                                const void* h, const int32_t* anchor, const int32_t* labels,
                                const void* W1, const void* W2, const void* w_conf,

@@ -114,14 +114,3 @@ def schedule_brute_force(survival, sps) -> dict:
         if t > best:
             best, arg = t, ls
     return dict(length=np.array(arg), theta=best)
-
-
-def plan_depth(a: float, gamma_max: int, draft_us: float, verify_fixed_us: float,
-               verify_token_us: float) -> dict:
-    best_g, best_t = 0, -np.inf
-    for g in range(gamma_max + 1):
-        tau = (1 - a ** (g + 1)) / (1 - a) if a != 1 else g + 1.0
-        t = tau / (draft_us * g + verify_fixed_us + verify_token_us * g)
-        if t > best_t:
-            best_g, best_t = g, t
-    return dict(gamma=best_g, theta=best_t)

@@ -18,7 +18,6 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 DSPARK_HEAD_MARKOV, DSPARK_HEAD_RNN = 0, 1
 DSPARK_CALL_DRAFT, DSPARK_CALL_LOSS, DSPARK_CALL_LOSS_BACKWARD, DSPARK_CALL_VERIFY = 0, 1, 2, 3
 DSPARK_OPT_DRAFT_PATH = 1
-DSPARK_OPT_PERSIST_LAUNCH = 2
 
 STATUS_NAMES = {0: "DSPARK_OK", 1: "DSPARK_EINVAL", 2: "DSPARK_EUNSUPPORTED",
                 3: "DSPARK_EWORKSPACE", 4: "DSPARK_EDEVICE"}
@@ -70,8 +69,9 @@ def load() -> ctypes.CDLL:
     lib.dspark_sts_calibrate.restype = ctypes.c_int
     lib.dspark_schedule_prefixes.argtypes = [I32, I32, P, P, I32, P, P]
     lib.dspark_schedule_prefixes.restype = ctypes.c_int
-    lib.dspark_plan_depth.argtypes = [F, I32, F, F, F, P, P]
-    lib.dspark_plan_depth.restype = ctypes.c_int
+    U32 = ctypes.c_uint32
+    lib.dspark_noise.argtypes = [U64, U64, U32, U32, I32, I32, P, P, P, P, P]
+    lib.dspark_noise.restype = ctypes.c_int
     lib.dspark_read_device_error.argtypes = [D, P, ctypes.POINTER(I32), P]
     lib.dspark_read_device_error.restype = ctypes.c_int
     lib.dspark_set_option.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -220,13 +220,12 @@ def dspark_schedule_prefixes(survival, sps):
     return length, th.value
 
 
-def dspark_plan_depth(a, gamma_max, draft_us, verify_fixed_us, verify_token_us):
-    """Returns (depth, theta)."""
-    g = ctypes.c_int32(0)
-    th = ctypes.c_float(0)
-    _check(load().dspark_plan_depth(a, gamma_max, draft_us, verify_fixed_us, verify_token_us,
-                                    ctypes.addressof(g), ctypes.addressof(th)))
-    return g.value, th.value
+def dspark_noise(seed, offset, c1, c2, v0, n, words_in=None, words=None, gumbel=None,
+                 gumbel_log2=None, stream=None):
+    """Device Philox words and Gumbel transforms (see include/dspark.h);
+    tensors are device buffers of n elements, each optional."""
+    _check(load().dspark_noise(seed, offset, c1, c2, v0, n, _p(words_in), _p(words), _p(gumbel),
+                               _p(gumbel_log2), _stream(stream)))
 
 
 def dspark_read_device_error(dims, workspace, stream=None) -> int:

@@ -76,9 +76,7 @@ hipError_t record(hipStream_t s) {
 }  // namespace
 
 thread_local int g_draft_path = 0;
-thread_local int g_persist_launch = 0;
 int draft_path_option() { return g_draft_path; }
-int persist_launch_option() { return g_persist_launch; }
 
 bool profiling_enabled() { return g_prof.on; }
 hipError_t profile_begin(hipStream_t s) { return g_prof.on ? record(s) : hipSuccess; }
@@ -313,18 +311,15 @@ dspark_status dspark_schedule_prefixes(int32_t R, int32_t gamma, const float* su
     return ok();
 }
 
-dspark_status dspark_plan_depth(float a, int32_t gamma_max, float draft_us, float verify_fixed_us,
-                                float verify_token_us, int32_t* gamma_out, float* theta) {
-    if (!(a >= 0.0f && a <= 1.0f)) return fail(DSPARK_EINVAL, "a = %g is outside [0, 1]", a);
-    if (gamma_max < 0 || !gamma_out) return fail(DSPARK_EINVAL, "gamma_max < 0 or gamma_out is NULL");
-    if (!(draft_us >= 0.0f) || !(verify_fixed_us >= 0.0f) || !(verify_token_us >= 0.0f) ||
-        !(verify_fixed_us > 0.0f || (gamma_max > 0 && draft_us + verify_token_us > 0.0f)))
-        return fail(DSPARK_EINVAL, "costs must be >= 0 with a positive cycle cost");
-    if (!(verify_fixed_us > 0.0f))
-        return fail(DSPARK_EINVAL, "verify_fixed_us must be positive (the g = 0 cycle)");
-    double t = 0.0;
-    *gamma_out = dspark::plan_depth(a, gamma_max, draft_us, verify_fixed_us, verify_token_us, &t);
-    if (theta) *theta = static_cast<float>(t);
+dspark_status dspark_noise(uint64_t seed, uint64_t offset, uint32_t c1, uint32_t c2, int32_t v0, int32_t n,
+                           const uint32_t* words_in, uint32_t* words, float* gumbel, float* gumbel_log2,
+                           void* hip_stream) {
+    if (n < 0 || v0 < 0 || static_cast<int64_t>(v0) + n > (int64_t(1) << 31))
+        return fail(DSPARK_EINVAL, "v0 = %d, n = %d: need v0 >= 0, n >= 0 and v0 + n <= 2^31", v0, n);
+    if (n == 0) return ok();
+    const hipError_t e = dspark::launch_noise(seed, offset, c1, c2, static_cast<uint32_t>(v0), n, words_in, words,
+                                              gumbel, gumbel_log2, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(DSPARK_EDEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 
@@ -354,11 +349,6 @@ dspark_status dspark_set_option(int option, int value) {
     if (option == DSPARK_OPT_DRAFT_PATH) {
         if (value < 0 || value > 2) return fail(DSPARK_EINVAL, "draft path %d is not 0, 1 or 2", value);
         dspark::g_draft_path = value;
-        return ok();
-    }
-    if (option == DSPARK_OPT_PERSIST_LAUNCH) {
-        if (value < 0 || value > 1) return fail(DSPARK_EINVAL, "launch mode %d is not 0 or 1", value);
-        dspark::g_persist_launch = value;
         return ok();
     }
     return fail(DSPARK_EINVAL, "unknown option %d", option);

@@ -148,6 +148,16 @@ __device__ __forceinline__ Stats shfl_xor_stats(const Stats& a, int mask) {
 
 __device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
 
+// Wait until every vector-memory operation this wave has issued -- loads,
+// stores and atomics, with or without return -- has completed.  A
+// workgroup-scope release fence does not do this on gfx950: the waves of a
+// workgroup share one vector L1, so the memory model emits no wait for it
+// and the operations may still be in flight.  A hand-off to other
+// workgroups through device-scope atomics (an arrival count, a done count)
+// must therefore be preceded by this wait in every wave whose earlier
+// atomics the other side will read.
+__device__ __forceinline__ void wait_vmem_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Block-wide float sum over blockDim.x threads (multiple of 64), fixed order.
 __device__ __forceinline__ float block_sum(float v, float* lds /* >= 16 */) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);

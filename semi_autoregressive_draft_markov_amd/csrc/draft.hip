@@ -15,6 +15,8 @@
 #include <math.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "device_common.h"
 #include "internal.h"
 #include "mfma_tile.h"
@@ -36,14 +38,22 @@ int draft_partials(const dspark_dims& d) {
 }
 
 // Upper bound on the single-launch grid: two workgroups per compute unit of
-// the current device (256 units if no device can be queried).
+// the current device (256 units if no device can be queried).  The count is
+// cached per device: it sizes the workspace of every call.
 int draft_persist_max_wg() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices] = {};
     int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
-        cus = 256;
+        return 2 * 256;
     }
+    if (dev >= 0 && dev < kMaxDevices && (cus = cached[dev].load(std::memory_order_relaxed)) > 0) return 2 * cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        return 2 * 256;
+    }
+    if (dev >= 0 && dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
     return 2 * cus;
 }
 

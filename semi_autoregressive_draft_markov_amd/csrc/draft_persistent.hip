@@ -32,6 +32,7 @@
 #include <atomic>
 #include <chrono>
 #include <mutex>
+#include <vector>
 
 #include "device_common.h"
 #include "internal.h"
@@ -89,7 +90,9 @@ __device__ __forceinline__ void start_barrier_arrive(const PersistArgs& a, int n
     if (wg == 0)
         for (int i = threadIdx.x; i < kDraftBarWords; i += blockDim.x)
             __hip_atomic_store(a.bar + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    // every wave's clearing stores complete before the flag is raised (a
+    // late clear would otherwise overwrite a step-0 maximum)
+    wait_vmem_complete();
     __syncthreads();
     if (threadIdx.x == 0) __hip_atomic_store(a.flags + wg, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -124,9 +127,11 @@ __device__ __forceinline__ void start_barrier_wait(const PersistArgs& a) {
 // the barrier words; the softmax partials are only read after the kernel):
 // those are coherent at the device level (sc1), so the barrier needs no L2
 // write-back or invalidate, which on this chip flush or drop a whole XCD's L2
-// and cost several microseconds each.  A workgroup-scope release (each wave
-// waits for its own memory operations, the key atomics included, to
-// complete) and the workgroup barrier come before the arrival.  Arrivals
+// and cost several microseconds each.  Before the arrival every wave waits
+// until its own memory operations, the key atomics included, have completed
+// (an explicit vmcnt wait: a workgroup-scope fence emits none), then the
+// workgroup barrier; so when a workgroup sees the last arrival, every key
+// maximum of the step is already in place.  Arrivals
 // are spread over 8 counters to limit the contention on any one of them:
 // workgroup wg adds 1 to counter wg % 8.  Every workgroup then polls all
 // 8 counters at once (one device-scope load per lane of its first wave, a
@@ -140,7 +145,7 @@ __device__ __forceinline__ void start_barrier_wait(const PersistArgs& a) {
 // so a broken launch cannot hang the device.
 // The barrier in two halves, so that independent work (the next step's
 // Gumbel terms) can run while the arrival's atomic is in flight:
-// barrier_arrive (after the release fence and a workgroup barrier) issues
+// barrier_arrive (after the completion wait and a workgroup barrier) issues
 // thread 0's add to its group counter; barrier_finish waits for all
 // counters.
 __device__ __forceinline__ void barrier_arrive(uint32_t* bar, uint32_t wg) {
@@ -747,12 +752,12 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         publish(k, 0, a.B);
         if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
         // next step's noise of group 0 while the key atomics complete,
-        // the release fence and workgroup barrier, the arrival and the
-        // wait for the other workgroups, with group 1's noise computed while
-        // the arrival is in flight (the barrier's latency, about as long,
-        // is hidden behind it)
+        // the wait for their completion and the workgroup barrier, the
+        // arrival and the wait for the other workgroups, with group 1's
+        // noise computed while the arrival is in flight (the barrier's
+        // latency, about as long, is hidden behind it)
         noise_ahead(k + 1, 0, scale_s[n] > 0.0f);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        wait_vmem_complete();
         __syncthreads();
         barrier_arrive(a.bar, static_cast<uint32_t>(wg));
         noise_ahead(k + 1, 1, 16 + n < a.B && scale_s[16 + n] > 0.0f);
@@ -903,6 +908,48 @@ static void (*persist_kernel(bool grouped, bool ahead))(PersistArgs) {
     return ahead ? k_draft_persistent<KC, false, true> : k_draft_persistent<KC, false, false>;
 }
 
+// Device facts a plan needs, cached per (device, kernel, LDS bytes): the
+// compute-unit count and the occupancy answer do not change while the
+// process runs, and asking the runtime again on every call costs host time
+// on a path that is otherwise a single launch.  The kernel's dynamic-LDS
+// limit is raised to the most any plan uses once per (device, kernel), so a
+// smaller plan met first cannot leave it too low for a larger one.
+struct SlotCacheEntry {
+    int dev;
+    const void* fn;
+    size_t lds;
+    int cus;
+    int per_cu;
+};
+static std::mutex g_slot_mu;
+static std::vector<SlotCacheEntry> g_slot_cache;
+
+static bool resident_slots(const void* fn, size_t lds, int* cus_out, int* per_cu_out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    std::lock_guard<std::mutex> lock(g_slot_mu);
+    bool attr_set = false;
+    for (const SlotCacheEntry& e : g_slot_cache) {
+        if (e.dev != dev || e.fn != fn) continue;
+        attr_set = true;
+        if (e.lds == lds) {
+            *cus_out = e.cus;
+            *per_cu_out = e.per_cu;
+            return true;
+        }
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+    if (!attr_set && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(kPersistLdsMax)) != hipSuccess)
+        return false;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kPThreads, lds) != hipSuccess) return false;
+    g_slot_cache.push_back(SlotCacheEntry{dev, fn, lds, cus, per_cu});
+    *cus_out = cus;
+    *per_cu_out = per_cu;
+    return true;
+}
+
 template <int KC>
 static PersistPlan plan_for(const dspark_dims& D) {
     PersistPlan p;
@@ -911,21 +958,14 @@ static PersistPlan plan_for(const dspark_dims& D) {
     p.ahead = !p.grouped && Bpad <= 32 && persist_lds<KC>(Bpad, D.B, false, true) <= kPersistLdsMax;
     p.lds = persist_lds<KC>(Bpad, D.B, p.grouped, p.ahead);
     if (p.lds > kPersistLdsMax) return p;
-    int dev = 0, cus = 0, coop = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return p;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return p;
-    if (persist_launch_option() == 1 &&
-        (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop))
-        return p;
+    int cus = 0, per_cu = 0;
     void (*fn)(PersistArgs) = persist_kernel<KC>(p.grouped, p.ahead);
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(p.lds)) != hipSuccess)
+    if (!resident_slots(reinterpret_cast<const void*>(fn), p.lds, &cus, &per_cu)) {
+        (void)hipGetLastError();
         return p;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kPThreads, p.lds) !=
-        hipSuccess)
-        return p;
+    }
     if (per_cu < 1) return p;
-    const int nWG = std::min(per_cu, 1) * cus;
+    const int nWG = cus;  // one workgroup per compute unit
     // columns held on chip: 64 per wave in registers + 16 per wave in LDS
     if (static_cast<int64_t>(D.V) > static_cast<int64_t>(kPWaves) * nWG * 80) return p;
     if (nWG > draft_persist_max_wg()) return p;
@@ -1011,13 +1051,8 @@ static hipError_t launch_persist_kc(const DraftArgs& A) {
     if (e != hipSuccess) return e;
     void* args[] = {&p};
     void (*fn)(PersistArgs) = persist_kernel<KC>(plan.grouped, plan.ahead);
-    const size_t lds = plan.lds;
-    if (persist_launch_option() == 0)
-        e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG), dim3(kPThreads), args, lds,
-                            A.stream);
-    else
-        e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG), dim3(kPThreads),
-                                       args, lds, A.stream);
+    e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(plan.nWG), dim3(kPThreads), args, plan.lds,
+                        A.stream);
     if (e != hipSuccess) return e;
     if ((e = profile_end(A.stream)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_persist_finish, dim3(D.B), dim3(kFinishWaves * kWave), 0, A.stream, p);

@@ -175,19 +175,20 @@ struct DraftArgs {
 // Enqueue the whole draft call.  Returns hipSuccess or the first launch error.
 hipError_t launch_draft(const DraftArgs& a);
 
+// Device random numbers of the kernels, one element per thread (noise.hip).
+hipError_t launch_noise(uint64_t seed, uint64_t offset, uint32_t ctr1, uint32_t ctr2, uint32_t v0, int n,
+                        const uint32_t* words_in, uint32_t* words, float* gumbel, float* gumbel2,
+                        hipStream_t stream);
+
 // Host-side post-draft stages (schedule.cpp).
 std::vector<double> sts_default_grid();
 void sts_calibrate(int N, int gamma, const float* logit, const int32_t* accepted,
                    const std::vector<double>& grid, int bins, float* temperature, float* ece_before,
                    float* ece_after);
 double schedule_prefixes(int R, int gamma, const float* survival, const float* sps, int32_t* length);
-int plan_depth(double a, int gamma_max, double draft_us, double verify_fixed_us,
-               double verify_token_us, double* theta);
 
 // Per-thread choice of drafting path (see dspark_set_option).
 int draft_path_option();
-// Per-thread launch mode of the single-launch kernel: 0 ordinary, 1 cooperative.
-int persist_launch_option();
 
 // Per-thread event timing of the dominant kernel (see dspark_profile_*).
 bool profiling_enabled();

@@ -126,26 +126,4 @@ double schedule_prefixes(int R, int gamma, const float* survival, const float* s
     return best;
 }
 
-int plan_depth(double a, int gamma_max, double draft_us, double verify_fixed_us,
-               double verify_token_us, double* theta) {
-    int best = 0;
-    double best_t = -INFINITY;
-    for (int g = 0; g <= gamma_max; ++g) {
-        // tau = (1 - a^(g+1)) / (1 - a) summed as the series 1 + a + ... + a^g,
-        // which also holds at a = 1
-        double tau = 0.0, ap = 1.0;
-        for (int i = 0; i <= g; ++i) {
-            tau += ap;
-            ap *= a;
-        }
-        const double t = tau / (draft_us * g + verify_fixed_us + verify_token_us * g);
-        if (t > best_t) {
-            best_t = t;
-            best = g;
-        }
-    }
-    *theta = best_t;
-    return best;
-}
-
 }  // namespace dspark

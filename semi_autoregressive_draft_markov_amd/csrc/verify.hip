@@ -544,9 +544,10 @@ __global__ __launch_bounds__(256) void k_v_sample(const T* __restrict__ Tl, cons
     if (threadIdx.x == 0) {
         if (kr[0] != kKeyNone) atomicMax(reinterpret_cast<unsigned long long*>(keys + 2 * b), kr[0]);
         atomicMax(reinterpret_cast<unsigned long long*>(keys + 2 * b + 1), kt[0]);
-        // the key atomics are device-coherent: waiting for their completion
-        // (no cache write-back) orders them before the count
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        // the key atomics are device-coherent: waiting here until both have
+        // completed (no cache write-back) orders them before the count, so
+        // the workgroup that counts last reads both maxima complete
+        wait_vmem_complete();
         last = __hip_atomic_fetch_add(done + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
     }
     __syncthreads();

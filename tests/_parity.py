@@ -2,7 +2,9 @@
 
 Tolerances (fixed for this method):
   tokens   exact, except where the oracle's two largest perturbed logits are
-           closer than 1e-5 and the GPU chose the runner-up;
+           closer than 1e-5 (but not equal) and the GPU chose the runner-up;
+           at an exact tie (gap 0) the lowest index, which is the oracle's
+           token, is required;
   logp     |delta log p| <= 2e-3, i.e. 2e-3 relative on the probability;
   conf, survival, c*, losses   relative 2e-3;
   dlogits  per-row relative L2 <= 2e-3; dW2 per-column and Frobenius
@@ -32,7 +34,7 @@ def check_draft(inp, gpu: dict, seed: int, offset: int, block_ids=None, label: s
     tok = np.asarray(gpu["tokens"])
     ora = oracle.draft_block(inp, seed=seed, offset=offset, forced_prev=tok, block_ids=block_ids)
     eq = tok == ora["tokens"]
-    tie_ok = (~eq) & (ora["gap"] < TIE) & (tok == ora["second"])
+    tie_ok = (~eq) & (ora["gap"] > 0) & (ora["gap"] < TIE) & (tok == ora["second"])
     bad = ~(eq | tie_ok)
     if bad.any():
         idx = np.argwhere(bad)[:5]

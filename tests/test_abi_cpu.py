@@ -100,6 +100,14 @@ def test_draft_rejects_null_pointers_and_small_workspace(lib):
     assert e.value.status == lib.DSPARK_EINVAL and "aligned" in str(e.value)
 
 
+def test_noise_rejects_bad_ranges(lib):
+    for v0, n in ((-1, 4), (0, -1), ((1 << 31) - 2, 4)):
+        with pytest.raises(lib.DsparkError) as e:
+            lib.dspark_noise(0, 0, 0, 0, v0, n, stream=0)
+        assert e.value.status == lib.DSPARK_EINVAL
+    lib.dspark_noise(0, 0, 0, 0, 0, 0, stream=0)  # n = 0: nothing to do, no device work
+
+
 def test_read_device_error_rejects_null(lib):
     d = lib.make_dims(1000, 64, 32, 7, 4)
     st = lib.load().dspark_read_device_error(ctypes.byref(d), None, None, None)
@@ -116,8 +124,7 @@ def test_product_path_never_imports_the_oracle():
 
 
 def test_set_option_validates(lib):
-    for opt, good, bad in ((lib.DSPARK_OPT_DRAFT_PATH, (0, 1, 2), (-1, 3)),
-                           (lib.DSPARK_OPT_PERSIST_LAUNCH, (0, 1), (-1, 2))):
+    for opt, good, bad in ((lib.DSPARK_OPT_DRAFT_PATH, (0, 1, 2), (-1, 3)),):
         for v in good:
             lib.dspark_set_option(opt, v)
         for v in bad:
@@ -125,7 +132,9 @@ def test_set_option_validates(lib):
                 lib.dspark_set_option(opt, v)
             assert e.value.status == lib.DSPARK_EINVAL
     lib.dspark_set_option(lib.DSPARK_OPT_DRAFT_PATH, 0)
-    lib.dspark_set_option(lib.DSPARK_OPT_PERSIST_LAUNCH, 0)
+    # the cooperative-launch option (formerly 2) no longer exists
+    with pytest.raises(lib.DsparkError):
+        lib.dspark_set_option(2, 0)
     with pytest.raises(lib.DsparkError) as e:
         lib.dspark_set_option(99, 0)
     assert "unknown option" in str(e.value)

@@ -29,11 +29,10 @@ def ops():
 MULTI, SINGLE = 1, 2  # per-step launches / single-launch kernel
 
 
-def run_gpu(ops, inp, seed=0, offset=0, path=0, launch=0):
+def run_gpu(ops, inp, seed=0, offset=0, path=0):
     import torch
     from semi_autoregressive_draft_markov_amd import binding
     binding.dspark_set_option(binding.DSPARK_OPT_DRAFT_PATH, path)
-    binding.dspark_set_option(binding.DSPARK_OPT_PERSIST_LAUNCH, launch)
     t = synth.to_torch(inp)
     out = ops.draft_block(t["U"], t["h"], t["anchor"], t["W1"], t["W2"], t["w_conf"],
                           t["temperature"], W_rnn=t["W_rnn"], seed=seed, offset=offset)
@@ -167,20 +166,6 @@ def test_paths_agree(ops):
     assert np.array_equal(a["conf"], b["conf"]) or np.allclose(a["conf"], b["conf"], rtol=1e-6)
 
 
-PLAIN, COOP = 0, 1  # launch modes of the single-launch kernel
-
-
-def test_cooperative_launch_matches_plain(ops):
-    # the single-launch kernel started with hipLaunchCooperativeKernel
-    # computes the same bits as with the default ordinary launch
-    inp = small(V=4104, r=256, d=64, gamma=7, B=40, seed=14, temperature=[1.0] * 30 + [0.0] * 10)
-    a = run_gpu(ops, inp, seed=5, path=SINGLE, launch=PLAIN)
-    b = run_gpu(ops, inp, seed=5, path=SINGLE, launch=COOP)
-    for k in ("tokens", "logp", "conf", "survival"):
-        assert np.array_equal(a[k], b[k], equal_nan=True), k
-    check_draft(inp, b, 5, 0, label="cooperative launch")
-
-
 @pytest.mark.parametrize("path", [MULTI, SINGLE])
 def test_out_of_range_anchor_is_flagged(ops, path):
     from semi_autoregressive_draft_markov_amd import binding
@@ -225,13 +210,87 @@ def test_sampler_law_on_gpu(ops, dtype, V, path):
 
 # -------------------------------------------------------------- full sizes
 
-@pytest.mark.parametrize("path,launch", [(MULTI, 0), (SINGLE, PLAIN), (SINGLE, COOP)])
-def test_qwen3_4b_shape_all_blocks(ops, path, launch):
+@pytest.mark.parametrize("path", [MULTI, SINGLE])
+def test_qwen3_4b_shape_all_blocks(ops, path):
     inp = synth.config_inputs(2)
-    note("case: qwen3-4b-shaped V151936 r256 B32 (all blocks) path %d launch %d" % (path, launch))
-    g = run_gpu(ops, inp, seed=0, path=path, launch=launch)
+    note("case: qwen3-4b-shaped V151936 r256 B32 (all blocks) path %d" % path)
+    g = run_gpu(ops, inp, seed=0, path=path)
     info = check_draft(inp, g, 0, 0, label="qwen3-4b shape")
     note("  ties allowed: %d, max |dlogp| %.2e" % (info["ties"], info["logp_err"]))
+
+
+@pytest.mark.parametrize("path", [MULTI, SINGLE])
+def test_qwen3_4b_shape_strong_bias_all_blocks(ops, path):
+    # W1, W2 ~ N(0, 0.25^2): the transition bias has std ~1 (r = 256), next
+    # to U's 3, so every column -- the register tiles and the 20864 columns
+    # past 131072 that the single-launch kernel holds in LDS fragments --
+    # moves the argmax; sampled, greedy and tempered blocks
+    temps = ([1.0, 0.0, 0.7, 1.0] * 8)[:32]
+    inp = synth.config_inputs(2, w1_std=0.25, w2_std=0.25, temperature=temps, seed=1202)
+    note("case: qwen3-4b-shaped strong bias V151936 r256 B32 (all blocks) path %d" % path)
+    g = run_gpu(ops, inp, seed=5, offset=3, path=path)
+    info = check_draft(inp, g, 5, 3, label="qwen3-4b shape strong bias")
+    note("  ties allowed: %d, max |dlogp| %.2e" % (info["ties"], info["logp_err"]))
+
+
+def plant_ties(inp, rng, cols_per_row):
+    """Greedy blocks with W2 = 0: the bias is exactly 0 on both sides, so z
+    = U exactly.  At every (block, position) the value 32 (above every
+    N(0, 9) draw in bf16) is planted at the given columns; the argmax is
+    then an exact tie whose lowest index must win."""
+    U = inp.U.copy()
+    top = synth.f32_to_bf16_bits(np.array([32.0], np.float32))[0] if inp.dtype == "bf16" else np.float32(32.0)
+    want = np.zeros((inp.B, inp.gamma), np.int32)
+    for b in range(inp.B):
+        for k in range(inp.gamma):
+            cols = cols_per_row(b, k, rng)
+            U[b, k, cols] = top
+            want[b, k] = min(cols)
+    inp.U = U
+    inp.W2 = np.zeros_like(inp.W2)
+    inp.temperature = np.zeros(inp.B, np.float32)
+    return want
+
+
+@pytest.mark.parametrize("path", [MULTI, SINGLE])
+def test_exact_ties_take_the_lowest_index(ops, path):
+    # pairs of equal maxima: in one lane's columns, across lanes, across
+    # waves and workgroups, and (single-launch kernel) between a register
+    # tile column and an LDS-fragment column past 131072
+    inp = synth.config_inputs(2, seed=1203)
+    V = inp.V
+
+    def cols(b, k, rng):
+        kind = (b + k) % 5
+        v = int(rng.integers(0, V - 70000))
+        if kind == 0:
+            return [v, v + 1]
+        if kind == 1:
+            return [v + 37, v + 5]
+        if kind == 2:
+            return [v + 64 * 9, v]
+        if kind == 3:
+            return [v + 60000, v + 3, v + 61000]
+        return [int(rng.integers(131072, V)), int(rng.integers(0, 131072))]
+
+    want = plant_ties(inp, np.random.default_rng(9), cols)
+    note("case: qwen3-4b-shaped exact ties, greedy, W2 = 0, path %d" % path)
+    g = run_gpu(ops, inp, seed=0, path=path)
+    assert np.array_equal(g["tokens"], want), np.argwhere(g["tokens"] != want)[:5]
+    check_draft(inp, g, 0, 0, label="exact ties")
+
+
+def test_exact_ties_small_vocabulary(ops):
+    # the per-step driver's vector path (f32) and a ragged bf16 tail
+    for dtype, V in (("f32", 999), ("bf16", 1000)):
+        inp = small(V=V, r=32 if dtype == "bf16" else 48, d=16, gamma=4, B=6, dtype=dtype, seed=61)
+        want = plant_ties(inp, np.random.default_rng(10),
+                          lambda b, k, rng: sorted(rng.choice(V, size=2 + (b % 2), replace=False)
+                                                   .tolist(), reverse=True))
+        note("case: exact ties %s V%d" % (dtype, V))
+        g = run_gpu(ops, inp, seed=0)
+        assert np.array_equal(g["tokens"], want), (dtype, np.argwhere(g["tokens"] != want)[:5])
+        check_draft(inp, g, 0, 0, label="exact ties " + dtype)
 
 
 def test_qwen3_4b_shape_mixed_temperature_single_launch(ops):
@@ -255,7 +314,6 @@ def test_single_launch_dirty_reused_workspace(ops):
     import torch
     from semi_autoregressive_draft_markov_amd import binding
     binding.dspark_set_option(binding.DSPARK_OPT_DRAFT_PATH, SINGLE)
-    binding.dspark_set_option(binding.DSPARK_OPT_PERSIST_LAUNCH, 0)
     big = small(V=4104, r=256, d=64, gamma=6, B=28, seed=51, temperature=[1.0] * 20 + [0.0] * 8)
     tb = synth.to_torch(big)
     dims = ops.draft_dims(tb["U"], tb["h"], tb["W1"])
@@ -278,22 +336,17 @@ def test_single_launch_dirty_reused_workspace(ops):
 
 
 @pytest.mark.parametrize("path", [MULTI, SINGLE])
-def test_qwen3_14b_shape_sampled_blocks(ops, path):
+def test_qwen3_14b_shape_all_blocks(ops, path):
     inp = synth.config_inputs(4)
-    note("case: qwen3-14b-shaped V151936 r256 B256 half greedy (16 sampled blocks) path %d" % path)
+    note("case: qwen3-14b-shaped V151936 r256 B256 half greedy (all blocks) path %d" % path)
     g = run_gpu(ops, inp, seed=0, path=path)
-    pick = np.array([0, 1, 37, 64, 100, 126, 127, 128, 129, 150, 200, 201, 222, 250, 254, 255])
-    sub = synth.subset(inp, pick)
-    check_draft(sub, {k: g[k][pick] for k in ("tokens", "logp", "conf", "survival")}, 0, 0,
-                block_ids=pick, label="qwen3-14b shape")
-    assert np.all(g["tokens"] >= 0)
+    info = check_draft(inp, g, 0, 0, label="qwen3-14b shape")
+    note("  ties allowed: %d, max |dlogp| %.2e" % (info["ties"], info["logp_err"]))
 
 
-def test_gemma4_rnn_shape_sampled_blocks(ops):
+def test_gemma4_rnn_shape_all_blocks(ops):
     inp = synth.config_inputs(5)
-    note("case: gemma4-12b-shaped rnn V262144 r256 B128 (8 sampled blocks)")
+    note("case: gemma4-12b-shaped rnn V262144 r256 B128 (all blocks)")
     g = run_gpu(ops, inp, seed=0)
-    pick = np.array([0, 5, 31, 64, 77, 100, 126, 127])
-    sub = synth.subset(inp, pick)
-    check_draft(sub, {k: g[k][pick] for k in ("tokens", "logp", "conf", "survival")}, 0, 0,
-                block_ids=pick, label="gemma4 rnn shape")
+    info = check_draft(inp, g, 0, 0, label="gemma4 rnn shape")
+    note("  ties allowed: %d, max |dlogp| %.2e" % (info["ties"], info["logp_err"]))

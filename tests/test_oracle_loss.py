@@ -341,3 +341,21 @@ def test_dw_conf_matches_finite_differences(oracle_lib):
     for m in (0, 2, inp.d, inp.d + 3):
         fd = _fd(oracle_lib, inp, "w_conf", (m,), alpha)
         assert abs(fd - dw[m]) < 1e-7 + 1e-5 * abs(dw[m]), (m, fd, dw[m])
+
+
+def test_column_subset_returns_the_same_values(oracle_lib):
+    oracle = oracle_lib
+    # the column-subset outputs are the full outputs at those columns (the
+    # full-size GPU check relies on this to avoid R x V float64 values)
+    inp = synth.make_inputs(V=300, r=16, d=8, gamma=3, B=4, dtype="bf16", seed=71, w1_std=0.3,
+                            w2_std=0.3, anchors="uniform", target_noise_std=1.0)
+    full = oracle.block_loss(inp)
+    cols = np.array([299, 0, 17, 150, 17])
+    sub = oracle.block_loss(inp, cols=cols)
+    assert np.array_equal(sub["dZ"], full["dZ"][:, cols])
+    assert np.allclose(sub["dW2"], full["dW2"][:, cols], rtol=1e-12, atol=1e-15)
+    for k in ("loss4", "c_star", "conf", "dA"):
+        assert np.array_equal(sub[k], full[k]), k
+    rows = np.array([5, 0, 11])
+    part = oracle.block_loss(inp, rows=rows, cols=cols, want_dW2=False)
+    assert np.array_equal(part["dZ"], full["dZ"][rows][:, cols])

@@ -7,10 +7,7 @@
     at the first position the calibrated ECE never exceeds the raw one;
   - scheduler: equals exhaustive search over every prefix-length combination
     on small batches with survivals that decrease along each request; a flat
-    steps/s curve verifies every drafted token, a steep one none;
-  - depth planner: tau(a, g) equals the geometric series, the choice equals
-    exhaustive search, a = 0 never drafts, a = 1 with free tokens drafts to
-    the limit.
+    steps/s curve verifies every drafted token, a steep one none.
 """
 import numpy as np
 
@@ -65,18 +62,3 @@ def test_scheduler_extremes():
     assert list(sched.schedule_prefixes(s, flat)["length"]) == [3, 3]
     steep = np.concatenate([[50.0] * 3, [1.0] * 6])  # any extra token costs almost everything
     assert list(sched.schedule_prefixes(s, steep)["length"]) == [0, 0]
-
-
-def test_depth_planner():
-    for a in (0.0, 0.3, 0.8, 0.95):
-        for g in range(8):
-            series = sum(a ** i for i in range(g + 1))
-            assert abs(((1 - a ** (g + 1)) / (1 - a)) - series) < 1e-12
-    rng = np.random.default_rng(4)
-    for _ in range(50):
-        a, d, f, t = rng.random(), rng.random() * 50, 10 + rng.random() * 100, rng.random() * 20
-        p = sched.plan_depth(a, 12, d, f, t)
-        vals = [sum(a ** i for i in range(g + 1)) / (d * g + f + t * g) for g in range(13)]
-        assert p["gamma"] == int(np.argmax(vals))
-    assert sched.plan_depth(0.0, 10, 5.0, 100.0, 1.0)["gamma"] == 0
-    assert sched.plan_depth(1.0, 10, 0.0, 100.0, 0.0)["gamma"] == 10
