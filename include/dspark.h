@@ -324,17 +324,25 @@ dspark_status dspark_read_device_error(const dspark_dims* dims, const void* work
 dspark_status dspark_set_option(int option, int value);
 
 /* Kernel timing for measurement.  While enabled on the calling thread, each
- * dspark_draft_block / dspark_block_loss / dspark_block_loss_backward /
- * dspark_verify_block call also records a pair of HIP events on `hip_stream`
- * around every launch of its dominant kernel (the V-streaming step kernel
- * when drafting, the V-streaming passes of the loss, the matrix-core dZ W2^T
- * kernel of the backward, the draft-row kernel of the verification).  dspark_profile_read() waits for those events and returns (HOST
+ * call records a pair of HIP events on `hip_stream` around every launch of
+ * its timed kernels, in this order per call:
+ *   dspark_draft_block          the single-launch drafting kernel (one pair),
+ *                               or the V-streaming step kernel (one per step);
+ *   dspark_block_loss           pass 1, pass 2, pass 3 (when dlogits is
+ *                               given) of the V-streaming passes, then the
+ *                               dW2 contraction (when dW2 is given);
+ *   dspark_block_loss_backward  the matrix-core dZ W2^T kernel;
+ *   dspark_verify_block         the draft-row kernel.
+ * dspark_profile_read() waits for those events and returns (HOST
  * out-pointers) the summed milliseconds and the number of timed launches
- * since the previous read, then forgets them.  Events are created on first
- * use and reused; enable = 0 stops recording.  Returns DSPARK_EDEVICE if a
- * HIP event call fails. */
+ * since the previous read, then forgets them; dspark_profile_read_each()
+ * returns each launch's milliseconds in recording order instead (EINVAL,
+ * with *launches set to the count, if `capacity` is too small; nothing is
+ * forgotten then).  Events are created on first use and reused; enable = 0
+ * stops recording.  Returns DSPARK_EDEVICE if a HIP event call fails. */
 dspark_status dspark_profile_enable(int enable);
 dspark_status dspark_profile_read(float* kernel_ms, int32_t* launches);
+dspark_status dspark_profile_read_each(float* kernel_ms, int32_t capacity, int32_t* launches);
 
 /* Name of the dominant kernel dspark_draft_block runs for `dims` on the
  * current device with this thread's options, as a kernel trace lists it

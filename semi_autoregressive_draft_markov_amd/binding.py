@@ -80,6 +80,8 @@ def load() -> ctypes.CDLL:
     lib.dspark_profile_enable.restype = ctypes.c_int
     lib.dspark_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I32)]
     lib.dspark_profile_read.restype = ctypes.c_int
+    lib.dspark_profile_read_each.argtypes = [P, I32, ctypes.POINTER(I32)]
+    lib.dspark_profile_read_each.restype = ctypes.c_int
     lib.dspark_draft_kernel_name.argtypes = [D]
     lib.dspark_draft_kernel_name.restype = ctypes.c_char_p
     lib.dspark_last_error.argtypes = []
@@ -245,6 +247,15 @@ def dspark_profile_read():
     n = ctypes.c_int32(0)
     _check(load().dspark_profile_read(ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def dspark_profile_read_each(capacity: int = 4096):
+    """Milliseconds of each timed launch since the last read, in recording
+    order (a list of floats)."""
+    buf = (ctypes.c_float * max(capacity, 1))()
+    n = ctypes.c_int32(0)
+    _check(load().dspark_profile_read_each(buf, capacity, ctypes.byref(n)))
+    return [buf[i] for i in range(n.value)]
 
 
 def dspark_set_option(option: int, value: int) -> None:

@@ -380,6 +380,30 @@ dspark_status dspark_profile_read(float* kernel_ms, int32_t* launches) {
     return ok();
 }
 
+dspark_status dspark_profile_read_each(float* kernel_ms, int32_t capacity, int32_t* launches) {
+    if (!launches || capacity < 0 || (capacity > 0 && !kernel_ms))
+        return fail(DSPARK_EINVAL, "launches must not be NULL, kernel_ms must hold capacity entries");
+    auto& P = dspark::g_prof;
+    const size_t pairs = P.used / 2;
+    if (pairs > static_cast<size_t>(capacity)) {
+        *launches = static_cast<int32_t>(pairs);
+        return fail(DSPARK_EINVAL, "%zu timed launches, capacity %d", pairs, capacity);
+    }
+    for (size_t i = 0; i < pairs; ++i) {
+        hipError_t e = hipEventSynchronize(P.pool[2 * i + 1]);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, P.pool[2 * i], P.pool[2 * i + 1]);
+        if (e != hipSuccess) {
+            P.used = 0;
+            return fail(DSPARK_EDEVICE, "profiling event failed: %s", hipGetErrorString(e));
+        }
+        kernel_ms[i] = ms;
+    }
+    P.used = 0;
+    *launches = static_cast<int32_t>(pairs);
+    return ok();
+}
+
 const char* dspark_draft_kernel_name(const dspark_dims* dims) {
     if (check_dims(dims) != DSPARK_OK) return "";
     return dspark::draft_kernel_name(*dims);

@@ -907,6 +907,7 @@ static hipError_t launch_loss_t(const LossArgs& la) {
         if ((pe = profile_end(la.stream)) != hipSuccess) return pe;
     }
     if (la.dW2) {
+        if ((pe = profile_begin(la.stream)) != hipSuccess) return pe;
         if (L.mfma) {
             const dim3 grid((D.V + kDw2Cols - 1) / kDw2Cols);
             if (a.dz_bf16)
@@ -924,6 +925,7 @@ static hipError_t launch_loss_t(const LossArgs& la) {
                                la.stream, static_cast<const float*>(la.dlogits), F(L.ef), D.V, D.r, R,
                                la.dW2);
         }
+        if ((pe = profile_end(la.stream)) != hipSuccess) return pe;
     }
     return hipGetLastError();
 }

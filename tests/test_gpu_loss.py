@@ -158,8 +158,15 @@ def test_qwen3_8b_shape_all_rows(ops):
         assert rel_l2(got, want) <= 2e-3, (dl, rel_l2(got, want))
         assert rel_l2(got, want, axis=0).max() <= 2e-3, dl
         if dl == "bf16":
+            # element by element within one bf16 ulp, except where p_d and
+            # p_t are so close that sign(p_d - p_t) of the TV subgradient
+            # comes out the other way under rounding: such an element moves
+            # by 2 alpha_tv w_k p_d / N (sign at equality is a reading; the
+            # norm-wise bounds above cover these elements)
             off = np.abs(got - want) / bf16_ulp(want)
-            assert off.max() <= 1.0 + 1e-9, (dl, off.max())
+            n_off = int(np.count_nonzero(off > 1.0 + 1e-9))
+            note("  bf16 dZ elements beyond one ulp: %d of %d" % (n_off, off.size))
+            assert n_off <= 1e-4 * off.size, (dl, n_off, off.max())
         # dW2 on those columns: float32 dlogits against the oracle's dW2;
         # bf16 dlogits (dW2 is then formed from the stored bf16 values)
         # against E^T times the oracle's dZ rounded the same way
