@@ -121,6 +121,27 @@ dspark_status dspark_draft_block(const dspark_dims* dims, const void* U, const v
                                  int32_t* tokens, float* logp, float* conf, float* survival,
                                  void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* dspark_draft_block without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, serving loops or
+ * harnesses that forbid allocation).  Same arguments, semantics and results
+ * as dspark_draft_block; the workspace is a fixed 32 MiB array in the
+ * library's device memory, one per GPU, held until the process ends (its
+ * address is looked up on the first call on each device).  The call itself
+ * allocates nothing.
+ * Limit: DSPARK_EWORKSPACE when dspark_workspace_size(dims,
+ * DSPARK_CALL_DRAFT) exceeds 32 MiB (the Qwen3-4B, Qwen3-14B and Gemma4
+ * shaped workloads need 1.7, 13.4 and 10.4 MiB).
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or different host threads) race and must be
+ * serialised by the caller.  The per-block error flags stay in the library's
+ * array; a block with a bad token id is still reported as token -1 / NaN. */
+dspark_status dspark_draft_block_noalloc(const dspark_dims* dims, const void* U, const void* h,
+                                         const int32_t* anchor, const void* W1, const void* W2,
+                                         const void* w_conf, const void* W_rnn,
+                                         const float* temperature, uint64_t seed, uint64_t offset,
+                                         int32_t* tokens, float* logp, float* conf, float* survival,
+                                         void* hip_stream);
+
 /* Teacher-forced DSpark objective (Eq 8-12) with dL/dlogits and dW2, Markov
  * head.  dims->B is the number of blocks N; rows i = n * gamma + k.
  * Position k is fed the previous ground-truth token (anchor[n] at k = 0,

@@ -58,6 +58,8 @@ def load() -> ctypes.CDLL:
     lib.dspark_workspace_size.restype = SZ
     lib.dspark_draft_block.argtypes = [D] + [P] * 8 + [U64, U64] + [P] * 5 + [SZ, P]
     lib.dspark_draft_block.restype = ctypes.c_int
+    lib.dspark_draft_block_noalloc.argtypes = [D] + [P] * 8 + [U64, U64] + [P] * 4 + [P]
+    lib.dspark_draft_block_noalloc.restype = ctypes.c_int
     lib.dspark_block_loss.argtypes = [D] + [P] * 13 + [P, I32, P, P, P, SZ, P]
     lib.dspark_block_loss.restype = ctypes.c_int
     lib.dspark_block_loss_backward.argtypes = [D, P, I32] + [P] * 11 + [SZ, P]
@@ -149,6 +151,13 @@ def dspark_draft_block(dims, U, h, anchor, W1, W2, w_conf, W_rnn, temperature, s
         ctypes.byref(dims), _p(U), _p(h), _p(anchor), _p(W1), _p(W2), _p(w_conf), _p(W_rnn),
         _p(temperature), seed, offset, _p(tokens), _p(logp), _p(conf), _p(survival),
         _p(workspace), nbytes, _stream(stream)))
+
+
+def dspark_draft_block_noalloc(dims, U, h, anchor, W1, W2, w_conf, W_rnn, temperature, seed, offset,
+                               tokens, logp, conf, survival, stream=None):
+    _check(load().dspark_draft_block_noalloc(
+        ctypes.byref(dims), _p(U), _p(h), _p(anchor), _p(W1), _p(W2), _p(w_conf), _p(W_rnn),
+        _p(temperature), seed, offset, _p(tokens), _p(logp), _p(conf), _p(survival), _stream(stream)))
 
 
 def dspark_block_loss(dims, U, T_logits, h, anchor, labels, W1, W2, w_conf, alpha, pos_weight,

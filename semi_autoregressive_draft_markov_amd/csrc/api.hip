@@ -134,6 +134,27 @@ dspark_status dspark_draft_block(const dspark_dims* dims, const void* U, const v
     return ok();
 }
 
+dspark_status dspark_draft_block_noalloc(const dspark_dims* dims, const void* U, const void* h,
+                                         const int32_t* anchor, const void* W1, const void* W2,
+                                         const void* w_conf, const void* W_rnn,
+                                         const float* temperature, uint64_t seed, uint64_t offset,
+                                         int32_t* tokens, float* logp, float* conf, float* survival,
+                                         void* hip_stream) {
+    dspark_status s = check_dims(dims);
+    if (s != DSPARK_OK) return s;
+    const size_t need = dspark::draft_layout(*dims).total;
+    if (need > dspark::kDraftScratchBytes)
+        return fail(DSPARK_EWORKSPACE,
+                    "this problem needs %zu bytes of scratch; the built-in scratch holds %zu "
+                    "(use dspark_draft_block with a workspace)",
+                    need, dspark::kDraftScratchBytes);
+    void* ws = nullptr;
+    const hipError_t e = dspark::draft_scratch(&ws);
+    if (e != hipSuccess) return fail(DSPARK_EDEVICE, "scratch lookup failed: %s", hipGetErrorString(e));
+    return dspark_draft_block(dims, U, h, anchor, W1, W2, w_conf, W_rnn, temperature, seed, offset, tokens, logp,
+                              conf, survival, ws, dspark::kDraftScratchBytes, hip_stream);
+}
+
 dspark_status dspark_block_loss(const dspark_dims* dims, const void* U, const void* T_logits,
                                 const void* h, const int32_t* anchor, const int32_t* labels,
                                 const void* W1, const void* W2, const void* w_conf,

@@ -175,6 +175,12 @@ struct DraftArgs {
 // Enqueue the whole draft call.  Returns hipSuccess or the first launch error.
 hipError_t launch_draft(const DraftArgs& a);
 
+// Built-in device scratch of the allocation-free drafting entry point
+// (noalloc.hip): its size, and its device address on the current device
+// (looked up on the first call there, then cached).
+constexpr size_t kDraftScratchBytes = size_t(32) << 20;
+hipError_t draft_scratch(void** ptr);
+
 // Device random numbers of the kernels, one element per thread (noise.hip).
 hipError_t launch_noise(uint64_t seed, uint64_t offset, uint32_t ctr1, uint32_t ctr2, uint32_t v0, int n,
                         const uint32_t* words_in, uint32_t* words, float* gumbel, float* gumbel2,

@@ -108,6 +108,18 @@ def test_noise_rejects_bad_ranges(lib):
     lib.dspark_noise(0, 0, 0, 0, 0, 0, stream=0)  # n = 0: nothing to do, no device work
 
 
+def test_noalloc_draft_refuses_a_problem_beyond_its_scratch(lib):
+    dims = lib.make_dims(151936, 256, 2560, 64, 1024)
+    assert lib.dspark_workspace_size(dims, lib.DSPARK_CALL_DRAFT) > (32 << 20)
+    with pytest.raises(lib.DsparkError) as e:
+        lib.dspark_draft_block_noalloc(dims, *([256] * 8), 0, 0, *([256] * 4), stream=0)
+    assert e.value.status == lib.DSPARK_EWORKSPACE and "scratch" in str(e.value)
+    with pytest.raises(lib.DsparkError) as e:
+        lib.dspark_draft_block_noalloc(lib.make_dims(1, 256, 2560, 7, 32), *([256] * 8), 0, 0,
+                                       *([256] * 4), stream=0)
+    assert e.value.status == lib.DSPARK_EINVAL
+
+
 def test_read_device_error_rejects_null(lib):
     d = lib.make_dims(1000, 64, 32, 7, 4)
     st = lib.load().dspark_read_device_error(ctypes.byref(d), None, None, None)
