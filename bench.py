@@ -7,14 +7,18 @@ d = 2560, bf16 weights and base logits, temperature 1 (Gumbel-max sampling).
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Each step uses a new noise offset (offset = step index).
 
-Timing: before every timed call a 1 GiB buffer is written (untimed), so that
+Timing: before every timed call a 1 GiB buffer is read (untimed), so that
 the weights and logits come from HBM and not from the 256 MB memory-side
-cache; each call is bracketed by HIP events on its stream and `value` is the
-drafted tokens over the summed call times.  The same calls back to back
+cache (a read leaves the caches holding clean lines; a 1 GiB write would
+leave dirty ones whose write-back the timed call would pay for); each call
+is bracketed by HIP events on its stream and `value` is the drafted tokens
+over the summed call times.  The same calls back to back
 without the flush give `warm_value` (context only).
 
 Prints one JSON line: the throughput, the roofline of the dominant kernel
-(timed live with the library's own HIP events around that kernel; the bound
+(timed live with the library's own HIP events around that kernel, in a
+second pass of the same flushed calls so that those events do not add to
+the value; the bound
 is the roof with the largest measured fraction -- HBM bytes, matrix-core
 flops, or vector-ALU instruction issue from committed rocprofv3 counters)
 and the CPU oracle's rate on a bounded sample of the same workload.
@@ -246,29 +250,37 @@ def copy_calibration() -> int:
 
 def run_timed(step, args, dev, kernels_per_call):
     """Warm-up, then args.steps calls each preceded by an untimed 1 GiB
-    write, each bracketed by HIP events on the current stream; then the
-    same number of calls back to back.  Returns per-call seconds (flushed),
-    the warm wall time, and the library's per-launch kernel times (flushed
-    calls, grouped per call)."""
+    read, each bracketed by HIP events on the current stream (the value);
+    then the same flushed calls again with the library's kernel timing
+    switched on (its events would otherwise add to the calls' time); then
+    the same number of calls back to back.  Returns per-call seconds
+    (flushed), the warm wall time, and the library's per-launch kernel
+    times (flushed calls, grouped per call)."""
     import torch
     from semi_autoregressive_draft_markov_amd import binding
     stream = torch.cuda.current_stream()
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    def flushed_calls(first):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            torch.sum(flush, dim=0, out=sink)  # reads 1 GiB: evicts the caches, leaves no dirty lines
+            evs[i][0].record(stream)
+            step(first + i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e-3 for a, b in evs]
+
+    call_s = flushed_calls(args.warmup)
     binding.dspark_profile_enable(True)
     binding.dspark_profile_read_each()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        flush.zero_()
-        evs[i][0].record(stream)
-        step(args.warmup + i)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    call_s = [a.elapsed_time(b) * 1e-3 for a, b in evs]
+    flushed_calls(args.warmup + args.steps)
     each = binding.dspark_profile_read_each(capacity=args.steps * kernels_per_call + 16)
     binding.dspark_profile_enable(False)
     assert len(each) == args.steps * kernels_per_call, (len(each), args.steps, kernels_per_call)
@@ -278,7 +290,7 @@ def run_timed(step, args, dev, kernels_per_call):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + args.steps + i)
+        step(args.warmup + 2 * args.steps + i)
     torch.cuda.synchronize()
     warm_s = time.perf_counter() - t0
     return call_s, warm_s, per_call
@@ -291,7 +303,7 @@ def base_line(metric, value, unit, args, ms_per_step, config, dtype="bf16"):
 
 
 def timing_summary(call_s, warm_s, count_per_call, steps):
-    return {"caches": "1 GiB written before every timed call",
+    return {"caches": "1 GiB read before every timed call",
             "call_us_median": round(statistics.median(call_s) * 1e6, 2),
             "call_us_min": round(min(call_s) * 1e6, 2),
             "warm_value": round(count_per_call * steps / warm_s, 1),

@@ -53,7 +53,7 @@ def _jobs() -> int:
 def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     """Compile every csrc/*.hip (and the host-only csrc/*.cpp) into `out`
     (libdspark.so by default); always recompiles."""
-    obj_dir = OBJ_DIR + ("" if out == LIB else "_" + os.path.basename(out).replace(".", "_"))
+    obj_dir = OBJ_DIR if out == LIB else os.path.join(os.path.dirname(os.path.abspath(out)), "_build")
     if os.path.isdir(obj_dir):
         shutil.rmtree(obj_dir)
     os.makedirs(obj_dir)

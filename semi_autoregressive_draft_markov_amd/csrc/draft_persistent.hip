@@ -205,6 +205,14 @@ __device__ __forceinline__ T get_shared(const T* p) {
 // workgroup loads the (16 kPWaves) x r block once per call with 16-byte row
 // loads (two rows per thread and pass) and writes each pair of rows as packed
 // words into the transposed layout.  Columns >= V read 0 (V % 8 == 0).
+//
+// Lane L of wave w finds its 16 bytes of chunk kc at 16-byte slot
+// kc * 64 + (L ^ w): with the slot index swizzled by the wave, the 64
+// threads of one staging store (8 waves' columns x 4 row pairs) write 32
+// distinct banks instead of 4, while a wave's operand reads stay one
+// contiguous, conflict-free kilobyte.
+__device__ __forceinline__ int xfrag_slot(int kc, int lane, int wave) { return kc * kWave + (lane ^ wave); }
+
 template <int KC>
 __device__ __forceinline__ void load_xfrags(const uint16_t* __restrict__ W2, int V, int c0, uint32_t* xf_all) {
     constexpr int kPairs = KC * 16;             // row pairs
@@ -226,7 +234,7 @@ __device__ __forceinline__ void load_xfrags(const uint16_t* __restrict__ W2, int
             const int w = cc >> 4, n = cc & 15;
             const uint32_t lo = (q & 1) ? (a[q >> 1] >> 16) : (a[q >> 1] & 0xFFFFu);
             const uint32_t hi = (q & 1) ? (b[q >> 1] & 0xFFFF0000u) : (b[q >> 1] << 16);
-            xf_all[w * (KC * kWave * 4) + (kc * kWave + 16 * g + n) * 4 + p] = lo | hi;
+            xf_all[w * (KC * kWave * 4) + xfrag_slot(kc, 16 * g + n, w) * 4 + p] = lo | hi;
         }
     }
 }
@@ -239,11 +247,11 @@ __device__ __forceinline__ void load_xfrags(const uint16_t* __restrict__ W2, int
 // branch.
 template <int KC, bool REG, bool XW>
 __device__ __forceinline__ void unit_mul(const W2Tile<KC>& w2, const uint32_t* xf, const uint16_t* erow, int lane,
-                                         f32x4 (&acc)[4], f32x4& accx) {
+                                         int wave, f32x4 (&acc)[4], f32x4& accx) {
     u32x4 ev[2], xv[2];
     auto fetch = [&](int kc, int slot) {
         ev[slot] = *reinterpret_cast<const u32x4*>(erow + kc * 32);
-        if (XW) xv[slot] = *reinterpret_cast<const u32x4*>(&xf[(kc * kWave + lane) * 4]);
+        if (XW) xv[slot] = *reinterpret_cast<const u32x4*>(&xf[xfrag_slot(kc, lane, wave) * 4]);
     };
     fetch(0, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, XW ? 2 : 1, 0);
@@ -593,9 +601,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     // tiles)
     auto mul_any = [&](int nb, f32x4 (&acc)[4], f32x4& accx) {
         if (has_x)
-            unit_mul<KC, true, true>(w2, xf, erow_of(nb), lane, acc, accx);
+            unit_mul<KC, true, true>(w2, xf, erow_of(nb), lane, wave, acc, accx);
         else if (has_reg)
-            unit_mul<KC, true, false>(w2, xf, erow_of(nb), lane, acc, accx);
+            unit_mul<KC, true, false>(w2, xf, erow_of(nb), lane, wave, acc, accx);
     };
     // lane statistics of a unit for any wave: absent columns hold -inf
     auto any_stats = [&](int kk, int nb, const f32x4 (&acc)[4], const f32x4& accx) {
@@ -658,10 +666,10 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     auto run_unit = [&](int kk, int nb) {
         f32x4 acc[4], accx;
         acc_from(ahead, acc, accx);
-        if (nb + 1 < NB)
-            ahead = fetch_u(kk, nb + 1);
-        else if (kk + 1 < a.gamma)
-            ahead = fetch_u(kk + 1, 0);
+        // (the next step's first unit is fetched after the barrier arrival:
+        // a load in flight at the arrival's completion wait would be
+        // waited for)
+        if (nb + 1 < NB) ahead = fetch_u(kk, nb + 1);
         mul_any(nb, acc, accx);
         PStats st;
         if (AHEAD) {
@@ -760,6 +768,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         wait_vmem_complete();
         __syncthreads();
         barrier_arrive(a.bar, static_cast<uint32_t>(wg));
+        ahead = fetch_u(k + 1, 0);
         noise_ahead(k + 1, 1, 16 + n < a.B && scale_s[16 + n] > 0.0f);
         barrier_finish(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG));
         read_keys(k, 0, a.B);
@@ -803,14 +812,17 @@ __device__ __forceinline__ float lane_dot_bf16(const uint16_t* x, const uint16_t
 }
 
 // Workgroup b, after the loop.  Wave w handles positions k = w, w + 8, ...:
-// x_k from the argmax keys, log p_k from the step's (max, sum) partials
-// (merged lane-strided, then across the wave) and the logit of x_k
-// (recomputed from U, W1 and W2), c_k = sigma(w[0:d] . h_{b,k} +
-// w[d:d+r] . W1[x_{k-1}]) (Eq 7, x_{-1} = the anchor); then S_k = c_0 ... c_k
-// in position order.  A block is invalid from its first position whose
+// x_k from the argmax keys, log p_k = (z2 - m) ln 2 - ln s from the step's
+// base-2 (max, sum) partials (merged lane-strided, then across the wave) and
+// z2 = z log2(e) / T, the scaled logit of x_k, recovered as the key's
+// perturbed value plus the Gumbel term of (x_k, k, b) (zero when greedy) --
+// the very sum the drafting kernel formed, so no column of W2 is re-read --
+// and c_k = sigma(w[0:d] . h_{b,k} + w[d:d+r] . W1[x_{k-1}]) (Eq 7, x_{-1} =
+// the anchor); then S_k = c_0 ... c_k in position order.  A block is invalid from its first position whose
 // previous token is out of range, or entirely when a grid barrier gave up.
 __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(PersistArgs a) {
     __shared__ int xs[kMaxGamma + 1];  // xs[0] = anchor, xs[k + 1] = x_k
+    __shared__ float ys[kMaxGamma];    // perturbed value at x_k (scaled units)
     __shared__ float cs[kMaxGamma];
     __shared__ int first_bad_s;
     const int b = blockIdx.x;
@@ -826,6 +838,9 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
             const uint32_t x = key_index(key);
             inval = key == kKeyNone || x >= static_cast<uint32_t>(a.V);
             xs[lane + 1] = static_cast<int>(x);
+            // the float back from the order-preserving key bits
+            const uint32_t kb = static_cast<uint32_t>(key >> 32);
+            ys[lane] = __uint_as_float((kb & 0x80000000u) ? (kb ^ 0x80000000u) : ~kb);
         }
         const int x0 = a.anchor[b];
         const uint64_t m = __ballot(inval);
@@ -858,17 +873,15 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
                   (s2 > 0.0f ? s2 * __builtin_amdgcn_exp2f(m2 - mm) : 0.0f);
             m = mm;
         }
-        const int xk = bad ? 0 : xs[k + 1];  // in range unless bad
-        // the draft logit at x_k, z = U[b, k, x_k] + W1[x_{k-1}] . W2[:, x_k]
-        // (Eq 4/5), recomputed here in float32
-        const int xp = bad ? 0 : xs[k];
-        float zp = 0.0f;
-        for (int j = lane; j < a.r; j += kWave)
-            zp = fmaf(bf16_to_f32(a.W1[static_cast<size_t>(xp) * a.r + j]),
-                      bf16_to_f32(a.W2[static_cast<size_t>(j) * a.V + xk]), zp);
-        const float zx_raw = wave_sum(zp) + bf16_to_f32(a.U[(static_cast<size_t>(b) * a.gamma + k) * a.V + xk]);
-        const float temp = a.temperature[b];
-        const float zx = zx_raw * (temp > 0.0f ? kLog2e / temp : kLog2e);
+        const uint32_t xk = bad ? 0u : static_cast<uint32_t>(xs[k + 1]);  // in range unless bad
+        float g2 = 0.0f;
+        if (a.temperature[b] > 0.0f) {
+            const u32x4 w = philox4x32_10(u32x4{xk >> 2, static_cast<uint32_t>(k), static_cast<uint32_t>(b), a.ctr3},
+                                          a.key0, a.key1);
+            const uint32_t q = xk & 3u;
+            g2 = log2_of_neg_log2_uniform(q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3]);
+        }
+        const float zx = ys[k] + g2;
         float part = lane_dot_bf16(a.w_conf, a.h + (static_cast<size_t>(b) * a.gamma + k) * a.d, a.d, lane);
         if (!bad) part += lane_dot_bf16(a.w_conf + a.d, a.W1 + static_cast<size_t>(xs[k]) * a.r, a.r, lane);
         const float logit = wave_sum(part);
