@@ -57,10 +57,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counters_for(workload: str, kernel: str):
-    """Per-launch counters of `kernel` in `workload` from the committed
-    rocprofv3 runs (profiles/counters.json), or None if absent or taken on a
-    different build of the kernel sources."""
+def counters_for(workload: str, kernels):
+    """Per-launch counters summed over `kernels` (names, or prefixes ending
+    in '<' for every instance of a template) of `workload`, from the
+    committed rocprofv3 runs (profiles/counters.json, written by
+    collect_profiles.py); None if absent or taken on other kernel sources."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
@@ -68,24 +69,34 @@ def counters_for(workload: str, kernel: str):
         return None
     if c.get("kernel_source_hash") != kernel_source_hash():
         return None
-    e = c.get("workloads", {}).get(workload)
-    if not e or e.get("kernel") != kernel:
+    ks = c.get("workloads", {}).get(workload, {}).get("kernels", {})
+    names = [kernels] if isinstance(kernels, str) else list(kernels)
+    hit = [e for k, e in ks.items() if any(k == n or (n.endswith("<") and k.startswith(n)) for n in names)]
+    if not hit:
         return None
-    out = dict(e)
+    out = {}
+    for key in ("fetch_kib", "write_kib", "sq_insts_valu"):
+        if all(e.get(key) is not None for e in hit):
+            out[key] = sum(e[key] for e in hit)
+    if len(hit) == 1:
+        for key in ("valu_busy_pct", "mfma_util_pct", "lds_bank_conflict_per_lds_cycle", "wait_any_per_wave_cycle"):
+            if key in hit[0]:
+                out[key] = hit[0][key]
     cal = c.get("copy_calibration", {})
-    if "fetch_kib" in e and "write_kib" in e and cal:
+    if "fetch_kib" in out and "write_kib" in out and cal:
         fs = FLUSH_BYTES / 1024.0 / cal["fetch_kib_per_gib"]
         ws = FLUSH_BYTES / 1024.0 / cal["write_kib_per_gib"]
-        out["traffic_bytes"] = round(e["fetch_kib"] * 1024 * fs + e["write_kib"] * 1024 * ws)
+        out["traffic_bytes"] = round(out["fetch_kib"] * 1024 * fs + out["write_kib"] * 1024 * ws)
         out["fetch_scale"], out["write_scale"] = round(fs, 4), round(ws, 4)
     return out
 
 
-def roofline(workload, kernel, kernel_s, alg_bytes, alg_flops, launches_per_counter=1):
-    """Fractions of the three roofs for one launch of `kernel` taking
-    `kernel_s` seconds; the bound is the largest.  The vector-ALU fraction
-    needs the committed SQ_INSTS_VALU count of the same build."""
-    c = counters_for(workload, kernel)
+def roofline(workload, kernel, kernel_s, alg_bytes, alg_flops, match=None):
+    """Fractions of the three roofs for one launch of `kernel` (or of the
+    kernels `match` names, summed) taking `kernel_s` seconds; the bound is
+    the largest.  The vector-ALU fraction needs the committed SQ_INSTS_VALU
+    count of the same build."""
+    c = counters_for(workload, match or kernel)
     fr = {"hbm": alg_bytes / kernel_s / 1e9 / HBM_PEAK_GBS,
           "mfma": alg_flops / kernel_s / 1e12 / MFMA_BF16_PEAK_TFLOPS}
     achieved = {"hbm": alg_bytes / kernel_s / 1e9, "mfma": alg_flops / kernel_s / 1e12}
@@ -104,7 +115,7 @@ def roofline(workload, kernel, kernel_s, alg_bytes, alg_flops, launches_per_coun
             "algorithmic_flops_per_launch": int(alg_flops),
             "fractions": {k: round(v, 4) for k, v in fr.items()}}
     if c:
-        for k in ("valu_busy_pct", "mfma_util_pct", "lds_bank_conflict_per_lds_cycle"):
+        for k in ("valu_busy_pct", "mfma_util_pct", "lds_bank_conflict_per_lds_cycle", "wait_any_per_wave_cycle"):
             if k in c:
                 line[k] = c[k]
     else:
@@ -409,10 +420,11 @@ def bench_loss(args) -> int:
     line = base_line("teacher-forced rows/s (V=151936, r=256, γ=7, 7168 rows)", R * args.steps / elapsed,
                      "rows/s", args, elapsed * 1e3 / args.steps, config)
     line["timing"] = timing_summary(call_s, warm_s, R, args.steps)
-    line["roofline"] = roofline("qwen3-8b-loss", "k_loss_mfma passes 1-3", passes_s, alg_bytes, 3 * gemm_flops)
+    line["roofline"] = roofline("qwen3-8b-loss", "k_loss_mfma passes 1-3", passes_s, alg_bytes, 3 * gemm_flops,
+                                match=["k_loss_mfma<"])
     # dW2 = E^T dZ: bf16 dZ and W2-shaped output, against the matrix cores
     dw2_bytes = R * V * 2 + r * V * 4 + r * R * 2
-    line["dw2"] = roofline("qwen3-8b-loss-dw2", "k_dw2_mfma<0>", dw2_s, dw2_bytes, gemm_flops)
+    line["dw2"] = roofline("qwen3-8b-loss", "k_dw2_mfma<0>", dw2_s, dw2_bytes, gemm_flops)
     line["dw2"]["mfma_tflops"] = round(gemm_flops / dw2_s / 1e12, 1)
     line["roofline"]["attainable_copy_GBps"] = round(copy_rate_gbs(dev), 1)
     line["cpu_baseline"] = cpu_baseline_loss(inp, args.cpu_seconds) if args.cpu_seconds > 0 else None

@@ -391,10 +391,11 @@ struct UAhead {
 // the MFMA operand comes from LDS, so its wait never covers the U loads
 // still in flight.  AHEAD (B <= 32, at most two block groups): the Gumbel
 // terms of every block group are computed while memory or other workgroups
-// are busy -- under the W2 loads before step 0; at each step end group 0's
-// while the key atomics complete and group 1's while the barrier arrival is
-// in flight -- and kept in LDS ([group][16 columns][threads] floats) for the
-// register-tile columns and in registers for the 4 LDS-fragment columns.
+// are busy -- under the W2 loads before step 0; at each step end after the
+// barrier arrival, spread over the wait for the other workgroups, the key
+// read and the W1 row loads -- and kept in LDS ([group][16 columns][threads]
+// floats) for the register-tile columns and in registers for the 4
+// LDS-fragment columns.
 constexpr size_t kPersistLdsMax = 160 * 1024;  // one workgroup per CU
 
 template <int KC>
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     // block is greedy, on = false): the 16 register-tile columns into LDS,
     // the 4 LDS-fragment columns into registers (nx0 / nx1)
     float nx0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, nx1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto noise_ahead = [&](int kk, int nb, bool on) {
+    auto noise_ahead = [&](int kk, int nb, bool on, int q0 = 0, int q1 = 4, bool with_x = true) {
         const int b = nb * 16 + n;
         if (!AHEAD || b >= a.B) return;
         // the counter words are opaque here, so that the compiler does not
@@ -464,14 +465,14 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         if (reg_live) {
             float* dst = gn + nb * 16 * kNoiseStride;
 #pragma unroll 2  // two independent Philox blocks at a time: their rounds interleave
-            for (int q = 0; q < 4; ++q) {
+            for (int q = q0; q < q1; ++q) {
                 const u32x4 w = philox4x32_10(u32x4{cv + static_cast<uint32_t>(q), static_cast<uint32_t>(kk), cb, a.ctr3},
                                               a.key0, a.key1);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) dst[kNoiseStride * (4 * q + c)] = on ? log2_of_neg_log2_uniform(w[c]) : 0.0f;
             }
         }
-        if (x_live) {
+        if (with_x && x_live) {
             uint32_t cx = static_cast<uint32_t>(vx) >> 2;
             asm volatile("" : "+v"(cx));
             const u32x4 w = philox4x32_10(u32x4{cx, static_cast<uint32_t>(kk), cb, a.ctr3}, a.key0, a.key1);
@@ -513,18 +514,22 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         }
         __syncthreads();
     };
-    // AHEAD (Bpad <= 32): the same with every load issued first, then the
-    // stores
-    auto stage_rows_ahead = [&]() {
-        constexpr int kMaxChunks = (32 * (r / 8) + kPThreads - 1) / kPThreads;
+    // AHEAD (Bpad <= 32): the same in two halves, every load issued
+    // first (rows_issue), the stores and the barrier later (rows_store), so
+    // that other work can run while the loads are in flight
+    constexpr int kMaxChunks = (32 * (r / 8) + kPThreads - 1) / kPThreads;
+    u32x4 e[kMaxChunks];
+    auto rows_issue = [&]() {
         const int chunks = a.Bpad * (r / 8);
-        u32x4 e[kMaxChunks];
 #pragma unroll
         for (int i = 0; i < kMaxChunks; ++i) {
             const int t = (threadIdx.x + kPThreads * i) % chunks;  // unconditional: stays in flight
             const int row = t / (r / 8), col = t % (r / 8);
             e[i] = *reinterpret_cast<const u32x4*>(a.W1 + static_cast<size_t>(prev[row]) * r + col * 8);
         }
+    };
+    auto rows_store = [&]() {
+        const int chunks = a.Bpad * (r / 8);
 #pragma unroll
         for (int i = 0; i < kMaxChunks; ++i) {
             const int t = threadIdx.x + kPThreads * i;
@@ -648,12 +653,13 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         return st;
     };
     // the unit's statistics over the 4 lanes of each block row, into this
-    // wave's slots
+    // wave's slot of each block (written once per step: every unit covers
+    // other blocks)
     auto to_slot = [&](PStats st, int nb) {
         const int b = nb * 16 + n;
         st = pstats_merge(st, shfl_xor_pstats(st, 16));
         st = pstats_merge(st, shfl_xor_pstats(st, 32));
-        if (g == 0 && b < a.B) slot[wave * a.B + b] = pstats_merge(slot[wave * a.B + b], st);
+        if (g == 0 && b < a.B) slot[wave * a.B + b] = st;
     };
 
     // wave-uniform: every column of the wave's register tile and LDS
@@ -744,9 +750,30 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
             finish_key(t, get_shared(&a.best[(base + t) * kKeyStride]));
         __syncthreads();
     };
+    // AHEAD (B * copies <= 256 < threads): the same in two halves, the load
+    // of one key copy per thread first (keys_issue), the merge, prev[] and
+    // the barrier later (keys_finish)
+    auto keys_issue = [&](int kk) -> uint64_t {
+        const int t = threadIdx.x;
+        const size_t base = static_cast<size_t>(kk) * a.B * kDraftKeyCopies;
+        return t < a.B * kDraftKeyCopies ? get_shared(&a.best[(base + t) * kKeyStride]) : kKeyNone;
+    };
+    auto keys_finish = [&](uint64_t key) {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int o = 1; o < kDraftKeyCopies; o <<= 1) {
+            const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o);
+            const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key >> 32), o);
+            const uint64_t other = (static_cast<uint64_t>(hi) << 32) | lo;
+            key = other > key ? other : key;
+        }
+        const uint32_t x = key_index(key);
+        if (t < a.B * kDraftKeyCopies && t % kDraftKeyCopies == 0)
+            prev[t / kDraftKeyCopies] = (key != kKeyNone && x < static_cast<uint32_t>(a.V)) ? static_cast<int>(x) : 0;
+        __syncthreads();
+    };
 
     for (int k = 0; k < a.gamma; ++k) {
-        for (int b = lane; b < a.B; b += 64) slot[wave * a.B + b] = pstats_empty();
         // every wave runs all NB units (GROUPED stages rows between
         // them); waves without columns skip the arithmetic
         for (int nb = 0; nb < NB; ++nb) {
@@ -759,23 +786,38 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         }
         publish(k, 0, a.B);
         if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
-        // next step's noise of group 0 while the key atomics complete,
-        // the wait for their completion and the workgroup barrier, the
-        // arrival and the wait for the other workgroups, with group 1's
-        // noise computed while the arrival is in flight (the barrier's
-        // latency, about as long, is hidden behind it)
-        noise_ahead(k + 1, 0, scale_s[n] > 0.0f);
-        wait_vmem_complete();
-        __syncthreads();
-        barrier_arrive(a.bar, static_cast<uint32_t>(wg));
-        ahead = fetch_u(k + 1, 0);
-        noise_ahead(k + 1, 1, 16 + n < a.B && scale_s[16 + n] > 0.0f);
-        barrier_finish(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG));
-        read_keys(k, 0, a.B);
-        if (AHEAD)
-            stage_rows_ahead();
-        else
+        if (AHEAD) {
+            // The next step's Gumbel terms fill the waits of the step's end,
+            // all after the arrival: the completion wait for the key
+            // atomics comes first (a workgroup that arrives earlier lets the
+            // barrier complete earlier), then group 0's terms and half of
+            // group 1's while the arrivals spread (about 2 us from a
+            // workgroup's own arrival to the last one being seen), the rest
+            // of group 1's register-tile terms while the keys are read, and
+            // its fragment terms while the W1 rows load.
+            const bool on0 = scale_s[n] > 0.0f, on1 = 16 + n < a.B && scale_s[16 + n] > 0.0f;
+            wait_vmem_complete();
+            __syncthreads();
+            barrier_arrive(a.bar, static_cast<uint32_t>(wg));
+            ahead = fetch_u(k + 1, 0);
+            noise_ahead(k + 1, 0, on0);
+            noise_ahead(k + 1, 1, on1, 0, 2, false);
+            barrier_finish(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG));
+            const uint64_t key = keys_issue(k);
+            noise_ahead(k + 1, 1, on1, 2, 4, false);
+            keys_finish(key);
+            rows_issue();
+            noise_ahead(k + 1, 1, on1, 0, 0, true);
+            rows_store();
+        } else {
+            wait_vmem_complete();
+            __syncthreads();
+            barrier_arrive(a.bar, static_cast<uint32_t>(wg));
+            ahead = fetch_u(k + 1, 0);
+            barrier_finish(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG));
+            read_keys(k, 0, a.B);
             stage_rows();
+        }
     }
 }
 
@@ -820,6 +862,12 @@ __device__ __forceinline__ float lane_dot_bf16(const uint16_t* x, const uint16_t
 // and c_k = sigma(w[0:d] . h_{b,k} + w[d:d+r] . W1[x_{k-1}]) (Eq 7, x_{-1} =
 // the anchor); then S_k = c_0 ... c_k in position order.  A block is invalid from its first position whose
 // previous token is out of range, or entirely when a grid barrier gave up.
+// Loads of the finish kernel held in registers so that they are issued
+// before the keys are known: the partials of up to 4 x 64 workgroups and the
+// h / w_conf operands of up to 12 x 64 16-byte chunks (d <= 6144).
+constexpr int kFinPms = 4;
+constexpr int kFinDot = 12;
+
 __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(PersistArgs a) {
     __shared__ int xs[kMaxGamma + 1];  // xs[0] = anchor, xs[k + 1] = x_k
     __shared__ float ys[kMaxGamma];    // perturbed value at x_k (scaled units)
@@ -827,6 +875,32 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
     __shared__ int first_bad_s;
     const int b = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+
+    // The first position of each wave (k = wave): its softmax partials and
+    // the h_{b,k} . w[0:d] operands do not depend on the keys, so they are
+    // loaded before the keys are read; only the W1 row of x_{k-1} waits.
+    const int k0 = wave;
+    const uint16_t* hrow0 = a.h + (static_cast<size_t>(b) * a.gamma + (k0 < a.gamma ? k0 : 0)) * a.d;
+    const bool pre = k0 < a.gamma && a.nWG <= kFinPms * kWave && a.d % 8 == 0 && a.d / 8 <= kFinDot * kWave &&
+                     (reinterpret_cast<uintptr_t>(a.w_conf) & 15) == 0 && (reinterpret_cast<uintptr_t>(hrow0) & 15) == 0;
+    float2 q[kFinPms];
+    u32x4 hw[kFinDot], hh[kFinDot];
+    if (pre) {
+        const size_t base = (static_cast<size_t>(k0) * a.B + b) * a.nWG;
+#pragma unroll
+        for (int i = 0; i < kFinPms; ++i) {
+            const int p = lane + kWave * i;
+            q[i] = p < a.nWG ? a.pms[base + p] : make_float2(-INFINITY, 0.0f);
+        }
+#pragma unroll
+        for (int i = 0; i < kFinDot; ++i) {
+            const int c = lane + kWave * i;
+            if (c < a.d / 8) {
+                hw[i] = *reinterpret_cast<const u32x4*>(a.w_conf + 8 * c);
+                hh[i] = *reinterpret_cast<const u32x4*>(hrow0 + 8 * c);
+            }
+        }
+    }
     if (wave == 0) {
         bool inval = false;
         if (lane < a.gamma) {
@@ -850,21 +924,14 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
             first_bad_s = head_bad ? 0 : (m ? __ffsll(static_cast<unsigned long long>(m)) - 1 : a.gamma);
         }
     }
-    __syncthreads();
-    const int first_bad = first_bad_s;
-    for (int k = wave; k < a.gamma; k += kFinishWaves) {
-        const bool bad = k >= first_bad;
-        // (max, sum) over all workgroups; the logit of x_k from the
-        // workgroup whose columns hold x_k
-        const size_t base = (static_cast<size_t>(k) * a.B + b) * a.nWG;
-        float m = -INFINITY, sum = 0.0f;
-        for (int p = lane; p < a.nWG; p += kWave) {
-            const float2 q = a.pms[base + p];
-            const float mm = fmaxf(m, q.x);
-            sum = (sum > 0.0f ? sum * __builtin_amdgcn_exp2f(m - mm) : 0.0f) +
-                  (q.y > 0.0f ? q.y * __builtin_amdgcn_exp2f(q.x - mm) : 0.0f);
-            m = mm;
-        }
+    // (max, sum) over all workgroups, lane-strided then across the wave
+    auto merge_pms = [&](float& m, float& sum, const float2 qq) {
+        const float mm = fmaxf(m, qq.x);
+        sum = (sum > 0.0f ? sum * __builtin_amdgcn_exp2f(m - mm) : 0.0f) +
+              (qq.y > 0.0f ? qq.y * __builtin_amdgcn_exp2f(qq.x - mm) : 0.0f);
+        m = mm;
+    };
+    auto wave_merge = [&](float& m, float& sum) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
             const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sum, o);
@@ -873,16 +940,46 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
                   (s2 > 0.0f ? s2 * __builtin_amdgcn_exp2f(m2 - mm) : 0.0f);
             m = mm;
         }
+    };
+    float m0 = -INFINITY, sum0 = 0.0f, part0 = 0.0f;
+    if (pre) {
+        // (a partial of a missing workgroup is (-inf, 0): merging it changes nothing)
+#pragma unroll
+        for (int i = 0; i < kFinPms; ++i) merge_pms(m0, sum0, q[i]);
+        wave_merge(m0, sum0);
+#pragma unroll
+        for (int i = 0; i < kFinDot; ++i) {
+            if (lane + kWave * i < a.d / 8) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    part0 = fmaf(lo_bf16(hw[i][j]), lo_bf16(hh[i][j]), part0);
+                    part0 = fmaf(hi_bf16(hw[i][j]), hi_bf16(hh[i][j]), part0);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int first_bad = first_bad_s;
+    for (int k = wave; k < a.gamma; k += kFinishWaves) {
+        const bool bad = k >= first_bad;
+        float m = m0, sum = sum0, part = part0;
+        if (!(pre && k == k0)) {
+            const size_t base = (static_cast<size_t>(k) * a.B + b) * a.nWG;
+            m = -INFINITY;
+            sum = 0.0f;
+            for (int p = lane; p < a.nWG; p += kWave) merge_pms(m, sum, a.pms[base + p]);
+            wave_merge(m, sum);
+            part = lane_dot_bf16(a.w_conf, a.h + (static_cast<size_t>(b) * a.gamma + k) * a.d, a.d, lane);
+        }
         const uint32_t xk = bad ? 0u : static_cast<uint32_t>(xs[k + 1]);  // in range unless bad
         float g2 = 0.0f;
         if (a.temperature[b] > 0.0f) {
             const u32x4 w = philox4x32_10(u32x4{xk >> 2, static_cast<uint32_t>(k), static_cast<uint32_t>(b), a.ctr3},
                                           a.key0, a.key1);
-            const uint32_t q = xk & 3u;
-            g2 = log2_of_neg_log2_uniform(q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3]);
+            const uint32_t qi = xk & 3u;
+            g2 = log2_of_neg_log2_uniform(qi == 0 ? w[0] : qi == 1 ? w[1] : qi == 2 ? w[2] : w[3]);
         }
         const float zx = ys[k] + g2;
-        float part = lane_dot_bf16(a.w_conf, a.h + (static_cast<size_t>(b) * a.gamma + k) * a.d, a.d, lane);
         if (!bad) part += lane_dot_bf16(a.w_conf + a.d, a.W1 + static_cast<size_t>(xs[k]) * a.r, a.r, lane);
         const float logit = wave_sum(part);
         if (lane == 0) {
