@@ -17,7 +17,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dspark_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# the in-tree build, or another build of dspark_oracle.c named by
+# DSPARK_ORACLE_LIBRARY (e.g. one compiled with sanitizers)
+_LIB = os.environ.get("DSPARK_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 
 _lib = None
 

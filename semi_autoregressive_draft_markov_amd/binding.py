@@ -11,7 +11,9 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdspark.so")
+# the in-tree build, or another build of the same sources named by
+# DSPARK_LIBRARY (e.g. one compiled with host sanitizers)
+LIB_PATH = os.environ.get("DSPARK_LIBRARY") or os.path.join(HERE, "libdspark.so")
 
 DSPARK_OK, DSPARK_EINVAL, DSPARK_EUNSUPPORTED, DSPARK_EWORKSPACE, DSPARK_EDEVICE = range(5)
 DSPARK_F32, DSPARK_BF16 = 0, 1
@@ -50,7 +52,7 @@ def load() -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError("libdspark.so is not built: run semi_autoregressive_draft_markov_amd.build.build()")
+        raise RuntimeError("%s is not built: run semi_autoregressive_draft_markov_amd.build.build()" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
     D = ctypes.POINTER(dspark_dims)

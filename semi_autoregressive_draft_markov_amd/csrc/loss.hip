@@ -659,16 +659,22 @@ __global__ __launch_bounds__(256) void k_loss_sum(const float* __restrict__ tce,
 //     and tile, loaded two chunks ahead (E is small and stays in cache).
 constexpr int kDw2Cols = 128;
 constexpr int kDw2Threads = 256;
-constexpr int kDw2Ld = 20;  // words per staged column: 16 row pairs + 4 pad (16-byte aligned)
-
-// Word offset of row pair p of staged column col.  Each group of 16 columns
-// is shifted by a further 16 bytes: with the 20-word column stride, the
-// staging stores of a wave (threads 8 columns apart) and the operand reads
-// (16 lanes on 16 consecutive columns, 16 bytes each) then both fall on
-// distinct banks of a 64-bank LDS; a lane's 4 pairs stay one aligned
-// 16-byte piece.
-__device__ __forceinline__ int dw2_word(int col, int p) { return col * kDw2Ld + 4 * (col >> 4) + p; }
-constexpr int kDw2Words = kDw2Cols * kDw2Ld + 4 * (kDw2Cols / 16);
+// Word offset of row pair p (of 16) of staged column col (of 128): the
+// 4-pair piece q = p / 4 of column tile t = col / 16 occupies a 64-word
+// (one bank each) row of its own, in which column col % 16 sits at quad
+// (col % 16 + t) % 16.  A ds_read_b128 serves, each cycle, one lane of each
+// residue mod 16 (measured on gfx950: lanes 16 apart never share a cycle,
+// and the cycle's 16 lanes are not always 16 consecutive ones), so the
+// operand reads -- lane (g, n) takes piece g of column 16 t + n -- are
+// conflict-free when a lane's bank depends on n alone: here quad (n + t) %
+// 16 for every g.  The rotation by t also spreads the staging stores (16
+// threads on columns 8 s + c, s = 0..15, times 4 row pairs) over all 64
+// banks.
+__device__ __forceinline__ int dw2_word(int col, int p) {
+    const int t = col >> 4;
+    return 64 * (4 * t + (p >> 2)) + 4 * (((col & 15) + t) & 15) + (p & 3);
+}
+constexpr int kDw2Words = kDw2Cols * 16;
 
 // (float32 dZ: the hi/lo planes need more registers, one workgroup per CU)
 template <int DZF32>

@@ -1,7 +1,6 @@
 // Host-side post-draft stages: Sequential Temperature Scaling of the
-// confidence head, the hardware-aware prefix scheduler and the i.i.d.
-// depth planner.  Plain C++ on host arrays (no device work); the C ABI is in
-// include/dspark.h.
+// confidence head and the hardware-aware prefix scheduler.  Plain C++ on
+// host arrays (no device work); the C ABI is in include/dspark.h.
 //
 // STS (dormouse "DSpark - paper verification", section 1, the transcription
 // of the paper's post-hoc calibration; bowenzhou "DSpark：既要猜得连贯，也要
@@ -16,9 +15,6 @@
 // resulting batch is largest, comparing the value of one more verified
 // token by its prefix survival and keeping every request's choice a prefix.
 //
-// Depth planner (Meridian, section 6): with i.i.d. per-position acceptance
-// a, expected tokens per cycle tau(a, g) = (1 - a^(g+1)) / (1 - a) over the
-// cycle cost draft_us g + verify_fixed_us + verify_token_us g.
 #include "internal.h"
 
 #include <math.h>
