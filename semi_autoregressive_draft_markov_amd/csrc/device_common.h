@@ -98,6 +98,51 @@ __device__ __forceinline__ uint32_t key_index(uint64_t key) {
 }
 constexpr uint64_t kKeyNone = 0;  // below every real key
 
+// ------------------------------------------------- cross-lane exchanges
+// Partner values for butterfly merges without an LDS round trip (the
+// generic shuffle compiles to ds_bpermute).  swap16 / swap32 return, in
+// every lane, its own 32-bit value and that of lane l ^ 16 / l ^ 32, in an
+// order that depends on the lane (v_permlane16_swap / v_permlane32_swap,
+// gfx950: each lane pair exchanges the halves); a merge that is
+// commutative bit for bit then gives both lanes of a pair the same result
+// as merge(own, partner).  dpp_ror8 is the value of lane l ^ 8 (a rotation
+// by 8 within each row of 16 lanes), dpp_xor1 / dpp_xor2 that of l ^ 1 /
+// l ^ 2, and dpp_half_mirror that of lane 8 r + 7 - (l - 8 r) (each half
+// row reversed, so lanes 0..3 and 4..7 of every group of 8 face each
+// other).
+struct LanePair {
+    uint32_t a, b;
+};
+__device__ __forceinline__ LanePair swap16(uint32_t x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return LanePair{static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1])};
+}
+__device__ __forceinline__ LanePair swap32(uint32_t x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return LanePair{static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1])};
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t x) { return dpp<0xB1>(x); }        // quad_perm [1,0,3,2]
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t x) { return dpp<0x4E>(x); }        // quad_perm [2,3,0,1]
+__device__ __forceinline__ uint32_t dpp_ror8(uint32_t x) { return dpp<0x128>(x); }       // row_ror:8
+__device__ __forceinline__ uint32_t dpp_half_mirror(uint32_t x) { return dpp<0x141>(x); }  // row_half_mirror
+
+// The larger 64-bit key over each group of 8 consecutive lanes, in every
+// lane of the group.
+__device__ __forceinline__ uint64_t max_key8(uint64_t key) {
+    auto step = [](uint64_t k, uint32_t lo, uint32_t hi) {
+        const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+        return o > k ? o : k;
+    };
+    key = step(key, dpp_xor1(static_cast<uint32_t>(key)), dpp_xor1(static_cast<uint32_t>(key >> 32)));
+    key = step(key, dpp_xor2(static_cast<uint32_t>(key)), dpp_xor2(static_cast<uint32_t>(key >> 32)));
+    key = step(key, dpp_half_mirror(static_cast<uint32_t>(key)), dpp_half_mirror(static_cast<uint32_t>(key >> 32)));
+    return key;
+}
+
 // Softmax statistics of a slice: running max m, sum of exp(z - m), plus the
 // argmax key of the (perturbed) logits and the tempered logit at that index.
 struct Stats {

@@ -298,14 +298,23 @@ __device__ __forceinline__ PStats pstats_merge(const PStats& a, const PStats& b)
     return r;
 }
 
-__device__ __forceinline__ PStats shfl_xor_pstats(const PStats& a, int mask) {
-    PStats r;
-    r.m = __shfl_xor(a.m, mask);
-    r.s = __shfl_xor(a.s, mask);
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(a.key), mask);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(a.key >> 32), mask);
-    r.key = (static_cast<uint64_t>(hi) << 32) | lo;
-    return r;
+// pstats_merge of the statistics of lanes l and l ^ 16, l ^ 32 or l ^ 8 (the
+// merge is commutative bit for bit: max, max, and one float sum)
+__device__ __forceinline__ PStats pstats_of(uint32_t m, uint32_t s, uint32_t lo, uint32_t hi) {
+    return PStats{__uint_as_float(m), __uint_as_float(s), (static_cast<uint64_t>(hi) << 32) | lo};
+}
+template <int X>
+__device__ __forceinline__ PStats pstats_merge_xor(const PStats& a) {
+    const uint32_t w[4] = {__float_as_uint(a.m), __float_as_uint(a.s), static_cast<uint32_t>(a.key),
+                           static_cast<uint32_t>(a.key >> 32)};
+    if (X == 8) {
+        return pstats_merge(a, pstats_of(dpp_ror8(w[0]), dpp_ror8(w[1]), dpp_ror8(w[2]), dpp_ror8(w[3])));
+    } else {
+        LanePair p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = X == 16 ? swap16(w[i]) : swap32(w[i]);
+        return pstats_merge(pstats_of(p[0].a, p[1].a, p[2].a, p[3].a), pstats_of(p[0].b, p[1].b, p[2].b, p[3].b));
+    }
 }
 
 // Statistics of the 20 logits z[j] of one lane (columns v0 + j for j < 16,
@@ -582,9 +591,6 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     };
     stage_rows();
     UAhead ahead = fetch_u(0, 0);
-    // the keys and barrier words are cleared everywhere before step 0
-    // publishes (the W2 loads above took far longer than the clearing)
-    start_barrier_wait(a);
 
     // accumulators start from U (bf16 -> f32 is exact)
     auto acc_from = [&](const UAhead& u, f32x4 (&acc)[4], f32x4& accx) {
@@ -657,8 +663,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     // other blocks)
     auto to_slot = [&](PStats st, int nb) {
         const int b = nb * 16 + n;
-        st = pstats_merge(st, shfl_xor_pstats(st, 16));
-        st = pstats_merge(st, shfl_xor_pstats(st, 32));
+        st = pstats_merge_xor<16>(st);
+        st = pstats_merge_xor<32>(st);
         if (g == 0 && b < a.B) slot[wave * a.B + b] = st;
     };
 
@@ -717,9 +723,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         for (int q = wave; q < groups; q += kPWaves) {  // wave-uniform trip count
             const int b = b0 + 8 * q + (lane & 7), w = lane >> 3;
             PStats t = b < b1 ? slot[w * a.B + b] : pstats_empty();
-            t = pstats_merge(t, shfl_xor_pstats(t, 8));
-            t = pstats_merge(t, shfl_xor_pstats(t, 16));
-            t = pstats_merge(t, shfl_xor_pstats(t, 32));
+            t = pstats_merge_xor<8>(t);
+            t = pstats_merge_xor<16>(t);
+            t = pstats_merge_xor<32>(t);
             if (w == 0 && b < b1) {
                 if (t.key != kKeyNone)
                     __hip_atomic_fetch_max(&a.best[((static_cast<size_t>(kk) * a.B + b) * kDraftKeyCopies +
@@ -733,14 +739,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     // x_kk of blocks [b0, b1) from the keys: the copies of a block's key sit
     // in 8 consecutive lanes (b0 is a multiple of 16)
     auto read_keys = [&](int kk, int b0, int b1) {
+        static_assert(kDraftKeyCopies == 8, "copies merged by max_key8");
         auto finish_key = [&](int t, uint64_t key) {
-#pragma unroll
-            for (int o = 1; o < kDraftKeyCopies; o <<= 1) {
-                const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o);
-                const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key >> 32), o);
-                const uint64_t other = (static_cast<uint64_t>(hi) << 32) | lo;
-                key = other > key ? other : key;
-            }
+            key = max_key8(key);
             const uint32_t x = key_index(key);
             if (t < b1 * kDraftKeyCopies && t % kDraftKeyCopies == 0)
                 prev[t / kDraftKeyCopies] = (key != kKeyNone && x < static_cast<uint32_t>(a.V)) ? static_cast<int>(x) : 0;
@@ -760,13 +761,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     };
     auto keys_finish = [&](uint64_t key) {
         const int t = threadIdx.x;
-#pragma unroll
-        for (int o = 1; o < kDraftKeyCopies; o <<= 1) {
-            const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), o);
-            const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key >> 32), o);
-            const uint64_t other = (static_cast<uint64_t>(hi) << 32) | lo;
-            key = other > key ? other : key;
-        }
+        key = max_key8(key);
         const uint32_t x = key_index(key);
         if (t < a.B * kDraftKeyCopies && t % kDraftKeyCopies == 0)
             prev[t / kDraftKeyCopies] = (key != kKeyNone && x < static_cast<uint32_t>(a.V)) ? static_cast<int>(x) : 0;
@@ -784,6 +779,10 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
                 __syncthreads();
             }
         }
+        // the keys and barrier words are cleared everywhere before step 0
+        // publishes or arrives (step 0's units do not touch them, so the
+        // wait runs after them)
+        if (k == 0) start_barrier_wait(a);
         publish(k, 0, a.B);
         if (k + 1 == a.gamma) break;  // the last keys are read after the kernel
         if (AHEAD) {
