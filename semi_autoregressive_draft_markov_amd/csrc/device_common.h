@@ -180,6 +180,24 @@ __device__ __forceinline__ Stats stats_merge2(const Stats& a, const Stats& b) {
     return r;
 }
 
+// stats_merge of the statistics of lanes l and l ^ X (X = 16 or 32) through
+// swap16 / swap32; the merge is commutative bit for bit (keys of different
+// lanes differ unless both are empty, when zx is 0 on both sides).
+template <int X>
+__device__ __forceinline__ Stats stats_merge_xor(const Stats& a) {
+    static_assert(X == 16 || X == 32, "lane distance");
+    const uint32_t w[5] = {__float_as_uint(a.m), __float_as_uint(a.s), static_cast<uint32_t>(a.key),
+                           static_cast<uint32_t>(a.key >> 32), __float_as_uint(a.zx)};
+    LanePair p[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) p[i] = X == 16 ? swap16(w[i]) : swap32(w[i]);
+    const Stats x{__uint_as_float(p[0].a), __uint_as_float(p[1].a), (static_cast<uint64_t>(p[3].a) << 32) | p[2].a,
+                  __uint_as_float(p[4].a)};
+    const Stats y{__uint_as_float(p[0].b), __uint_as_float(p[1].b), (static_cast<uint64_t>(p[3].b) << 32) | p[2].b,
+                  __uint_as_float(p[4].b)};
+    return stats_merge(x, y);
+}
+
 __device__ __forceinline__ Stats shfl_xor_stats(const Stats& a, int mask) {
     Stats r;
     r.m = __shfl_xor(a.m, mask);

@@ -636,8 +636,8 @@ __global__ __launch_bounds__(256, 2) void k_stream_mfma(
             else
                 st = lane_stats16<false>(z, v0, V, b, k, sampling, invT, key0, key1, ctr3);
         }
-        st = stats_merge(st, shfl_xor_stats(st, 16));
-        st = stats_merge(st, shfl_xor_stats(st, 32));
+        st = stats_merge_xor<16>(st);
+        st = stats_merge_xor<32>(st);
         if (g == 0) red[nb & 1][wave][n] = st;
         if (nb + 1 < NB) stage((nb + 1) & 1);
         __syncthreads();
@@ -648,8 +648,8 @@ __global__ __launch_bounds__(256, 2) void k_stream_mfma(
         if (wave == (nb & (kWavesPerWG - 1))) {
             static_assert(kWavesPerWG == 4, "one lane per (wave, block)");
             Stats t = red[nb & 1][g][n];
-            t = stats_merge(t, shfl_xor_stats(t, 16));
-            t = stats_merge(t, shfl_xor_stats(t, 32));
+            t = stats_merge_xor<16>(t);
+            t = stats_merge_xor<32>(t);
             if (g == 0 && b < B) {
                 const size_t o = static_cast<size_t>(b) * P + blockIdx.x;
                 pm[o] = t.m;

@@ -209,6 +209,21 @@ __device__ __forceinline__ RowPart rowpart_merge(int pass, const RowPart& a, con
     return r;
 }
 
+// rowpart_merge of the partials of lanes l and l ^ X (X = 16 or 32) through
+// swap16 / swap32 (the merge is commutative bit for bit)
+template <int PASS, int X>
+__device__ __forceinline__ RowPart rowpart_merge_xor(const RowPart& a) {
+    static_assert(X == 16 || X == 32, "lane distance");
+    RowPart x = rowpart_empty(PASS), y = rowpart_empty(PASS);
+#pragma unroll
+    for (int q = 0; q < kPartVals[PASS]; ++q) {
+        const LanePair p = X == 16 ? swap16(__float_as_uint(a.v[q])) : swap32(__float_as_uint(a.v[q]));
+        x.v[q] = __uint_as_float(p.a);
+        y.v[q] = __uint_as_float(p.b);
+    }
+    return rowpart_merge(PASS, x, y);
+}
+
 __device__ __forceinline__ RowPart rowpart_shfl(const RowPart& a, int mask) {
     RowPart r;
 #pragma unroll
@@ -468,8 +483,8 @@ __global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
             // absorb the lanes without a row or columns)
             if (PASS == kPass2) a.smask[static_cast<size_t>(cols ? v0 >> 4 : a.mask_groups) * a.Rpad + row] = bits;
             if (PASS != kPass3) {
-                p = rowpart_merge(PASS, p, rowpart_shfl(p, 16));
-                p = rowpart_merge(PASS, p, rowpart_shfl(p, 32));
+                p = rowpart_merge_xor<PASS, 16>(p);
+                p = rowpart_merge_xor<PASS, 32>(p);
                 if (g == 0) red[rb & 1][wave][n] = p;
             }
             if (rb + 1 < rb1) stage((rb + 1) & 1);
@@ -481,8 +496,8 @@ __global__ __launch_bounds__(256, 2) void k_loss_mfma(PassArgs a) {
             if (PASS != kPass3 && wave == (rb & (kLossWaves - 1))) {
                 static_assert(kLossWaves == 4, "one lane per (wave, row)");
                 RowPart t = red[rb & 1][g][n];
-                t = rowpart_merge(PASS, t, rowpart_shfl(t, 16));
-                t = rowpart_merge(PASS, t, rowpart_shfl(t, 32));
+                t = rowpart_merge_xor<PASS, 16>(t);
+                t = rowpart_merge_xor<PASS, 32>(t);
                 if (g == 0 && row < a.R) {
                     const size_t o = static_cast<size_t>(cg) * a.Rpad + row;
 #pragma unroll
