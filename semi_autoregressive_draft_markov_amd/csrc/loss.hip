@@ -81,6 +81,17 @@ struct LossConsts {
     float pos_weight[64];  // w_k / N for k < gamma
 };
 
+// Position of E[i][j] in the transposed copy the dW2 contraction reads:
+// chunk-major, the 32-row chunk i / 32 of all r columns contiguous, column j
+// of it 32 consecutive values.  An MFMA operand (16 columns j, 8 rows i of
+// one chunk) is then 1 KB of whole cache lines, and a chunk is read once: in
+// a plain [r, Rpad] layout each operand piece is half a line whose other
+// half belongs to the next chunk, and the streaming dZ evicts it between
+// the two.
+__host__ __device__ __forceinline__ size_t et_index(int i, int j, int r) {
+    return (static_cast<size_t>(i >> 5) * r + j) * 32 + (i & 31);
+}
+
 // Workgroup = one row i (rows in [R, Rpad) only zero their operand rows).
 // Teacher forcing: prev = anchor[n] at k = 0, labels[n, k-1] after.  The row
 // k = 0 workgroup of block n also checks every token id of the block.  Also
@@ -100,7 +111,7 @@ __global__ __launch_bounds__(256) void k_loss_prep(
         for (int j = threadIdx.x; j < r; j += blockDim.x) {
             ebf[static_cast<size_t>(i) * r + j] = 0;
             ef[static_cast<size_t>(i) * r + j] = 0.0f;
-            et[static_cast<size_t>(j) * Rpad + i] = 0;
+            et[et_index(i, j, r)] = 0;
         }
         if (threadIdx.x == 0) {
             label_out[i] = 0;
@@ -130,7 +141,7 @@ __global__ __launch_bounds__(256) void k_loss_prep(
         const uint16_t eb = static_cast<uint16_t>(f32_to_bf16(e));
         ebf[static_cast<size_t>(i) * r + j] = eb;
         ef[static_cast<size_t>(i) * r + j] = e;
-        et[static_cast<size_t>(j) * Rpad + i] = eb;
+        et[et_index(i, j, r)] = eb;
         part += load_f(w_conf, d + j) * e;
         zl = fmaf(e, load_f(W2, static_cast<int64_t>(j) * V + lab), zl);
     }
@@ -670,8 +681,8 @@ __global__ __launch_bounds__(256) void k_loss_sum(const float* __restrict__ tce,
 //     workgroup barrier per chunk.  A float32 dZ is split into bf16 hi + lo
 //     planes (two MFMAs per tile), so the product keeps about 16 bits of its
 //     mantissa.
-//   A (E^T) -- from the transposed copy of E, 16 contiguous bytes per lane
-//     and tile, loaded two chunks ahead (E is small and stays in cache).
+//   A (E^T) -- from the chunk-major transposed copy of E (et_index), 16
+//     contiguous bytes per lane and tile, loaded two chunks ahead.
 constexpr int kDw2Cols = 128;
 constexpr int kDw2Threads = 256;
 // Word offset of row pair p (of 16) of staged column col (of 128): the
@@ -756,7 +767,7 @@ __global__ __launch_bounds__(kDw2Threads, DZF32 ? 1 : 2) void k_dw2_mfma(const v
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int j = min(j0 + 16 * it + n, r - 1);
-            dst[it] = *reinterpret_cast<const u32x4*>(et + static_cast<size_t>(j) * Rpad + 32 * cc + 8 * g);
+            dst[it] = *reinterpret_cast<const u32x4*>(et + et_index(32 * cc + 8 * g, j, r));
         }
     };
     f32x4 acc[4][8];
@@ -775,12 +786,16 @@ __global__ __launch_bounds__(kDw2Threads, DZF32 ? 1 : 2) void k_dw2_mfma(const v
     __syncthreads();
     // chunk c: B in Bs[c & 1], A in afr[c & 1]; ring slot (c + 1) % kAhead
     // holds chunk c + 1, staged at the end of the step, then refilled with
-    // chunk c + 1 + kAhead
-    for (int c0 = 0; c0 < nchunks; c0 += kAhead) {
+    // chunk c + 1 + kAhead.  The chunk count is padded to a multiple of
+    // kAhead (chunks past the end stage zeros: their rows are past R, and
+    // their A operands are clamped), so the unrolled body has no exit: with
+    // one, the compiler's count of loads in flight became conservative at the
+    // loop head and its waits drained the ring every step.
+    const int nchunks_pad = (nchunks + kAhead - 1) / kAhead * kAhead;
+    for (int c0 = 0; c0 < nchunks_pad; c0 += kAhead) {
 #pragma unroll
         for (int u = 0; u < kAhead; ++u) {
             const int c = c0 + u;
-            if (c >= nchunks) break;
             if (rows_live) {
 #pragma unroll
                 for (int pl = 0; pl < kPlanes; ++pl)
@@ -797,7 +812,7 @@ __global__ __launch_bounds__(kDw2Threads, DZF32 ? 1 : 2) void k_dw2_mfma(const v
             }
             load_a(c + 2, afr[u & 1]);
             const int slot = (u + 1) % kAhead;
-            if (c + 1 < nchunks) store_b(ring[slot], (u + 1) & 1, c + 1);
+            store_b(ring[slot], (u + 1) & 1, c + 1);
             load_b(c + 1 + kAhead, ring[slot]);
             __syncthreads();
         }
