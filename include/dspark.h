@@ -328,9 +328,13 @@ dspark_status dspark_noise(uint64_t seed, uint64_t offset, uint32_t c1, uint32_t
 
 /* Synchronises `hip_stream`, then reads the per-block error flags the last
  * call with these dims left at the start of `workspace`: *code (HOST
- * pointer) = the number of blocks that met a token id outside [0, V) (0
- * when all were valid).  Returns DSPARK_EDEVICE if the synchronisation or
- * the copy fails. */
+ * pointer) = the number of blocks whose outputs are invalid (0 when all
+ * are valid): a block that met a token id outside [0, V), or every block
+ * when a grid barrier of the single-launch kernel gave up waiting (for
+ * ~2^20 polling rounds, ~0.5 s: it assumes one workgroup per compute unit
+ * can run at once, which other work on the device can prevent).  Returns
+ * DSPARK_EDEVICE, with *code set, when a barrier gave up, or when the
+ * synchronisation or the copy fails. */
 dspark_status dspark_read_device_error(const dspark_dims* dims, const void* workspace,
                                        int32_t* code, void* hip_stream);
 
@@ -342,6 +346,11 @@ dspark_status dspark_read_device_error(const dspark_dims* dims, const void* work
  * (DSPARK_EUNSUPPORTED when the problem does not fit it).  Both paths give
  * the same results.  Returns DSPARK_EINVAL for an unknown option or value. */
 #define DSPARK_OPT_DRAFT_PATH 1
+/* DSPARK_OPT_BARRIER_SPIN: polling rounds before a grid barrier of the
+ * single-launch kernel gives up (0, the default: 2^20); -1 makes every wait
+ * give up at once, which lets a caller test its handling of that failure
+ * (the kernel then completes normally with every block invalid). */
+#define DSPARK_OPT_BARRIER_SPIN 3
 dspark_status dspark_set_option(int option, int value);
 
 /* Kernel timing for measurement.  While enabled on the calling thread, each

@@ -20,6 +20,7 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 DSPARK_HEAD_MARKOV, DSPARK_HEAD_RNN = 0, 1
 DSPARK_CALL_DRAFT, DSPARK_CALL_LOSS, DSPARK_CALL_LOSS_BACKWARD, DSPARK_CALL_VERIFY = 0, 1, 2, 3
 DSPARK_OPT_DRAFT_PATH = 1
+DSPARK_OPT_BARRIER_SPIN = 3
 
 STATUS_NAMES = {0: "DSPARK_OK", 1: "DSPARK_EINVAL", 2: "DSPARK_EUNSUPPORTED",
                 3: "DSPARK_EWORKSPACE", 4: "DSPARK_EDEVICE"}

@@ -77,6 +77,8 @@ hipError_t record(hipStream_t s) {
 
 thread_local int g_draft_path = 0;
 int draft_path_option() { return g_draft_path; }
+thread_local int g_barrier_spin = 0;
+int barrier_spin_option() { return g_barrier_spin; }
 
 bool profiling_enabled() { return g_prof.on; }
 hipError_t profile_begin(hipStream_t s) { return g_prof.on ? record(s) : hipSuccess; }
@@ -357,12 +359,18 @@ dspark_status dspark_read_device_error(const dspark_dims* dims, const void* work
     e = hipMemcpy(&flags[0], workspace, sizeof(int32_t) * n, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return fail(DSPARK_EDEVICE, "reading the error flags failed: %s", hipGetErrorString(e));
     int32_t count = 0;
+    bool timed_out = false;
     for (int i = 0; i < n; ++i) {
         int32_t f;
         memcpy(&f, &flags[sizeof(int32_t) * i], sizeof f);
         count += f != 0;
+        timed_out |= f == 2;
     }
     *code = count;
+    if (timed_out)
+        return fail(DSPARK_EDEVICE,
+                    "a grid barrier of the single-launch drafting kernel gave up waiting (other work may hold "
+                    "compute units); every block of the call is invalid");
     return ok();
 }
 
@@ -370,6 +378,11 @@ dspark_status dspark_set_option(int option, int value) {
     if (option == DSPARK_OPT_DRAFT_PATH) {
         if (value < 0 || value > 2) return fail(DSPARK_EINVAL, "draft path %d is not 0, 1 or 2", value);
         dspark::g_draft_path = value;
+        return ok();
+    }
+    if (option == DSPARK_OPT_BARRIER_SPIN) {
+        if (value < -1) return fail(DSPARK_EINVAL, "barrier spin %d is below -1", value);
+        dspark::g_barrier_spin = value;
         return ok();
     }
     return fail(DSPARK_EINVAL, "unknown option %d", option);

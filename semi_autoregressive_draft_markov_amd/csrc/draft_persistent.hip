@@ -63,6 +63,8 @@ struct PersistArgs {
     uint32_t* bar;       // barrier words (cleared at the kernel's start)
     uint64_t* flags;     // [nWG + 1] start-barrier flags, then the start barrier's time-out slot
     uint64_t epoch;      // this call's flag value (never repeats within a process)
+    uint32_t spin_limit; // polling rounds before a barrier wait gives up
+    int fail_waits;      // test hook: every barrier wait gives up at once
     float2* pms;         // [gamma, B, nWG] softmax (max, sum) partials of every step, base 2
     int32_t* dead;       // [B]
     int32_t* tokens;
@@ -103,13 +105,15 @@ __device__ __forceinline__ void start_barrier_arrive(const PersistArgs& a, int n
 __device__ __forceinline__ void start_barrier_wait(const PersistArgs& a) {
     if (threadIdx.x < kWave) {
         uint32_t spins = 0;
-        while (true) {
+        if (a.fail_waits && threadIdx.x == 0)
+            __hip_atomic_store(a.flags + a.nWG, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        while (!a.fail_waits) {
             bool late = false;
             for (int i = threadIdx.x; i < a.nWG; i += kWave)
                 late |= __hip_atomic_load(a.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch;
             if (__ballot(late) == 0) break;
             __builtin_amdgcn_s_sleep(2);
-            if (++spins > (1u << 20)) {
+            if (++spins > a.spin_limit) {
                 if (threadIdx.x == 0)
                     __hip_atomic_store(a.flags + a.nWG, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
@@ -153,19 +157,21 @@ __device__ __forceinline__ void barrier_arrive(uint32_t* bar, uint32_t wg) {
         __hip_atomic_fetch_add(bar + 32 * (wg % kBarGroups), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void barrier_finish(uint32_t* bar, uint32_t step, uint32_t nwg) {
+__device__ __forceinline__ void barrier_finish(uint32_t* bar, uint32_t step, uint32_t nwg, uint32_t spin_limit,
+                                               int fail_waits) {
     if (threadIdx.x < kWave) {
         const uint32_t l = threadIdx.x;
         const uint32_t ngroups = nwg < kBarGroups ? nwg : kBarGroups;
         // group l holds the workgroups wg = l, l + 8, ... < nwg
         const uint32_t target = l < ngroups ? step * ((nwg - l + kBarGroups - 1) / kBarGroups) : 0u;
         uint32_t spins = 0;
-        while (true) {
+        if (fail_waits && l == 0) __hip_atomic_store(bar + kTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        while (!fail_waits) {
             const uint32_t v =
                 l < ngroups ? __hip_atomic_load(bar + 32 * l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
             if (__ballot(v < target) == 0) break;
             __builtin_amdgcn_s_sleep(2);
-            if (++spins > (1u << 20)) {
+            if (++spins > spin_limit) {
                 if (l == 0) __hip_atomic_store(bar + kTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
@@ -801,7 +807,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
             ahead = fetch_u(k + 1, 0);
             noise_ahead(k + 1, 0, on0);
             noise_ahead(k + 1, 1, on1, 0, 2, false);
-            barrier_finish(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG));
+            barrier_finish(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG), a.spin_limit, a.fail_waits);
             const uint64_t key = keys_issue(k);
             noise_ahead(k + 1, 1, on1, 2, 4, false);
             keys_finish(key);
@@ -813,7 +819,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
             __syncthreads();
             barrier_arrive(a.bar, static_cast<uint32_t>(wg));
             ahead = fetch_u(k + 1, 0);
-            barrier_finish(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG));
+            barrier_finish(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG), a.spin_limit, a.fail_waits);
             read_keys(k, 0, a.B);
             stage_rows();
         }
@@ -871,7 +877,7 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
     __shared__ int xs[kMaxGamma + 1];  // xs[0] = anchor, xs[k + 1] = x_k
     __shared__ float ys[kMaxGamma];    // perturbed value at x_k (scaled units)
     __shared__ float cs[kMaxGamma];
-    __shared__ int first_bad_s;
+    __shared__ int first_bad_s, timed_out_s;
     const int b = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
 
@@ -917,9 +923,11 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
         }
         const int x0 = a.anchor[b];
         const uint64_t m = __ballot(inval);
-        const bool head_bad = a.bar[kTimeoutWord] != 0 || a.flags[a.nWG] == a.epoch || x0 < 0 || x0 >= a.V;
+        const bool timed_out = a.bar[kTimeoutWord] != 0 || a.flags[a.nWG] == a.epoch;
+        const bool head_bad = timed_out || x0 < 0 || x0 >= a.V;
         if (lane == 0) {
             xs[0] = x0;
+            timed_out_s = timed_out ? 1 : 0;
             first_bad_s = head_bad ? 0 : (m ? __ffsll(static_cast<unsigned long long>(m)) - 1 : a.gamma);
         }
     }
@@ -997,7 +1005,9 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void k_persist_finish(Persist
             a.conf[out] = cs[k];
             a.survival[out] = S;
         }
-        a.dead[b] = first_bad < a.gamma ? 1 : 0;
+        // 2: a grid barrier gave up (every block of the call), 1: a token
+        // id out of range in this block
+        a.dead[b] = timed_out_s ? 2 : (first_bad < a.gamma ? 1 : 0);
     }
 }
 
@@ -1156,6 +1166,9 @@ static hipError_t launch_persist_kc(const DraftArgs& A) {
 
     p.flags = reinterpret_cast<uint64_t*>(ws + L.flags);
     p.epoch = next_epoch();
+    const int spin = barrier_spin_option();
+    p.spin_limit = spin > 0 ? static_cast<uint32_t>(spin) : (1u << 20);
+    p.fail_waits = spin < 0 ? 1 : 0;
     hipError_t e = profile_begin(A.stream);
     if (e != hipSuccess) return e;
     void* args[] = {&p};

@@ -195,6 +195,8 @@ double schedule_prefixes(int R, int gamma, const float* survival, const float* s
 
 // Per-thread choice of drafting path (see dspark_set_option).
 int draft_path_option();
+// DSPARK_OPT_BARRIER_SPIN of the calling thread (0: the default limit)
+int barrier_spin_option();
 
 // Per-thread event timing of the dominant kernel (see dspark_profile_*).
 bool profiling_enabled();

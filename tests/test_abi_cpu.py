@@ -136,7 +136,8 @@ def test_product_path_never_imports_the_oracle():
 
 
 def test_set_option_validates(lib):
-    for opt, good, bad in ((lib.DSPARK_OPT_DRAFT_PATH, (0, 1, 2), (-1, 3)),):
+    for opt, good, bad in ((lib.DSPARK_OPT_DRAFT_PATH, (0, 1, 2), (-1, 3)),
+                           (lib.DSPARK_OPT_BARRIER_SPIN, (0, 100, -1), (-2,))):
         for v in good:
             lib.dspark_set_option(opt, v)
         for v in bad:
@@ -144,6 +145,7 @@ def test_set_option_validates(lib):
                 lib.dspark_set_option(opt, v)
             assert e.value.status == lib.DSPARK_EINVAL
     lib.dspark_set_option(lib.DSPARK_OPT_DRAFT_PATH, 0)
+    lib.dspark_set_option(lib.DSPARK_OPT_BARRIER_SPIN, 0)
     # the cooperative-launch option (formerly 2) no longer exists
     with pytest.raises(lib.DsparkError):
         lib.dspark_set_option(2, 0)

@@ -335,6 +335,34 @@ def test_single_launch_dirty_reused_workspace(ops):
                 label="reused workspace")
 
 
+def test_single_launch_barrier_time_out_is_reported(ops):
+    # every grid-barrier wait forced to give up at once (the kernel's own
+    # bounded waits, set from the host): the call completes, every block is
+    # invalid and dspark_read_device_error reports the time-out; the next
+    # call with the default limit is correct again
+    import torch
+    from semi_autoregressive_draft_markov_amd import binding
+    inp = small(V=4104, r=256, d=64, gamma=4, B=12, seed=61)
+    t = synth.to_torch(inp)
+    binding.dspark_set_option(binding.DSPARK_OPT_DRAFT_PATH, SINGLE)
+    binding.dspark_set_option(binding.DSPARK_OPT_BARRIER_SPIN, -1)
+    try:
+        note("case: single launch, barrier waits forced to give up, V4104 B12 gamma4")
+        out = ops.draft_block(t["U"], t["h"], t["anchor"], t["W1"], t["W2"], t["w_conf"], t["temperature"], seed=6)
+        torch.cuda.synchronize()
+        assert (out["tokens"].cpu().numpy() == -1).all()
+        assert np.isnan(out["survival"].cpu().numpy()).all()
+        with pytest.raises(binding.DsparkError) as e:
+            binding.dspark_read_device_error(out["_dims"], out["_ws"])
+        assert e.value.status == binding.DSPARK_EDEVICE and "gave up" in str(e.value)
+    finally:
+        binding.dspark_set_option(binding.DSPARK_OPT_BARRIER_SPIN, 0)
+    note("case: the same call with the default limit")
+    g = run_gpu(ops, inp, seed=6, path=SINGLE)
+    check_draft(inp, g, 6, 0, label="after forced time-out")
+    assert binding.dspark_read_device_error(g["_out"]["_dims"], g["_out"]["_ws"]) == 0
+
+
 @pytest.mark.parametrize("path", [MULTI, SINGLE])
 def test_qwen3_14b_shape_all_blocks(ops, path):
     inp = synth.config_inputs(4)
