@@ -47,7 +47,10 @@ constexpr int kBarGroups = 8;     // arrival counters at bar[32 g]
 constexpr int kTimeoutWord = 320; // set when a barrier wait gave up
 static_assert(kTimeoutWord < kDraftBarWords, "barrier words");
 constexpr int kMaxGamma = 64;     // largest gamma the C ABI accepts
-constexpr int kNoiseStride = kPThreads;  // noise buffer: [unit][16 columns][threads] floats
+// noise buffer: [block group][q = 0..3][threads][4 columns] floats, so that a
+// thread's 4 terms of one Philox block are one 16-byte slot and the 64 slots
+// of a wave's access are consecutive (conflict-free)
+constexpr int kNoiseQStride = 4 * kPThreads;  // floats between the q slots of a thread
 
 struct PersistArgs {
     const uint16_t* U;
@@ -363,12 +366,15 @@ __device__ __forceinline__ PStats unit_stats(const float (&z)[20], const float (
 __device__ __forceinline__ PStats unit_stats_pre(const f32x4 (&acc)[4], const f32x4& accx, const float* gnu,
                                                  const float (&nx)[4], float scale, int v0, int vx) {
     float z[20], y[20];
+    f32x4 gq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gq[q] = *reinterpret_cast<const f32x4*>(gnu + q * kNoiseQStride);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             z[4 * q + c] = acc[c][q];
-            y[4 * q + c] = fmaf(acc[c][q], scale, -gnu[kNoiseStride * (4 * q + c)]);
+            y[4 * q + c] = fmaf(acc[c][q], scale, -gq[q][c]);
         }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -408,8 +414,8 @@ struct UAhead {
 // terms of every block group are computed while memory or other workgroups
 // are busy -- under the W2 loads before step 0; at each step end after the
 // barrier arrival, spread over the wait for the other workgroups, the key
-// read and the W1 row loads -- and kept in LDS ([group][16 columns][threads]
-// floats) for the register-tile columns and in registers for the 4
+// read and the W1 row loads -- and kept in LDS (16-byte slots, see
+// kNoiseQStride) for the register-tile columns and in registers for the 4
 // LDS-fragment columns.
 constexpr size_t kPersistLdsMax = 160 * 1024;  // one workgroup per CU
 
@@ -421,7 +427,7 @@ template <int KC>
 __host__ __device__ constexpr size_t persist_e_bytes(int rows) {
     return static_cast<size_t>(rows) * (KC * 32 + 8) * 2;
 }
-constexpr size_t kNoiseBytesPerGroup = 16 * kNoiseStride * 4;
+constexpr size_t kNoiseBytesPerGroup = 4 * kNoiseQStride * 4;
 template <int KC>
 __host__ __device__ constexpr size_t persist_lds(int Bpad, int B, bool grouped, bool ahead) {
     return persist_xfrag_bytes<KC>() + persist_e_bytes<KC>(grouped ? 32 : Bpad) +
@@ -447,7 +453,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     PStats* slot = reinterpret_cast<PStats*>(smem + persist_xfrag_bytes<KC>() + e_bytes + 2 * bp4);
     float* gn = reinterpret_cast<float*>(smem + persist_xfrag_bytes<KC>() + e_bytes + 2 * bp4 +
                                          align_up(sizeof(PStats) * kPWaves * static_cast<size_t>(a.B), 16)) +
-                threadIdx.x;  // this thread's noise column
+                4 * threadIdx.x;  // this thread's noise slot
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: wave-uniform branches
@@ -478,13 +484,15 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         uint32_t cb = static_cast<uint32_t>(b), cv = static_cast<uint32_t>(v0) >> 2;
         asm volatile("" : "+v"(cb), "+v"(cv));
         if (reg_live) {
-            float* dst = gn + nb * 16 * kNoiseStride;
+            float* dst = gn + nb * 4 * kNoiseQStride;
 #pragma unroll 2  // two independent Philox blocks at a time: their rounds interleave
             for (int q = q0; q < q1; ++q) {
                 const u32x4 w = philox4x32_10(u32x4{cv + static_cast<uint32_t>(q), static_cast<uint32_t>(kk), cb, a.ctr3},
                                               a.key0, a.key1);
+                f32x4 gv;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) dst[kNoiseStride * (4 * q + c)] = on ? log2_of_neg_log2_uniform(w[c]) : 0.0f;
+                for (int c = 0; c < 4; ++c) gv[c] = on ? log2_of_neg_log2_uniform(w[c]) : 0.0f;
+                *reinterpret_cast<f32x4*>(dst + q * kNoiseQStride) = gv;
             }
         }
         if (with_x && x_live) {
@@ -707,7 +715,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
                     for (int c = 0; c < 4; ++c)
                         if (!x_live) accx[c] = -INFINITY;
                 }
-                st = unit_stats_pre(acc, accx, gn + nb * 16 * kNoiseStride, nb == 0 ? nx0 : nx1,
+                st = unit_stats_pre(acc, accx, gn + nb * 4 * kNoiseQStride, nb == 0 ? nx0 : nx1,
                                     fabsf(scale_s[nb * 16 + n]), v0, vx);
             } else {
                 st = pstats_empty();
