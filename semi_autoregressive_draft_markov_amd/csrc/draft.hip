@@ -802,8 +802,13 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
         }
         hipError_t pe = profile_begin(a.stream);
         if (pe != hipSuccess) return pe;
-        if (mfma) {
-            if (D.head == DSPARK_HEAD_RNN)
+        int P = L.P;
+        const int npl = D.head == DSPARK_HEAD_RNN ? 2 : 1;
+        if (mfma && stream_pipe_ok(D, npl)) {
+            pe = launch_stream_pipe(a, L, k, ws, npl, &P);
+            if (pe != hipSuccess) return pe;
+        } else if (mfma) {
+            if (npl == 2)
                 launch_mfma_kc<2>(a, L, k, ws);
             else
                 launch_mfma_kc<1>(a, L, k, ws);
@@ -821,7 +826,7 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
                            reinterpret_cast<const float*>(ws + L.pm),
                            reinterpret_cast<const float*>(ws + L.ps),
                            reinterpret_cast<const uint64_t*>(ws + L.pkey),
-                           reinterpret_cast<const float*>(ws + L.pzx), L.P, W1, wc,
+                           reinterpret_cast<const float*>(ws + L.pzx), P, W1, wc,
                            reinterpret_cast<const float*>(ws + L.hdot), D.V, D.r, D.d,
                            D.gamma, k, D.head, mfma ? 1 : 0, dead, emb, coef, ebf, a.tokens, a.logp,
                            a.conf, a.survival);
@@ -833,6 +838,8 @@ const char* draft_kernel_name(const dspark_dims& d) {
     if (draft_path_option() != 1 && persist_path_ok(d)) return persist_kernel_name(d);
     if (draft_path_option() == 2) return "";
     if (!mfma_path_ok(d)) return d.dtype == DSPARK_BF16 ? "k_stream_generic<unsigned short>" : "k_stream_generic<float>";
+    const int npl = d.head == DSPARK_HEAD_RNN ? 2 : 1;
+    if (stream_pipe_ok(d, npl)) return stream_pipe_name(npl, (d.B + 15) / 16 * 16);
     static char buf[64];
     snprintf(buf, sizeof buf, "k_stream_mfma<%d, %d>", d.r / 32, d.head == DSPARK_HEAD_RNN ? 2 : 1);
     return buf;

@@ -49,6 +49,11 @@ int draft_persist_max_wg();
 hipError_t launch_draft_persistent(const struct DraftArgs& a);
 int draft_partials(const dspark_dims& d);
 DraftLayout draft_layout(const dspark_dims& d);
+// Pipelined per-step streaming kernel (r = 256, B <= 128); npl = coef
+// planes.  launch_stream_pipe stores the number of partials per block in *P.
+bool stream_pipe_ok(const dspark_dims& d, int npl);
+hipError_t launch_stream_pipe(const struct DraftArgs& a, const DraftLayout& L, int k, char* ws, int npl, int* P);
+const char* stream_pipe_name(int npl, int Bpad);
 
 // Loss-call workspace carve-up.  Rows i = n * gamma + k, padded to Rpad.
 struct LossLayout {
