@@ -76,9 +76,13 @@ struct Tile32 {
     }
 };
 
-// Running statistics of a lane: m = max z/T, s = sum exp(z/T - m) and the
-// argmax key of the perturbed values (Stats without z/T at the argmax, which
-// is recovered once per block from the winning key; see the kernel's end).
+// Running statistics of a lane in base-2 units: with z2 = z log2(e) / T
+// (z log2(e) when greedy), s = sum of 2^(z2 - m) over the columns seen so
+// far for a reference m no smaller than their largest perturbed value, and
+// the argmax key of the perturbed values y = z2 - log2(-log2 u) (sampling;
+// the Gumbel-max value up to a positive factor and a constant, as in
+// log2_of_neg_log2_uniform) or y = z2 (greedy).  z at the argmax is not
+// carried: it is recovered once per block from the winning key at the end.
 struct RStats {
     float m;
     float s;
@@ -88,8 +92,8 @@ struct RStats {
 __device__ __forceinline__ RStats rstats_merge(const RStats& a, const RStats& b) {
     RStats r;
     r.m = fmaxf(a.m, b.m);
-    const float sa = (a.s > 0.0f) ? a.s * __expf(a.m - r.m) : 0.0f;
-    const float sb = (b.s > 0.0f) ? b.s * __expf(b.m - r.m) : 0.0f;
+    const float sa = (a.s > 0.0f) ? a.s * __builtin_amdgcn_exp2f(a.m - r.m) : 0.0f;
+    const float sb = (b.s > 0.0f) ? b.s * __builtin_amdgcn_exp2f(b.m - r.m) : 0.0f;
     r.s = sa + sb;
     r.key = b.key > a.key ? b.key : a.key;
     return r;
@@ -108,15 +112,14 @@ __device__ __forceinline__ RStats rstats_merge_xor(const RStats& a) {
     return rstats_merge(x, y);
 }
 
-// Softmax / Gumbel-argmax statistics of the 8 columns v0 .. v0 + 7 of block
-// b (all present: V % 8 == 0), in the units k_stream_mfma uses: m = max z/T,
-// s = sum exp(z/T - m), and the argmax key of z/T + Gumbel (sampling) or z/T
-// (greedy).
-__device__ __forceinline__ RStats lane_stats8(const float (&z)[8], int v0, int b, int k, bool sampling, float invT,
-                                             uint32_t key0, uint32_t key1, uint32_t ctr3) {
-    float zs[8], y[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) zs[j] = z[j] * invT;
+// Adds the 8 columns v0 .. v0 + 7 of block b (all present: V % 8 == 0) to
+// the running statistics st; scale = log2(e) / T (sampling) or log2(e).  The
+// new reference is the larger of the old one and the columns' largest
+// perturbed value: z2 - y <= log2(24) for every column, so no term of the
+// sum overflows, and the winner's term is at least 2^-24.
+__device__ __forceinline__ void lane_update8(RStats& st, const float (&z)[8], int v0, int b, int k, bool sampling,
+                                             float scale, uint32_t key0, uint32_t key1, uint32_t ctr3) {
+    float y[8];
     if (sampling) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -124,26 +127,26 @@ __device__ __forceinline__ RStats lane_stats8(const float (&z)[8], int v0, int b
                                static_cast<uint32_t>(b), ctr3};
             const u32x4 w = philox4x32_10(ctr, key0, key1);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) y[4 * q + c] = zs[4 * q + c] + gumbel_from_word(w[c]);
+            for (int c = 0; c < 4; ++c) y[4 * q + c] = fmaf(z[4 * q + c], scale, -log2_of_neg_log2_uniform(w[c]));
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] = zs[j];
+        for (int j = 0; j < 8; ++j) y[j] = z[j] * scale;
     }
-    float m = zs[0], ybest = y[0];
+    float ybest = y[0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) {
-        m = fmaxf(m, zs[j]);
-        ybest = fmaxf(ybest, y[j]);
-    }
-    const float mb = m * kLog2e;
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s += __builtin_amdgcn_exp2f(fmaf(zs[j], kLog2e, -mb));
+    for (int j = 1; j < 8; ++j) ybest = fmaxf(ybest, y[j]);
     int idx = 7;
 #pragma unroll
     for (int j = 6; j >= 0; --j) idx = y[j] == ybest ? j : idx;
-    return RStats{m, s, argmax_key(ybest, static_cast<uint32_t>(v0 + idx))};
+    const float m = fmaxf(st.m, ybest);
+    float s = st.s > 0.0f ? st.s * __builtin_amdgcn_exp2f(st.m - m) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += __builtin_amdgcn_exp2f(fmaf(z[j], scale, -m));
+    const uint64_t key = argmax_key(ybest, static_cast<uint32_t>(v0 + idx));
+    st.m = m;
+    st.s = s;
+    st.key = key > st.key ? key : st.key;
 }
 
 template <int NPL>
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(kSpThreads, 1) void k_stream_pipe(
     // piece 4 kc + g of block 16 nb + n, so a read's bank group is n + const
     // (conflict-free) without padding
     u32x4* Es = reinterpret_cast<u32x4*>(smem);
-    // per block: 1/T when it samples, -1 when greedy
+    // per block: log2(e) / T when it samples, -log2(e) when greedy
     float* inv_s = reinterpret_cast<float*>(smem + static_cast<size_t>(NPL) * kPieces * kSpRows * 16);
 
     const int lane = threadIdx.x & 63;
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kSpThreads, 1) void k_stream_pipe(
         }
         for (int b = threadIdx.x; b < Bpad; b += kSpThreads) {
             const float t = b < B ? temperature[b] : 0.0f;
-            inv_s[b] = t > 0.0f ? 1.0f / t : -1.0f;
+            inv_s[b] = t > 0.0f ? kLog2e / t : -kLog2e;
         }
     }
     __syncthreads();
@@ -218,9 +221,9 @@ __global__ __launch_bounds__(kSpThreads, 1) void k_stream_pipe(
 
     // One tile at a time, chunk-major: the products of chunk kc for every
     // unit, then chunk kc of the next tile is loaded into the same registers
-    // (its last use is issued), and after the products the next tile's U
-    // values; the U values start the accumulators (z = U + bias comes out of
-    // the matrix cores).  Every load is waited for only at the start of the
+    // (its last use is issued), and halfway through the statistics the next
+    // tile's U values; the U values start the accumulators (z = U + bias
+    // comes out of the matrix cores).  Every load is waited for only at the start of the
     // next tile, a whole statistics phase later (vector-memory counts
     // complete in issue order, so a load issued before a later wait would be
     // waited for too).  The loads are unconditional (after the last tile
@@ -279,25 +282,28 @@ __global__ __launch_bounds__(kSpThreads, 1) void k_stream_pipe(
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < NU; ++u) uall[u] = fetch_u(c1, u);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
         for (int u = 0; u < NU; ++u) {
             int b = u * 16 + n;
             asm volatile("" : "+v"(b));
             if (live && b < B) {
-                const float is = inv_s[b];
-                const bool sampling = is > 0.0f;
+                const float sc = inv_s[b];
+                const bool sampling = sc > 0.0f;
                 float z[8];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
                     for (int c = 0; c < 2; ++c) z[2 * q + c] = acc[u][c][q];
-                st[u] = rstats_merge(st[u], lane_stats8(z, v0, b, k, sampling, sampling ? is : 1.0f, key0, key1, ctr3));
+                lane_update8(st[u], z, v0, b, k, sampling, fabsf(sc), key0, key1, ctr3);
             }
             // one unit's statistics at a time (interleaving units would hold
             // all their temporaries at once)
             __builtin_amdgcn_sched_barrier(0);
+            // the next tile's U values once half the accumulators are free
+            if (u == (NU - 1) / 2) {
+#pragma unroll
+                for (int w = 0; w < NU; ++w) uall[w] = fetch_u(c1, w);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
@@ -313,9 +319,10 @@ __global__ __launch_bounds__(kSpThreads, 1) void k_stream_pipe(
         if (g == 0) red[wave * kSpRows + u * 16 + n] = m;
     }
     __syncthreads();
-    // z/T at the argmax: the winning perturbed value (the key's high word,
-    // order-preserving bits inverted) minus the winner's Gumbel term,
-    // recomputed from its counter (zero when greedy)
+    // back to the units of the partials (natural log): m ln 2, and z/T at
+    // the argmax = (the winning perturbed value, from the key's high word
+    // with the order-preserving bits inverted, plus the winner's
+    // log2(-log2 u) recomputed from its counter; nothing when greedy) ln 2
     const int P = gridDim.x;
     for (int b = threadIdx.x; b < B; b += kSpThreads) {
         RStats t = red[b];
@@ -325,17 +332,18 @@ __global__ __launch_bounds__(kSpThreads, 1) void k_stream_pipe(
         if (t.key != kKeyNone) {
             const uint32_t kb = static_cast<uint32_t>(t.key >> 32);
             const float y = __uint_as_float((kb & 0x80000000u) ? (kb ^ 0x80000000u) : ~kb);
-            zx = y;
+            float z2 = y;
             if (inv_s[b] > 0.0f) {
                 const uint32_t x = key_index(t.key);
                 const u32x4 w = philox4x32_10(u32x4{x >> 2, static_cast<uint32_t>(k), static_cast<uint32_t>(b), ctr3},
                                               key0, key1);
                 const uint32_t q = x & 3u;
-                zx = y - gumbel_from_word(q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3]);
+                z2 = y + log2_of_neg_log2_uniform(q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3]);
             }
+            zx = z2 * kLn2;
         }
         const size_t o = static_cast<size_t>(b) * P + blockIdx.x;
-        pm[o] = t.m;
+        pm[o] = t.m * kLn2;
         ps[o] = t.s;
         pkey[o] = t.key;
         pzx[o] = zx;
