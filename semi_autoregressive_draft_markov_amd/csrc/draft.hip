@@ -73,6 +73,7 @@ DraftLayout draft_layout(const dspark_dims& d) {
     L.coef = take(sizeof(float) * rows * d.r);
     L.ebf = take(sizeof(uint16_t) * 2 * rows * d.r);
     L.state = take(sizeof(float) * rows * d.r);
+    L.state2 = take(d.head == DSPARK_HEAD_RNN ? sizeof(float) * rows * d.r : 0);
     L.gates = take(sizeof(float) * rows * 3 * d.r);
     L.gh = take(d.head == DSPARK_HEAD_RNN ? sizeof(float) * static_cast<size_t>(d.B) * d.gamma * 3 * d.r : 0);
     L.hdot = take(sizeof(float) * static_cast<size_t>(d.B) * d.gamma);
@@ -193,18 +194,18 @@ __global__ __launch_bounds__(256) void k_rnn_gates(
 // d % 8 == 0).  The columns of W_rnn that multiply h_k do not depend on the
 // drafted tokens, so their part of G is one GEMM over all B x gamma
 // positions before the loop (k_gate_h); each step then only adds the s and
-// e columns (k_gate_step).  D[q][m] = sum_j W_rnn[q][col(j)] A[m][j] is
+// e columns (k_gate_update).  D[q][m] = sum_j W_rnn[q][col(j)] A[m][j] is
 // built from v_mfma_f32_16x16x32_bf16 tiles with A = 16 rows of W_rnn and
 // B = 16 operand rows: lane (g, n) supplies W_rnn row q0 + n and operand row
 // m0 + n at k = 8 g .. 8 g + 7 of a 32-wide chunk and receives D[q0 + 4 g +
 // i][m0 + n] in accumulator element i.  A workgroup computes one 32 (q) x 32
-// (m) tile; its 4 waves take every 4th chunk of K, so each wave has few
-// dependent loads in flight, and the 4 partial tiles are added in wave order
+// (m) tile; its 8 waves take every 8th chunk of K, so each wave has few
+// dependent loads in flight, and the partial tiles are added in wave order
 // through LDS (deterministic).  Products of bf16 values are exact in fp32;
 // the fp32 state s is fed as three bf16 pieces hi + mid + lo, which sum to s
 // exactly, so the step GEMM keeps fp32 accuracy.
 constexpr int kGateTile = 32;
-constexpr int kGateWaves = 4;
+constexpr int kGateHWaves = 8;  // h projection (K = d): K split over 8 waves
 
 __device__ __forceinline__ u32x4 load8_bf16_or0(const uint16_t* p, bool ok) {
     return ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
@@ -232,11 +233,11 @@ __device__ __forceinline__ void gate_mfma2x2(const u32x4 (&wa)[2], const u32x4 (
                                                                 __builtin_bit_cast(bf16x8, ob[j]), acc[i][j], 0, 0, 0);
 }
 
-// Adds the partial tiles of the 4 waves in wave order; wave 0 calls
+// Adds the partial tiles of the NW waves in wave order; wave 0 calls
 // store(i, j, e, value) for every element of the tile.
-template <typename Store>
+template <int NW, typename Store>
 __device__ __forceinline__ void gate_reduce(const f32x4 (&acc)[2][2], Store store) {
-    __shared__ f32x4 part[kGateWaves][4][kWave];
+    __shared__ f32x4 part[NW][4][kWave];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -250,7 +251,7 @@ __device__ __forceinline__ void gate_reduce(const f32x4 (&acc)[2][2], Store stor
         for (int j = 0; j < 2; ++j) {
             f32x4 t = part[0][2 * i + j][lane];
 #pragma unroll
-            for (int w = 1; w < kGateWaves; ++w) {
+            for (int w = 1; w < NW; ++w) {
                 const f32x4 u = part[w][2 * i + j][lane];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) t[e] += u[e];
@@ -262,7 +263,7 @@ __device__ __forceinline__ void gate_reduce(const f32x4 (&acc)[2][2], Store stor
 
 // Gh[m][q] = sum_{i<d} W_rnn[q][2r + i] h[m][i] for the M = B x gamma rows
 // of h (row m = b gamma + k).  Grid: one workgroup per 32 x 32 tile.
-__global__ __launch_bounds__(256) void k_gate_h(const uint16_t* __restrict__ W_rnn, const uint16_t* __restrict__ h,
+__global__ __launch_bounds__(kGateHWaves * kWave) void k_gate_h(const uint16_t* __restrict__ W_rnn, const uint16_t* __restrict__ h,
                                                 int r, int d, int M, float* __restrict__ Gh) {
     const int Q = 3 * r, ldw = 2 * r + d;
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(256) void k_gate_h(const uint16_t* __restrict__ W_r
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     // this wave's chunks: k0 = 32 (wave + 4 t); two chunks in flight
-    constexpr int kStride = 32 * kGateWaves;
+    constexpr int kStride = 32 * kGateHWaves;
     u32x4 wa[2][2], ob[2][2];
     auto fetch = [&](int slot, int k0) {
         const int kk = k0 + 8 * g;
@@ -302,51 +303,60 @@ __global__ __launch_bounds__(256) void k_gate_h(const uint16_t* __restrict__ W_r
         if (k0 + 3 * kStride < d) fetch(1, k0 + 3 * kStride);
         gate_mfma2x2(da, db, acc);
     }
-    gate_reduce(acc, [&](int i, int j, int e, float v) {
+    gate_reduce<kGateHWaves>(acc, [&](int i, int j, int e, float v) {
         const int m = m0 + 16 * j + n;
         if (m < M) Gh[static_cast<size_t>(m) * Q + q0 + 16 * i + 4 * g + e] = v;
     });
 }
 
-// G[b][q] = Gh[b gamma + k][q] + sum_j W_rnn[q][j] s[b][j] + sum_j
-// W_rnn[q][r + j] e[b][j] for the B blocks at step k.  Grid: one workgroup
-// per 32 x 32 tile.
-__global__ __launch_bounds__(256) void k_gate_step(const uint16_t* __restrict__ W_rnn, const float* __restrict__ Gh,
-                                                   const float* __restrict__ state, const float* __restrict__ emb,
-                                                   int r, int d, int gamma, int k, int B, float* __restrict__ gates) {
+// One step of Eq 6 after the h columns, in one launch: G[b][q] = Gh[b gamma
+// + k][q] + sum_j W_rnn[q][j] s[b][j] + sum_j W_rnn[q][r + j] e[b][j], then
+// the gated state update and the bias coefficients o = tanh(G_o), with the
+// formulas of k_rnn_update.  A workgroup owns state columns j0 .. j0 + 15
+// of blocks m0 .. m0 + 31 and computes the three gate rows that update them
+// (q = j, r + j, 2r + j) as 16 x 16 matrix-core tiles (the fp32 state as
+// three exact bf16 pieces, as in k_gate_h's layout); its 8 waves take every
+// 8th 32-wide chunk of K, the partial tiles are added in wave order through
+// LDS, and each thread updates one (block, column).  The state is read from
+// s_in and written to s_out (two buffers, alternating by step): the other
+// workgroups still read s_in as the projection's operand.
+constexpr int kGuWaves = 8;
+constexpr int kGuCols = 16;
+
+__global__ __launch_bounds__(kGuWaves * kWave) void k_gate_update(
+    const uint16_t* __restrict__ W_rnn, const float* __restrict__ Gh, const float* __restrict__ s_in,
+    const float* __restrict__ emb, int r, int d, int gamma, int k, int B, int Bpad, float* __restrict__ s_out,
+    float* __restrict__ coef, uint16_t* __restrict__ ebf) {
+    __shared__ f32x4 part[kGuWaves][6][kWave];
     const int Q = 3 * r, ldw = 2 * r + d;
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
     const int wave = threadIdx.x >> 6;
-    const int tq = Q / kGateTile;
-    const int q0 = (blockIdx.x % tq) * kGateTile, m0 = (blockIdx.x / tq) * kGateTile;
-    const uint16_t* wrow[2] = {W_rnn + static_cast<size_t>(q0 + n) * ldw,
-                               W_rnn + static_cast<size_t>(q0 + 16 + n) * ldw};
+    const int tj = r / kGuCols;
+    const int j0 = (blockIdx.x % tj) * kGuCols, m0 = (blockIdx.x / tj) * kGateTile;
     const bool mok[2] = {m0 + n < B, m0 + 16 + n < B};
     const size_t brow[2] = {static_cast<size_t>(mok[0] ? m0 + n : 0) * r,
                             static_cast<size_t>(mok[1] ? m0 + 16 + n : 0) * r};
-    f32x4 acc[2][2];
+    f32x4 acc[3][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = 32 * wave; k0 < r; k0 += 32 * kGateWaves) {
+    for (int h = 0; h < 3; ++h) acc[h][0] = acc[h][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 32 * wave; k0 < r; k0 += 32 * kGuWaves) {
         const int kk = k0 + 8 * g;
-        u32x4 ws_[2], we[2];
-        f32x4 sv[2][2], ev[2][2];
+        u32x4 ws_[3], we[3];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            ws_[i] = *reinterpret_cast<const u32x4*>(wrow[i] + kk);
-            we[i] = *reinterpret_cast<const u32x4*>(wrow[i] + r + kk);
+        for (int h = 0; h < 3; ++h) {
+            const uint16_t* wrow = W_rnn + static_cast<size_t>(h * r + j0 + n) * ldw;
+            ws_[h] = *reinterpret_cast<const u32x4*>(wrow + kk);
+            we[h] = *reinterpret_cast<const u32x4*>(wrow + r + kk);
         }
+        f32x4 sv[2][2], ev[2][2];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-                sv[j][h2] = mok[j] ? *reinterpret_cast<const f32x4*>(state + brow[j] + kk + 4 * h2) : z;
+                sv[j][h2] = mok[j] ? *reinterpret_cast<const f32x4*>(s_in + brow[j] + kk + 4 * h2) : z;
                 ev[j][h2] = mok[j] ? *reinterpret_cast<const f32x4*>(emb + brow[j] + kk + 4 * h2) : z;
             }
-        u32x4 shi[2], smid[2], slo[2], eb[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             float s8[8], e8[8], t[8];
@@ -355,26 +365,54 @@ __global__ __launch_bounds__(256) void k_gate_step(const uint16_t* __restrict__ 
                 s8[q] = sv[j][q >> 2][q & 3];
                 e8[q] = ev[j][q >> 2][q & 3];
             }
-            shi[j] = pack8_bf16(s8);
+            const u32x4 shi = pack8_bf16(s8);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) t[q] = s8[q] - unpack8_at(shi[j], q);
-            smid[j] = pack8_bf16(t);
+            for (int q = 0; q < 8; ++q) t[q] = s8[q] - unpack8_at(shi, q);
+            const u32x4 smid = pack8_bf16(t);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) t[q] -= unpack8_at(smid[j], q);
-            slo[j] = pack8_bf16(t);
-            eb[j] = pack8_bf16(e8);  // exact: e is a bf16 row of W1
+            for (int q = 0; q < 8; ++q) t[q] -= unpack8_at(smid, q);
+            const u32x4 slo = pack8_bf16(t);
+            const u32x4 eb = pack8_bf16(e8);  // exact: e is a bf16 row of W1
+#pragma unroll
+            for (int h = 0; h < 3; ++h) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, ws_[h]), ae = __builtin_bit_cast(bf16x8, we[h]);
+                acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, shi), acc[h][j], 0, 0, 0);
+                acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, smid), acc[h][j], 0, 0, 0);
+                acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, slo), acc[h][j], 0, 0, 0);
+                acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae, __builtin_bit_cast(bf16x8, eb), acc[h][j], 0, 0, 0);
+            }
         }
-        gate_mfma2x2(ws_, shi, acc);
-        gate_mfma2x2(ws_, smid, acc);
-        gate_mfma2x2(ws_, slo, acc);
-        gate_mfma2x2(we, eb, acc);
     }
-    gate_reduce(acc, [&](int i, int j, int e, float v) {
-        const int m = m0 + 16 * j + n;
-        if (m >= B) return;
-        const int q = q0 + 16 * i + 4 * g + e;
-        gates[static_cast<size_t>(m) * Q + q] = Gh[(static_cast<size_t>(m) * gamma + k) * Q + q] + v;
-    });
+#pragma unroll
+    for (int h = 0; h < 3; ++h)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) part[wave][2 * h + j][lane] = acc[h][j];
+    __syncthreads();
+    // thread (wave, lane g n): block m0 + 16 (wave % 2) + n, column
+    // j0 + 4 g + wave / 2 (accumulator element wave / 2 of lane g n)
+    const int j = wave & 1, e = wave >> 1;
+    const int m = m0 + 16 * j + n;
+    if (m >= B) return;
+    float G[3];
+#pragma unroll
+    for (int h = 0; h < 3; ++h) {
+        float v = part[0][2 * h + j][lane][e];
+#pragma unroll
+        for (int w = 1; w < kGuWaves; ++w) v += part[w][2 * h + j][lane][e];
+        G[h] = v;
+    }
+    const int jc = j0 + 4 * g + e;
+    const float* gh = Gh + (static_cast<size_t>(m) * gamma + k) * Q;
+    const size_t row = static_cast<size_t>(m) * r;
+    const float gate = 1.0f / (1.0f + expf(-(gh[jc] + G[0])));
+    const float cand = tanhf(gh[r + jc] + G[1]);
+    const float o = tanhf(gh[2 * r + jc] + G[2]);
+    s_out[row + jc] = gate * s_in[row + jc] + (1.0f - gate) * cand;
+    coef[row + jc] = o;
+    const uint32_t hi = f32_to_bf16(o);
+    const uint32_t lo = f32_to_bf16(o - __uint_as_float(hi << 16));
+    ebf[row + jc] = static_cast<uint16_t>(hi);
+    ebf[static_cast<size_t>(Bpad) * r + row + jc] = static_cast<uint16_t>(lo);
 }
 
 bool rnn_gate_mfma_ok(const dspark_dims& d) {
@@ -761,6 +799,7 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
     float* coef = reinterpret_cast<float*>(ws + L.coef);
     uint16_t* ebf = reinterpret_cast<uint16_t*>(ws + L.ebf);
     float* state = reinterpret_cast<float*>(ws + L.state);
+    float* state2 = reinterpret_cast<float*>(ws + L.state2);
     float* gates = reinterpret_cast<float*>(ws + L.gates);
     const T* U = static_cast<const T*>(a.U);
     const T* h = static_cast<const T*>(a.h);
@@ -782,23 +821,26 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
     if (gate_mfma) {
         const int M = D.B * D.gamma;
         const int tiles = gate_tq * ((M + kGateTile - 1) / kGateTile);
-        hipLaunchKernelGGL(k_gate_h, dim3(tiles), dim3(kGateWaves * kWave), 0, a.stream,
+        hipLaunchKernelGGL(k_gate_h, dim3(tiles), dim3(kGateHWaves * kWave), 0, a.stream,
                            reinterpret_cast<const uint16_t*>(Wr), reinterpret_cast<const uint16_t*>(h), D.r, D.d, M,
                            gh);
     }
     for (int k = 0; k < D.gamma; ++k) {
         if (D.head == DSPARK_HEAD_RNN) {
             if (gate_mfma) {
-                const int tiles = gate_tq * ((D.B + kGateTile - 1) / kGateTile);
-                hipLaunchKernelGGL(k_gate_step, dim3(tiles), dim3(kGateWaves * kWave), 0, a.stream,
-                                   reinterpret_cast<const uint16_t*>(Wr), gh, state, emb, D.r, D.d, D.gamma, k, D.B,
-                                   gates);
+                // s_k in buffer k % 2, s_{k+1} into the other
+                float* s_in = (k & 1) ? state2 : state;
+                float* s_out = (k & 1) ? state : state2;
+                const int tiles = (D.r / kGuCols) * ((D.B + kGateTile - 1) / kGateTile);
+                hipLaunchKernelGGL(k_gate_update, dim3(tiles), dim3(kGuWaves * kWave), 0, a.stream,
+                                   reinterpret_cast<const uint16_t*>(Wr), gh, s_in, emb, D.r, D.d, D.gamma, k, D.B,
+                                   L.Bpad, s_out, coef, ebf);
             } else {
                 hipLaunchKernelGGL((k_rnn_gates<T>), dim3((3 * D.r + 15) / 16, (D.B + 15) / 16), dim3(256), 0,
                                    a.stream, Wr, state, emb, h, D.r, D.d, D.gamma, k, D.B, gates);
+                hipLaunchKernelGGL(k_rnn_update, dim3(D.B), dim3(256), 0, a.stream, gates, state, coef, ebf,
+                                   D.r, L.Bpad);
             }
-            hipLaunchKernelGGL(k_rnn_update, dim3(D.B), dim3(256), 0, a.stream, gates, state, coef, ebf,
-                               D.r, L.Bpad);
         }
         hipError_t pe = profile_begin(a.stream);
         if (pe != hipSuccess) return pe;

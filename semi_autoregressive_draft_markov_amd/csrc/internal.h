@@ -29,6 +29,7 @@ struct DraftLayout {
     size_t coef;       // f32 [Bpad, r]  bias coefficients (emb, or tanh(W_o z))
     size_t ebf;        // u16 [2, Bpad, r] bf16 planes of coef (hi, lo)
     size_t state;      // f32 [Bpad, r]  RNN state s
+    size_t state2;     // f32 [Bpad, r]  second RNN state buffer (steps alternate)
     size_t gates;      // f32 [Bpad, 3r] RNN joint projection output
     size_t gh;         // f32 [B, gamma, 3r] h columns of the RNN projection (RNN head only)
     size_t hdot;       // f32 [B, gamma]  h part of the Eq 7 logit, w[0:d] . h_k

@@ -228,6 +228,11 @@ __global__ __launch_bounds__(kSpThreads, 1) void k_stream_pipe(
     // complete in issue order, so a load issued before a later wait would be
     // waited for too).  The loads are unconditional (after the last tile
     // they repeat it).
+    // Waves w and w + 4 share a SIMD.  The second starts about a microsecond
+    // later, and a wave's products run at raised priority, so that one
+    // wave's matrix-core phase tends to overlap the other's statistics
+    // (measured: 71.2 -> 69.0 us per step at the Gemma4 shape).
+    if (wave >= 4) __builtin_amdgcn_s_sleep(40);
     Tile32<KC> t;
     u32x4 uall[NU];
     if (S > 0) {
@@ -256,6 +261,7 @@ __global__ __launch_bounds__(kSpThreads, 1) void k_stream_pipe(
         // product i + kAhead read while product i is issued (LDS latency off
         // the matrix-core path); chunk kc of the next tile is loaded after
         // the last product of chunk kc
+        __builtin_amdgcn_s_setprio(2);
         const u32x4* erow = Es + g * kSpRows + n;
         constexpr int kN = KC * NPL * NU, kAhead = 2;
         auto piece = [&](int i) {
@@ -281,6 +287,7 @@ __global__ __launch_bounds__(kSpThreads, 1) void k_stream_pipe(
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             int b = u * 16 + n;
