@@ -198,12 +198,11 @@ __global__ __launch_bounds__(256) void k_rnn_gates(
 // built from v_mfma_f32_16x16x32_bf16 tiles with A = 16 rows of W_rnn and
 // B = 16 operand rows: lane (g, n) supplies W_rnn row q0 + n and operand row
 // m0 + n at k = 8 g .. 8 g + 7 of a 32-wide chunk and receives D[q0 + 4 g +
-// i][m0 + n] in accumulator element i.  A workgroup computes one 32 (q) x 32
-// (m) tile; its 8 waves take every 8th chunk of K, so each wave has few
-// dependent loads in flight, and the partial tiles are added in wave order
-// through LDS (deterministic).  Products of bf16 values are exact in fp32;
-// the fp32 state s is fed as three bf16 pieces hi + mid + lo, which sum to s
-// exactly, so the step GEMM keeps fp32 accuracy.
+// i][m0 + n] in accumulator element i.  The waves of a workgroup take
+// interleaved chunks of K and their partial tiles are added in a fixed
+// order through LDS (deterministic).  Products of bf16 values are exact in
+// fp32; the fp32 state s is fed as three bf16 pieces hi + mid + lo, which
+// sum to s exactly, so the step GEMM keeps fp32 accuracy.
 constexpr int kGateTile = 32;
 constexpr int kGateHWaves = 8;  // h projection (K = d): K split over 8 waves
 
@@ -224,89 +223,103 @@ __device__ __forceinline__ float unpack8_at(const u32x4& v, int q) {
     return (q & 1) ? hi_bf16(v[q >> 1]) : lo_bf16(v[q >> 1]);
 }
 
-__device__ __forceinline__ void gate_mfma2x2(const u32x4 (&wa)[2], const u32x4 (&ob)[2], f32x4 (&acc)[2][2]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[i]),
-                                                                __builtin_bit_cast(bf16x8, ob[j]), acc[i][j], 0, 0, 0);
-}
-
-// Adds the partial tiles of the NW waves in wave order; wave 0 calls
-// store(i, j, e, value) for every element of the tile.
-template <int NW, typename Store>
-__device__ __forceinline__ void gate_reduce(const f32x4 (&acc)[2][2], Store store) {
-    __shared__ f32x4 part[NW][4][kWave];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) part[wave][2 * i + j][lane] = acc[i][j];
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            f32x4 t = part[0][2 * i + j][lane];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) {
-                const f32x4 u = part[w][2 * i + j][lane];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] += u[e];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) store(i, j, e, t[e]);
-        }
-}
-
 // Gh[m][q] = sum_{i<d} W_rnn[q][2r + i] h[m][i] for the M = B x gamma rows
-// of h (row m = b gamma + k).  Grid: one workgroup per 32 x 32 tile.
-__global__ __launch_bounds__(kGateHWaves * kWave) void k_gate_h(const uint16_t* __restrict__ W_rnn, const uint16_t* __restrict__ h,
-                                                int r, int d, int M, float* __restrict__ Gh) {
+// of h (row m = b gamma + k).  One workgroup per 64 (q) x 64 (m) tile, so
+// that each operand row is read by fewer workgroups (K = d is long); each of
+// its 8 waves accumulates the whole 4 x 4 grid of 16 x 16 tiles over every
+// 8th 32-wide chunk of K with two chunks in flight, and the 8 partial tiles
+// are added in a fixed order through LDS (waves w and w + 4 first).
+constexpr int kGhTile = 64;
+
+__global__ __launch_bounds__(kGateHWaves * kWave) void k_gate_h(const uint16_t* __restrict__ W_rnn,
+                                                                const uint16_t* __restrict__ h, int r, int d, int M,
+                                                                float* __restrict__ Gh) {
+    __shared__ f32x4 part[4][16][kWave];  // 64 KB
     const int Q = 3 * r, ldw = 2 * r + d;
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
     const int wave = threadIdx.x >> 6;
-    const int tq = Q / kGateTile;
-    const int q0 = (blockIdx.x % tq) * kGateTile, m0 = (blockIdx.x / tq) * kGateTile;
-    const uint16_t* wrow[2] = {W_rnn + static_cast<size_t>(q0 + n) * ldw + 2 * r,
-                               W_rnn + static_cast<size_t>(q0 + 16 + n) * ldw + 2 * r};
-    const bool mok[2] = {m0 + n < M, m0 + 16 + n < M};
-    const uint16_t* hrow[2] = {h + static_cast<size_t>(mok[0] ? m0 + n : 0) * d,
-                               h + static_cast<size_t>(mok[1] ? m0 + 16 + n : 0) * d};
-    f32x4 acc[2][2];
+    const int tq = (Q + kGhTile - 1) / kGhTile;
+    const int q0 = (blockIdx.x % tq) * kGhTile, m0 = (blockIdx.x / tq) * kGhTile;
+    // rows past Q or M read row 0 (their results are not stored)
+    const uint16_t* wrow[4];
+    const uint16_t* hrow[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i) {
+        const int q = q0 + 16 * i + n, m = m0 + 16 * i + n;
+        wrow[i] = W_rnn + static_cast<size_t>(q < Q ? q : 0) * ldw + 2 * r;
+        hrow[i] = h + static_cast<size_t>(m < M ? m : 0) * d;
+    }
+    f32x4 acc[4][4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // this wave's chunks: k0 = 32 (wave + 4 t); two chunks in flight
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     constexpr int kStride = 32 * kGateHWaves;
-    u32x4 wa[2][2], ob[2][2];
+    u32x4 wa[2][4], ob[2][4];
     auto fetch = [&](int slot, int k0) {
         const int kk = k0 + 8 * g;
         const bool kin = kk < d;  // d % 8 == 0: a lane's 8 values are all in or all out
 #pragma unroll
-        for (int i = 0; i < 2; ++i) wa[slot][i] = load8_bf16_or0(wrow[i] + kk, kin);
+        for (int i = 0; i < 4; ++i) {
+            wa[slot][i] = load8_bf16_or0(wrow[i] + kk, kin);
+            ob[slot][i] = load8_bf16_or0(hrow[i] + kk, kin);
+        }
+    };
+    auto mma = [&](int slot) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) ob[slot][j] = load8_bf16_or0(hrow[j] + kk, kin && mok[j]);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[slot][i]),
+                                                                    __builtin_bit_cast(bf16x8, ob[slot][j]), acc[i][j],
+                                                                    0, 0, 0);
     };
     const int kfirst = 32 * wave;
     fetch(0, kfirst);
     fetch(1, kfirst + kStride);
     for (int k0 = kfirst; k0 < d; k0 += 2 * kStride) {
-        const u32x4 ca[2] = {wa[0][0], wa[0][1]}, cb[2] = {ob[0][0], ob[0][1]};
+        mma(0);
         if (k0 + 2 * kStride < d) fetch(0, k0 + 2 * kStride);
-        gate_mfma2x2(ca, cb, acc);
         if (k0 + kStride >= d) break;
-        const u32x4 da[2] = {wa[1][0], wa[1][1]}, db[2] = {ob[1][0], ob[1][1]};
+        mma(1);
         if (k0 + 3 * kStride < d) fetch(1, k0 + 3 * kStride);
-        gate_mfma2x2(da, db, acc);
     }
-    gate_reduce<kGateHWaves>(acc, [&](int i, int j, int e, float v) {
+    // waves 4..7 hand their tiles to waves 0..3, which then publish the sums
+    if (wave >= 4)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) part[wave - 4][t][lane] = acc[t >> 2][t & 3];
+    __syncthreads();
+    if (wave < 4)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const f32x4 u = part[wave][t][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[t >> 2][t & 3][e] += u[e];
+        }
+    __syncthreads();
+    if (wave < 4)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) part[wave][t][lane] = acc[t >> 2][t & 3];
+    __syncthreads();
+    // wave w stores tiles w and w + 8: the four pair sums added in order
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int t = wave + 8 * tt, i = t >> 2, j = t & 3;
+        f32x4 v = part[0][t][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            const f32x4 u = part[w][t][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += u[e];
+        }
         const int m = m0 + 16 * j + n;
-        if (m < M) Gh[static_cast<size_t>(m) * Q + q0 + 16 * i + 4 * g + e] = v;
-    });
+        if (m < M)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int q = q0 + 16 * i + 4 * g + e;
+                if (q < Q) Gh[static_cast<size_t>(m) * Q + q] = v[e];
+            }
+    }
 }
 
 // One step of Eq 6 after the h columns, in one launch: G[b][q] = Gh[b gamma
@@ -817,10 +830,9 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
                            (reinterpret_cast<uintptr_t>(a.W_rnn) & 15) == 0 &&
                            (reinterpret_cast<uintptr_t>(a.h) & 15) == 0;
     float* gh = reinterpret_cast<float*>(ws + L.gh);
-    const int gate_tq = 3 * D.r / kGateTile;
     if (gate_mfma) {
         const int M = D.B * D.gamma;
-        const int tiles = gate_tq * ((M + kGateTile - 1) / kGateTile);
+        const int tiles = ((3 * D.r + kGhTile - 1) / kGhTile) * ((M + kGhTile - 1) / kGhTile);
         hipLaunchKernelGGL(k_gate_h, dim3(tiles), dim3(kGateHWaves * kWave), 0, a.stream,
                            reinterpret_cast<const uint16_t*>(Wr), reinterpret_cast<const uint16_t*>(h), D.r, D.d, M,
                            gh);
