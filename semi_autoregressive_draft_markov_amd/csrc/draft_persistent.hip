@@ -511,6 +511,11 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     };
 
     start_barrier_arrive(a, a.gamma * a.B * kDraftKeyCopies);
+    // Waves w and w + 4 share a SIMD: the second starts its tile loads a
+    // little later and products are issued at raised priority (see
+    // mul_any), so that one wave's matrix-core work tends to overlap the
+    // other's statistics (about 1 us per call at the Qwen3-4B shape).
+    if (wave >= 4) __builtin_amdgcn_s_sleep(8);
     W2Tile<KC> w2;
     if (has_reg) w2.load(a.W2, a.V, wv * 64, g, n);
     // while the tile loads are in flight
@@ -623,8 +628,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     };
     // bias of one unit on the matrix cores, for whichever column parts the
     // wave has (has_x implies has_reg: the fragment columns start past all
-    // tiles)
+    // tiles), issued at raised wave priority
     auto mul_any = [&](int nb, f32x4 (&acc)[4], f32x4& accx) {
+        __builtin_amdgcn_s_setprio(2);
         if (has_x)
             unit_mul<KC, true, true>(w2, xf, erow_of(nb), lane, wave, acc, accx);
         else if (has_reg)
@@ -697,6 +703,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         // waited for)
         if (nb + 1 < NB) ahead = fetch_u(kk, nb + 1);
         mul_any(nb, acc, accx);
+        __builtin_amdgcn_s_setprio(0);
         PStats st;
         if (AHEAD) {
             if (active) {
