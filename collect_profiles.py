@@ -18,6 +18,10 @@ kernel the per-dispatch averages of every counter, tagged with the hash of
 the kernel sources they were taken on -- and one markdown summary per
 workload with the commands, the kernel table and the derived figures.
 Raw rocprofv3 output stays under gpurun_out/prof_raw/.
+
+`--merge A.json B.json ... --out DIR` (no GPU) joins counters.json files of
+separate runs over different workloads, taken on the same kernel sources,
+into DIR/counters.json (for runs that do not fit one time limit together).
 """
 from __future__ import annotations
 
@@ -175,7 +179,12 @@ def main() -> int:
     ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "prof_raw"))
     ap.add_argument("--trace-steps", type=int, default=20)
     ap.add_argument("--pmc-steps", type=int, default=3)
+    ap.add_argument("--merge", nargs="+", help="counters.json files to join (no GPU work)")
     args = ap.parse_args()
+    # (the passes run with /tmp as working directory)
+    args.out, args.raw = os.path.abspath(args.out), os.path.abspath(args.raw)
+    if args.merge:
+        return merge(args.merge, args.out)
     os.makedirs(args.out, exist_ok=True)
     os.makedirs(args.raw, exist_ok=True)
     result = {"kernel_source_hash": bench.kernel_source_hash(), "workloads": {}, "commands": {}}
@@ -230,6 +239,28 @@ def main() -> int:
     with open(os.path.join(args.out, "counters.json"), "w") as f:
         json.dump(result, f, indent=1, sort_keys=True)
     print("wrote %s" % os.path.join(args.out, "counters.json"), flush=True)
+    return 0
+
+
+def merge(files, out_dir) -> int:
+    parts = [json.load(open(f)) for f in files]
+    hashes = {p["kernel_source_hash"] for p in parts}
+    if len(hashes) != 1:
+        raise SystemExit("counter files taken on different kernel sources: %s" % sorted(hashes))
+    result = {"kernel_source_hash": hashes.pop(), "workloads": {}, "commands": {},
+              "copy_calibration": parts[0]["copy_calibration"]}
+    for p in parts:
+        for w, v in p["workloads"].items():
+            if w in result["workloads"]:
+                raise SystemExit("workload %s appears in more than one file" % w)
+            result["workloads"][w] = v
+        for k, v in p["commands"].items():
+            if k != "copy_calibration" or k not in result["commands"]:
+                result["commands"][k] = v
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "counters.json"), "w") as f:
+        json.dump(result, f, indent=1, sort_keys=True)
+    print("wrote %s (%s)" % (os.path.join(out_dir, "counters.json"), ", ".join(sorted(result["workloads"]))))
     return 0
 
 
