@@ -16,6 +16,7 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -93,61 +94,128 @@ DraftLayout draft_layout(const dspark_dims& d) {
 
 // ------------------------------------------------------------------ init
 
-// Workgroup (b, k): the h part of position k's confidence logit,
-// w[0:d] . h_{b,k}, which does not depend on the drafted tokens and so leaves
-// the sequential loop.  Workgroups (b, 0) also gather e = W1[anchor_b]
-// (Eq 5 at the first position) and emit c_1 and S_1 (Eq 7).  Rows b in
-// [B, Bpad) only clear the padding rows of the MFMA operand.
+// Arguments of the per-block set-up before the sequential loop.
 template <typename T>
-__global__ __launch_bounds__(256) void k_draft_init(
-    const int32_t* __restrict__ anchor, const T* __restrict__ W1, const T* __restrict__ w_conf,
-    const T* __restrict__ h, int V, int r, int d, int gamma, int B, int Bpad, int head,
-    int32_t* __restrict__ dead, float* __restrict__ emb, float* __restrict__ coef,
-    uint16_t* __restrict__ ebf, float* __restrict__ state, float* __restrict__ hdot,
-    float* __restrict__ conf, float* __restrict__ survival) {
-    __shared__ float red[16];
-    const int b = blockIdx.x, k = blockIdx.y;
-    const size_t row = static_cast<size_t>(b) * r;
-    if (b >= B) {
-        if (k == 0) {
-            for (int j = threadIdx.x; j < r; j += blockDim.x) {
-                emb[row + j] = 0.0f;
-                coef[row + j] = 0.0f;
-                state[row + j] = 0.0f;
-                ebf[row + j] = 0;
-                ebf[static_cast<size_t>(Bpad) * r + row + j] = 0;
-            }
+struct InitArgs {
+    const int32_t* anchor;
+    const T* W1;
+    const T* w_conf;
+    const T* h;
+    int V, r, d, gamma, B, Bpad, head;
+    int32_t* dead;
+    float* emb;
+    float* coef;
+    uint16_t* ebf;
+    float* state;
+    float* hdot;
+    float* conf;
+    float* survival;
+};
+
+constexpr int kInitPos = 8;  // positions whose h rows are read at the same time
+
+// Block b, by one workgroup: the h part of every position's confidence
+// logit, w[0:d] . h_{b,k}, which does not depend on the drafted tokens and
+// so leaves the sequential loop (kInitPos positions at a time, partial sums
+// added over the waves in wave order); then e = W1[anchor_b] (Eq 5 at the
+// first position), c_1 and S_1 (Eq 7).  Rows b in [B, Bpad) only clear the
+// padding rows of the MFMA operand.  red: 16 x kInitPos floats of LDS.
+template <typename T>
+__device__ void draft_init_block(const InitArgs<T>& a, int b, float* red) {
+    const size_t row = static_cast<size_t>(b) * a.r;
+    if (b >= a.B) {
+        for (int j = threadIdx.x; j < a.r; j += blockDim.x) {
+            a.emb[row + j] = 0.0f;
+            a.coef[row + j] = 0.0f;
+            a.state[row + j] = 0.0f;
+            a.ebf[row + j] = 0;
+            a.ebf[static_cast<size_t>(a.Bpad) * a.r + row + j] = 0;
         }
         return;
     }
-    const int64_t hrow = (static_cast<int64_t>(b) * gamma + k) * d;
-    float hp = 0.0f;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) hp += load_f(w_conf, i) * load_f(h, hrow + i);
-    const float hk = block_sum(hp, red);
-    if (threadIdx.x == 0) hdot[static_cast<size_t>(b) * gamma + k] = hk;
-    if (k != 0) return;
-
-    const int prev = anchor[b];
-    const bool bad = prev < 0 || prev >= V;
-    if (threadIdx.x == 0) dead[b] = bad ? 1 : 0;
-    float part = 0.0f;
-    for (int j = threadIdx.x; j < r; j += blockDim.x) {
-        const float ej = bad ? 0.0f : load_f(W1, static_cast<int64_t>(prev) * r + j);
-        emb[row + j] = ej;
-        state[row + j] = 0.0f;  // Eq 6: s_0 = 0
-        if (head == DSPARK_HEAD_MARKOV) {
-            coef[row + j] = ej;
-            ebf[row + j] = static_cast<uint16_t>(f32_to_bf16(ej));  // exact: W1 is bf16 here
-            ebf[static_cast<size_t>(Bpad) * r + row + j] = 0;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int nw = blockDim.x / kWave;
+    float hk0 = 0.0f;  // thread 0: the h part of position 0
+    for (int k0 = 0; k0 < a.gamma; k0 += kInitPos) {
+        float hp[kInitPos];
+#pragma unroll
+        for (int j = 0; j < kInitPos; ++j) hp[j] = 0.0f;
+        const int64_t hrow = (static_cast<int64_t>(b) * a.gamma + k0) * a.d;
+        bool vec = false;
+        if constexpr (std::is_same<T, uint16_t>::value)
+            vec = a.d % 8 == 0 && (reinterpret_cast<uintptr_t>(a.h) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(a.w_conf) & 15) == 0;
+        if (vec) {
+            // 8 bf16 values per 16-byte load, the rows' loads issued together
+            for (int c = threadIdx.x; c < a.d / 8; c += blockDim.x) {
+                const u32x4 wv = *reinterpret_cast<const u32x4*>(a.w_conf + 8 * c);
+                u32x4 hv[kInitPos];
+#pragma unroll
+                for (int j = 0; j < kInitPos; ++j)
+                    if (k0 + j < a.gamma)
+                        hv[j] = *reinterpret_cast<const u32x4*>(a.h + hrow + static_cast<int64_t>(j) * a.d + 8 * c);
+#pragma unroll
+                for (int j = 0; j < kInitPos; ++j)
+                    if (k0 + j < a.gamma)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            hp[j] = fmaf(lo_bf16(wv[q]), lo_bf16(hv[j][q]), hp[j]);
+                            hp[j] = fmaf(hi_bf16(wv[q]), hi_bf16(hv[j][q]), hp[j]);
+                        }
+            }
+        } else {
+            for (int i = threadIdx.x; i < a.d; i += blockDim.x) {
+                const float wi = load_f(a.w_conf, i);
+#pragma unroll
+                for (int j = 0; j < kInitPos; ++j)
+                    if (k0 + j < a.gamma) hp[j] = fmaf(wi, load_f(a.h, hrow + static_cast<int64_t>(j) * a.d + i), hp[j]);
+            }
         }
-        part += load_f(w_conf, d + j) * ej;
+#pragma unroll
+        for (int j = 0; j < kInitPos; ++j)
+            for (int o = 32; o > 0; o >>= 1) hp[j] += __shfl_xor(hp[j], o);
+        __syncthreads();  // red is free
+        if (lane == 0)
+#pragma unroll
+            for (int j = 0; j < kInitPos; ++j) red[wave * kInitPos + j] = hp[j];
+        __syncthreads();
+        if (threadIdx.x < kInitPos && k0 + static_cast<int>(threadIdx.x) < a.gamma) {
+            float t = 0.0f;
+            for (int w = 0; w < nw; ++w) t += red[w * kInitPos + threadIdx.x];
+            a.hdot[static_cast<size_t>(b) * a.gamma + k0 + threadIdx.x] = t;
+            if (k0 == 0) hk0 = t;
+        }
+    }
+
+    const int prev = a.anchor[b];
+    const bool bad = prev < 0 || prev >= a.V;
+    if (threadIdx.x == 0) a.dead[b] = bad ? 1 : 0;
+    float part = 0.0f;
+    for (int j = threadIdx.x; j < a.r; j += blockDim.x) {
+        const float ej = bad ? 0.0f : load_f(a.W1, static_cast<int64_t>(prev) * a.r + j);
+        a.emb[row + j] = ej;
+        a.state[row + j] = 0.0f;  // Eq 6: s_0 = 0
+        if (a.head == DSPARK_HEAD_MARKOV) {
+            a.coef[row + j] = ej;
+            a.ebf[row + j] = static_cast<uint16_t>(f32_to_bf16(ej));  // exact: W1 is bf16 here
+            a.ebf[static_cast<size_t>(a.Bpad) * a.r + row + j] = 0;
+        }
+        part += load_f(a.w_conf, a.d + j) * ej;
     }
     const float ae = block_sum(part, red);
     if (threadIdx.x == 0) {
-        const float c = bad ? NAN : sigmoidf_(hk + ae);
-        conf[static_cast<size_t>(b) * gamma] = c;
-        survival[static_cast<size_t>(b) * gamma] = c;
+        const float c = bad ? NAN : sigmoidf_(hk0 + ae);
+        a.conf[static_cast<size_t>(b) * a.gamma] = c;
+        a.survival[static_cast<size_t>(b) * a.gamma] = c;
     }
+}
+
+constexpr int kInitThreads = 512;
+
+template <typename T>
+__global__ __launch_bounds__(kInitThreads) void k_draft_init(InitArgs<T> a) {
+    __shared__ float red[16 * kInitPos];
+    draft_init_block(a, blockIdx.x, red);
 }
 
 // ------------------------------------------------------------ RNN step
@@ -193,7 +261,7 @@ __global__ __launch_bounds__(256) void k_rnn_gates(
 // Matrix-core form of the same projection (bf16 weights, r % 32 == 0,
 // d % 8 == 0).  The columns of W_rnn that multiply h_k do not depend on the
 // drafted tokens, so their part of G is one GEMM over all B x gamma
-// positions before the loop (k_gate_h); each step then only adds the s and
+// positions before the loop (gate_h_tile); each step then only adds the s and
 // e columns (k_gate_update).  D[q][m] = sum_j W_rnn[q][col(j)] A[m][j] is
 // built from v_mfma_f32_16x16x32_bf16 tiles with A = 16 rows of W_rnn and
 // B = 16 operand rows: lane (g, n) supplies W_rnn row q0 + n and operand row
@@ -231,15 +299,14 @@ __device__ __forceinline__ float unpack8_at(const u32x4& v, int q) {
 // are added in a fixed order through LDS (waves w and w + 4 first).
 constexpr int kGhTile = 64;
 
-__global__ __launch_bounds__(kGateHWaves * kWave) void k_gate_h(const uint16_t* __restrict__ W_rnn,
-                                                                const uint16_t* __restrict__ h, int r, int d, int M,
-                                                                float* __restrict__ Gh) {
-    __shared__ f32x4 part[4][16][kWave];  // 64 KB
+__device__ __forceinline__ void gate_h_tile(const uint16_t* __restrict__ W_rnn, const uint16_t* __restrict__ h,
+                                            int r, int d, int M, float* __restrict__ Gh, int tile,
+                                            f32x4 (*part)[16][kWave] /* [4][16][kWave] */) {
     const int Q = 3 * r, ldw = 2 * r + d;
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
     const int wave = threadIdx.x >> 6;
     const int tq = (Q + kGhTile - 1) / kGhTile;
-    const int q0 = (blockIdx.x % tq) * kGhTile, m0 = (blockIdx.x / tq) * kGhTile;
+    const int q0 = (tile % tq) * kGhTile, m0 = (tile / tq) * kGhTile;
     // rows past Q or M read row 0 (their results are not stored)
     const uint16_t* wrow[4];
     const uint16_t* hrow[4];
@@ -322,13 +389,28 @@ __global__ __launch_bounds__(kGateHWaves * kWave) void k_gate_h(const uint16_t* 
     }
 }
 
+// The RNN head's set-up in one launch: workgroups [0, tiles) compute the
+// h-projection tiles, the rest the per-block set-up (block = index -
+// tiles).  The two are independent and the tiles leave compute units idle,
+// which the set-up then uses.
+__global__ __launch_bounds__(kGateHWaves * kWave) void k_rnn_prologue(const uint16_t* __restrict__ W_rnn,
+                                                                      int M, float* __restrict__ Gh, int tiles,
+                                                                      InitArgs<uint16_t> ia) {
+    __shared__ f32x4 part[4][16][kWave];
+    __shared__ float red[16 * kInitPos];
+    if (static_cast<int>(blockIdx.x) < tiles)
+        gate_h_tile(W_rnn, ia.h, ia.r, ia.d, M, Gh, blockIdx.x, part);
+    else
+        draft_init_block(ia, static_cast<int>(blockIdx.x) - tiles, red);
+}
+
 // One step of Eq 6 after the h columns, in one launch: G[b][q] = Gh[b gamma
 // + k][q] + sum_j W_rnn[q][j] s[b][j] + sum_j W_rnn[q][r + j] e[b][j], then
 // the gated state update and the bias coefficients o = tanh(G_o), with the
 // formulas of k_rnn_update.  A workgroup owns state columns j0 .. j0 + 15
 // of blocks m0 .. m0 + 31 and computes the three gate rows that update them
 // (q = j, r + j, 2r + j) as 16 x 16 matrix-core tiles (the fp32 state as
-// three exact bf16 pieces, as in k_gate_h's layout); its 8 waves take every
+// three exact bf16 pieces, as in gate_h_tile's layout); its 8 waves take every
 // 8th 32-wide chunk of K, the partial tiles are added in wave order through
 // LDS, and each thread updates one (block, column).  The state is read from
 // s_in and written to s_out (two buffers, alternating by step): the other
@@ -821,22 +903,26 @@ static hipError_t launch_draft_t(const DraftArgs& a) {
     const T* wc = static_cast<const T*>(a.w_conf);
     const T* Wr = static_cast<const T*>(a.W_rnn);
 
-    hipLaunchKernelGGL((k_draft_init<T>), dim3(L.Bpad, D.gamma), dim3(256), 0, a.stream, a.anchor, W1, wc, h,
-                       D.V, D.r, D.d, D.gamma, D.B, L.Bpad, D.head, dead, emb, coef, ebf, state,
-                       reinterpret_cast<float*>(ws + L.hdot), a.conf, a.survival);
+    const InitArgs<T> ia{a.anchor, W1,     wc,   h,     D.V,   D.r,   D.d,
+                         D.gamma,  D.B,    L.Bpad, D.head, dead, emb,  coef,
+                         ebf,      state,  reinterpret_cast<float*>(ws + L.hdot), a.conf, a.survival};
     // RNN on matrix cores: the h columns of the joint projection for every
-    // position at once, before the loop
+    // position at once, before the loop, in the same launch as the set-up
     const bool gate_mfma = D.head == DSPARK_HEAD_RNN && rnn_gate_mfma_ok(D) &&
                            (reinterpret_cast<uintptr_t>(a.W_rnn) & 15) == 0 &&
                            (reinterpret_cast<uintptr_t>(a.h) & 15) == 0;
     float* gh = reinterpret_cast<float*>(ws + L.gh);
-    if (gate_mfma) {
-        const int M = D.B * D.gamma;
-        const int tiles = ((3 * D.r + kGhTile - 1) / kGhTile) * ((M + kGhTile - 1) / kGhTile);
-        hipLaunchKernelGGL(k_gate_h, dim3(tiles), dim3(kGateHWaves * kWave), 0, a.stream,
-                           reinterpret_cast<const uint16_t*>(Wr), reinterpret_cast<const uint16_t*>(h), D.r, D.d, M,
-                           gh);
+    bool set_up = false;
+    if constexpr (std::is_same<T, uint16_t>::value) {  // gate_mfma implies bf16
+        if (gate_mfma) {
+            const int M = D.B * D.gamma;
+            const int tiles = ((3 * D.r + kGhTile - 1) / kGhTile) * ((M + kGhTile - 1) / kGhTile);
+            hipLaunchKernelGGL(k_rnn_prologue, dim3(tiles + L.Bpad), dim3(kGateHWaves * kWave), 0, a.stream,
+                               reinterpret_cast<const uint16_t*>(Wr), M, gh, tiles, ia);
+            set_up = true;
+        }
     }
+    if (!set_up) hipLaunchKernelGGL((k_draft_init<T>), dim3(L.Bpad), dim3(kInitThreads), 0, a.stream, ia);
     for (int k = 0; k < D.gamma; ++k) {
         if (D.head == DSPARK_HEAD_RNN) {
             if (gate_mfma) {
