@@ -108,17 +108,20 @@ __device__ __forceinline__ void start_barrier_arrive(const PersistArgs& a, int n
 __device__ __forceinline__ void start_barrier_wait(const PersistArgs& a) {
     if (threadIdx.x < kWave) {
         uint32_t spins = 0;
+        // (read here: kept live from the kernel's start it would take registers)
+        uint64_t epoch = a.epoch;
+        asm volatile("" : "+s"(epoch));
         if (a.fail_waits && threadIdx.x == 0)
-            __hip_atomic_store(a.flags + a.nWG, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.flags + a.nWG, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         while (!a.fail_waits) {
             bool late = false;
             for (int i = threadIdx.x; i < a.nWG; i += kWave)
-                late |= __hip_atomic_load(a.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch;
+                late |= __hip_atomic_load(a.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch;
             if (__ballot(late) == 0) break;
             __builtin_amdgcn_s_sleep(2);
             if (++spins > a.spin_limit) {
                 if (threadIdx.x == 0)
-                    __hip_atomic_store(a.flags + a.nWG, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(a.flags + a.nWG, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
         }
@@ -163,7 +166,10 @@ __device__ __forceinline__ void barrier_arrive(uint32_t* bar, uint32_t wg) {
 __device__ __forceinline__ void barrier_finish(uint32_t* bar, uint32_t step, uint32_t nwg, uint32_t spin_limit,
                                                int fail_waits) {
     if (threadIdx.x < kWave) {
-        const uint32_t l = threadIdx.x;
+        // (opaque: the per-lane group size would otherwise be kept in a
+        // register across the whole step loop)
+        uint32_t l = threadIdx.x;
+        asm volatile("" : "+v"(l));
         const uint32_t ngroups = nwg < kBarGroups ? nwg : kBarGroups;
         // group l holds the workgroups wg = l, l + 8, ... < nwg
         const uint32_t target = l < ngroups ? step * ((nwg - l + kBarGroups - 1) / kBarGroups) : 0u;
@@ -568,28 +574,30 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
         }
         __syncthreads();
     };
-    // GROUPED: rows of block group nb, loaded into registers ...
-    u32x4 staged[kStage];
-    auto load_group = [&](int nb) {
+    // GROUPED: rows of block group nb, loaded into registers two units
+    // before their unit (the gathered rows come from anywhere in W1, and a
+    // greedy unit is shorter than that load) ...
+    u32x4 staged0[kStage], staged1[kStage];  // groups of even / odd index
+    auto load_group = [&](int nb, u32x4 (&dst)[kStage]) {
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
             const int t = threadIdx.x + kPThreads * i;
             if (t < kGroupChunks) {
                 const int row = t / (r / 8), col = t % (r / 8);
-                staged[i] = *reinterpret_cast<const u32x4*>(a.W1 + static_cast<size_t>(prev[nb * 16 + row]) * r +
-                                                             col * 8);
+                dst[i] = *reinterpret_cast<const u32x4*>(a.W1 + static_cast<size_t>(prev[nb * 16 + row]) * r +
+                                                         col * 8);
             }
         }
     };
     // ... and stored to buffer nb % 2 once the unit before it is done
-    auto store_group = [&](int nb) {
+    auto store_group = [&](int nb, const u32x4 (&src)[kStage]) {
         uint16_t* buf = Es + (nb & 1) * 16 * ldE;
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
             const int t = threadIdx.x + kPThreads * i;
             if (t < kGroupChunks) {
                 const int row = t / (r / 8), col = t % (r / 8);
-                *reinterpret_cast<u32x4*>(&buf[row * ldE + col * 8]) = staged[i];
+                *reinterpret_cast<u32x4*>(&buf[row * ldE + col * 8]) = src[i];
             }
         }
     };
@@ -792,13 +800,26 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     for (int k = 0; k < a.gamma; ++k) {
         // every wave runs all NB units (GROUPED stages rows between
         // them); waves without columns skip the arithmetic
-        for (int nb = 0; nb < NB; ++nb) {
-            if (GROUPED && nb + 1 < NB) load_group(nb + 1);
-            run_unit(k, nb);
-            if (GROUPED && nb + 1 < NB) {
-                store_group(nb + 1);
-                __syncthreads();
+        if (GROUPED) {
+            // unit nb loads group nb + 2 into the registers group nb came
+            // through (its rows are in LDS by then) and stores group nb + 1;
+            // the loop runs two units per trip so that both register sets
+            // are named at compile time
+            if (NB > 1) load_group(1, staged1);
+            auto grouped_unit = [&](int nb, u32x4 (&nxt2)[kStage], const u32x4 (&nxt1)[kStage]) {
+                if (nb + 2 < NB) load_group(nb + 2, nxt2);
+                run_unit(k, nb);
+                if (nb + 1 < NB) {
+                    store_group(nb + 1, nxt1);
+                    __syncthreads();
+                }
+            };
+            for (int nb = 0; nb < NB; nb += 2) {
+                grouped_unit(nb, staged0, staged1);
+                if (nb + 1 < NB) grouped_unit(nb + 1, staged1, staged0);
             }
+        } else {
+            for (int nb = 0; nb < NB; ++nb) run_unit(k, nb);
         }
         // the keys and barrier words are cleared everywhere before step 0
         // publishes or arrives (step 0's units do not touch them, so the
