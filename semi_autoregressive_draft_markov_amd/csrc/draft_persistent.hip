@@ -618,6 +618,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     };
     stage_rows();
     UAhead ahead = fetch_u(0, 0);
+    // GROUPED: U is loaded two units ahead, units of even index through
+    // `ahead`, of odd index through `ahead1` (NB >= 3 there)
+    UAhead ahead1 = GROUPED ? fetch_u(0, 1) : ahead;
 
     // accumulators start from U (bf16 -> f32 is exact)
     auto acc_from = [&](const UAhead& u, f32x4 (&acc)[4], f32x4& accx) {
@@ -703,13 +706,17 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     // One unit: step kk, block group nb (16 blocks): accumulators from U,
     // bias on the matrix cores, lane statistics, merged into this wave's
     // slots.  The U of the next unit is fetched here.
-    auto run_unit = [&](int kk, int nb) {
+    auto run_unit = [&](int kk, int nb, UAhead& u) {
         f32x4 acc[4], accx;
-        acc_from(ahead, acc, accx);
-        // (the next step's first unit is fetched after the barrier arrival:
-        // a load in flight at the arrival's completion wait would be
-        // waited for)
-        if (nb + 1 < NB) ahead = fetch_u(kk, nb + 1);
+        acc_from(u, acc, accx);
+        // (the next step's first units are fetched after the barrier
+        // arrival: a load in flight at the arrival's completion wait would
+        // be waited for)
+        if (GROUPED) {
+            if (nb + 2 < NB) u = fetch_u(kk, nb + 2);
+        } else if (nb + 1 < NB) {
+            u = fetch_u(kk, nb + 1);
+        }
         mul_any(nb, acc, accx);
         __builtin_amdgcn_s_setprio(0);
         PStats st;
@@ -806,20 +813,20 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
             // the loop runs two units per trip so that both register sets
             // are named at compile time
             if (NB > 1) load_group(1, staged1);
-            auto grouped_unit = [&](int nb, u32x4 (&nxt2)[kStage], const u32x4 (&nxt1)[kStage]) {
+            auto grouped_unit = [&](int nb, u32x4 (&nxt2)[kStage], const u32x4 (&nxt1)[kStage], UAhead& u) {
                 if (nb + 2 < NB) load_group(nb + 2, nxt2);
-                run_unit(k, nb);
+                run_unit(k, nb, u);
                 if (nb + 1 < NB) {
                     store_group(nb + 1, nxt1);
                     __syncthreads();
                 }
             };
             for (int nb = 0; nb < NB; nb += 2) {
-                grouped_unit(nb, staged0, staged1);
-                if (nb + 1 < NB) grouped_unit(nb + 1, staged1, staged0);
+                grouped_unit(nb, staged0, staged1, ahead);
+                if (nb + 1 < NB) grouped_unit(nb + 1, staged1, staged0, ahead1);
             }
         } else {
-            for (int nb = 0; nb < NB; ++nb) run_unit(k, nb);
+            for (int nb = 0; nb < NB; ++nb) run_unit(k, nb, ahead);
         }
         // the keys and barrier words are cleared everywhere before step 0
         // publishes or arrives (step 0's units do not touch them, so the
@@ -855,6 +862,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
             __syncthreads();
             barrier_arrive(a.bar, static_cast<uint32_t>(wg));
             ahead = fetch_u(k + 1, 0);
+            if (GROUPED) ahead1 = fetch_u(k + 1, 1);
             barrier_finish(a.bar, static_cast<uint32_t>(k + 1), static_cast<uint32_t>(nWG), a.spin_limit, a.fail_waits);
             read_keys(k, 0, a.B);
             stage_rows();
