@@ -337,23 +337,24 @@ __device__ __forceinline__ PStats pstats_merge_xor(const PStats& a) {
 // g with g[j] = log2(-log2 u), the Gumbel-max value up to a positive factor
 // and a constant (see log2_of_neg_log2_uniform); greedy: y = z2.  The key
 // takes the maximum y and the lowest column attaining it.
+// The softmax reference is the largest perturbed value ŷ, not the largest
+// scaled logit: z2 - ŷ <= g <= log2(24) for every column (u >= 2^-24), so no
+// term of the sum overflows, and the winner's term is 2^g >= 2^-24, so the
+// sum keeps its mass; greedy (g = 0) it is the plain maximum.
 template <bool SAMPLING>
 __device__ __forceinline__ PStats unit_stats(const float (&z)[20], const float (&g)[20], int v0, int vx,
                                              float scale) {
     float y[20];
 #pragma unroll
     for (int j = 0; j < 20; ++j) y[j] = SAMPLING ? fmaf(z[j], scale, -g[j]) : z[j] * scale;
-    float ybest = y[0], zmax = z[0];
+    float ybest = y[0];
 #pragma unroll
-    for (int j = 1; j < 20; ++j) {
-        ybest = fmaxf(ybest, y[j]);
-        zmax = fmaxf(zmax, z[j]);
-    }
+    for (int j = 1; j < 20; ++j) ybest = fmaxf(ybest, y[j]);
     int idx = 19;
 #pragma unroll
     for (int j = 18; j >= 0; --j) idx = (y[j] == ybest) ? j : idx;
-    if (zmax == -INFINITY) return pstats_empty();  // no column of this lane exists
-    const float m = zmax * scale;
+    if (ybest == -INFINITY) return pstats_empty();  // no column of this lane exists
+    const float m = ybest;
     float s = 0.0f;
 #pragma unroll
     for (int j = 0; j < 20; ++j) s += __builtin_amdgcn_exp2f(fmaf(z[j], scale, -m));
