@@ -704,9 +704,10 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persistent(PersistArgs a
     // fragment exists
     const bool full = has_x && c0 + 16 <= a.V;
 
-    // One unit: step kk, block group nb (16 blocks): accumulators from U,
-    // bias on the matrix cores, lane statistics, merged into this wave's
-    // slots.  The U of the next unit is fetched here.
+    // One unit: step kk, block group nb (16 blocks): accumulators from U
+    // (held in u), bias on the matrix cores, lane statistics, merged into
+    // this wave's slots.  u then receives the U of a later unit of the step:
+    // the next one, or (GROUPED) the one after it.
     auto run_unit = [&](int kk, int nb, UAhead& u) {
         f32x4 acc[4], accx;
         acc_from(u, acc, accx);
