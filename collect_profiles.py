@@ -13,11 +13,12 @@ and two counter passes (FETCH_SIZE, WRITE_SIZE) of a plain 1 GiB device
 copy (`bench.py --copy-calibration`), which scale the byte counters to
 bytes.  Every pass runs under its own `timeout -s KILL`.
 
-Output (default gpurun_out/profiles/): counters.json -- per workload and
+Output (default prof_out/profiles/): counters.json -- per workload and
 kernel the per-dispatch averages of every counter, tagged with the hash of
 the kernel sources they were taken on -- and one markdown summary per
 workload with the commands, the kernel table and the derived figures.
-Raw rocprofv3 output stays under gpurun_out/prof_raw/.
+Raw rocprofv3 output stays under prof_out/raw/ (neither is kept in the
+repository; the summaries are copied into profiles/).
 
 `--merge A.json B.json ... --out DIR` (no GPU) joins counters.json files of
 separate runs over different workloads, taken on the same kernel sources,
@@ -175,8 +176,8 @@ def derived(c: dict) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--workloads", default=",".join(WORKLOADS))
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profiles"))
-    ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "prof_raw"))
+    ap.add_argument("--out", default=os.path.join(ROOT, "prof_out", "profiles"))
+    ap.add_argument("--raw", default=os.path.join(ROOT, "prof_out", "raw"))
     ap.add_argument("--trace-steps", type=int, default=20)
     ap.add_argument("--pmc-steps", type=int, default=3)
     ap.add_argument("--merge", nargs="+", help="counters.json files to join (no GPU work)")
