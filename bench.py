@@ -119,7 +119,7 @@ def roofline(workload, kernel, kernel_s, alg_bytes, alg_flops, match=None):
             if k in c:
                 line[k] = c[k]
     else:
-        line["counters"] = "none for this build (profiles/counters.json is from other sources)"
+        line["counters"] = "none for these kernel sources (profiles/counters.json was taken on other sources)"
     return line
 
 
@@ -555,8 +555,8 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build runs the drafting path on a single GPU "
-              "(blocks are independent; the multi-GPU layout is a design note); run it with --gpus 1",
+        print("bench.py measures one GPU only: the library runs the drafting path on a single GPU "
+              "(blocks are independent; sharding them over GPUs is not implemented); run it with --gpus 1",
               file=sys.stderr)
         return 2
     if args.workload == "qwen3-8b-loss":
